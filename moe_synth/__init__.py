@@ -1,0 +1,210 @@
+"""Seeded synthetic inputs for the routed MoE layer.
+
+This module only draws inputs.  It holds none of the layer's arithmetic: the
+router, the activation quantisation, the permutation, the FFN and the combine
+live in the GPU library and, independently, in the CPU oracle.  Both receive
+the same tensors from here.
+
+Workloads (shapes from the pages' per-device shares, see the design notes):
+
+=====  ======  =====  =====  ====  ===  ======  ================================
+name   T       H      I      E     k    format  extras
+=====  ======  =====  =====  ====  ===  ======  ================================
+tiny   64      256    128    8     2    fp8     --
+prefill 2048   8192   2048   8     2    fp8     shared expert 8192->2048->8192
+decode 64      8192   2048   8     2    fp8     --
+latent 512     3584   3072   896   16   mxfp4   RMSNorm (gamma = 1, eps = 1e-6)
+skewed 16384   8192   2048   256   8    fp8     Zipf-biased logits, hottest ~5x
+=====  ======  =====  =====  ====  ===  ======  ================================
+
+Recipe: activations ~ N(0,1) rounded to bf16; router logits ~ N(0,1) in fp32
+(plus, for ``skewed``, a per-expert bias -alpha*1.1*ln(rank) over a seeded
+rank permutation, alpha bisected so the hottest expert gets 4.9-5.1x the mean
+row count); weights ~ 0.02*N(0,1) in fp32, quantised per output row to fp8
+e4m3 with scale amax/448 (torch's float8_e4m3fn cast) or per 32-element block
+to MXFP4 (e2m1 codes, e8m0 scale 2^(floor(log2 amax) - 2)).
+
+Every tensor comes from its own torch.Generator seeded by
+(2026, workload, tensor, expert), so any expert can be regenerated alone.
+torch's CPU and GPU generators differ; a run draws on one device and hands
+host copies of the same tensors to the oracle.
+"""
+
+import torch
+
+CONFIGS = {
+    "tiny":    dict(cfg=1, T=64,    H=256,  I=128,  E=8,   k=2,  fmt="fp8",   shared=False, norm=False, skew=False),
+    "prefill": dict(cfg=2, T=2048,  H=8192, I=2048, E=8,   k=2,  fmt="fp8",   shared=True,  norm=False, skew=False),
+    "decode":  dict(cfg=3, T=64,    H=8192, I=2048, E=8,   k=2,  fmt="fp8",   shared=False, norm=False, skew=False),
+    "latent":  dict(cfg=4, T=512,   H=3584, I=3072, E=896, k=16, fmt="mxfp4", shared=False, norm=True,  skew=False),
+    "skewed":  dict(cfg=5, T=16384, H=8192, I=2048, E=256, k=8,  fmt="fp8",   shared=False, norm=False, skew=True),
+}
+
+T_LOGITS, T_X, T_W1, T_W3, T_W2, T_SW1, T_SW3, T_SW2, T_RANK = range(9)
+NORM_EPS = 1e-6
+WEIGHT_STD = 0.02
+
+
+def seed_of(cfg, tensor, expert=0, base=2026):
+    return ((base * 100 + cfg) * 100 + tensor) * 100000 + expert
+
+
+def _gen(device, seed):
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return g
+
+
+def randn(shape, device, seed, std=1.0):
+    t = torch.randn(shape, generator=_gen(device, seed), device=device, dtype=torch.float32)
+    return t * std if std != 1.0 else t
+
+
+# ----------------------------------------------------------------------------
+# weight quantisers (input preparation only)
+# ----------------------------------------------------------------------------
+
+
+def fp8_rows(w):
+    """float32 [N][K] -> (e4m3 codes uint8 [N][K], per-row scale float32 [N])."""
+    amax = w.abs().amax(dim=1)
+    s = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+    q = (w / s[:, None]).clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
+    return q.contiguous(), s.contiguous()
+
+
+_E2M1_MIDS_DOWN = (0.25, 1.25, 2.5, 5.0)   # a tie here goes to the lower (even) code
+_E2M1_MIDS_UP = (0.75, 1.75, 3.5)          # a tie here goes to the upper (even) code
+
+
+def mxfp4_rows(w, group=32):
+    """float32 [N][K] -> (packed uint8 [N][K/2], e8m0 uint8 [N][K/group])."""
+    N, K = w.shape
+    wb = w.reshape(N, K // group, group)
+    amax = wb.abs().amax(dim=2)
+    e = torch.floor(torch.log2(torch.where(amax > 0, amax, torch.ones_like(amax)))) - 2
+    e = torch.where(amax > 0, e, torch.full_like(e, -127.0)).clamp(-127, 127)
+    v = wb / torch.pow(2.0, e)[..., None]
+    mag = v.abs().clamp(max=6.0)
+    code = torch.zeros_like(mag, dtype=torch.uint8)
+    for m in _E2M1_MIDS_DOWN:
+        code += (mag > m).to(torch.uint8)
+    for m in _E2M1_MIDS_UP:
+        code += (mag >= m).to(torch.uint8)
+    code = code | ((v < 0) & (code > 0)).to(torch.uint8) << 3
+    code = code.reshape(N, K)
+    packed = (code[:, 0::2] | (code[:, 1::2] << 4)).contiguous()
+    scale = (e + 127).to(torch.uint8).contiguous()
+    return packed, scale
+
+
+def expert_weights(cfg, device, fmt, n_experts, hidden, inter, tensors=(T_W1, T_W3, T_W2)):
+    """Stacked weights {w1,w3,w2,s1,s3,s2} of n_experts experts on ``device``."""
+    out = {}
+    shapes = {tensors[0]: (inter, hidden), tensors[1]: (inter, hidden), tensors[2]: (hidden, inter)}
+    for name, tid in zip(("1", "3", "2"), tensors):
+        codes, scales = [], []
+        for e in range(n_experts):
+            w = randn(shapes[tid], device, seed_of(cfg, tid, e), WEIGHT_STD)
+            q, s = fp8_rows(w) if fmt == "fp8" else mxfp4_rows(w)
+            codes.append(q)
+            scales.append(s)
+        out["w" + name] = torch.stack(codes).contiguous()
+        out["s" + name] = torch.stack(scales).contiguous()
+    return out
+
+
+# ----------------------------------------------------------------------------
+# activations and logits
+# ----------------------------------------------------------------------------
+
+
+def _hottest_over_mean(logits, k):
+    ids = torch.topk(logits, k, dim=1).indices.reshape(-1)
+    counts = torch.bincount(ids, minlength=logits.shape[1]).double()
+    return (counts.max() / counts.mean()).item()
+
+
+def skew_bias(cfg, T, E, k, base_logits, device, target=5.0):
+    """Per-expert bias -alpha*1.1*ln(rank) with alpha bisected to the target skew."""
+    perm = torch.randperm(E, generator=_gen("cpu", seed_of(cfg, T_RANK)))
+    rank = torch.empty(E, dtype=torch.float64)
+    rank[perm] = torch.arange(1, E + 1, dtype=torch.float64)
+    shape = (-1.1 * torch.log(rank)).to(torch.float32).to(device)
+    lo, hi = 0.0, 2.0
+    alpha = 1.0
+    for _ in range(40):
+        alpha = 0.5 * (lo + hi)
+        r = _hottest_over_mean(base_logits + alpha * shape[None, :], k)
+        if abs(r - target) <= 0.1:
+            break
+        if r < target:
+            lo = alpha
+        else:
+            hi = alpha
+    return alpha * shape, alpha
+
+
+def make_inputs(name, device="cpu", weights=True):
+    """All inputs of one workload as torch tensors on ``device``.
+
+    Returns a dict: cfg (the CONFIGS entry plus alpha), x (bfloat16 [T][H]),
+    logits (float32 [T][E]), routed (dict w1,w3,w2,s1,s3,s2), shared (dict or
+    None), gamma (float32 [H] or None), eps.
+    """
+    c = dict(CONFIGS[name])
+    T, H, I, E, k = c["T"], c["H"], c["I"], c["E"], c["k"]
+    x = randn((T, H), device, seed_of(c["cfg"], T_X)).to(torch.bfloat16)
+    logits = randn((T, E), device, seed_of(c["cfg"], T_LOGITS))
+    c["alpha"] = None
+    if c["skew"]:
+        bias, alpha = skew_bias(c["cfg"], T, E, k, logits, device)
+        logits = (logits + bias[None, :]).contiguous()
+        c["alpha"] = alpha
+    routed = expert_weights(c["cfg"], device, c["fmt"], E, H, I) if weights else None
+    shared = None
+    if c["shared"] and weights:
+        shared = expert_weights(c["cfg"], device, "fp8", 1, H, I, (T_SW1, T_SW3, T_SW2))
+    gamma = torch.ones(H, dtype=torch.float32, device=device) if c["norm"] else None
+    return dict(cfg=c, x=x, logits=logits, routed=routed, shared=shared, gamma=gamma, eps=NORM_EPS)
+
+
+def custom_inputs(T, H, I, E, k, fmt="fp8", seed=7, device="cpu", shared=False, norm=False,
+                  logits=None):
+    """Inputs of an arbitrary shape with the same recipe (for edge-case tests)."""
+    cfg = 90 + (seed % 10)
+    x = randn((T, H), device, seed_of(cfg, T_X, seed)).to(torch.bfloat16)
+    if logits is None:
+        logits = randn((T, E), device, seed_of(cfg, T_LOGITS, seed))
+    routed = expert_weights(cfg * 1000 + seed, device, fmt, E, H, I)
+    sh = expert_weights(cfg * 1000 + seed, device, "fp8", 1, H, I, (T_SW1, T_SW3, T_SW2)) if shared else None
+    gamma = torch.ones(H, dtype=torch.float32, device=device) if norm else None
+    c = dict(cfg=cfg, T=T, H=H, I=I, E=E, k=k, fmt=fmt, shared=shared, norm=norm, skew=False, alpha=None)
+    return dict(cfg=c, x=x, logits=logits, routed=routed, shared=sh, gamma=gamma, eps=NORM_EPS)
+
+
+def to_numpy(inputs):
+    """Host NumPy copies for the oracle: x as uint16 bf16 bits, the rest as is."""
+    import numpy as np
+
+    def cpu(t):
+        return None if t is None else t.detach().cpu()
+
+    out = dict(cfg=inputs["cfg"], eps=inputs["eps"])
+    out["x"] = cpu(inputs["x"]).view(torch.int16).numpy().view(np.uint16)
+    out["logits"] = cpu(inputs["logits"]).numpy()
+    for key in ("routed", "shared"):
+        d = inputs[key]
+        out[key] = None if d is None else {n: cpu(t).numpy() for n, t in d.items()}
+    out["gamma"] = None if inputs["gamma"] is None else cpu(inputs["gamma"]).numpy()
+    return out
+
+
+def weight_bytes_per_expert(H, I, fmt):
+    return 3 * H * I if fmt == "fp8" else 3 * H * I // 2 + 3 * H * I // 32
+
+
+def ceil_div(a, b):
+    return -(-a // b)
+
+

@@ -1,0 +1,320 @@
+"""The routed MoE layer, step by step, in float64 (plain definition).
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+Steps and where the pages describe them:
+
+1. ``route``            -- softmax router, top-k, renormalised weights.
+   *Ling-2.6-1T on TPU*: overview (256 routed experts, top-8 plus one shared
+   expert) and §1 cost model; *Kimi K3 on TPU*, §2.4 LatentMoE
+   (renormalised top-k weights, routed scaling factor 1.0).
+2. ``quantize_tokens``  -- dynamic per-token fp8 quantisation of the bf16
+   activations before the scatter.  *Ling-2.6-1T on TPU*, §5 "activation
+   quantisation".
+3. ``expert_counts_offsets`` and ``permute_rows`` -- routing metadata
+   (token-to-expert map, per-expert counts and offsets, scatter/gather
+   indices) and the scatter of token rows to experts.  *Ling-2.6-1T on TPU*,
+   §1 ("scatter tokens -> local expert FFN -> gather results") and §6 (the
+   metadata block).
+4. ``expert_ffn``       -- gated expert FFN: W1/W3 gate-up projection, SiLU,
+   gate multiply, scale multiply, W2 down projection, with per-channel scales
+   applied after the full-K reduction.  *Ling-2.6-1T on TPU*, §2 (table of
+   hardware units and the MoE work each does) and §5 "per-channel
+   direct_scaled_dot".
+5. ``combine``          -- weighted gather back into token order, optional
+   per-token RMSNorm of the routed sum (*Kimi K3 on TPU*, §2.4
+   routed_expert_norm), plus the shared expert's output (*Ling-2.6-1T on TPU*,
+   §1 and §5 "in-kernel shared expert").
+
+Readings where the pages are silent (each listed in the design notes):
+top-k compares the raw fp32 logits with ties to the lower expert index and
+keeps slots in that order; fp8 is OCP E4M3FN with round-half-even and
+saturation; scales are amax/448 by IEEE binary32 division (1 when amax is 0);
+W1 is the gate and W3 the up projection; the FFN intermediate h is rounded to
+binary32 and quantised per routed row like the tokens; the shared expert reads
+the same quantised tokens and is added with weight 1 after the routed sum
+(after the RMSNorm when there is one); the output is bfloat16.
+"""
+
+import numpy as np
+
+from .codecs import (
+    e4m3_decode,
+    e4m3_encode,
+    bf16_decode,
+    bf16_encode,
+    mxfp4_decode,
+    E4M3_MAX,
+)
+
+
+# ----------------------------------------------------------------------------
+# 1. Router
+# ----------------------------------------------------------------------------
+
+
+def route(logits, top_k):
+    """Top-k experts per token and their renormalised softmax weights.
+
+    logits: float32 [T][E].  Returns (topk_ids int32 [T][k], topk_w float64
+    [T][k]).  Experts are ordered by descending logit, equal logits by
+    ascending expert index; that order is both the selection and the slot
+    order.  p = softmax(logits[t]) in float64 (max subtracted), and
+    w_j = p[id_j] / sum_j' p[id_j'].
+    """
+    logits = np.asarray(logits, dtype=np.float32)
+    T, E = logits.shape
+    if not 1 <= top_k <= E:
+        raise ValueError("top_k out of range")
+    ids = np.empty((T, top_k), dtype=np.int32)
+    w = np.empty((T, top_k), dtype=np.float64)
+    index = np.arange(E)
+    for t in range(T):
+        row = logits[t].astype(np.float64)
+        # np.lexsort sorts by the last key first: primary -logit, then index.
+        order = np.lexsort((index, -row))
+        sel = order[:top_k]
+        ids[t] = sel
+        p = np.exp(row - row.max())
+        p = p / p.sum()
+        w[t] = p[sel] / p[sel].sum()
+    return ids, w
+
+
+# ----------------------------------------------------------------------------
+# 2. Per-row fp8 quantisation (tokens, and the FFN intermediate)
+# ----------------------------------------------------------------------------
+
+
+def quantize_rows_f32(values):
+    """Per-row e4m3 quantisation of binary32 values.
+
+    a = max|v|; s = a / 448 as an IEEE binary32 division (s = 1 when a = 0);
+    q = e4m3(v / s) with the division again in binary32.  Returns
+    (codes uint8 [N][D], scales float32 [N]).
+    """
+    v = np.asarray(values, dtype=np.float32)
+    a = np.max(np.abs(v), axis=1)
+    s = a / np.float32(E4M3_MAX)                      # binary32 division
+    s = np.where(a == 0, np.float32(1.0), s).astype(np.float32)
+    q = e4m3_encode(v / s[:, None])                   # binary32 division
+    return q, s
+
+
+def quantize_tokens(x_bf16):
+    """bf16 activations [T][H] (uint16 bits) -> (xq uint8 [T][H], xs float32 [T])."""
+    x = bf16_decode(x_bf16).astype(np.float32)        # exact
+    return quantize_rows_f32(x)
+
+
+# ----------------------------------------------------------------------------
+# 3. Routing metadata and the scatter
+# ----------------------------------------------------------------------------
+
+
+def expert_counts_offsets(topk_ids, n_experts):
+    """counts[e] = number of (t, j) with topk_ids[t][j] == e; offsets is the
+    exclusive prefix sum with offsets[0] = 0 and offsets[E] = T*k."""
+    ids = np.asarray(topk_ids).ravel()
+    counts = np.zeros(n_experts, dtype=np.int64)
+    for e in ids:
+        counts[e] += 1
+    offsets = np.zeros(n_experts + 1, dtype=np.int64)
+    for e in range(n_experts):
+        offsets[e + 1] = offsets[e] + counts[e]
+    return counts.astype(np.int32), offsets.astype(np.int32)
+
+
+def permute_rows(topk_ids, offsets, xq, xs):
+    """Stable scatter of token rows into expert-grouped rows.
+
+    Pairs (t, j) are visited in row-major order; each takes the next free row
+    of its expert's segment.  Returns (pair_to_row int32 [T][k], row_to_pair
+    int32 [R], xq_rows uint8 [R][H], xs_rows float32 [R]) with R = T*k and
+    pair index p = t*k + j.
+    """
+    ids = np.asarray(topk_ids)
+    T, k = ids.shape
+    R = T * k
+    cursor = np.array(offsets[:-1], dtype=np.int64).copy()
+    pair_to_row = np.empty((T, k), dtype=np.int32)
+    row_to_pair = np.empty(R, dtype=np.int32)
+    for t in range(T):
+        for j in range(k):
+            e = ids[t, j]
+            r = cursor[e]
+            cursor[e] += 1
+            pair_to_row[t, j] = r
+            row_to_pair[r] = t * k + j
+    tok = row_to_pair // k
+    xq_rows = np.asarray(xq)[tok]
+    xs_rows = np.asarray(xs, dtype=np.float32)[tok]
+    return pair_to_row, row_to_pair, xq_rows, xs_rows
+
+
+# ----------------------------------------------------------------------------
+# 4. Expert FFN
+# ----------------------------------------------------------------------------
+
+
+class ExpertWeights:
+    """Weights of a group of experts in one of the two formats.
+
+    fmt "fp8":   w1, w3 uint8 [E][I][H]; w2 uint8 [E][H][I] (e4m3 codes, the
+                 contraction index last); s1, s3 float32 [E][I], s2 float32
+                 [E][H] (one scale per output channel).
+    fmt "mxfp4": w1, w3 uint8 [E][I][H/2]; w2 uint8 [E][H][I/2] (two e2m1 per
+                 byte, element 2i in the low nibble); s1, s3 uint8
+                 [E][I][H/32], s2 uint8 [E][H][I/32] (e8m0 per 32 consecutive
+                 contraction elements of one output channel).
+    W1 is the gate projection and W3 the up projection.
+    """
+
+    def __init__(self, fmt, w1, w3, w2, s1, s3, s2):
+        if fmt not in ("fp8", "mxfp4"):
+            raise ValueError(fmt)
+        self.fmt = fmt
+        self.w1, self.w3, self.w2 = (np.asarray(a) for a in (w1, w3, w2))
+        self.s1, self.s3, self.s2 = (np.asarray(a) for a in (s1, s3, s2))
+        self.n_experts = self.w1.shape[0]
+        self.inter = self.w1.shape[1]
+        self.hidden = self.w2.shape[1]
+
+    def decode(self, e):
+        """Expert e as float64 matrices and per-channel scales:
+        (W1 [I][H], W3 [I][H], W2 [H][I], c1 [I], c3 [I], c2 [H])."""
+        if self.fmt == "fp8":
+            return (e4m3_decode(self.w1[e]), e4m3_decode(self.w3[e]),
+                    e4m3_decode(self.w2[e]),
+                    self.s1[e].astype(np.float64), self.s3[e].astype(np.float64),
+                    self.s2[e].astype(np.float64))
+        ones_i = np.ones(self.inter)
+        return (mxfp4_decode(self.w1[e], self.s1[e]),
+                mxfp4_decode(self.w3[e], self.s3[e]),
+                mxfp4_decode(self.w2[e], self.s2[e]),
+                ones_i, ones_i, np.ones(self.hidden))
+
+
+def silu(z):
+    """SiLU(z) = z * sigmoid(z) = z / (1 + e^-z)."""
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
+
+
+def expert_ffn(xq_rows, xs_rows, offsets, weights):
+    """Gated FFN of every routed row with its expert's weights.
+
+    For row r in expert e's segment (rows offsets[e] .. offsets[e+1]-1):
+      g = (sum_k q_r[k] W1[e][n][k]) * xs_r * s1[e][n]
+      u = (sum_k q_r[k] W3[e][n][k]) * xs_r * s3[e][n]
+      h = binary32( SiLU(g) * u )
+      hq, hs = per-row e4m3 quantisation of h (as for tokens)
+      y[r][j] = (sum_n hq_r[n] W2[e][j][n]) * hs_r * s2[e][j]
+    The sums of fp8 (or e2m1 * 2^k) products are exact in float64.
+    Returns (y float64 [R][H], h float32 [R][I], hq uint8 [R][I], hs float32 [R]).
+    """
+    xq_rows = np.asarray(xq_rows)
+    xs_rows = np.asarray(xs_rows, dtype=np.float64)
+    R = xq_rows.shape[0]
+    H, I = weights.hidden, weights.inter
+    y = np.zeros((R, H), dtype=np.float64)
+    h_all = np.zeros((R, I), dtype=np.float32)
+    hq_all = np.zeros((R, I), dtype=np.uint8)
+    hs_all = np.ones(R, dtype=np.float32)
+    for e in range(len(offsets) - 1):
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        if r1 == r0:
+            continue
+        W1, W3, W2, c1, c3, c2 = weights.decode(e)
+        a = e4m3_decode(xq_rows[r0:r1])
+        g = (a @ W1.T) * xs_rows[r0:r1, None] * c1[None, :]
+        u = (a @ W3.T) * xs_rows[r0:r1, None] * c3[None, :]
+        h = (silu(g) * u).astype(np.float32)
+        hq, hs = quantize_rows_f32(h)
+        y[r0:r1] = (e4m3_decode(hq) @ W2.T) * hs.astype(np.float64)[:, None] * c2[None, :]
+        h_all[r0:r1], hq_all[r0:r1], hs_all[r0:r1] = h, hq, hs
+    return y, h_all, hq_all, hs_all
+
+
+# ----------------------------------------------------------------------------
+# 5. Combine
+# ----------------------------------------------------------------------------
+
+
+def rms_norm(o, gamma, eps):
+    """Per-row RMSNorm: o / sqrt(mean(o^2) + eps) * gamma."""
+    return o / np.sqrt(np.mean(o * o, axis=1, keepdims=True) + eps) * gamma[None, :]
+
+
+def combine(y_rows, pair_to_row, topk_w, y_shared=None, norm_gamma=None, norm_eps=1e-6):
+    """out[t] = bf16( [RMSNorm]( sum_j w[t][j] * y_rows[pair_to_row[t][j]] ) + y_shared[t] ).
+
+    The routed sum runs over slots j = 0..k-1 in order.  Returns uint16 bf16 bits.
+    """
+    p2r = np.asarray(pair_to_row)
+    w = np.asarray(topk_w, dtype=np.float64)
+    T, k = p2r.shape
+    o = np.zeros((T, y_rows.shape[1]), dtype=np.float64)
+    for j in range(k):
+        o += w[:, j, None] * y_rows[p2r[:, j]]
+    if norm_gamma is not None:
+        o = rms_norm(o, np.asarray(norm_gamma, dtype=np.float64), norm_eps)
+    if y_shared is not None:
+        o = o + y_shared
+    return bf16_encode(o)
+
+
+# ----------------------------------------------------------------------------
+# The whole layer
+# ----------------------------------------------------------------------------
+
+
+def forward(x_bf16, logits, top_k, routed, shared=None, norm_gamma=None, norm_eps=1e-6):
+    """Route -> quantise -> count/offset -> permute -> expert FFN -> combine.
+
+    x_bf16 uint16 [T][H]; logits float32 [T][E]; routed/shared ExpertWeights
+    (shared has one expert and runs on every token in token order).  Returns a
+    dict with every intermediate and ``out`` (uint16 bf16 [T][H]).
+    """
+    ids, w = route(logits, top_k)
+    xq, xs = quantize_tokens(x_bf16)
+    counts, offsets = expert_counts_offsets(ids, routed.n_experts)
+    pair_to_row, row_to_pair, xq_rows, xs_rows = permute_rows(ids, offsets, xq, xs)
+    y_rows, h, hq, hs = expert_ffn(xq_rows, xs_rows, offsets, routed)
+    y_shared = None
+    if shared is not None:
+        T = xq.shape[0]
+        y_shared = expert_ffn(xq, xs, np.array([0, T]), shared)[0]
+    out = combine(y_rows, pair_to_row, w, y_shared, norm_gamma, norm_eps)
+    return dict(topk_ids=ids, topk_w=w, xq=xq, xs=xs, counts=counts, offsets=offsets,
+                pair_to_row=pair_to_row, row_to_pair=row_to_pair, xq_rows=xq_rows,
+                xs_rows=xs_rows, h=h, hq=hq, hs=hs, y_rows=y_rows, y_shared=y_shared,
+                out=out)
+
+
+def forward_sampled(x_bf16, logits, top_k, routed, tokens, shared=None,
+                    norm_gamma=None, norm_eps=1e-6):
+    """The layer's output for a subset of tokens only (rows are independent).
+
+    Routing, quantisation, counts/offsets and the permutation are computed for
+    all tokens (they are cheap and bit-exact targets); the FFN and combine run
+    only for the pairs of ``tokens``.  Returns the same dict as ``forward``
+    with ``out`` of shape [len(tokens)][H] (row i is token tokens[i]) and no
+    per-row FFN intermediates.
+    """
+    tokens = np.asarray(tokens, dtype=np.int64)
+    ids, w = route(logits, top_k)
+    xq, xs = quantize_tokens(x_bf16)
+    counts, offsets = expert_counts_offsets(ids, routed.n_experts)
+    pair_to_row, row_to_pair, xq_rows, xs_rows = permute_rows(ids, offsets, xq, xs)
+    sub_ids = ids[tokens]
+    _, sub_off = expert_counts_offsets(sub_ids, routed.n_experts)
+    sub_p2r, _, sub_q, sub_s = permute_rows(sub_ids, sub_off, xq[tokens], xs[tokens])
+    y_sub = expert_ffn(sub_q, sub_s, sub_off, routed)[0]
+    y_shared = None
+    if shared is not None:
+        y_shared = expert_ffn(xq[tokens], xs[tokens], np.array([0, len(tokens)]), shared)[0]
+    out = combine(y_sub, sub_p2r, w[tokens], y_shared, norm_gamma, norm_eps)
+    return dict(topk_ids=ids, topk_w=w, xq=xq, xs=xs, counts=counts, offsets=offsets,
+                pair_to_row=pair_to_row, row_to_pair=row_to_pair, xq_rows=xq_rows,
+                xs_rows=xs_rows, out=out)
