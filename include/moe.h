@@ -1,0 +1,246 @@
+/*
+ * moe.h -- C ABI of the routed mixture-of-experts layer on one MI355X (gfx950).
+ *
+ * The layer is the one described on the page "Optimising Ling-2.6-1T on TPU
+ * with SGLang-JAX: hiding MoE data movement behind compute with one Pallas
+ * kernel" (cited below as [Ling]):
+ *
+ *   route (softmax, top-k, renormalise)
+ *     -> per-token fp8 e4m3 activation quantisation        [Ling] §5, activation quantisation
+ *     -> per-expert counts / offsets and a stable scatter  [Ling] §1 and §6 (routing metadata)
+ *     -> grouped gate-up GEMM with a SiLU * gate epilogue  [Ling] §2 table, §5 direct_scaled_dot
+ *     -> grouped down GEMM
+ *     -> top-k weighted combine (+ shared expert)          [Ling] §1, §5 in-kernel shared expert
+ *
+ * Weights are per-output-channel fp8 e4m3 ([Ling] §5) or MXFP4: e2m1 codes two
+ * per byte with one e8m0 scale per 32 contiguous contraction elements (page
+ * "Implementation gaps: advanced optimisations" of the sglang-jax wiki, §4
+ * MXFP4; page "Feasibility of porting Kimi K3 to the Google TPU ecosystem",
+ * §2.5).  The optional RMSNorm of the routed sum is the LatentMoE
+ * routed_expert_norm of that Kimi K3 page, §2.4.
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ *  - Tensor pointers are DEVICE pointers to row-major, contiguous arrays.
+ *    bf16 is passed as uint16_t bit patterns; fp8 e4m3 (OCP E4M3FN), packed
+ *    e2m1 pairs and e8m0 scales as uint8_t.  `stream` is a hipStream_t
+ *    (NULL = the default stream).
+ *  - Ownership: the caller allocates and owns every buffer, including the
+ *    workspace sized by the *_workspace_size functions.  The library never
+ *    allocates or frees device memory, never synchronises the device, never
+ *    copies device data to the host and never reads device data on the
+ *    host.  All work is enqueued on `stream`, so every call can be captured
+ *    into a HIP graph.  No global mutable state: calls on different streams
+ *    with distinct workspaces may run concurrently.
+ *  - Errors: arguments are validated on the host before anything is enqueued;
+ *    on a non-OK return nothing has been enqueued or written.  A launch
+ *    failure reported by the runtime returns MOE_ERR_DEVICE (work enqueued
+ *    before it may have run).  Faults inside kernels surface at the caller's
+ *    next synchronisation.  moe_last_error() gives a thread-local message
+ *    for the last non-OK return on the calling thread.
+ *  - T = 0 is valid and does nothing.  Inputs holding NaN or Inf give
+ *    undefined results.
+ *  - Limits: 1 <= E <= 1024; 1 <= top_k <= min(E, 32); T * top_k < 2^31;
+ *    H and I multiples of 128 (one MFMA contraction step) and at most 65536;
+ *    pointers 16-byte aligned.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_NULL = 1,        /* a required pointer is NULL                          */
+  MOE_ERR_SHAPE = 2,       /* a size is out of range or inconsistent              */
+  MOE_ERR_ALIGN = 3,       /* a pointer is not 16-byte aligned                    */
+  MOE_ERR_WORKSPACE = 4,   /* the workspace is smaller than *_workspace_size()   */
+  MOE_ERR_UNSUPPORTED = 5, /* valid, but no kernel exists for this case           */
+  MOE_ERR_DEVICE = 6       /* the HIP runtime reported an error                   */
+} moe_status_t;
+
+typedef enum {
+  MOE_W_FP8_E4M3_PERCHANNEL = 0, /* e4m3 codes + one fp32 scale per output channel */
+  MOE_W_MXFP4_E2M1_E8M0_G32 = 1  /* e2m1 pairs + one e8m0 scale per 32 K-elements   */
+} moe_wfmt_t;
+
+/*
+ * A group of experts that share one shape.  Host struct holding device
+ * pointers; caller-owned.  W1 is the gate projection (through SiLU), W3 the
+ * up projection, W2 the down projection; the contraction index is last
+ * ("K contiguous").
+ *
+ *   fmt = FP8:   w1, w3  uint8 [E][I][H]      s1, s3  float [E][I]
+ *                w2      uint8 [E][H][I]      s2      float [E][H]
+ *   fmt = MXFP4: w1, w3  uint8 [E][I][H/2]    s1, s3  uint8 [E][I][H/32]
+ *                w2      uint8 [E][H][I/2]    s2      uint8 [E][H][I/32]
+ *                (element 2i in the low nibble of byte i; scale 255 = NaN is
+ *                 not allowed)
+ */
+typedef struct {
+  int32_t fmt;       /* moe_wfmt_t */
+  int32_t n_experts; /* E */
+  int32_t hidden;    /* H: model dimension (FFN input and output width) */
+  int32_t inter;     /* I: intermediate dimension */
+  const uint8_t* w1;
+  const uint8_t* w3;
+  const uint8_t* w2;
+  const void* s1;
+  const void* s3;
+  const void* s2;
+} moe_weights_t;
+
+/* Stage boundaries at which moe_forward records the events of a moe_debug_t. */
+enum {
+  MOE_STAGE_ROUTE = 0,   /* router                                   */
+  MOE_STAGE_PERMUTE = 1, /* counts, offsets, ranks, quantise+scatter,
+                            GEMM tile prefix                         */
+  MOE_STAGE_GEMM1 = 2,   /* gate-up grouped GEMM + SiLU * gate (only) */
+  MOE_STAGE_QUANT_H = 3, /* per-row fp8 quantisation of h            */
+  MOE_STAGE_GEMM2 = 4,   /* down grouped GEMM                        */
+  MOE_STAGE_COMBINE = 5, /* weighted gather (+ RMSNorm) (+ shared)   */
+  MOE_N_STAGES = 6
+};
+
+/*
+ * Optional capture of intermediates and stage timing for moe_forward.  Every
+ * non-NULL device pointer receives the named intermediate (and is used in
+ * place of the corresponding workspace slice).  events[i], when non-NULL, is
+ * a hipEvent_t recorded on `stream` just before stage i; events[MOE_N_STAGES]
+ * after the last stage.  `variant` receives a NUL-terminated name of the
+ * kernel variants chosen.
+ */
+typedef struct {
+  int32_t* topk_ids;       /* [T][k]   */
+  float* topk_w;           /* [T][k]   */
+  int32_t* expert_counts;  /* [E]      */
+  int32_t* expert_offsets; /* [E+1]; [E+2] with a shared expert, whose token-order
+                              rows are the extra group T*k .. T*k+T-1 */
+  int32_t* pair_to_row;    /* [T][k]   */
+  int32_t* row_to_pair;    /* [T*k]    */
+  uint8_t* xq_rows;        /* [T*k][H] */
+  float* xs_rows;          /* [T*k]    */
+  void* events[MOE_N_STAGES + 1];
+  char variant[96];
+} moe_debug_t;
+
+/* ------------------------------------------------------------------------ */
+
+/*
+ * moe_route -- softmax router with top-k selection.
+ *   logits    float [T][E]   router logits
+ *   topk_ids  int32 [T][k]   out: chosen experts, slot order = descending
+ *                            logit, equal logits by ascending expert index
+ *                            (-0.0 equals +0.0); the raw fp32 logits decide
+ *   topk_w    float [T][k]   out: w_j = p[id_j] / sum_j' p[id_j'] with
+ *                            p = softmax(logits[t]) (routed scaling 1.0)
+ * [Ling] overview and §1 (top-8 of 256 routed experts); renormalised weights
+ * as in the Kimi K3 page, §2.4.
+ */
+moe_status_t moe_route(const float* logits, int32_t T, int32_t E, int32_t top_k,
+                       int32_t* topk_ids, float* topk_w, void* stream);
+
+/*
+ * moe_permute -- per-token fp8 quantisation, per-expert counts and offsets,
+ * and the stable scatter of quantised token rows into expert order.
+ *   x              bf16  [T][H]   activations
+ *   topk_ids       int32 [T][k]   from moe_route
+ *   expert_counts  int32 [E]      out: rows per expert
+ *   expert_offsets int32 [E+1]    out: exclusive prefix sum, [0] = 0, [E] = T*k
+ *   pair_to_row    int32 [T][k]   out: row of pair (t, j)
+ *   row_to_pair    int32 [T*k]    out: pair index t*k + j of each row
+ *   xq_rows        uint8 [T*k][H] out: e4m3 codes of token t at row pair_to_row[t][j]
+ *   xs_rows        float [T*k]    out: its scale
+ *   xq_tok, xs_tok uint8 [T][H], float [T]  out, optional (NULL = skip): the
+ *                  same quantised tokens in token order
+ * Quantisation: a = max|x[t]|, s = a/448 (IEEE binary32 division; s = 1 if
+ * a = 0), q = e4m3(x/s) with round-half-even, saturation at +-448 and signed
+ * zero ([Ling] §5, activation quantisation before the scatter).  Rows are
+ * ordered by expert, and within an expert by pair index (t*k + j): the
+ * permutation is unique and deterministic.
+ */
+size_t moe_permute_workspace_size(int32_t T, int32_t top_k, int32_t E);
+moe_status_t moe_permute(const uint16_t* x, int32_t T, int32_t H, const int32_t* topk_ids,
+                         int32_t top_k, int32_t E, int32_t* expert_counts,
+                         int32_t* expert_offsets, int32_t* pair_to_row, int32_t* row_to_pair,
+                         uint8_t* xq_rows, float* xs_rows, uint8_t* xq_tok, float* xs_tok,
+                         void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_expert_ffn -- gated FFN of expert-grouped rows.
+ *   xq_rows        uint8 [n_rows][H]  e4m3 rows grouped by expert
+ *   xs_rows        float [n_rows]     per-row scales
+ *   expert_offsets int32 [E+1]        device; rows of expert e are
+ *                                     offsets[e] .. offsets[e+1]-1, offsets[E] = n_rows
+ *   y_rows         bf16  [n_rows][H]  out
+ * For row r of expert e ([Ling] §5, per-channel direct_scaled_dot: scales
+ * applied after the full-K reduction; fp32 accumulation):
+ *   g = (sum_k q_r[k] W1[e][n][k]) * xs_r * s1[e][n];  u likewise with W3, s3
+ *   h = SiLU(g) * u  (binary32),  hs_r = max|h_r| / 448,  hq = e4m3(h / hs_r)
+ *   y_r[j] = bf16( (sum_n hq_r[n] W2[e][j][n]) * hs_r * s2[e][j] )
+ * For MXFP4 the e8m0 block scales enter each 32-element partial sum and
+ * s1/s3/s2 are not per-channel.  A shared expert is a call with E = 1 and
+ * offsets {0, T} over token-order rows.
+ */
+size_t moe_expert_ffn_workspace_size(int32_t n_rows, const moe_weights_t* w);
+moe_status_t moe_expert_ffn(const uint8_t* xq_rows, const float* xs_rows, int32_t n_rows,
+                            const int32_t* expert_offsets, const moe_weights_t* w,
+                            uint16_t* y_rows, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_combine -- weighted gather back into token order.
+ *   y_rows      bf16  [T*k][H]  expert outputs
+ *   pair_to_row int32 [T][k]
+ *   topk_w      float [T][k]
+ *   y_shared    bf16  [T][H]    optional (NULL = none): shared expert output
+ *   norm_gamma  float [H]       optional (NULL = no RMSNorm)
+ *   out         bf16  [T][H]    out
+ * o = sum_{j<k} w[t][j] * y_rows[pair_to_row[t][j]] in fp32, slot order;
+ * with norm_gamma: o = o / sqrt(mean(o^2) + norm_eps) * gamma (the LatentMoE
+ * routed_expert_norm, Kimi K3 page §2.4); then o += y_shared[t];
+ * out = bf16(o), round-half-even.  [Ling] §1 (gather results) and the
+ * SparseCore gather-reduce of the sglang-jax gap list, §8.
+ */
+moe_status_t moe_combine(const uint16_t* y_rows, const int32_t* pair_to_row, const float* topk_w,
+                         int32_t T, int32_t H, int32_t top_k, const uint16_t* y_shared,
+                         const float* norm_gamma, float norm_eps, uint16_t* out, void* stream);
+
+/*
+ * moe_forward -- the whole layer: route -> permute -> expert FFN (routed
+ * experts and, if use_shared, the shared expert on every token) -> combine.
+ *   x       bf16  [T][H]         logits float [T][E] (E = routed->n_experts)
+ *   routed  the routed experts; shared: one expert of the same H and I, fp8
+ *           (required iff use_shared)
+ *   out     bf16  [T][H]
+ *   dbg     optional (NULL = none), see moe_debug_t
+ * The shared expert reads the same quantised tokens as the routed experts
+ * and is added with weight 1 after the routed sum (and after the RMSNorm)
+ * ([Ling] §5, in-kernel shared expert).
+ */
+size_t moe_forward_workspace_size(int32_t T, int32_t top_k, const moe_weights_t* routed,
+                                  int32_t use_shared);
+moe_status_t moe_forward(const uint16_t* x, const float* logits, int32_t T, int32_t top_k,
+                         const moe_weights_t* routed, int32_t use_shared,
+                         const moe_weights_t* shared, const float* norm_gamma, float norm_eps,
+                         uint16_t* out, moe_debug_t* dbg, void* ws, size_t ws_bytes,
+                         void* stream);
+
+/* Static description of a status code. */
+const char* moe_status_string(moe_status_t s);
+
+/* Thread-local detail of the last non-OK return on this thread ("" if none). */
+const char* moe_last_error(void);
+
+/* Library version string. */
+const char* moe_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,144 @@
+"""Routed mixture-of-experts layer on MI355X (gfx950): Python binding.
+
+Thin wrappers with the names of the C ABI (include/moe.h).  They marshal
+torch tensors (device memory) and the current HIP stream into the library
+and allocate outputs / workspaces with torch; every step of the layer runs in
+the library's kernels.  There is no fallback: if libmoe.so is missing the
+import of the library fails with an error.
+"""
+
+import ctypes
+
+import torch
+
+from . import _lib
+from ._lib import (MOE_W_FP8, MOE_W_MXFP4, MOE_N_STAGES, STAGE_NAMES, MoeDebug, MoeError,
+                   MoeWeights, check)
+
+__all__ = ["Weights", "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_forward",
+           "forward_workspace_size", "MoeError", "lib"]
+
+
+def lib():
+    return _lib.load()
+
+
+def _p(t):
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+class Weights:
+    """A group of experts: keeps the tensors alive and holds the moe_weights_t.
+
+    ``d`` has w1, w3, w2, s1, s3, s2 as produced by ``moe_synth`` (uint8 codes;
+    float32 per-channel scales for fp8, uint8 e8m0 block scales for mxfp4).
+    """
+
+    def __init__(self, d, fmt):
+        self.tensors = {k: v.contiguous() for k, v in d.items()}
+        t = self.tensors
+        self.fmt = MOE_W_FP8 if fmt == "fp8" else MOE_W_MXFP4
+        E, I = t["w1"].shape[0], t["w1"].shape[1]
+        H = t["w2"].shape[1]
+        self.n_experts, self.hidden, self.inter = E, H, I
+        self.c = MoeWeights(self.fmt, E, H, I, *(t[k].data_ptr() for k in ("w1", "w3", "w2", "s1", "s3", "s2")))
+
+    def ref(self):
+        return ctypes.byref(self.c)
+
+
+def _empty(shape, dtype, device):
+    return torch.empty(shape, dtype=dtype, device=device)
+
+
+def moe_route(logits, top_k, topk_ids=None, topk_w=None, stream=None):
+    T, E = logits.shape
+    dev = logits.device
+    topk_ids = _empty((T, top_k), torch.int32, dev) if topk_ids is None else topk_ids
+    topk_w = _empty((T, top_k), torch.float32, dev) if topk_w is None else topk_w
+    check(lib().moe_route(_p(logits), T, E, top_k, _p(topk_ids), _p(topk_w), _stream(stream)))
+    return topk_ids, topk_w
+
+
+def moe_permute(x, topk_ids, n_experts, token_order=False, stream=None):
+    """Returns dict(counts, offsets, pair_to_row, row_to_pair, xq_rows, xs_rows[, xq_tok, xs_tok])."""
+    T, H = x.shape
+    k = topk_ids.shape[1]
+    dev = x.device
+    R = T * k
+    out = dict(counts=_empty((n_experts,), torch.int32, dev),
+               offsets=_empty((n_experts + 1,), torch.int32, dev),
+               pair_to_row=_empty((T, k), torch.int32, dev),
+               row_to_pair=_empty((R,), torch.int32, dev),
+               xq_rows=_empty((R, H), torch.uint8, dev),
+               xs_rows=_empty((R,), torch.float32, dev))
+    if token_order:
+        out["xq_tok"] = _empty((T, H), torch.uint8, dev)
+        out["xs_tok"] = _empty((T,), torch.float32, dev)
+    nbytes = lib().moe_permute_workspace_size(T, k, n_experts)
+    ws = _empty((nbytes,), torch.uint8, dev)
+    check(lib().moe_permute(_p(x), T, H, _p(topk_ids), k, n_experts, _p(out["counts"]),
+                            _p(out["offsets"]), _p(out["pair_to_row"]), _p(out["row_to_pair"]),
+                            _p(out["xq_rows"]), _p(out["xs_rows"]), _p(out.get("xq_tok")),
+                            _p(out.get("xs_tok")), _p(ws), nbytes, _stream(stream)))
+    return out
+
+
+def moe_expert_ffn(xq_rows, xs_rows, expert_offsets, weights, stream=None):
+    n_rows = xq_rows.shape[0]
+    dev = xq_rows.device
+    y = _empty((n_rows, weights.hidden), torch.bfloat16, dev)
+    nbytes = lib().moe_expert_ffn_workspace_size(n_rows, weights.ref())
+    ws = _empty((max(nbytes, 1),), torch.uint8, dev)
+    check(lib().moe_expert_ffn(_p(xq_rows), _p(xs_rows), n_rows, _p(expert_offsets), weights.ref(),
+                               _p(y), _p(ws), nbytes, _stream(stream)))
+    return y
+
+
+def moe_combine(y_rows, pair_to_row, topk_w, y_shared=None, norm_gamma=None, norm_eps=1e-6,
+                stream=None):
+    T, k = pair_to_row.shape
+    H = y_rows.shape[1]
+    out = _empty((T, H), torch.bfloat16, y_rows.device)
+    check(lib().moe_combine(_p(y_rows), _p(pair_to_row), _p(topk_w), T, H, k, _p(y_shared),
+                            _p(norm_gamma), float(norm_eps), _p(out), _stream(stream)))
+    return out
+
+
+def forward_workspace_size(T, top_k, routed, use_shared):
+    return lib().moe_forward_workspace_size(T, top_k, routed.ref(), int(bool(use_shared)))
+
+
+def moe_forward(x, logits, top_k, routed, shared=None, norm_gamma=None, norm_eps=1e-6, out=None,
+                ws=None, debug=None, events=None, stream=None):
+    """The whole layer.  ``debug``: dict of device tensors to capture
+    (keys topk_ids, topk_w, expert_counts, expert_offsets, pair_to_row,
+    row_to_pair, xq_rows, xs_rows).  ``events``: list of MOE_N_STAGES + 1
+    torch.cuda.Event (or None) recorded at the stage boundaries.  Returns
+    ``out`` (and the chosen kernel variant string when debug is given)."""
+    T, H = x.shape
+    dev = x.device
+    out = _empty((T, H), torch.bfloat16, dev) if out is None else out
+    nbytes = forward_workspace_size(T, top_k, routed, shared is not None)
+    if ws is None:
+        ws = _empty((nbytes,), torch.uint8, dev)
+    dbg = None
+    if debug is not None or events is not None:
+        dbg = MoeDebug()
+        for key, t in (debug or {}).items():
+            setattr(dbg, key, t.data_ptr())
+        for i, ev in enumerate(events or []):
+            if ev is not None:
+                dbg.events[i] = ev.cuda_event
+    check(lib().moe_forward(_p(x), _p(logits), T, top_k, routed.ref(), int(shared is not None),
+                            shared.ref() if shared is not None else None, _p(norm_gamma),
+                            float(norm_eps), _p(out), ctypes.byref(dbg) if dbg is not None else None,
+                            _p(ws), ws.numel(), _stream(stream)))
+    if debug is not None:
+        return out, dbg.variant.decode()
+    return out

@@ -1,0 +1,68 @@
+"""Builds libmoe.so (all HIP kernels + the C ABI) for gfx950 with hipcc.
+
+Objects go to _build/ next to this file; the shared library is written
+in-tree next to this file so that it travels with the source tree.
+"""
+
+import concurrent.futures
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+BUILD = os.path.join(HERE, "_build")
+LIB = os.path.join(HERE, "libmoe.so")
+SOURCES = ["route.hip", "permute.hip", "gemm.hip", "combine.hip", "moe_api.cpp"]
+ARCH = "gfx950"
+
+# -packed-fp32-ops: keep the compiler from forming packed fp32 instructions.
+# -disable-promote-alloca-to-lds: keep per-thread address arrays in registers
+# rather than moving them into LDS (which the GEMM tiles need).
+COMMON = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-disable-promote-alloca-to-lds",
+    "-Wno-unused-command-line-argument",
+    "-I", os.path.join(ROOT, "include"),
+]
+
+
+def hipcc():
+    path = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(path):
+        raise RuntimeError("hipcc not found")
+    return path
+
+
+def _compile(src):
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+    lang = ["-x", "hip"] if src.endswith(".hip") else []
+    cmd = [hipcc(), *COMMON, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
+    return obj
+
+
+def build(verbose=False):
+    """Compile every source and link libmoe.so (always rebuilds)."""
+    os.makedirs(BUILD, exist_ok=True)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+        objs = list(ex.map(_compile, SOURCES))
+    tmp = LIB + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, LIB)
+    if verbose:
+        print("built", LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose=True)
+    sys.exit(0)

@@ -1,0 +1,119 @@
+// Weighted gather of the expert outputs back into token order.
+//
+// The Ling-2.6-1T page, §1 (scatter -> local expert FFN -> gather results)
+// and §5 (the shared expert's output is added to the routed result); the
+// sglang-jax gap list, §8 (gather-reduce: a weighted reduction of each
+// token's top-k rows); the Kimi K3 page, §2.4 (routed_expert_norm: an RMSNorm
+// of the routed sum before the up-projection, with the shared experts on a
+// separate path).
+//
+// One workgroup per token.  Each thread owns CPT chunks of 8 channels, reads
+// the k expert rows with 16-byte loads (coalesced along the row), accumulates
+// w_j * y in fp32 in slot order, optionally normalises, adds the shared row
+// and stores bf16 (round to nearest even).
+#include <math.h>
+
+#include "device_common.h"
+#include "internal.h"
+
+namespace moe {
+
+template <int CPT>
+__global__ __launch_bounds__(1024) void combine_kernel(const uint16_t* __restrict__ y_rows,
+                                                       const int* __restrict__ pair_to_row,
+                                                       const float* __restrict__ topk_w, int H,
+                                                       int k, const uint16_t* __restrict__ y_shared,
+                                                       const float* __restrict__ gamma, float eps,
+                                                       uint16_t* __restrict__ out) {
+  __shared__ float red[16];
+  const long t = blockIdx.x;
+  const int nchk = H >> 3;
+  float acc[CPT][8];
+#pragma unroll
+  for (int c = 0; c < CPT; ++c)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[c][i] = 0.0f;
+
+  for (int j = 0; j < k; ++j) {
+    const int r = pair_to_row[t * k + j];
+    const float w = topk_w[t * k + j];
+    if (r < 0) continue;
+    const uint4* src = reinterpret_cast<const uint4*>(y_rows + (long)r * H);
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int idx = threadIdx.x + c * blockDim.x;
+      if (idx < nchk) {
+        const uint4 v = src[idx];
+        const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          acc[c][2 * q] += w * bf16_lo(wd[q]);
+          acc[c][2 * q + 1] += w * bf16_hi(wd[q]);
+        }
+      }
+    }
+  }
+
+  if (gamma) {
+    float ss = 0.0f;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ss += acc[c][i] * acc[c][i];
+    ss = block_sum(ss, red);
+    const float inv = 1.0f / sqrtf(ss / (float)H + eps);
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int idx = threadIdx.x + c * blockDim.x;
+      if (idx < nchk) {
+        const float4 g0 = reinterpret_cast<const float4*>(gamma)[2 * idx];
+        const float4 g1 = reinterpret_cast<const float4*>(gamma)[2 * idx + 1];
+        const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[c][i] = acc[c][i] * inv * g[i];
+      }
+    }
+  }
+
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) {
+    const int idx = threadIdx.x + c * blockDim.x;
+    if (idx >= nchk) continue;
+    if (y_shared) {
+      const uint4 v = reinterpret_cast<const uint4*>(y_shared + t * H)[idx];
+      const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc[c][2 * q] += bf16_lo(wd[q]);
+        acc[c][2 * q + 1] += bf16_hi(wd[q]);
+      }
+    }
+    uint32_t o[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) o[q] = bf16_rne(acc[c][2 * q]) | (bf16_rne(acc[c][2 * q + 1]) << 16);
+    reinterpret_cast<uint4*>(out + t * H)[idx] = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
+hipError_t launch_combine(const uint16_t* y_rows, const int* pair_to_row, const float* w, int T,
+                          int H, int k, const uint16_t* y_shared, const float* gamma, float eps,
+                          uint16_t* out, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  const int chunks = H / 8;
+  int cpt = 1;
+  while (chunks > 1024 * cpt) cpt *= 2;
+  int threads = (chunks + cpt - 1) / cpt;
+  threads = ((threads + 63) / 64) * 64;
+#define MOE_CB(C) \
+  combine_kernel<C><<<T, threads, 0, s>>>(y_rows, pair_to_row, w, H, k, y_shared, gamma, eps, out)
+  switch (cpt) {
+    case 1: MOE_CB(1); break;
+    case 2: MOE_CB(2); break;
+    case 4: MOE_CB(4); break;
+    default: MOE_CB(8); break;
+  }
+#undef MOE_CB
+  return hipGetLastError();
+}
+
+}  // namespace moe

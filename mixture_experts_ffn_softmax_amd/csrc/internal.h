@@ -1,0 +1,97 @@
+// Internal launch interface between the C ABI layer (moe_api.cpp) and the
+// kernels.  Every launcher enqueues on `stream`, never synchronises, and
+// returns hipGetLastError() of its launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxTopK = 32;
+constexpr int kPermuteChunk = 1024;  // pairs per counting / ranking chunk
+
+// ---- router ---------------------------------------------------------------
+hipError_t launch_route(const float* logits, int T, int E, int k, int* ids, float* w,
+                        hipStream_t s);
+
+// ---- counts, offsets, ranks, quantise + scatter ---------------------------
+inline int permute_chunks(long pairs) { return (int)((pairs + kPermuteChunk - 1) / kPermuteChunk); }
+
+// chunk_hist / chunk_base: int [chunks][E] each.  extra_rows > 0 appends one
+// group of that many rows after the E expert segments: offsets[E+1] =
+// offsets[E] + extra_rows (offsets must then hold E+2 ints).
+hipError_t launch_counts(const int* ids, int pairs, int E, int* chunk_hist, int* chunk_base,
+                         int* counts, int* offsets, int extra_rows, hipStream_t s);
+hipError_t launch_rank(const int* ids, int pairs, int E, const int* chunk_base, int* pair_to_row,
+                       int* row_to_pair, hipStream_t s);
+// Quantise each token and write its codes / scale to rows pair_to_row[t][*]
+// (skipped when negative) and, when xq_tok is non-NULL, to xq_tok[t] / xs_tok[t].
+hipError_t launch_quant_scatter(const uint16_t* x, int T, int H, int k, const int* pair_to_row,
+                                uint8_t* xq_rows, float* xs_rows, uint8_t* xq_tok, float* xs_tok,
+                                hipStream_t s);
+
+// ---- grouped expert FFN ---------------------------------------------------
+enum WeightFormat { kFp8 = 0, kMxfp4 = 1 };
+
+// One grouped GEMM launch covers groups 0..n_groups-1.  Rows of group g are
+// offsets[g] .. offsets[g+1]-1 of the row operand.  Groups g < n_routed take
+// their weights from the routed base pointers (expert g); group n_routed (if
+// n_groups > n_routed) from the shared base pointers.
+struct FfnGroups {
+  int fmt;            // WeightFormat (routed); the shared group is always fp8
+  int n_groups;
+  int n_routed;
+  int hidden;         // H
+  int inter;          // I
+  const int* offsets; // device [n_groups + 1]
+  // routed / shared weights (index 0 / 1)
+  const uint8_t* w1[2];
+  const uint8_t* w3[2];
+  const uint8_t* w2[2];
+  const void* s1[2];
+  const void* s3[2];
+  const void* s2[2];
+};
+
+// Row operand of a grouped GEMM: e4m3 codes and per-row scales.  Rows below
+// shared_row0 are read from q[0]/s[0] at their row index; the shared group's
+// rows from q[1]/s[1] at (row - shared_row0).
+struct RowOperand {
+  const uint8_t* q[2];
+  const float* s[2];
+  long shared_row0;
+};
+
+enum GemmVariant { kVariantLarge = 0, kVariantSmall = 1 };
+
+// Rows per tile of each variant.
+constexpr int kLargeBM = 128;
+constexpr int kSmallBM = 32;
+
+int choose_variant(const FfnGroups& g, long n_rows);
+long max_row_tiles(long n_rows, int n_groups, int bm);
+
+// tile_prefix[g] = sum over g' < g of ceil(rows(g') / bm); also zeroes
+// amax[0 .. n_rows).
+hipError_t launch_tile_prefix(const int* offsets, int n_groups, int bm, int* tile_prefix,
+                              uint32_t* amax, long n_rows, hipStream_t s);
+// GEMM1: h[r][n] = SiLU(g) * u for the gate/up pair, atomicMax of |h| into amax[r].
+hipError_t launch_gemm1(int variant, const FfnGroups& g, const RowOperand& x,
+                        const int* tile_prefix, long n_rows, float* h, uint32_t* amax,
+                        hipStream_t s);
+// hs[r] = amax[r] / 448 (1 if 0), hq[r] = e4m3(h[r] / hs[r]).
+hipError_t launch_quant_h(const float* h, const uint32_t* amax, long n_rows, int I, uint8_t* hq,
+                          float* hs, hipStream_t s);
+// GEMM2: y[r][j] = bf16((hq_r . W2[j]) * hs[r] * s2[j]).
+hipError_t launch_gemm2(int variant, const FfnGroups& g, const RowOperand& hq,
+                        const int* tile_prefix, long n_rows, uint16_t* y, hipStream_t s);
+
+// ---- combine --------------------------------------------------------------
+hipError_t launch_combine(const uint16_t* y_rows, const int* pair_to_row, const float* w, int T,
+                          int H, int k, const uint16_t* y_shared, const float* gamma, float eps,
+                          uint16_t* out, hipStream_t s);
+
+}  // namespace moe

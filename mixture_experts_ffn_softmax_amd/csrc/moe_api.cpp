@@ -1,0 +1,426 @@
+// C ABI of the routed MoE layer: argument validation, workspace carve-up and
+// launch sequencing.  Validation runs on the host before anything is
+// enqueued and touches no device state, so every error path can be exercised
+// without a GPU.  See include/moe.h for the contract of each entry point.
+#include "../../include/moe.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+moe_status_t fail(moe_status_t st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+moe_status_t ok() {
+  g_last_error.clear();
+  return MOE_OK;
+}
+
+moe_status_t device_status(hipError_t e, const char* where) {
+  if (e == hipSuccess) return ok();
+  return fail(MOE_ERR_DEVICE, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr int kMaxDim = 65536;
+
+// Validation helpers return MOE_OK or the first failing status.
+#define MOE_CHECK(expr)                 \
+  do {                                  \
+    const moe_status_t st_ = (expr);    \
+    if (st_ != MOE_OK) return st_;      \
+  } while (0)
+
+moe_status_t need(const void* p, const char* name) {
+  if (!p) return fail(MOE_ERR_NULL, "%s is NULL", name);
+  if (!aligned16(p)) return fail(MOE_ERR_ALIGN, "%s is not 16-byte aligned", name);
+  return MOE_OK;
+}
+
+moe_status_t opt(const void* p, const char* name) {
+  if (p && !aligned16(p)) return fail(MOE_ERR_ALIGN, "%s is not 16-byte aligned", name);
+  return MOE_OK;
+}
+
+moe_status_t check_route_shape(int32_t T, int32_t E, int32_t k) {
+  if (T < 0) return fail(MOE_ERR_SHAPE, "T = %d < 0", T);
+  if (E < 1 || E > moe::kMaxExperts) return fail(MOE_ERR_SHAPE, "E = %d outside [1, %d]", E, moe::kMaxExperts);
+  if (k < 1 || k > E || k > moe::kMaxTopK)
+    return fail(MOE_ERR_SHAPE, "top_k = %d outside [1, min(E=%d, %d)]", k, E, moe::kMaxTopK);
+  if ((int64_t)T * k >= (int64_t)1 << 31) return fail(MOE_ERR_SHAPE, "T * top_k overflows int32");
+  return MOE_OK;
+}
+
+moe_status_t check_dim(int32_t v, const char* name) {
+  if (v < 128 || v > kMaxDim || v % 128 != 0)
+    return fail(MOE_ERR_SHAPE, "%s = %d is not a multiple of 128 in [128, %d]", name, v, kMaxDim);
+  return MOE_OK;
+}
+
+moe_status_t check_weights(const moe_weights_t* w, const char* name) {
+  if (!w) return fail(MOE_ERR_NULL, "%s is NULL", name);
+  if (w->fmt != MOE_W_FP8_E4M3_PERCHANNEL && w->fmt != MOE_W_MXFP4_E2M1_E8M0_G32)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: unknown weight format %d", name, w->fmt);
+  if (w->n_experts < 1 || w->n_experts > moe::kMaxExperts)
+    return fail(MOE_ERR_SHAPE, "%s: n_experts = %d outside [1, %d]", name, w->n_experts, moe::kMaxExperts);
+  MOE_CHECK(check_dim(w->hidden, "hidden"));
+  MOE_CHECK(check_dim(w->inter, "inter"));
+  MOE_CHECK(need(w->w1, "w1"));
+  MOE_CHECK(need(w->w3, "w3"));
+  MOE_CHECK(need(w->w2, "w2"));
+  MOE_CHECK(need(w->s1, "s1"));
+  MOE_CHECK(need(w->s3, "s3"));
+  MOE_CHECK(need(w->s2, "s2"));
+  return MOE_OK;
+}
+
+// Bump allocator over the caller's workspace: 256-byte aligned slices.
+struct Carve {
+  uint8_t* base;
+  size_t used = 0;
+  explicit Carve(void* b) : base(static_cast<uint8_t*>(b)) {}
+  template <class T>
+  T* take(size_t count) {
+    used = (used + 255) & ~size_t(255);
+    T* p = base ? reinterpret_cast<T*>(base + used) : nullptr;
+    used += count * sizeof(T);
+    return p;
+  }
+};
+
+size_t ffn_ws(Carve& c, long n_rows, int n_groups, int inter, int32_t** tile_prefix, uint32_t** amax,
+              float** h, uint8_t** hq, float** hs) {
+  *tile_prefix = c.take<int32_t>(n_groups + 1);
+  *amax = c.take<uint32_t>(n_rows);
+  *h = c.take<float>((size_t)n_rows * inter);
+  *hq = c.take<uint8_t>((size_t)n_rows * inter);
+  *hs = c.take<float>(n_rows);
+  return c.used;
+}
+
+moe::FfnGroups make_groups(const moe_weights_t* r, const moe_weights_t* sh, const int32_t* offsets) {
+  moe::FfnGroups g{};
+  g.fmt = r->fmt == MOE_W_MXFP4_E2M1_E8M0_G32 ? moe::kMxfp4 : moe::kFp8;
+  g.n_routed = r->n_experts;
+  g.n_groups = r->n_experts + (sh ? 1 : 0);
+  g.hidden = r->hidden;
+  g.inter = r->inter;
+  g.offsets = offsets;
+  const moe_weights_t* src[2] = {r, sh ? sh : r};
+  for (int i = 0; i < 2; ++i) {
+    g.w1[i] = src[i]->w1;
+    g.w3[i] = src[i]->w3;
+    g.w2[i] = src[i]->w2;
+    g.s1[i] = src[i]->s1;
+    g.s3[i] = src[i]->s3;
+    g.s2[i] = src[i]->s2;
+  }
+  return g;
+}
+
+// GEMM1 -> quantise h -> GEMM2 over the groups of `g`.
+moe_status_t run_ffn(const moe::FfnGroups& g, const moe::RowOperand& x, long n_rows, uint16_t* y,
+                     int32_t* tile_prefix, uint32_t* amax, float* h, uint8_t* hq, float* hs,
+                     hipStream_t s, void* const* events, char* variant_out, size_t variant_len) {
+  const int variant = moe::choose_variant(g, n_rows);
+  const int bm = variant == moe::kVariantLarge ? moe::kLargeBM : moe::kSmallBM;
+  if (variant_out)
+    snprintf(variant_out, variant_len, "%s/%s", variant == moe::kVariantLarge ? "large128" : "small32",
+             g.fmt == moe::kMxfp4 ? "mxfp4" : "fp8");
+  hipError_t e;
+  e = moe::launch_tile_prefix(g.offsets, g.n_groups, bm, tile_prefix, amax, n_rows, s);
+  if (e != hipSuccess) return device_status(e, "tile_prefix");
+  if (events && events[MOE_STAGE_GEMM1]) hipEventRecord((hipEvent_t)events[MOE_STAGE_GEMM1], s);
+  e = moe::launch_gemm1(variant, g, x, tile_prefix, n_rows, h, amax, s);
+  if (e != hipSuccess) return device_status(e, "gemm1");
+  if (events && events[MOE_STAGE_QUANT_H]) hipEventRecord((hipEvent_t)events[MOE_STAGE_QUANT_H], s);
+  e = moe::launch_quant_h(h, amax, n_rows, g.inter, hq, hs, s);
+  if (e != hipSuccess) return device_status(e, "quant_h");
+  if (events && events[MOE_STAGE_GEMM2]) hipEventRecord((hipEvent_t)events[MOE_STAGE_GEMM2], s);
+  moe::RowOperand hrows{{hq, hq + (size_t)x.shared_row0 * g.inter}, {hs, hs + x.shared_row0}, x.shared_row0};
+  e = moe::launch_gemm2(variant, g, hrows, tile_prefix, n_rows, y, s);
+  if (e != hipSuccess) return device_status(e, "gemm2");
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_version(void) { return "moe-mi355x 0.1 (gfx950)"; }
+
+const char* moe_status_string(moe_status_t s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_NULL: return "a required pointer is NULL";
+    case MOE_ERR_SHAPE: return "a size is out of range or inconsistent";
+    case MOE_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case MOE_ERR_WORKSPACE: return "the workspace is too small";
+    case MOE_ERR_UNSUPPORTED: return "no kernel exists for this case";
+    case MOE_ERR_DEVICE: return "the HIP runtime reported an error";
+  }
+  return "unknown status";
+}
+
+const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+// ---------------------------------------------------------------------------
+moe_status_t moe_route(const float* logits, int32_t T, int32_t E, int32_t top_k, int32_t* topk_ids,
+                       float* topk_w, void* stream) {
+  MOE_CHECK(check_route_shape(T, E, top_k));
+  if (T == 0) return ok();
+  MOE_CHECK(need(logits, "logits"));
+  MOE_CHECK(need(topk_ids, "topk_ids"));
+  MOE_CHECK(need(topk_w, "topk_w"));
+  return device_status(moe::launch_route(logits, T, E, top_k, topk_ids, topk_w, (hipStream_t)stream),
+                       "route");
+}
+
+// ---------------------------------------------------------------------------
+size_t moe_permute_workspace_size(int32_t T, int32_t top_k, int32_t E) {
+  if (T < 0 || top_k < 1 || E < 1) return 0;
+  Carve c(nullptr);
+  const long chunks = moe::permute_chunks((long)T * top_k);
+  c.take<int32_t>(chunks * E);
+  c.take<int32_t>(chunks * E);
+  return c.used + 256;
+}
+
+moe_status_t moe_permute(const uint16_t* x, int32_t T, int32_t H, const int32_t* topk_ids,
+                         int32_t top_k, int32_t E, int32_t* expert_counts, int32_t* expert_offsets,
+                         int32_t* pair_to_row, int32_t* row_to_pair, uint8_t* xq_rows, float* xs_rows,
+                         uint8_t* xq_tok, float* xs_tok, void* ws, size_t ws_bytes, void* stream) {
+  MOE_CHECK(check_route_shape(T, E, top_k));
+  MOE_CHECK(check_dim(H, "H"));
+  MOE_CHECK(need(expert_counts, "expert_counts"));
+  MOE_CHECK(need(expert_offsets, "expert_offsets"));
+  if ((xq_tok == nullptr) != (xs_tok == nullptr))
+    return fail(MOE_ERR_NULL, "xq_tok and xs_tok must both be set or both be NULL");
+  if (T > 0) {
+    MOE_CHECK(need(x, "x"));
+    MOE_CHECK(need(topk_ids, "topk_ids"));
+    MOE_CHECK(need(pair_to_row, "pair_to_row"));
+    MOE_CHECK(need(row_to_pair, "row_to_pair"));
+    MOE_CHECK(need(xq_rows, "xq_rows"));
+    MOE_CHECK(need(xs_rows, "xs_rows"));
+    MOE_CHECK(opt(xq_tok, "xq_tok"));
+    MOE_CHECK(opt(xs_tok, "xs_tok"));
+  }
+  const size_t need_ws = moe_permute_workspace_size(T, top_k, E);
+  if (!ws || ws_bytes < need_ws)
+    return fail(MOE_ERR_WORKSPACE, "workspace %zu B < %zu B", ws ? ws_bytes : 0, need_ws);
+  MOE_CHECK(need(ws, "ws"));
+  hipStream_t s = (hipStream_t)stream;
+  const long pairs = (long)T * top_k;
+  const long chunks = moe::permute_chunks(pairs);
+  Carve c(ws);
+  int32_t* hist = c.take<int32_t>(chunks * E);
+  int32_t* base = c.take<int32_t>(chunks * E);
+  hipError_t e = moe::launch_counts(topk_ids, (int)pairs, E, hist, base, expert_counts,
+                                    expert_offsets, 0, s);
+  if (e != hipSuccess) return device_status(e, "counts");
+  if (T == 0) return ok();
+  e = moe::launch_rank(topk_ids, (int)pairs, E, base, pair_to_row, row_to_pair, s);
+  if (e != hipSuccess) return device_status(e, "rank");
+  e = moe::launch_quant_scatter(x, T, H, top_k, pair_to_row, xq_rows, xs_rows, xq_tok, xs_tok, s);
+  return device_status(e, "quant_scatter");
+}
+
+// ---------------------------------------------------------------------------
+size_t moe_expert_ffn_workspace_size(int32_t n_rows, const moe_weights_t* w) {
+  if (!w || n_rows < 0 || w->n_experts < 1 || w->inter < 1) return 0;
+  Carve c(nullptr);
+  int32_t* tp;
+  uint32_t* am;
+  float *h, *hs;
+  uint8_t* hq;
+  return ffn_ws(c, n_rows, w->n_experts, w->inter, &tp, &am, &h, &hq, &hs) + 256;
+}
+
+moe_status_t moe_expert_ffn(const uint8_t* xq_rows, const float* xs_rows, int32_t n_rows,
+                            const int32_t* expert_offsets, const moe_weights_t* w, uint16_t* y_rows,
+                            void* ws, size_t ws_bytes, void* stream) {
+  MOE_CHECK(check_weights(w, "weights"));
+  if (n_rows < 0) return fail(MOE_ERR_SHAPE, "n_rows = %d < 0", n_rows);
+  if (n_rows == 0) return ok();
+  MOE_CHECK(need(xq_rows, "xq_rows"));
+  MOE_CHECK(need(xs_rows, "xs_rows"));
+  MOE_CHECK(need(expert_offsets, "expert_offsets"));
+  MOE_CHECK(need(y_rows, "y_rows"));
+  const size_t need_ws = moe_expert_ffn_workspace_size(n_rows, w);
+  if (!ws || ws_bytes < need_ws)
+    return fail(MOE_ERR_WORKSPACE, "workspace %zu B < %zu B", ws ? ws_bytes : 0, need_ws);
+  MOE_CHECK(need(ws, "ws"));
+  Carve c(ws);
+  int32_t* tp;
+  uint32_t* am;
+  float *h, *hs;
+  uint8_t* hq;
+  ffn_ws(c, n_rows, w->n_experts, w->inter, &tp, &am, &h, &hq, &hs);
+  const moe::FfnGroups g = make_groups(w, nullptr, expert_offsets);
+  moe::RowOperand x{{xq_rows, xq_rows}, {xs_rows, xs_rows}, (long)n_rows};
+  return run_ffn(g, x, n_rows, y_rows, tp, am, h, hq, hs, (hipStream_t)stream, nullptr, nullptr, 0);
+}
+
+// ---------------------------------------------------------------------------
+moe_status_t moe_combine(const uint16_t* y_rows, const int32_t* pair_to_row, const float* topk_w,
+                         int32_t T, int32_t H, int32_t top_k, const uint16_t* y_shared,
+                         const float* norm_gamma, float norm_eps, uint16_t* out, void* stream) {
+  if (T < 0) return fail(MOE_ERR_SHAPE, "T = %d < 0", T);
+  if (top_k < 1 || top_k > moe::kMaxTopK) return fail(MOE_ERR_SHAPE, "top_k = %d outside [1, %d]", top_k, moe::kMaxTopK);
+  MOE_CHECK(check_dim(H, "H"));
+  if (norm_gamma && !(norm_eps >= 0.0f)) return fail(MOE_ERR_SHAPE, "norm_eps must be >= 0");
+  if (T == 0) return ok();
+  MOE_CHECK(need(y_rows, "y_rows"));
+  MOE_CHECK(need(pair_to_row, "pair_to_row"));
+  MOE_CHECK(need(topk_w, "topk_w"));
+  MOE_CHECK(need(out, "out"));
+  MOE_CHECK(opt(y_shared, "y_shared"));
+  MOE_CHECK(opt(norm_gamma, "norm_gamma"));
+  return device_status(moe::launch_combine(y_rows, pair_to_row, topk_w, T, H, top_k, y_shared, norm_gamma,
+                                           norm_eps, out, (hipStream_t)stream),
+                       "combine");
+}
+
+// ---------------------------------------------------------------------------
+struct ForwardLayout {
+  int32_t *ids, *counts, *offsets, *p2r, *r2p, *hist, *base, *tile_prefix;
+  float *w, *xs_rows, *xs_tok, *h, *hs;
+  uint8_t *xq_rows, *xq_tok, *hq;
+  uint32_t* amax;
+  uint16_t* y_rows;
+  size_t bytes;
+};
+
+static ForwardLayout forward_layout(void* ws, int32_t T, int32_t k, int32_t E, int32_t H, int32_t I,
+                                    bool shared) {
+  ForwardLayout L{};
+  Carve c(ws);
+  const long R = (long)T * k;
+  const long rows = R + (shared ? T : 0);
+  const long chunks = moe::permute_chunks(R);
+  L.ids = c.take<int32_t>(R);
+  L.w = c.take<float>(R);
+  L.counts = c.take<int32_t>(E);
+  L.offsets = c.take<int32_t>(E + 2);
+  L.p2r = c.take<int32_t>(R);
+  L.r2p = c.take<int32_t>(R);
+  L.hist = c.take<int32_t>(chunks * E);
+  L.base = c.take<int32_t>(chunks * E);
+  L.xq_rows = c.take<uint8_t>((size_t)R * H);
+  L.xs_rows = c.take<float>(R);
+  L.xq_tok = shared ? c.take<uint8_t>((size_t)T * H) : nullptr;
+  L.xs_tok = shared ? c.take<float>(T) : nullptr;
+  L.y_rows = c.take<uint16_t>((size_t)rows * H);
+  ffn_ws(c, rows, E + (shared ? 1 : 0), I, &L.tile_prefix, &L.amax, &L.h, &L.hq, &L.hs);
+  L.bytes = c.used + 256;
+  return L;
+}
+
+size_t moe_forward_workspace_size(int32_t T, int32_t top_k, const moe_weights_t* routed, int32_t use_shared) {
+  if (!routed || T < 0 || top_k < 1 || routed->n_experts < 1) return 0;
+  return forward_layout(nullptr, T, top_k, routed->n_experts, routed->hidden, routed->inter, use_shared != 0)
+      .bytes;
+}
+
+moe_status_t moe_forward(const uint16_t* x, const float* logits, int32_t T, int32_t top_k,
+                         const moe_weights_t* routed, int32_t use_shared, const moe_weights_t* shared,
+                         const float* norm_gamma, float norm_eps, uint16_t* out, moe_debug_t* dbg,
+                         void* ws, size_t ws_bytes, void* stream) {
+  MOE_CHECK(check_weights(routed, "routed"));
+  const int32_t E = routed->n_experts, H = routed->hidden, I = routed->inter;
+  MOE_CHECK(check_route_shape(T, E, top_k));
+  if (use_shared) {
+    MOE_CHECK(check_weights(shared, "shared"));
+    if (shared->n_experts != 1) return fail(MOE_ERR_SHAPE, "shared expert must have n_experts = 1");
+    if (shared->hidden != H || shared->inter != I)
+      return fail(MOE_ERR_UNSUPPORTED, "shared expert shape %dx%d differs from routed %dx%d",
+                  shared->hidden, shared->inter, H, I);
+    if (shared->fmt != MOE_W_FP8_E4M3_PERCHANNEL)
+      return fail(MOE_ERR_UNSUPPORTED, "shared expert must use per-channel fp8 weights");
+    if (E + 1 > moe::kMaxExperts)
+      return fail(MOE_ERR_UNSUPPORTED, "with a shared expert E must be at most %d", moe::kMaxExperts - 1);
+  }
+  if (norm_gamma && !(norm_eps >= 0.0f)) return fail(MOE_ERR_SHAPE, "norm_eps must be >= 0");
+  if (T == 0) return ok();
+  MOE_CHECK(need(x, "x"));
+  MOE_CHECK(need(logits, "logits"));
+  MOE_CHECK(need(out, "out"));
+  MOE_CHECK(opt(norm_gamma, "norm_gamma"));
+  if (dbg) {
+    MOE_CHECK(opt(dbg->topk_ids, "dbg.topk_ids"));
+    MOE_CHECK(opt(dbg->topk_w, "dbg.topk_w"));
+    MOE_CHECK(opt(dbg->expert_counts, "dbg.expert_counts"));
+    MOE_CHECK(opt(dbg->expert_offsets, "dbg.expert_offsets"));
+    MOE_CHECK(opt(dbg->pair_to_row, "dbg.pair_to_row"));
+    MOE_CHECK(opt(dbg->row_to_pair, "dbg.row_to_pair"));
+    MOE_CHECK(opt(dbg->xq_rows, "dbg.xq_rows"));
+    MOE_CHECK(opt(dbg->xs_rows, "dbg.xs_rows"));
+  }
+  const bool sh = use_shared != 0;
+  const size_t need_ws = moe_forward_workspace_size(T, top_k, routed, use_shared);
+  if (!ws || ws_bytes < need_ws)
+    return fail(MOE_ERR_WORKSPACE, "workspace %zu B < %zu B", ws ? ws_bytes : 0, need_ws);
+  MOE_CHECK(need(ws, "ws"));
+
+  ForwardLayout L = forward_layout(ws, T, top_k, E, H, I, sh);
+  void* const* ev = dbg ? dbg->events : nullptr;
+  if (dbg) {
+    if (dbg->topk_ids) L.ids = dbg->topk_ids;
+    if (dbg->topk_w) L.w = dbg->topk_w;
+    if (dbg->expert_counts) L.counts = dbg->expert_counts;
+    if (dbg->expert_offsets) L.offsets = dbg->expert_offsets;
+    if (dbg->pair_to_row) L.p2r = dbg->pair_to_row;
+    if (dbg->row_to_pair) L.r2p = dbg->row_to_pair;
+    if (dbg->xq_rows) L.xq_rows = dbg->xq_rows;
+    if (dbg->xs_rows) L.xs_rows = dbg->xs_rows;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  const long R = (long)T * top_k;
+  hipError_t e;
+
+  if (ev && ev[MOE_STAGE_ROUTE]) hipEventRecord((hipEvent_t)ev[MOE_STAGE_ROUTE], s);
+  e = moe::launch_route(logits, T, E, top_k, L.ids, L.w, s);
+  if (e != hipSuccess) return device_status(e, "route");
+
+  if (ev && ev[MOE_STAGE_PERMUTE]) hipEventRecord((hipEvent_t)ev[MOE_STAGE_PERMUTE], s);
+  e = moe::launch_counts(L.ids, (int)R, E, L.hist, L.base, L.counts, L.offsets, sh ? T : 0, s);
+  if (e != hipSuccess) return device_status(e, "counts");
+  e = moe::launch_rank(L.ids, (int)R, E, L.base, L.p2r, L.r2p, s);
+  if (e != hipSuccess) return device_status(e, "rank");
+  e = moe::launch_quant_scatter(x, T, H, top_k, L.p2r, L.xq_rows, L.xs_rows, L.xq_tok, L.xs_tok, s);
+  if (e != hipSuccess) return device_status(e, "quant_scatter");
+
+  const moe::FfnGroups g = make_groups(routed, sh ? shared : nullptr, L.offsets);
+  const long rows = R + (sh ? T : 0);
+  moe::RowOperand xr{{L.xq_rows, sh ? L.xq_tok : L.xq_rows}, {L.xs_rows, sh ? L.xs_tok : L.xs_rows}, R};
+  char* vout = dbg ? dbg->variant : nullptr;
+  MOE_CHECK(run_ffn(g, xr, rows, L.y_rows, L.tile_prefix, L.amax, L.h, L.hq, L.hs, s, ev, vout,
+                    dbg ? sizeof(dbg->variant) : 0));
+
+  if (ev && ev[MOE_STAGE_COMBINE]) hipEventRecord((hipEvent_t)ev[MOE_STAGE_COMBINE], s);
+  e = moe::launch_combine(L.y_rows, L.p2r, L.w, T, H, top_k, sh ? L.y_rows + (size_t)R * H : nullptr,
+                          norm_gamma, norm_eps, out, s);
+  if (e != hipSuccess) return device_status(e, "combine");
+  if (ev && ev[MOE_N_STAGES]) hipEventRecord((hipEvent_t)ev[MOE_N_STAGES], s);
+  return ok();
+}
+
+}  // extern "C"

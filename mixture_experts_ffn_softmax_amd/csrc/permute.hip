@@ -1,0 +1,239 @@
+// Routing metadata and the scatter of token rows to experts.
+//
+// The Ling-2.6-1T page (§1: scatter tokens -> local expert FFN -> gather
+// results; §6: the metadata block of token-to-expert map, per-expert
+// offsets/counts and scatter/gather indices) and its §5 (tokens quantised to
+// fp8 per token before the scatter).
+//
+// Pairs p = t*k + j are cut into chunks of kPermuteChunk.  Kernels:
+//   hist_kernel    per-chunk expert histograms (LDS atomics: counts only, so
+//                  the result does not depend on their order)
+//   scan_kernel    per-expert totals, exclusive offsets, and per-(chunk,
+//                  expert) starting rows, expert-major then chunk-minor
+//   rank_kernel    stable rank of each pair inside its chunk, by wave ballots
+//                  in pair order -> pair_to_row / row_to_pair
+//   quant_scatter  per token: amax, scale, e4m3 codes, written to each of the
+//                  token's rows (and optionally in token order)
+// Rows are ordered by expert and, inside an expert, by pair index; this order
+// is unique, so the result is deterministic.  Expert ids outside [0, E) are
+// skipped (their pairs get row -1) so that no access leaves its buffer.
+#include "device_common.h"
+#include "internal.h"
+
+namespace moe {
+
+__global__ __launch_bounds__(256) void hist_kernel(const int* __restrict__ ids, int pairs, int E,
+                                                   int* __restrict__ chunk_hist) {
+  __shared__ int h[kMaxExperts];
+  for (int e = threadIdx.x; e < E; e += 256) h[e] = 0;
+  __syncthreads();
+  const long base = (long)blockIdx.x * kPermuteChunk;
+  for (int i = threadIdx.x; i < kPermuteChunk; i += 256) {
+    const long p = base + i;
+    if (p < pairs) {
+      const int e = ids[p];
+      if ((unsigned)e < (unsigned)E) atomicAdd(&h[e], 1);
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += 256) chunk_hist[(long)blockIdx.x * E + e] = h[e];
+}
+
+// One block of 1024 threads; thread e owns expert e.
+__global__ __launch_bounds__(1024) void scan_kernel(const int* __restrict__ chunk_hist, int chunks,
+                                                    int E, int* __restrict__ chunk_base,
+                                                    int* __restrict__ counts,
+                                                    int* __restrict__ offsets, int extra_rows) {
+  __shared__ int off[kMaxExperts];
+  __shared__ int tmp[16];
+  const int e = threadIdx.x;
+  int total = 0;
+  if (e < E) {
+    int c = 0;
+    for (; c + 4 <= chunks; c += 4) {
+      const int a0 = chunk_hist[(long)(c + 0) * E + e];
+      const int a1 = chunk_hist[(long)(c + 1) * E + e];
+      const int a2 = chunk_hist[(long)(c + 2) * E + e];
+      const int a3 = chunk_hist[(long)(c + 3) * E + e];
+      total += a0 + a1 + a2 + a3;
+    }
+    for (; c < chunks; ++c) total += chunk_hist[(long)c * E + e];
+    off[e] = total;
+  }
+  __syncthreads();
+  const int all = block_exclusive_scan_1024(off, tmp, E);
+  if (e < E) {
+    counts[e] = total;
+    offsets[e] = off[e];
+    int run = off[e];
+    for (int c = 0; c < chunks; ++c) {
+      const int n = chunk_hist[(long)c * E + e];
+      chunk_base[(long)c * E + e] = run;
+      run += n;
+    }
+  }
+  if (e == 0) {
+    offsets[E] = all;
+    if (extra_rows > 0) offsets[E + 1] = all + extra_rows;
+  }
+}
+
+// Block of 256 threads = 4 waves per chunk of 1024 pairs; wave w ranks pairs
+// [w*256, w*256+256) of the chunk in four windows of 64, in order.
+__global__ __launch_bounds__(256) void rank_kernel(const int* __restrict__ ids, int pairs, int E,
+                                                   const int* __restrict__ chunk_base,
+                                                   int* __restrict__ pair_to_row,
+                                                   int* __restrict__ row_to_pair) {
+  __shared__ int cnt[4][kMaxExperts];
+  const int w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const long cbase = (long)blockIdx.x * kPermuteChunk;
+  for (int i = threadIdx.x; i < 4 * E; i += 256) cnt[i / E][i % E] = 0;
+  __syncthreads();
+  int my_e[4];
+#pragma unroll
+  for (int win = 0; win < 4; ++win) {
+    const long p = cbase + w * 256 + win * 64 + lane;
+    int e = -1;
+    if (p < pairs) {
+      e = ids[p];
+      if ((unsigned)e >= (unsigned)E) e = -1;
+    }
+    my_e[win] = e;
+    if (e >= 0) atomicAdd(&cnt[w][e], 1);
+  }
+  __syncthreads();
+  // per-wave starting rows: chunk base plus the counts of the earlier waves
+  for (int e = threadIdx.x; e < E; e += 256) {
+    int run = chunk_base[(long)blockIdx.x * E + e];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int n = cnt[q][e];
+      cnt[q][e] = run;
+      run += n;
+    }
+  }
+  __syncthreads();
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+#pragma unroll
+  for (int win = 0; win < 4; ++win) {
+    const long p = cbase + w * 256 + win * 64 + lane;
+    const int e = my_e[win];
+    uint64_t pending = __ballot(e >= 0);
+    int row = -1;
+    while (pending) {
+      const int leader = __ffsll((unsigned long long)pending) - 1;
+      const int el = __builtin_amdgcn_readlane(e, leader);
+      const uint64_t same = __ballot(e == el) & pending;
+      if (e == el) row = cnt[w][el] + __popcll(same & lt_mask);
+      __builtin_amdgcn_wave_barrier();
+      if (lane == leader) cnt[w][el] += __popcll(same);
+      __builtin_amdgcn_wave_barrier();
+      pending &= ~same;
+    }
+    if (p < pairs) {
+      pair_to_row[p] = row;
+      if (row >= 0) row_to_pair[row] = (int)p;
+    }
+  }
+}
+
+// One block per token.  The row is nchk chunks of 8 bf16; thread i handles
+// chunks i, i + blockDim, ..., (CPT of them, some possibly past nchk).
+// blockDim is a multiple of 64 so that the wave reductions see full waves.
+template <int CPT>
+__global__ __launch_bounds__(1024) void quant_scatter_kernel(
+    const uint16_t* __restrict__ x, int H, int k, const int* __restrict__ pair_to_row,
+    uint8_t* __restrict__ xq_rows, float* __restrict__ xs_rows, uint8_t* __restrict__ xq_tok,
+    float* __restrict__ xs_tok) {
+  __shared__ float red[16];
+  const long t = blockIdx.x;
+  const int nchk = H >> 3;
+  const uint4* src = reinterpret_cast<const uint4*>(x + t * H);
+  uint4 in[CPT];
+  float amax = 0.0f;
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) {
+    const int idx = threadIdx.x + c * blockDim.x;
+    in[c] = (idx < nchk) ? src[idx] : make_uint4(0, 0, 0, 0);
+    const uint32_t wds[4] = {in[c].x, in[c].y, in[c].z, in[c].w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(wds[q])), fabsf(bf16_hi(wds[q]))));
+  }
+  amax = block_max(amax, red);
+  const float s = (amax == 0.0f) ? 1.0f : amax / kE4M3Max;
+  uint2 q8[CPT];
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) {
+    const uint32_t wds[4] = {in[c].x, in[c].y, in[c].z, in[c].w};
+    uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t lo = e4m3_encode(bf16_lo(wds[q]) / s);
+      const uint32_t hi = e4m3_encode(bf16_hi(wds[q]) / s);
+      packed[q >> 1] |= (lo | (hi << 8)) << ((q & 1) * 16);
+    }
+    q8[c] = make_uint2(packed[0], packed[1]);
+  }
+  for (int j = 0; j < k; ++j) {
+    const int r = pair_to_row[t * k + j];
+    if (r < 0) continue;
+    uint2* dst = reinterpret_cast<uint2*>(xq_rows + (long)r * H);
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int idx = threadIdx.x + c * blockDim.x;
+      if (idx < nchk) dst[idx] = q8[c];
+    }
+    if (threadIdx.x == 0) xs_rows[r] = s;
+  }
+  if (xq_tok) {
+    uint2* dst = reinterpret_cast<uint2*>(xq_tok + t * H);
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int idx = threadIdx.x + c * blockDim.x;
+      if (idx < nchk) dst[idx] = q8[c];
+    }
+    if (threadIdx.x == 0) xs_tok[t] = s;
+  }
+}
+
+hipError_t launch_counts(const int* ids, int pairs, int E, int* chunk_hist, int* chunk_base,
+                         int* counts, int* offsets, int extra_rows, hipStream_t s) {
+  const int chunks = permute_chunks(pairs);
+  if (chunks > 0) hist_kernel<<<chunks, 256, 0, s>>>(ids, pairs, E, chunk_hist);
+  scan_kernel<<<1, 1024, 0, s>>>(chunk_hist, chunks, E, chunk_base, counts, offsets, extra_rows);
+  return hipGetLastError();
+}
+
+hipError_t launch_rank(const int* ids, int pairs, int E, const int* chunk_base, int* pair_to_row,
+                       int* row_to_pair, hipStream_t s) {
+  const int chunks = permute_chunks(pairs);
+  if (chunks > 0)
+    rank_kernel<<<chunks, 256, 0, s>>>(ids, pairs, E, chunk_base, pair_to_row, row_to_pair);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_scatter(const uint16_t* x, int T, int H, int k, const int* pair_to_row,
+                                uint8_t* xq_rows, float* xs_rows, uint8_t* xq_tok, float* xs_tok,
+                                hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  const int chunks = H / 8;  // H is a multiple of 128: chunks is a multiple of 16
+  int cpt = 1;
+  while (chunks > 1024 * cpt) cpt *= 2;
+  int threads = (chunks + cpt - 1) / cpt;
+  threads = ((threads + 63) / 64) * 64;
+#define MOE_QS(C)                                                                          \
+  quant_scatter_kernel<C><<<T, threads, 0, s>>>(x, H, k, pair_to_row, xq_rows, xs_rows, xq_tok, \
+                                                xs_tok)
+  switch (cpt) {
+    case 1: MOE_QS(1); break;
+    case 2: MOE_QS(2); break;
+    case 4: MOE_QS(4); break;
+    default: MOE_QS(8); break;
+  }
+#undef MOE_QS
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,87 @@
+// Softmax router with top-k selection: one wavefront per token.
+//
+// The k experts with the largest logits are chosen in k rounds of a
+// wave-wide arg-max over the key (logit, -expert index), so equal logits go
+// to the lower index and the slots come out in descending order.  The raw
+// fp32 logits decide the selection, which therefore does not depend on the
+// rounding of exp.  Weights: w_j = exp(l_j - l_max) / sum_sel exp(l - l_max),
+// which equals p_j / sum_sel p for p = softmax over all experts.
+// Top-8 of 256 routed experts on the Ling-2.6-1T page (overview, §1 cost
+// model); renormalised top-k weights on the Kimi K3 page, §2.4.
+#include <math.h>
+
+#include "device_common.h"
+#include "internal.h"
+
+namespace moe {
+
+constexpr int kRouteSlots = kMaxExperts / 64;  // logits held per lane
+
+__device__ __forceinline__ bool route_better(float va, int ia, float vb, int ib) {
+  return va > vb || (va == vb && ia < ib);
+}
+
+__global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ logits, int T, int E,
+                                                    int k, int* __restrict__ ids,
+                                                    float* __restrict__ w) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const float* row = logits + (size_t)t * E;
+  const int slots = (E + 63) >> 6;
+
+  float v[kRouteSlots];
+  uint32_t avail = 0;
+#pragma unroll
+  for (int i = 0; i < kRouteSlots; ++i) {
+    const int e = i * 64 + lane;
+    const bool ok = (i < slots) && (e < E);
+    v[i] = ok ? row[e] : 0.0f;
+    avail |= ok ? (1u << i) : 0u;
+  }
+
+  float vmax = 0.0f, sum = 0.0f, mine = 0.0f;
+  int my_id = 0;
+  for (int j = 0; j < k; ++j) {
+    float bv = -INFINITY;
+    int bi = 0x7FFFFFFF;
+#pragma unroll
+    for (int i = 0; i < kRouteSlots; ++i) {
+      const int e = i * 64 + lane;
+      if (((avail >> i) & 1u) && route_better(v[i], e, bv, bi)) {
+        bv = v[i];
+        bi = e;
+      }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float ov = __shfl_xor(bv, off);
+      const int oi = __shfl_xor(bi, off);
+      if (route_better(ov, oi, bv, bi)) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    if ((bi & 63) == lane) avail &= ~(1u << (bi >> 6));
+    if (j == 0) vmax = bv;
+    const float ex = expf(bv - vmax);
+    sum += ex;
+    if (lane == j) {
+      my_id = bi;
+      mine = ex;
+    }
+  }
+  if (lane < k) {
+    ids[(size_t)t * k + lane] = my_id;
+    w[(size_t)t * k + lane] = mine / sum;
+  }
+}
+
+hipError_t launch_route(const float* logits, int T, int E, int k, int* ids, float* w,
+                        hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  route_kernel<<<(T + 3) / 4, 256, 0, s>>>(logits, T, E, k, ids, w);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -183,6 +183,21 @@ def custom_inputs(T, H, I, E, k, fmt="fp8", seed=7, device="cpu", shared=False, 
     return dict(cfg=c, x=x, logits=logits, routed=routed, shared=sh, gamma=gamma, eps=NORM_EPS)
 
 
+def random_topk_ids(T, E, k, seed, device="cpu", hot=None):
+    """Seeded routing choices: k distinct experts per token, in a random slot
+    order; with ``hot`` = e, every token's first slot is expert e (so other
+    experts may get no rows)."""
+    g = _gen("cpu", seed_of(95, T_RANK, seed))
+    ids = torch.argsort(torch.rand((T, E), generator=g), dim=1)[:, :k].to(torch.int32)
+    if hot is not None and T > 0:
+        # swap `hot` into slot 0; the k experts stay distinct
+        first = ids[:, 0].clone()
+        ids[:, 0] = hot
+        pos = ids[:, 1:] == hot
+        ids[:, 1:] = torch.where(pos, first[:, None].expand_as(ids[:, 1:]), ids[:, 1:])
+    return ids.contiguous().to(device)
+
+
 def to_numpy(inputs):
     """Host NumPy copies for the oracle: x as uint16 bf16 bits, the rest as is."""
     import numpy as np

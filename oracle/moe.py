@@ -167,15 +167,18 @@ class ExpertWeights:
                  byte, element 2i in the low nibble); s1, s3 uint8
                  [E][I][H/32], s2 uint8 [E][H][I/32] (e8m0 per 32 consecutive
                  contraction elements of one output channel).
-    W1 is the gate projection and W3 the up projection.
+    W1 is the gate projection and W3 the up projection.  The six stacks may
+    be any objects with a ``shape`` whose ``[e]`` gives expert e as a NumPy
+    array (so very large stacks can be fetched one expert at a time).
     """
 
     def __init__(self, fmt, w1, w3, w2, s1, s3, s2):
         if fmt not in ("fp8", "mxfp4"):
             raise ValueError(fmt)
         self.fmt = fmt
-        self.w1, self.w3, self.w2 = (np.asarray(a) for a in (w1, w3, w2))
-        self.s1, self.s3, self.s2 = (np.asarray(a) for a in (s1, s3, s2))
+        wrap = lambda a: a if hasattr(a, "shape") and not isinstance(a, (list, tuple)) else np.asarray(a)  # noqa: E731
+        self.w1, self.w3, self.w2 = (wrap(a) for a in (w1, w3, w2))
+        self.s1, self.s3, self.s2 = (wrap(a) for a in (s1, s3, s2))
         self.n_experts = self.w1.shape[0]
         self.inter = self.w1.shape[1]
         self.hidden = self.w2.shape[1]
@@ -186,8 +189,8 @@ class ExpertWeights:
         if self.fmt == "fp8":
             return (e4m3_decode(self.w1[e]), e4m3_decode(self.w3[e]),
                     e4m3_decode(self.w2[e]),
-                    self.s1[e].astype(np.float64), self.s3[e].astype(np.float64),
-                    self.s2[e].astype(np.float64))
+                    np.asarray(self.s1[e], dtype=np.float64), np.asarray(self.s3[e], dtype=np.float64),
+                    np.asarray(self.s2[e], dtype=np.float64))
         ones_i = np.ones(self.inter)
         return (mxfp4_decode(self.w1[e], self.s1[e]),
                 mxfp4_decode(self.w3[e], self.s3[e]),
@@ -293,28 +296,22 @@ def forward(x_bf16, logits, top_k, routed, shared=None, norm_gamma=None, norm_ep
 
 
 def forward_sampled(x_bf16, logits, top_k, routed, tokens, shared=None,
-                    norm_gamma=None, norm_eps=1e-6):
+                    norm_gamma=None, norm_eps=1e-6, routing=None):
     """The layer's output for a subset of tokens only (rows are independent).
 
-    Routing, quantisation, counts/offsets and the permutation are computed for
-    all tokens (they are cheap and bit-exact targets); the FFN and combine run
-    only for the pairs of ``tokens``.  Returns the same dict as ``forward``
-    with ``out`` of shape [len(tokens)][H] (row i is token tokens[i]) and no
-    per-row FFN intermediates.
+    Routing runs for all tokens (or is taken from ``routing`` = (topk_ids,
+    topk_w) as returned by ``route``); quantisation, permutation, FFN and
+    combine run only for the pairs of ``tokens``.  Returns ``out`` of shape
+    [len(tokens)][H] (row i is token tokens[i]).
     """
     tokens = np.asarray(tokens, dtype=np.int64)
-    ids, w = route(logits, top_k)
-    xq, xs = quantize_tokens(x_bf16)
-    counts, offsets = expert_counts_offsets(ids, routed.n_experts)
-    pair_to_row, row_to_pair, xq_rows, xs_rows = permute_rows(ids, offsets, xq, xs)
+    ids, w = route(logits, top_k) if routing is None else routing
+    xq, xs = quantize_tokens(np.asarray(x_bf16)[tokens])
     sub_ids = ids[tokens]
     _, sub_off = expert_counts_offsets(sub_ids, routed.n_experts)
-    sub_p2r, _, sub_q, sub_s = permute_rows(sub_ids, sub_off, xq[tokens], xs[tokens])
+    sub_p2r, _, sub_q, sub_s = permute_rows(sub_ids, sub_off, xq, xs)
     y_sub = expert_ffn(sub_q, sub_s, sub_off, routed)[0]
     y_shared = None
     if shared is not None:
-        y_shared = expert_ffn(xq[tokens], xs[tokens], np.array([0, len(tokens)]), shared)[0]
-    out = combine(y_sub, sub_p2r, w[tokens], y_shared, norm_gamma, norm_eps)
-    return dict(topk_ids=ids, topk_w=w, xq=xq, xs=xs, counts=counts, offsets=offsets,
-                pair_to_row=pair_to_row, row_to_pair=row_to_pair, xq_rows=xq_rows,
-                xs_rows=xs_rows, out=out)
+        y_shared = expert_ffn(xq, xs, np.array([0, len(tokens)]), shared)[0]
+    return combine(y_sub, sub_p2r, w[tokens], y_shared, norm_gamma, norm_eps)

@@ -1,0 +1,164 @@
+"""The C ABI on the CPU: the library loads, exports every function the header
+declares, and rejects bad arguments on the host before anything is enqueued
+(no GPU is touched: every call here fails validation).
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from mixture_experts_ffn_softmax_amd import _lib
+from mixture_experts_ffn_softmax_amd._lib import (MOE_ERR_ALIGN, MOE_ERR_NULL, MOE_ERR_SHAPE,
+                                                  MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_OK,
+                                                  MoeDebug, MoeWeights)
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "moe.h")
+
+A = 0x10000          # fake, 16-byte aligned "device" addresses: never dereferenced here
+MIS = 0x10008        # misaligned
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.skip("libmoe.so not built (run __graft_entry__.build())")
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert declared_functions() == sorted(_lib.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings(lib):
+    assert b"gfx950" in lib.moe_version()
+    for s in range(7):
+        assert lib.moe_status_string(s)
+    assert lib.moe_status_string(99) == b"unknown status"
+
+
+def test_struct_layouts():
+    # moe_weights_t: 4 int32 then 6 pointers; moe_debug_t: 8 pointers, 7 events, 96 chars
+    assert ctypes.sizeof(MoeWeights) == 16 + 6 * 8
+    assert ctypes.sizeof(MoeDebug) == 8 * 8 + 7 * 8 + 96
+
+
+def fp8_weights(E=8, H=256, I=128, fmt=0, **over):
+    w = MoeWeights(fmt, E, H, I, A, A, A, A, A, A)
+    for k, v in over.items():
+        setattr(w, k, v)
+    return w
+
+
+def test_route_validation(lib):
+    r = lib.moe_route
+    assert r(A, -1, 8, 2, A, A, None) == MOE_ERR_SHAPE
+    assert r(A, 4, 0, 1, A, A, None) == MOE_ERR_SHAPE
+    assert r(A, 4, 1025, 1, A, A, None) == MOE_ERR_SHAPE
+    assert r(A, 4, 8, 9, A, A, None) == MOE_ERR_SHAPE          # k > E
+    assert r(A, 4, 64, 33, A, A, None) == MOE_ERR_SHAPE         # k > 32
+    assert r(A, 1 << 30, 8, 2, A, A, None) == MOE_ERR_SHAPE     # T*k overflows
+    assert r(None, 4, 8, 2, A, A, None) == MOE_ERR_NULL
+    assert b"logits" in lib.moe_last_error()
+    assert r(A, 4, 8, 2, MIS, A, None) == MOE_ERR_ALIGN
+    assert r(A, 0, 8, 2, None, None, None) == MOE_OK            # T = 0: nothing to do
+    assert lib.moe_last_error() == b""
+
+
+def test_permute_validation(lib):
+    p = lib.moe_permute
+    ws = lib.moe_permute_workspace_size(16, 2, 8)
+    assert ws > 0
+    args = [A, 16, 256, A, 2, 8, A, A, A, A, A, A, None, None, A, ws, None]
+
+    def call(**kw):
+        a = list(args)
+        names = ["x", "T", "H", "ids", "k", "E", "counts", "offsets", "p2r", "r2p", "xq", "xs",
+                 "xq_tok", "xs_tok", "ws", "ws_bytes", "stream"]
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return p(*a)
+
+    assert call(H=200) == MOE_ERR_SHAPE
+    assert call(H=0) == MOE_ERR_SHAPE
+    assert call(x=None) == MOE_ERR_NULL
+    assert call(xq=MIS) == MOE_ERR_ALIGN
+    assert call(xq_tok=A) == MOE_ERR_NULL                       # xq_tok without xs_tok
+    assert call(ws_bytes=ws - 1) == MOE_ERR_WORKSPACE
+    assert call(ws=None) == MOE_ERR_WORKSPACE
+
+
+def test_expert_ffn_validation(lib):
+    f = lib.moe_expert_ffn
+    w = fp8_weights()
+    ws = lib.moe_expert_ffn_workspace_size(64, ctypes.byref(w))
+    assert ws >= 64 * 128 * 5
+    assert f(A, A, 64, A, None, A, A, ws, None) == MOE_ERR_NULL
+    assert f(A, A, 64, A, ctypes.byref(fp8_weights(fmt=7)), A, A, ws, None) == MOE_ERR_UNSUPPORTED
+    assert f(A, A, 64, A, ctypes.byref(fp8_weights(H=100)), A, A, ws, None) == MOE_ERR_SHAPE
+    assert f(A, A, 64, A, ctypes.byref(fp8_weights(I=0)), A, A, ws, None) == MOE_ERR_SHAPE
+    assert f(A, A, 64, A, ctypes.byref(fp8_weights(E=0)), A, A, ws, None) == MOE_ERR_SHAPE
+    assert f(A, A, 64, A, ctypes.byref(fp8_weights(w2=None)), A, A, ws, None) == MOE_ERR_NULL
+    assert f(A, A, 64, A, ctypes.byref(fp8_weights(s3=MIS)), A, A, ws, None) == MOE_ERR_ALIGN
+    assert f(A, A, -1, A, ctypes.byref(w), A, A, ws, None) == MOE_ERR_SHAPE
+    assert f(A, A, 64, A, ctypes.byref(w), A, A, ws - 1, None) == MOE_ERR_WORKSPACE
+    assert f(None, None, 0, None, ctypes.byref(w), None, None, 0, None) == MOE_OK
+
+
+def test_combine_validation(lib):
+    c = lib.moe_combine
+    assert c(A, A, A, 4, 256, 0, None, None, 1e-6, A, None) == MOE_ERR_SHAPE
+    assert c(A, A, A, 4, 255, 2, None, None, 1e-6, A, None) == MOE_ERR_SHAPE
+    assert c(A, A, A, 4, 256, 2, None, A, -1.0, A, None) == MOE_ERR_SHAPE
+    assert c(A, A, A, 4, 256, 2, MIS, None, 1e-6, A, None) == MOE_ERR_ALIGN
+    assert c(A, None, A, 4, 256, 2, None, None, 1e-6, A, None) == MOE_ERR_NULL
+    assert c(None, None, None, 0, 256, 2, None, None, 1e-6, None, None) == MOE_OK
+
+
+def test_forward_validation(lib):
+    fw = lib.moe_forward
+    w = fp8_weights()
+    ws = lib.moe_forward_workspace_size(16, 2, ctypes.byref(w), 0)
+    sh = fp8_weights(E=1)
+    ws_sh = lib.moe_forward_workspace_size(16, 2, ctypes.byref(w), 1)
+    assert ws_sh > ws
+
+    def call(T=16, k=2, routed=w, use_shared=0, shared=None, out=A, dbg=None, wsb=ws, x=A):
+        return fw(x, A, T, k, ctypes.byref(routed), use_shared,
+                  ctypes.byref(shared) if shared is not None else None, None, 1e-6, out,
+                  ctypes.byref(dbg) if dbg is not None else None, A, wsb, None)
+
+    assert call(k=9) == MOE_ERR_SHAPE
+    assert call(use_shared=1) == MOE_ERR_NULL
+    assert call(use_shared=1, shared=fp8_weights(E=2)) == MOE_ERR_SHAPE
+    assert call(use_shared=1, shared=fp8_weights(E=1, I=256)) == MOE_ERR_UNSUPPORTED
+    assert call(use_shared=1, shared=fp8_weights(E=1, fmt=1)) == MOE_ERR_UNSUPPORTED
+    assert call(use_shared=1, shared=sh, wsb=ws) == MOE_ERR_WORKSPACE
+    assert call(out=None) == MOE_ERR_NULL
+    assert call(x=MIS) == MOE_ERR_ALIGN
+    d = MoeDebug()
+    d.xq_rows = MIS
+    assert call(dbg=d) == MOE_ERR_ALIGN
+    assert call(routed=fp8_weights(E=1024), use_shared=1, shared=sh, wsb=1 << 40) == MOE_ERR_UNSUPPORTED
+    assert call(T=0) == MOE_OK
+
+
+def test_workspace_sizes_grow(lib):
+    w = fp8_weights(E=8, H=8192, I=2048)
+    a = lib.moe_forward_workspace_size(64, 2, ctypes.byref(w), 0)
+    b = lib.moe_forward_workspace_size(2048, 2, ctypes.byref(w), 0)
+    # the intermediate h (fp32), hq, y (bf16) and xq rows dominate: ~ rows * (4I + I + 2H + H)
+    assert b > a and b >= 4096 * (5 * 2048 + 3 * 8192)
+    assert lib.moe_forward_workspace_size(-1, 2, ctypes.byref(w), 0) == 0

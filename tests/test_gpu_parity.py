@@ -1,0 +1,283 @@
+"""GPU parity: the HIP library through its C ABI against the CPU oracle.
+
+Bar: routing ids, per-expert counts/offsets, the permutation and the
+quantised token bytes/scales bit-exact; router weights within 1e-6 relative;
+layer outputs within max|err| <= 2e-2 * RMS(oracle).  Small cases are checked
+everywhere; the full-size workloads (the pages' prefill and decode shares,
+the LatentMoE decode and the skewed full layer) are checked on all metadata
+and on the outputs of sampled tokens.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import moe_synth
+import oracle
+from gpu_helpers import (DEV, OUT_TOL, assert_weights_close, bits, check_metadata, host,
+                         oracle_weights, run_forward, say, to_device, tolerance_ratio)
+
+pytestmark = pytest.mark.gpu
+
+
+def bf16_np(t):
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+# ----------------------------------------------------------------------------
+# router
+# ----------------------------------------------------------------------------
+
+ROUTE_CASES = {
+    "tiny": lambda: moe_synth.make_inputs("tiny", weights=False)["logits"],
+    "integer_ties": lambda: torch.randint(-3, 3, (300, 16), generator=torch.Generator().manual_seed(1)).float(),
+    "signed_zeros": lambda: torch.tensor([[-1.0, 0.0, -0.0, 0.0, -2.0, -0.0, 5.0, 5.0]] * 4),
+    "all_equal": lambda: torch.zeros((33, 64)),
+    "E1024_k32": lambda: torch.randn((100, 1024), generator=torch.Generator().manual_seed(2)),
+    "latent_E896_k16": lambda: moe_synth.make_inputs("latent", weights=False)["logits"],
+    "skewed_full": lambda: moe_synth.make_inputs("skewed", weights=False)["logits"],
+    "E1": lambda: torch.randn((5, 1)),
+}
+ROUTE_K = {"tiny": 2, "integer_ties": 4, "signed_zeros": 3, "all_equal": 8, "E1024_k32": 32,
+           "latent_E896_k16": 16, "skewed_full": 8, "E1": 1}
+
+
+@pytest.mark.parametrize("case", list(ROUTE_CASES))
+def test_route(lib, case):
+    logits = ROUTE_CASES[case]().float().contiguous()
+    k = ROUTE_K[case]
+    say("route", case, tuple(logits.shape), k)
+    ids, w = lib.moe_route(logits.to(DEV), k)
+    torch.cuda.synchronize()
+    ref_ids, ref_w = oracle.route(logits.numpy(), k)
+    assert (host(ids) == ref_ids).all()
+    assert_weights_close(host(w), ref_w)
+
+
+# ----------------------------------------------------------------------------
+# permutation and quantisation (moe_permute)
+# ----------------------------------------------------------------------------
+
+PERMUTE_CASES = [  # T, H, E, k, hot expert
+    (64, 256, 8, 2, None),
+    (333, 384, 7, 3, None),
+    (100, 128, 5, 1, 3),          # every token on expert 3: the other experts are empty
+    (2000, 256, 16, 4, 0),
+    (512, 3584, 896, 16, None),
+    (2048, 8192, 8, 2, None),
+    (1, 128, 1024, 32, None),
+]
+
+
+@pytest.mark.parametrize("T,H,E,k,hot", PERMUTE_CASES)
+def test_permute(lib, T, H, E, k, hot):
+    say("permute", T, H, E, k, hot)
+    x = moe_synth.randn((T, H), "cpu", moe_synth.seed_of(91, 1, T)).to(torch.bfloat16)
+    if T > 1:
+        x[1] = 0.0                                    # a zero row: scale 1, signed-zero codes
+        x[0, :7] = torch.tensor([448.0, -448.0, 1e-3, -1e-30, 3.0, -0.0, 0.0])
+    ids = moe_synth.random_topk_ids(T, E, k, seed=T + E, hot=hot)
+    res = lib.moe_permute(x.to(DEV), ids.to(DEV), E, token_order=True)
+    torch.cuda.synchronize()
+    xq, xs = oracle.quantize_tokens(bf16_np(x))
+    counts, offsets = oracle.expert_counts_offsets(ids.numpy(), E)
+    p2r, r2p, xq_rows, xs_rows = oracle.permute_rows(ids.numpy(), offsets, xq, xs)
+    assert (host(res["counts"]) == counts).all()
+    assert (host(res["offsets"]) == offsets).all()
+    assert (host(res["pair_to_row"]) == p2r).all()
+    assert (host(res["row_to_pair"]) == r2p).all()
+    assert (host(res["xq_rows"]) == xq_rows).all()
+    assert (host(res["xs_rows"]).view(np.uint32) == xs_rows.view(np.uint32)).all()
+    assert (host(res["xq_tok"]) == xq).all()
+    assert (host(res["xs_tok"]).view(np.uint32) == xs.view(np.uint32)).all()
+
+
+def test_permute_skewed_full_size(lib):
+    """The skewed full layer (16384 tokens, top-8 of 256): all metadata
+    bit-exact; quantised bytes of 256 sampled rows."""
+    inp = moe_synth.make_inputs("skewed", device=DEV, weights=False)
+    c = inp["cfg"]
+    T, H, E, k = c["T"], c["H"], c["E"], c["k"]
+    say("permute skewed full", T, H, E, k, "alpha", c["alpha"])
+    ids, _ = lib.moe_route(inp["logits"], k)
+    res = lib.moe_permute(inp["x"], ids, E)
+    torch.cuda.synchronize()
+    ref_ids, _ = oracle.route(host(inp["logits"]), k)
+    assert (host(ids) == ref_ids).all()
+    counts, offsets = oracle.expert_counts_offsets(ref_ids, E)
+    dummy = np.zeros((T, 1), np.uint8)
+    p2r, r2p, _, _ = oracle.permute_rows(ref_ids, offsets, dummy, np.zeros(T, np.float32))
+    assert (host(res["counts"]) == counts).all()
+    assert counts.max() / counts.mean() == pytest.approx(5.0, abs=0.11)
+    assert (host(res["offsets"]) == offsets).all()
+    assert (host(res["pair_to_row"]) == p2r).all()
+    assert (host(res["row_to_pair"]) == r2p).all()
+    rows = np.random.default_rng(5).choice(T * k, 256, replace=False)
+    toks = r2p[rows] // k
+    xq, xs = oracle.quantize_tokens(bits(inp["x"][torch.as_tensor(toks, device=DEV)]))
+    assert (host(res["xq_rows"][torch.as_tensor(rows, device=DEV)]) == xq).all()
+    assert (host(res["xs_rows"])[rows].view(np.uint32) == xs.view(np.uint32)).all()
+
+
+# ----------------------------------------------------------------------------
+# whole layer, small shapes: every output element
+# ----------------------------------------------------------------------------
+
+FULL_CASES = {
+    # name: (T, H, I, E, k, fmt, shared, norm)
+    "tiny_config": None,
+    "ragged_small_variant": (45, 384, 256, 6, 3, "fp8", False, False),
+    "shared_small_variant": (40, 256, 256, 4, 2, "fp8", True, False),
+    "large_variant": (300, 256, 256, 4, 2, "fp8", False, False),
+    "large_variant_shared": (333, 512, 384, 3, 2, "fp8", True, False),
+    "mxfp4_rmsnorm": (48, 256, 128, 8, 2, "mxfp4", False, True),
+    "mxfp4_k_equals_E": (20, 384, 256, 4, 4, "mxfp4", False, False),
+    "dense_E1_k1": (70, 256, 128, 1, 1, "fp8", False, False),
+    "one_token": (1, 128, 128, 16, 4, "fp8", True, False),
+}
+
+
+@pytest.mark.parametrize("case", list(FULL_CASES))
+def test_forward_full(lib, case):
+    spec = FULL_CASES[case]
+    if spec is None:
+        inp = moe_synth.make_inputs("tiny")
+    else:
+        T, H, I, E, k, fmt, shared, norm = spec
+        inp = moe_synth.custom_inputs(T, H, I, E, k, fmt=fmt, seed=len(case), shared=shared, norm=norm)
+    c = inp["cfg"]
+    say("forward full", case, {key: c[key] for key in ("T", "H", "I", "E", "k", "fmt", "shared", "norm")})
+    out, dbg, variant = run_forward(to_device(inp))
+    say("  variant", variant)
+    ref = oracle.forward(bf16_np(inp["x"]), inp["logits"].numpy(), c["k"],
+                         oracle_weights(inp["routed"], c["fmt"]),
+                         oracle_weights(inp["shared"], "fp8"),
+                         None if inp["gamma"] is None else inp["gamma"].numpy(), inp["eps"])
+    check_metadata(dbg, ref, c["T"], c["k"], c["E"], c["shared"])
+    assert (host(dbg["xq_rows"]) == ref["xq_rows"]).all()
+    assert (host(dbg["xs_rows"]).view(np.uint32) == ref["xs_rows"].view(np.uint32)).all()
+    ratio = tolerance_ratio(bits(out), ref["out"])
+    say("  max|err|/rms", ratio)
+    assert ratio <= OUT_TOL
+
+
+def test_forward_zero_tokens(lib):
+    inp = to_device(moe_synth.custom_inputs(0, 256, 128, 4, 2))
+    out, _, _ = run_forward(inp, capture=False)
+    assert out.shape == (0, 256)
+
+
+def test_forward_deterministic(lib):
+    inp = to_device(moe_synth.custom_inputs(300, 256, 256, 4, 2, seed=3, shared=True))
+    a, _, _ = run_forward(inp, capture=False)
+    b, _, _ = run_forward(inp, capture=False)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+# ----------------------------------------------------------------------------
+# whole layer, the full-size workloads: all metadata, sampled outputs
+# ----------------------------------------------------------------------------
+
+SAMPLED = {"prefill": 24, "decode": 64, "latent": 3, "skewed": 4}
+
+
+@pytest.mark.parametrize("name", list(SAMPLED))
+def test_forward_full_size(lib, name):
+    inp = moe_synth.make_inputs(name, device=DEV)
+    c = inp["cfg"]
+    T, E, k = c["T"], c["E"], c["k"]
+    say("forward full size", name, c)
+    out, dbg, variant = run_forward(inp)
+    say("  variant", variant)
+    ids, w = oracle.route(host(inp["logits"]), k)
+    counts, offsets = oracle.expert_counts_offsets(ids, E)
+    p2r, r2p, _, _ = oracle.permute_rows(ids, offsets, np.zeros((T, 1), np.uint8), np.zeros(T, np.float32))
+    ref = dict(topk_ids=ids, topk_w=w, counts=counts, offsets=offsets, pair_to_row=p2r, row_to_pair=r2p)
+    check_metadata(dbg, ref, T, k, E, c["shared"])
+    rng = np.random.default_rng(c["cfg"])
+    n = SAMPLED[name]
+    tokens = np.arange(T) if n >= T else np.sort(rng.choice(T, n, replace=False))
+    tok_d = torch.as_tensor(tokens, device=DEV)
+    # quantised bytes of the sampled tokens' rows
+    xq, xs = oracle.quantize_tokens(bits(inp["x"][tok_d]))
+    rows = p2r[tokens]
+    for j in range(k):
+        r_d = torch.as_tensor(rows[:, j], device=DEV)
+        assert (host(dbg["xq_rows"][r_d]) == xq).all()
+        assert (host(dbg["xs_rows"][r_d]).view(np.uint32) == xs.view(np.uint32)).all()
+    ref_out = oracle.moe.forward_sampled(
+        bits(inp["x"]), None, k, oracle_weights(inp["routed"], c["fmt"], lazy=True), tokens,
+        shared=oracle_weights(inp["shared"], "fp8", lazy=True),
+        norm_gamma=None if inp["gamma"] is None else host(inp["gamma"]), norm_eps=inp["eps"],
+        routing=(ids, w))
+    ratio = tolerance_ratio(bits(out[tok_d]), ref_out)
+    say("  max|err|/rms", ratio, "over", len(tokens), "tokens")
+    assert ratio <= OUT_TOL
+
+
+# ----------------------------------------------------------------------------
+# moe_expert_ffn and moe_combine on their own
+# ----------------------------------------------------------------------------
+
+
+def synthetic_rows(counts, H, seed):
+    """Expert-grouped rows: random e4m3 codes of moderate magnitude, scales."""
+    n = int(sum(counts))
+    g = torch.Generator().manual_seed(seed)
+    vals = torch.randn((n, H), generator=g) * 64.0
+    q = vals.clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8)
+    s = (torch.rand((n,), generator=g) * 0.01 + 1e-3).float()
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    return q, s, offsets
+
+
+@pytest.mark.parametrize("counts,fmt", [
+    ([5, 0, 17, 1, 40, 0, 3, 32], "fp8"),          # small variant: ragged, empty experts
+    ([300, 0, 129, 64, 1], "fp8"),                  # large variant
+    ([9, 33, 0, 2, 16, 1, 0, 20], "mxfp4"),
+])
+def test_expert_ffn(lib, counts, fmt):
+    E, H, I = len(counts), 256, 256
+    say("expert_ffn", counts, fmt)
+    q, s, offsets = synthetic_rows(counts, H, seed=sum(counts))
+    W = moe_synth.expert_weights(77, "cpu", fmt, E, H, I)
+    y = lib.moe_expert_ffn(q.to(DEV), s.to(DEV), torch.as_tensor(offsets, device=DEV),
+                           lib.Weights(to_device(W), fmt))
+    torch.cuda.synchronize()
+    y_ref = oracle.expert_ffn(q.numpy(), s.numpy(), offsets, oracle_weights(W, fmt))[0]
+    ratio = tolerance_ratio(bits(y), oracle.codecs.bf16_encode(y_ref))
+    say("  max|err|/rms", ratio)
+    assert ratio <= OUT_TOL
+
+
+@pytest.mark.parametrize("T,H,k,shared,norm", [(50, 256, 2, False, False), (17, 384, 4, True, True),
+                                               (8, 8192, 8, True, False)])
+def test_combine(lib, T, H, k, shared, norm):
+    say("combine", T, H, k, shared, norm)
+    g = torch.Generator().manual_seed(T * k)
+    R = T * k
+    y = torch.randn((R, H), generator=g).to(torch.bfloat16)
+    p2r = torch.randperm(R, generator=g).to(torch.int32).reshape(T, k)
+    w = torch.rand((T, k), generator=g)
+    w = (w / w.sum(dim=1, keepdim=True)).float()
+    ysh = torch.randn((T, H), generator=g).to(torch.bfloat16) if shared else None
+    gamma = (torch.rand(H, generator=g) + 0.5).float() if norm else None
+    out = lib.moe_combine(y.to(DEV), p2r.to(DEV), w.to(DEV), None if ysh is None else ysh.to(DEV),
+                          None if gamma is None else gamma.to(DEV), 1e-6)
+    torch.cuda.synchronize()
+    ref = oracle.combine(oracle.codecs.bf16_decode(bf16_np(y)), p2r.numpy(), w.numpy().astype(np.float64),
+                         None if ysh is None else oracle.codecs.bf16_decode(bf16_np(ysh)),
+                         None if gamma is None else gamma.numpy(), 1e-6)
+    ratio = tolerance_ratio(bits(out), ref)
+    assert ratio <= 1e-2
+    # fp32 accumulation of the same bf16 inputs: at most one bf16 ulp apart
+    d = np.abs(bits(out).astype(np.int32) - ref.astype(np.int32))
+    assert d.max() <= 1
+
+
+def test_combine_zero_weights(lib):
+    y = torch.randn((40, 256)).to(torch.bfloat16).to(DEV)
+    p2r = torch.arange(40, dtype=torch.int32).reshape(20, 2).to(DEV)
+    out = lib.moe_combine(y, p2r, torch.zeros((20, 2), device=DEV))
+    torch.cuda.synchronize()
+    assert (out.float() == 0).all()

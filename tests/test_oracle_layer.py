@@ -348,4 +348,4 @@ def test_forward_sampled_matches_forward():
     full = oracle.forward(x, logits, k, W, shared=Ws)
     toks = np.array([3, 17, 0, 29])
     samp = oracle.moe.forward_sampled(x, logits, k, W, toks, shared=Ws)
-    assert (samp["out"] == full["out"][toks]).all()
+    assert (samp == full["out"][toks]).all()
