@@ -191,7 +191,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8-e4m3 MFMA, fp32 accumulate",
+        "dtype": "fp8-e4m3 x e4m3 (gate-up) and bf16 x bf16 (down) MFMA, fp32 accumulate",
         "data": "synthetic (seeded; shapes of the pages' per-device prefill share)",
         "config": {"workload": f"{args.config}: T={c['T']} H={c['H']} I={c['I']} E={c['E']} top_k={c['k']} "
                                f"{c['fmt']}{' +shared expert' if c['shared'] else ''}",

@@ -97,14 +97,13 @@ typedef struct {
 
 /* Stage boundaries at which moe_forward records the events of a moe_debug_t. */
 enum {
-  MOE_STAGE_ROUTE = 0,   /* router                                   */
-  MOE_STAGE_PERMUTE = 1, /* counts, offsets, ranks, quantise+scatter,
-                            GEMM tile prefix                         */
-  MOE_STAGE_GEMM1 = 2,   /* gate-up grouped GEMM + SiLU * gate (only) */
-  MOE_STAGE_QUANT_H = 3, /* per-row fp8 quantisation of h            */
-  MOE_STAGE_GEMM2 = 4,   /* down grouped GEMM                        */
-  MOE_STAGE_COMBINE = 5, /* weighted gather (+ RMSNorm) (+ shared)   */
-  MOE_N_STAGES = 6
+  MOE_STAGE_ROUTE = 0,   /* router                                            */
+  MOE_STAGE_PERMUTE = 1, /* counts, offsets, ranks, quantise+scatter, GEMM
+                            tile prefix                                       */
+  MOE_STAGE_GEMM1 = 2,   /* gate-up grouped GEMM + SiLU * gate (one kernel)   */
+  MOE_STAGE_GEMM2 = 3,   /* down grouped GEMM (one kernel)                    */
+  MOE_STAGE_COMBINE = 4, /* weighted gather (+ RMSNorm) (+ shared)            */
+  MOE_N_STAGES = 5
 };
 
 /*
@@ -177,12 +176,15 @@ moe_status_t moe_permute(const uint16_t* x, int32_t T, int32_t H, const int32_t*
  *   xs_rows        float [n_rows]     per-row scales
  *   expert_offsets int32 [E+1]        device; rows of expert e are
  *                                     offsets[e] .. offsets[e+1]-1, offsets[E] = n_rows
- *   y_rows         bf16  [n_rows][H]  out
+ *   y_rows         float [n_rows][H]  out (fp32: the output is rounded only once,
+ *                                     by the combine)
  * For row r of expert e ([Ling] §5, per-channel direct_scaled_dot: scales
  * applied after the full-K reduction; fp32 accumulation):
  *   g = (sum_k q_r[k] W1[e][n][k]) * xs_r * s1[e][n];  u likewise with W3, s3
- *   h = SiLU(g) * u  (binary32),  hs_r = max|h_r| / 448,  hq = e4m3(h / hs_r)
- *   y_r[j] = bf16( (sum_n hq_r[n] W2[e][j][n]) * hs_r * s2[e][j] )
+ *   h = bf16( SiLU(g) * u )
+ *   y_r[j] = (sum_n h_r[n] W2[e][j][n]) * s2[e][j]
+ * GEMM1 runs e4m3 x e4m3 on the matrix cores; GEMM2 runs bf16 h x W2 with
+ * W2's codes converted exactly to bf16.
  * For MXFP4 the e8m0 block scales enter each 32-element partial sum and
  * s1/s3/s2 are not per-channel.  A shared expert is a call with E = 1 and
  * offsets {0, T} over token-order rows.
@@ -190,14 +192,14 @@ moe_status_t moe_permute(const uint16_t* x, int32_t T, int32_t H, const int32_t*
 size_t moe_expert_ffn_workspace_size(int32_t n_rows, const moe_weights_t* w);
 moe_status_t moe_expert_ffn(const uint8_t* xq_rows, const float* xs_rows, int32_t n_rows,
                             const int32_t* expert_offsets, const moe_weights_t* w,
-                            uint16_t* y_rows, void* ws, size_t ws_bytes, void* stream);
+                            float* y_rows, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * moe_combine -- weighted gather back into token order.
- *   y_rows      bf16  [T*k][H]  expert outputs
+ *   y_rows      float [T*k][H]  expert outputs
  *   pair_to_row int32 [T][k]
  *   topk_w      float [T][k]
- *   y_shared    bf16  [T][H]    optional (NULL = none): shared expert output
+ *   y_shared    float [T][H]    optional (NULL = none): shared expert output
  *   norm_gamma  float [H]       optional (NULL = no RMSNorm)
  *   out         bf16  [T][H]    out
  * o = sum_{j<k} w[t][j] * y_rows[pair_to_row[t][j]] in fp32, slot order;
@@ -206,8 +208,8 @@ moe_status_t moe_expert_ffn(const uint8_t* xq_rows, const float* xs_rows, int32_
  * out = bf16(o), round-half-even.  [Ling] §1 (gather results) and the
  * SparseCore gather-reduce of the sglang-jax gap list, §8.
  */
-moe_status_t moe_combine(const uint16_t* y_rows, const int32_t* pair_to_row, const float* topk_w,
-                         int32_t T, int32_t H, int32_t top_k, const uint16_t* y_shared,
+moe_status_t moe_combine(const float* y_rows, const int32_t* pair_to_row, const float* topk_w,
+                         int32_t T, int32_t H, int32_t top_k, const float* y_shared,
                          const float* norm_gamma, float norm_eps, uint16_t* out, void* stream);
 
 /*

@@ -92,7 +92,7 @@ def moe_permute(x, topk_ids, n_experts, token_order=False, stream=None):
 def moe_expert_ffn(xq_rows, xs_rows, expert_offsets, weights, stream=None):
     n_rows = xq_rows.shape[0]
     dev = xq_rows.device
-    y = _empty((n_rows, weights.hidden), torch.bfloat16, dev)
+    y = _empty((n_rows, weights.hidden), torch.float32, dev)
     nbytes = lib().moe_expert_ffn_workspace_size(n_rows, weights.ref())
     ws = _empty((max(nbytes, 1),), torch.uint8, dev)
     check(lib().moe_expert_ffn(_p(xq_rows), _p(xs_rows), n_rows, _p(expert_offsets), weights.ref(),

@@ -14,9 +14,9 @@ LIB_PATH = os.path.join(HERE, "libmoe.so")
 
 MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_ALIGN, MOE_ERR_WORKSPACE, MOE_ERR_UNSUPPORTED, MOE_ERR_DEVICE = range(7)
 MOE_W_FP8, MOE_W_MXFP4 = 0, 1
-(MOE_STAGE_ROUTE, MOE_STAGE_PERMUTE, MOE_STAGE_GEMM1, MOE_STAGE_QUANT_H, MOE_STAGE_GEMM2,
- MOE_STAGE_COMBINE, MOE_N_STAGES) = range(7)
-STAGE_NAMES = ["route", "permute", "gemm1", "quant_h", "gemm2", "combine"]
+(MOE_STAGE_ROUTE, MOE_STAGE_PERMUTE, MOE_STAGE_GEMM1, MOE_STAGE_GEMM2, MOE_STAGE_COMBINE,
+ MOE_N_STAGES) = range(6)
+STAGE_NAMES = ["route", "permute", "gemm1", "gemm2", "combine"]
 
 # Every function include/moe.h declares.
 EXPORTS = [

@@ -8,9 +8,10 @@
 // separate path).
 //
 // One workgroup per token.  Each thread owns CPT chunks of 8 channels, reads
-// the k expert rows with 16-byte loads (coalesced along the row), accumulates
-// w_j * y in fp32 in slot order, optionally normalises, adds the shared row
-// and stores bf16 (round to nearest even).
+// the k fp32 expert rows with 16-byte loads (coalesced along the row),
+// accumulates w_j * y in fp32 in slot order, optionally normalises, adds the
+// shared row and stores bf16 (round to nearest even): the output is rounded
+// once.
 #include <math.h>
 
 #include "device_common.h"
@@ -19,10 +20,10 @@
 namespace moe {
 
 template <int CPT>
-__global__ __launch_bounds__(1024) void combine_kernel(const uint16_t* __restrict__ y_rows,
+__global__ __launch_bounds__(1024) void combine_kernel(const float* __restrict__ y_rows,
                                                        const int* __restrict__ pair_to_row,
                                                        const float* __restrict__ topk_w, int H,
-                                                       int k, const uint16_t* __restrict__ y_shared,
+                                                       int k, const float* __restrict__ y_shared,
                                                        const float* __restrict__ gamma, float eps,
                                                        uint16_t* __restrict__ out) {
   __shared__ float red[16];
@@ -38,18 +39,14 @@ __global__ __launch_bounds__(1024) void combine_kernel(const uint16_t* __restric
     const int r = pair_to_row[t * k + j];
     const float w = topk_w[t * k + j];
     if (r < 0) continue;
-    const uint4* src = reinterpret_cast<const uint4*>(y_rows + (long)r * H);
+    const float4* src = reinterpret_cast<const float4*>(y_rows + (long)r * H);
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
       const int idx = threadIdx.x + c * blockDim.x;
       if (idx < nchk) {
-        const uint4 v = src[idx];
-        const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          acc[c][2 * q] += w * bf16_lo(wd[q]);
-          acc[c][2 * q + 1] += w * bf16_hi(wd[q]);
-        }
+        const float4 v0 = src[2 * idx], v1 = src[2 * idx + 1];
+        acc[c][0] += w * v0.x; acc[c][1] += w * v0.y; acc[c][2] += w * v0.z; acc[c][3] += w * v0.w;
+        acc[c][4] += w * v1.x; acc[c][5] += w * v1.y; acc[c][6] += w * v1.z; acc[c][7] += w * v1.w;
       }
     }
   }
@@ -80,13 +77,10 @@ __global__ __launch_bounds__(1024) void combine_kernel(const uint16_t* __restric
     const int idx = threadIdx.x + c * blockDim.x;
     if (idx >= nchk) continue;
     if (y_shared) {
-      const uint4 v = reinterpret_cast<const uint4*>(y_shared + t * H)[idx];
-      const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        acc[c][2 * q] += bf16_lo(wd[q]);
-        acc[c][2 * q + 1] += bf16_hi(wd[q]);
-      }
+      const float4* sh = reinterpret_cast<const float4*>(y_shared + t * H);
+      const float4 v0 = sh[2 * idx], v1 = sh[2 * idx + 1];
+      acc[c][0] += v0.x; acc[c][1] += v0.y; acc[c][2] += v0.z; acc[c][3] += v0.w;
+      acc[c][4] += v1.x; acc[c][5] += v1.y; acc[c][6] += v1.z; acc[c][7] += v1.w;
     }
     uint32_t o[4];
 #pragma unroll
@@ -95,8 +89,8 @@ __global__ __launch_bounds__(1024) void combine_kernel(const uint16_t* __restric
   }
 }
 
-hipError_t launch_combine(const uint16_t* y_rows, const int* pair_to_row, const float* w, int T,
-                          int H, int k, const uint16_t* y_shared, const float* gamma, float eps,
+hipError_t launch_combine(const float* y_rows, const int* pair_to_row, const float* w, int T,
+                          int H, int k, const float* y_shared, const float* gamma, float eps,
                           uint16_t* out, hipStream_t s) {
   if (T == 0) return hipSuccess;
   const int chunks = H / 8;

@@ -56,42 +56,35 @@ struct FfnGroups {
   const void* s2[2];
 };
 
-// Row operand of a grouped GEMM: e4m3 codes and per-row scales.  Rows below
-// shared_row0 are read from q[0]/s[0] at their row index; the shared group's
-// rows from q[1]/s[1] at (row - shared_row0).
+// Row operand of a grouped GEMM: GEMM1 reads e4m3 codes q with per-row
+// scales s, GEMM2 reads bf16 h (s unused).  Rows below shared_row0 are read
+// from q[0]/s[0] at their row index; the shared group's rows from q[1]/s[1]
+// at (row - shared_row0).
 struct RowOperand {
-  const uint8_t* q[2];
+  const void* q[2];
   const float* s[2];
   long shared_row0;
 };
 
-enum GemmVariant { kVariantLarge = 0, kVariantSmall = 1 };
-
-// Rows per tile of each variant.
-constexpr int kLargeBM = 128;
-constexpr int kSmallBM = 32;
+enum GemmVariant { kVariantSmall = 0, kVariantLarge128 = 1, kVariantLarge256 = 2 };
 
 int choose_variant(const FfnGroups& g, long n_rows);
+int variant_rows(int variant);          // rows per tile
+const char* variant_name(int variant);
 long max_row_tiles(long n_rows, int n_groups, int bm);
 
-// tile_prefix[g] = sum over g' < g of ceil(rows(g') / bm); also zeroes
-// amax[0 .. n_rows).
-hipError_t launch_tile_prefix(const int* offsets, int n_groups, int bm, int* tile_prefix,
-                              uint32_t* amax, long n_rows, hipStream_t s);
-// GEMM1: h[r][n] = SiLU(g) * u for the gate/up pair, atomicMax of |h| into amax[r].
-hipError_t launch_gemm1(int variant, const FfnGroups& g, const RowOperand& x,
-                        const int* tile_prefix, long n_rows, float* h, uint32_t* amax,
-                        hipStream_t s);
-// hs[r] = amax[r] / 448 (1 if 0), hq[r] = e4m3(h[r] / hs[r]).
-hipError_t launch_quant_h(const float* h, const uint32_t* amax, long n_rows, int I, uint8_t* hq,
-                          float* hs, hipStream_t s);
-// GEMM2: y[r][j] = bf16((hq_r . W2[j]) * hs[r] * s2[j]).
-hipError_t launch_gemm2(int variant, const FfnGroups& g, const RowOperand& hq,
-                        const int* tile_prefix, long n_rows, uint16_t* y, hipStream_t s);
+// tile_prefix[g] = sum over g' < g of ceil(rows(g') / bm), g = 0..n_groups.
+hipError_t launch_tile_prefix(const int* offsets, int n_groups, int bm, int* tile_prefix, hipStream_t s);
+// GEMM1: h[r][n] = bf16(SiLU(g) * u) for the gate/up pair of channel n.
+hipError_t launch_gemm1(int variant, const FfnGroups& g, const RowOperand& x, const int* tile_prefix,
+                        long n_rows, uint16_t* h, hipStream_t s);
+// GEMM2: y[r][j] = (h_r . W2[j]) * s2[j] in fp32.
+hipError_t launch_gemm2(int variant, const FfnGroups& g, const RowOperand& h, const int* tile_prefix,
+                        long n_rows, float* y, hipStream_t s);
 
 // ---- combine --------------------------------------------------------------
-hipError_t launch_combine(const uint16_t* y_rows, const int* pair_to_row, const float* w, int T,
-                          int H, int k, const uint16_t* y_shared, const float* gamma, float eps,
+hipError_t launch_combine(const float* y_rows, const int* pair_to_row, const float* w, int T,
+                          int H, int k, const float* y_shared, const float* gamma, float eps,
                           uint16_t* out, hipStream_t s);
 
 }  // namespace moe

@@ -105,13 +105,9 @@ struct Carve {
   }
 };
 
-size_t ffn_ws(Carve& c, long n_rows, int n_groups, int inter, int32_t** tile_prefix, uint32_t** amax,
-              float** h, uint8_t** hq, float** hs) {
+size_t ffn_ws(Carve& c, long n_rows, int n_groups, int inter, int32_t** tile_prefix, uint16_t** h) {
   *tile_prefix = c.take<int32_t>(n_groups + 1);
-  *amax = c.take<uint32_t>(n_rows);
-  *h = c.take<float>((size_t)n_rows * inter);
-  *hq = c.take<uint8_t>((size_t)n_rows * inter);
-  *hs = c.take<float>(n_rows);
+  *h = c.take<uint16_t>((size_t)n_rows * inter);
   return c.used;
 }
 
@@ -135,26 +131,21 @@ moe::FfnGroups make_groups(const moe_weights_t* r, const moe_weights_t* sh, cons
   return g;
 }
 
-// GEMM1 -> quantise h -> GEMM2 over the groups of `g`.
-moe_status_t run_ffn(const moe::FfnGroups& g, const moe::RowOperand& x, long n_rows, uint16_t* y,
-                     int32_t* tile_prefix, uint32_t* amax, float* h, uint8_t* hq, float* hs,
-                     hipStream_t s, void* const* events, char* variant_out, size_t variant_len) {
+// GEMM1 -> GEMM2 over the groups of `g`.
+moe_status_t run_ffn(const moe::FfnGroups& g, const moe::RowOperand& x, long n_rows, float* y,
+                     int32_t* tile_prefix, uint16_t* h, hipStream_t s, void* const* events,
+                     char* variant_out, size_t variant_len) {
   const int variant = moe::choose_variant(g, n_rows);
-  const int bm = variant == moe::kVariantLarge ? moe::kLargeBM : moe::kSmallBM;
   if (variant_out)
-    snprintf(variant_out, variant_len, "%s/%s", variant == moe::kVariantLarge ? "large128" : "small32",
+    snprintf(variant_out, variant_len, "%s/%s", moe::variant_name(variant),
              g.fmt == moe::kMxfp4 ? "mxfp4" : "fp8");
-  hipError_t e;
-  e = moe::launch_tile_prefix(g.offsets, g.n_groups, bm, tile_prefix, amax, n_rows, s);
+  hipError_t e = moe::launch_tile_prefix(g.offsets, g.n_groups, moe::variant_rows(variant), tile_prefix, s);
   if (e != hipSuccess) return device_status(e, "tile_prefix");
   if (events && events[MOE_STAGE_GEMM1]) hipEventRecord((hipEvent_t)events[MOE_STAGE_GEMM1], s);
-  e = moe::launch_gemm1(variant, g, x, tile_prefix, n_rows, h, amax, s);
+  e = moe::launch_gemm1(variant, g, x, tile_prefix, n_rows, h, s);
   if (e != hipSuccess) return device_status(e, "gemm1");
-  if (events && events[MOE_STAGE_QUANT_H]) hipEventRecord((hipEvent_t)events[MOE_STAGE_QUANT_H], s);
-  e = moe::launch_quant_h(h, amax, n_rows, g.inter, hq, hs, s);
-  if (e != hipSuccess) return device_status(e, "quant_h");
   if (events && events[MOE_STAGE_GEMM2]) hipEventRecord((hipEvent_t)events[MOE_STAGE_GEMM2], s);
-  moe::RowOperand hrows{{hq, hq + (size_t)x.shared_row0 * g.inter}, {hs, hs + x.shared_row0}, x.shared_row0};
+  moe::RowOperand hrows{{h, h + (size_t)x.shared_row0 * g.inter}, {nullptr, nullptr}, x.shared_row0};
   e = moe::launch_gemm2(variant, g, hrows, tile_prefix, n_rows, y, s);
   if (e != hipSuccess) return device_status(e, "gemm2");
   return ok();
@@ -248,14 +239,12 @@ size_t moe_expert_ffn_workspace_size(int32_t n_rows, const moe_weights_t* w) {
   if (!w || n_rows < 0 || w->n_experts < 1 || w->inter < 1) return 0;
   Carve c(nullptr);
   int32_t* tp;
-  uint32_t* am;
-  float *h, *hs;
-  uint8_t* hq;
-  return ffn_ws(c, n_rows, w->n_experts, w->inter, &tp, &am, &h, &hq, &hs) + 256;
+  uint16_t* h;
+  return ffn_ws(c, n_rows, w->n_experts, w->inter, &tp, &h) + 256;
 }
 
 moe_status_t moe_expert_ffn(const uint8_t* xq_rows, const float* xs_rows, int32_t n_rows,
-                            const int32_t* expert_offsets, const moe_weights_t* w, uint16_t* y_rows,
+                            const int32_t* expert_offsets, const moe_weights_t* w, float* y_rows,
                             void* ws, size_t ws_bytes, void* stream) {
   MOE_CHECK(check_weights(w, "weights"));
   if (n_rows < 0) return fail(MOE_ERR_SHAPE, "n_rows = %d < 0", n_rows);
@@ -270,18 +259,16 @@ moe_status_t moe_expert_ffn(const uint8_t* xq_rows, const float* xs_rows, int32_
   MOE_CHECK(need(ws, "ws"));
   Carve c(ws);
   int32_t* tp;
-  uint32_t* am;
-  float *h, *hs;
-  uint8_t* hq;
-  ffn_ws(c, n_rows, w->n_experts, w->inter, &tp, &am, &h, &hq, &hs);
+  uint16_t* h;
+  ffn_ws(c, n_rows, w->n_experts, w->inter, &tp, &h);
   const moe::FfnGroups g = make_groups(w, nullptr, expert_offsets);
   moe::RowOperand x{{xq_rows, xq_rows}, {xs_rows, xs_rows}, (long)n_rows};
-  return run_ffn(g, x, n_rows, y_rows, tp, am, h, hq, hs, (hipStream_t)stream, nullptr, nullptr, 0);
+  return run_ffn(g, x, n_rows, y_rows, tp, h, (hipStream_t)stream, nullptr, nullptr, 0);
 }
 
 // ---------------------------------------------------------------------------
-moe_status_t moe_combine(const uint16_t* y_rows, const int32_t* pair_to_row, const float* topk_w,
-                         int32_t T, int32_t H, int32_t top_k, const uint16_t* y_shared,
+moe_status_t moe_combine(const float* y_rows, const int32_t* pair_to_row, const float* topk_w,
+                         int32_t T, int32_t H, int32_t top_k, const float* y_shared,
                          const float* norm_gamma, float norm_eps, uint16_t* out, void* stream) {
   if (T < 0) return fail(MOE_ERR_SHAPE, "T = %d < 0", T);
   if (top_k < 1 || top_k > moe::kMaxTopK) return fail(MOE_ERR_SHAPE, "top_k = %d outside [1, %d]", top_k, moe::kMaxTopK);
@@ -302,10 +289,10 @@ moe_status_t moe_combine(const uint16_t* y_rows, const int32_t* pair_to_row, con
 // ---------------------------------------------------------------------------
 struct ForwardLayout {
   int32_t *ids, *counts, *offsets, *p2r, *r2p, *hist, *base, *tile_prefix;
-  float *w, *xs_rows, *xs_tok, *h, *hs;
-  uint8_t *xq_rows, *xq_tok, *hq;
-  uint32_t* amax;
-  uint16_t* y_rows;
+  float *w, *xs_rows, *xs_tok;
+  uint8_t *xq_rows, *xq_tok;
+  uint16_t* h;
+  float* y_rows;
   size_t bytes;
 };
 
@@ -328,8 +315,8 @@ static ForwardLayout forward_layout(void* ws, int32_t T, int32_t k, int32_t E, i
   L.xs_rows = c.take<float>(R);
   L.xq_tok = shared ? c.take<uint8_t>((size_t)T * H) : nullptr;
   L.xs_tok = shared ? c.take<float>(T) : nullptr;
-  L.y_rows = c.take<uint16_t>((size_t)rows * H);
-  ffn_ws(c, rows, E + (shared ? 1 : 0), I, &L.tile_prefix, &L.amax, &L.h, &L.hq, &L.hs);
+  L.y_rows = c.take<float>((size_t)rows * H);
+  ffn_ws(c, rows, E + (shared ? 1 : 0), I, &L.tile_prefix, &L.h);
   L.bytes = c.used + 256;
   return L;
 }
@@ -412,7 +399,7 @@ moe_status_t moe_forward(const uint16_t* x, const float* logits, int32_t T, int3
   const long rows = R + (sh ? T : 0);
   moe::RowOperand xr{{L.xq_rows, sh ? L.xq_tok : L.xq_rows}, {L.xs_rows, sh ? L.xs_tok : L.xs_rows}, R};
   char* vout = dbg ? dbg->variant : nullptr;
-  MOE_CHECK(run_ffn(g, xr, rows, L.y_rows, L.tile_prefix, L.amax, L.h, L.hq, L.hs, s, ev, vout,
+  MOE_CHECK(run_ffn(g, xr, rows, L.y_rows, L.tile_prefix, L.h, s, ev, vout,
                     dbg ? sizeof(dbg->variant) : 0));
 
   if (ev && ev[MOE_STAGE_COMBINE]) hipEventRecord((hipEvent_t)ev[MOE_STAGE_COMBINE], s);

@@ -30,8 +30,9 @@ Readings where the pages are silent (each listed in the design notes):
 top-k compares the raw fp32 logits with ties to the lower expert index and
 keeps slots in that order; fp8 is OCP E4M3FN with round-half-even and
 saturation; scales are amax/448 by IEEE binary32 division (1 when amax is 0);
-W1 is the gate and W3 the up projection; the FFN intermediate h is rounded to
-binary32 and quantised per routed row like the tokens; the shared expert reads
+W1 is the gate and W3 the up projection; the FFN intermediate h stays in the
+activation dtype, bf16 (only the tokens are quantised, before the scatter);
+the shared expert reads
 the same quantised tokens and is added with weight 1 after the routed sum
 (after the RMSNorm when there is one); the output is bfloat16.
 """
@@ -82,7 +83,7 @@ def route(logits, top_k):
 
 
 # ----------------------------------------------------------------------------
-# 2. Per-row fp8 quantisation (tokens, and the FFN intermediate)
+# 2. Per-token fp8 quantisation
 # ----------------------------------------------------------------------------
 
 
@@ -210,20 +211,17 @@ def expert_ffn(xq_rows, xs_rows, offsets, weights):
     For row r in expert e's segment (rows offsets[e] .. offsets[e+1]-1):
       g = (sum_k q_r[k] W1[e][n][k]) * xs_r * s1[e][n]
       u = (sum_k q_r[k] W3[e][n][k]) * xs_r * s3[e][n]
-      h = binary32( SiLU(g) * u )
-      hq, hs = per-row e4m3 quantisation of h (as for tokens)
-      y[r][j] = (sum_n hq_r[n] W2[e][j][n]) * hs_r * s2[e][j]
-    The sums of fp8 (or e2m1 * 2^k) products are exact in float64.
-    Returns (y float64 [R][H], h float32 [R][I], hq uint8 [R][I], hs float32 [R]).
+      h = bf16( SiLU(g) * u )                  (the activation dtype)
+      y[r][j] = (sum_n h_r[n] W2[e][j][n]) * s2[e][j]
+    The sums of fp8 (or e2m1 * 2^k) products, and of bf16 x fp8 products,
+    are exact in float64.  Returns (y float64 [R][H], h uint16 bf16 bits [R][I]).
     """
     xq_rows = np.asarray(xq_rows)
     xs_rows = np.asarray(xs_rows, dtype=np.float64)
     R = xq_rows.shape[0]
     H, I = weights.hidden, weights.inter
     y = np.zeros((R, H), dtype=np.float64)
-    h_all = np.zeros((R, I), dtype=np.float32)
-    hq_all = np.zeros((R, I), dtype=np.uint8)
-    hs_all = np.ones(R, dtype=np.float32)
+    h_all = np.zeros((R, I), dtype=np.uint16)
     for e in range(len(offsets) - 1):
         r0, r1 = int(offsets[e]), int(offsets[e + 1])
         if r1 == r0:
@@ -232,11 +230,10 @@ def expert_ffn(xq_rows, xs_rows, offsets, weights):
         a = e4m3_decode(xq_rows[r0:r1])
         g = (a @ W1.T) * xs_rows[r0:r1, None] * c1[None, :]
         u = (a @ W3.T) * xs_rows[r0:r1, None] * c3[None, :]
-        h = (silu(g) * u).astype(np.float32)
-        hq, hs = quantize_rows_f32(h)
-        y[r0:r1] = (e4m3_decode(hq) @ W2.T) * hs.astype(np.float64)[:, None] * c2[None, :]
-        h_all[r0:r1], hq_all[r0:r1], hs_all[r0:r1] = h, hq, hs
-    return y, h_all, hq_all, hs_all
+        h = bf16_encode(silu(g) * u)
+        y[r0:r1] = (bf16_decode(h) @ W2.T) * c2[None, :]
+        h_all[r0:r1] = h
+    return y, h_all
 
 
 # ----------------------------------------------------------------------------
@@ -249,10 +246,12 @@ def rms_norm(o, gamma, eps):
     return o / np.sqrt(np.mean(o * o, axis=1, keepdims=True) + eps) * gamma[None, :]
 
 
-def combine(y_rows, pair_to_row, topk_w, y_shared=None, norm_gamma=None, norm_eps=1e-6):
+def combine(y_rows, pair_to_row, topk_w, y_shared=None, norm_gamma=None, norm_eps=1e-6,
+            rounded=True):
     """out[t] = bf16( [RMSNorm]( sum_j w[t][j] * y_rows[pair_to_row[t][j]] ) + y_shared[t] ).
 
-    The routed sum runs over slots j = 0..k-1 in order.  Returns uint16 bf16 bits.
+    The routed sum runs over slots j = 0..k-1 in order.  Returns uint16 bf16
+    bits, or with rounded=False the float64 value before the bf16 rounding.
     """
     p2r = np.asarray(pair_to_row)
     w = np.asarray(topk_w, dtype=np.float64)
@@ -264,7 +263,7 @@ def combine(y_rows, pair_to_row, topk_w, y_shared=None, norm_gamma=None, norm_ep
         o = rms_norm(o, np.asarray(norm_gamma, dtype=np.float64), norm_eps)
     if y_shared is not None:
         o = o + y_shared
-    return bf16_encode(o)
+    return bf16_encode(o) if rounded else o
 
 
 # ----------------------------------------------------------------------------
@@ -283,16 +282,16 @@ def forward(x_bf16, logits, top_k, routed, shared=None, norm_gamma=None, norm_ep
     xq, xs = quantize_tokens(x_bf16)
     counts, offsets = expert_counts_offsets(ids, routed.n_experts)
     pair_to_row, row_to_pair, xq_rows, xs_rows = permute_rows(ids, offsets, xq, xs)
-    y_rows, h, hq, hs = expert_ffn(xq_rows, xs_rows, offsets, routed)
+    y_rows, h = expert_ffn(xq_rows, xs_rows, offsets, routed)
     y_shared = None
     if shared is not None:
         T = xq.shape[0]
         y_shared = expert_ffn(xq, xs, np.array([0, T]), shared)[0]
-    out = combine(y_rows, pair_to_row, w, y_shared, norm_gamma, norm_eps)
+    exact = combine(y_rows, pair_to_row, w, y_shared, norm_gamma, norm_eps, rounded=False)
     return dict(topk_ids=ids, topk_w=w, xq=xq, xs=xs, counts=counts, offsets=offsets,
                 pair_to_row=pair_to_row, row_to_pair=row_to_pair, xq_rows=xq_rows,
-                xs_rows=xs_rows, h=h, hq=hq, hs=hs, y_rows=y_rows, y_shared=y_shared,
-                out=out)
+                xs_rows=xs_rows, h=h, y_rows=y_rows, y_shared=y_shared,
+                out_exact=exact, out=bf16_encode(exact))
 
 
 def forward_sampled(x_bf16, logits, top_k, routed, tokens, shared=None,
@@ -301,8 +300,9 @@ def forward_sampled(x_bf16, logits, top_k, routed, tokens, shared=None,
 
     Routing runs for all tokens (or is taken from ``routing`` = (topk_ids,
     topk_w) as returned by ``route``); quantisation, permutation, FFN and
-    combine run only for the pairs of ``tokens``.  Returns ``out`` of shape
-    [len(tokens)][H] (row i is token tokens[i]).
+    combine run only for the pairs of ``tokens``.  Returns the float64 output
+    before its bf16 rounding, shape [len(tokens)][H] (row i is token
+    tokens[i]).
     """
     tokens = np.asarray(tokens, dtype=np.int64)
     ids, w = route(logits, top_k) if routing is None else routing
@@ -314,4 +314,4 @@ def forward_sampled(x_bf16, logits, top_k, routed, tokens, shared=None,
     y_shared = None
     if shared is not None:
         y_shared = expert_ffn(xq, xs, np.array([0, len(tokens)]), shared)[0]
-    return combine(y_sub, sub_p2r, w[tokens], y_shared, norm_gamma, norm_eps)
+    return combine(y_sub, sub_p2r, w[tokens], y_shared, norm_gamma, norm_eps, rounded=False)

@@ -179,9 +179,8 @@ def check_closed_form(forward=oracle.forward):
     """One token, H=2, I=1, one expert, worked by hand.
 
     x = [448, 224] -> s = 1, codes exact.  W1 = [2^-8, 0] -> g = 1.75;
-    W3 = [0, 2^-7] with s3 = 2 -> u = 3.5.  h = SiLU(1.75) * 3.5.  The
-    intermediate quantises to 448 * hs with hs = h/448, and W2 = [1, -0.5]
-    gives y = [h, -h/2] up to binary32 rounding.  A swapped gate/up would give
+    W3 = [0, 2^-7] with s3 = 2 -> u = 3.5.  h = bf16(SiLU(1.75) * 3.5) and
+    W2 = [1, -0.5] gives y = [h, -h/2].  A swapped gate/up would give
     SiLU(3.5) * 1.75 instead.
     """
     x = bf16_bits(np.array([[448.0, 224.0]]))
@@ -203,8 +202,8 @@ def test_closed_form():
 def check_dense_reduction(forward=oracle.forward):
     """E = 1, k = 1: the layer is a dense gated FFN on the quantised tokens.
 
-    Reference built from torch library calls in float64: linear, silu, the
-    float8_e4m3fn cast for the intermediate's per-row quantisation.
+    Reference built from torch library calls in float64: linear, silu, and the
+    bfloat16 cast of the intermediate.
     """
     x, _, W, _ = small_case(T=9, H=64, I=48, E=1, k=1, seed=11)
     res = forward(x, np.zeros((9, 1), np.float32), 1, W)
@@ -215,14 +214,12 @@ def check_dense_reduction(forward=oracle.forward):
     xs_t = torch.from_numpy(xs.astype(np.float64))[:, None]
     g = torch.nn.functional.linear(A, W1) * xs_t * torch.from_numpy(W.s1[0].astype(np.float64))
     u = torch.nn.functional.linear(A, W3) * xs_t * torch.from_numpy(W.s3[0].astype(np.float64))
-    h = (torch.nn.functional.silu(g) * u).to(torch.float32)
-    hs = (h.abs().amax(dim=1) / 448.0).to(torch.float32)
-    hq = (h / hs[:, None]).clamp(-448, 448).to(torch.float8_e4m3fn).to(torch.float64)
-    y = torch.nn.functional.linear(hq, W2) * hs.to(torch.float64)[:, None] * torch.from_numpy(W.s2[0].astype(np.float64))
+    h = (torch.nn.functional.silu(g) * u).to(torch.float32).to(torch.bfloat16).to(torch.float64)
+    y = torch.nn.functional.linear(h, W2) * torch.from_numpy(W.s2[0].astype(np.float64))
     ref = y.to(torch.float32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     # the oracle rounds float64 -> bf16 once; torch goes via binary32: allow 1 ulp
     diff = np.abs(res["out"].astype(np.int32) - ref.astype(np.int32))
-    assert diff.max() <= 1 and (diff == 0).mean() > 0.99
+    assert diff.max() <= 1 and (diff == 0).mean() > 0.97
 
 
 def test_dense_reduction():
@@ -348,4 +345,4 @@ def test_forward_sampled_matches_forward():
     full = oracle.forward(x, logits, k, W, shared=Ws)
     toks = np.array([3, 17, 0, 29])
     samp = oracle.moe.forward_sampled(x, logits, k, W, toks, shared=Ws)
-    assert (samp == full["out"][toks]).all()
+    assert (samp == full["out_exact"][toks]).all()
