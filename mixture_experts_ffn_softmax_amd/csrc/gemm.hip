@@ -148,6 +148,15 @@ __device__ __forceinline__ void wait_barrier() {
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)p; }
 
+// LDS swizzles: the 16-byte slot that holds logical chunk c of tile row r.
+// A fragment read has 32 lanes on 32 consecutive rows reading the same chunk;
+// these make every 8 and every 16 consecutive lanes hit distinct bank groups
+// (conflict-free whether the LDS serves 8 or 16 lanes of a 16-byte read per
+// cycle).
+__device__ __forceinline__ int swz64(int r, int c) { return c ^ (((r >> 1) ^ (r >> 2)) & 3); }   // 64-byte rows
+__device__ __forceinline__ int swz128(int r, int c) { return c ^ (r & 7) ^ ((r >> 3) & 1); }    // 128-byte rows
+
+
 // ---- tile lookup -----------------------------------------------------------
 
 // Workgroup b < total -> logical tile; each XCD gets a contiguous range.
@@ -204,19 +213,40 @@ __device__ __forceinline__ const uint8_t* row_ptr(const GemmParams& p, const Til
 // ============================================================================
 //
 // LDS stage: BM token rows then 256 channel rows (W1 rows n0.., then W3 rows
-// n0..), each 64 bytes of the K step, as 4 16-byte slots with slot =
-// chunk ^ ((row >> 1) & 3) (8 consecutive rows of one chunk hit 8 distinct
-// bank groups).  One dma16 fills 16 rows.
+// n0..), each 64 bytes of the K step, as 4 16-byte slots (swz64).  One dma16
+// fills 16 rows.  Each K step issues this stage's successor STAGES-1 steps
+// ahead, one pair of dma16 after each group of MFMAs, so the loads drain
+// while the matrix cores work instead of stalling the wave in one burst.
 
 constexpr int kLgCh = 256;    // channel rows per tile
+#ifndef MOE_LARGE_WN
+#define MOE_LARGE_WN 4
+#endif
+constexpr int kLgWN = MOE_LARGE_WN;   // waves along the channel rows (2 x kLgWN waves)
 
-template <int BM, int STAGES>
-__global__ __launch_bounds__(256, 1) void gemm1_large_kernel(GemmParams p) {
+// fast SiLU for the epilogue (h is rounded to bf16 afterwards): g * 1/(1 + 2^(-g log2 e))
+__device__ __forceinline__ float silu_fast(float g) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * g));
+}
+
+// Waves form a 2 x WN grid: wave (wm, wn) owns tokens [wm * BM/2, +BM/2) and,
+// of the 128 gate and 128 up channel rows, the slice [wn * 128/WN, +128/WN)
+// of each (so gate and up of one channel meet in the same lane).  WN = 4
+// gives 8 waves, two per SIMD: while one waits on its loads or the barrier,
+// the other keeps the matrix core busy.
+template <int BM, int WN, int STAGES>
+__global__ __launch_bounds__(128 * WN, 1) void gemm1_large_kernel(GemmParams p) {
+  constexpr int NW = 2 * WN;                // waves
   constexpr int kRows = BM + kLgCh;
   constexpr int kStage = kRows * 64;
   constexpr int kDma = kRows / 16;          // dma16 per stage
-  constexpr int kPer = kDma / 4;            // per wave
+  constexpr int kPer = kDma / NW;           // per wave
+  static_assert(kDma % NW == 0, "dma split");
   constexpr int TF = BM / 64;               // token fragments per wave (32 rows each)
+  constexpr int CF = 4 / WN;                // gate fragments per wave (= up fragments)
+  constexpr int NF = 2 * CF;
+  constexpr int kHRow = 128 * 2 + 16;       // padded LDS row of the h tile (bytes)
+  static_assert(STAGES * kStage >= BM * kHRow, "h staging fits in the ring");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * kStage];
   __shared__ int s_tp[kMaxExperts + 2];
   MOE_TILE_PROLOGUE(BM);
@@ -234,7 +264,7 @@ __global__ __launch_bounds__(256, 1) void gemm1_large_kernel(GemmParams p) {
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     const int row = (wave * kPer + i) * 16 + (lane >> 2);
-    const int chunk = (lane & 3) ^ ((row >> 1) & 3);
+    const int chunk = swz64(row, lane & 3);
     const uint8_t* base;
     if (row < BM) {
       int r = ti.row0 + row;
@@ -247,26 +277,26 @@ __global__ __launch_bounds__(256, 1) void gemm1_large_kernel(GemmParams p) {
     src[i] = base + chunk * 16;
   }
   const uint32_t lds0 = lds_addr(smem);
-  auto issue = [&](int ks) {
+  auto issue = [&](int ks, int i0, int i1) {
     const uint32_t st = lds0 + (ks % STAGES) * kStage;
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) dma16(src[i] + ((long)ks << 6), st + (wave * kPer + i) * 1024);
+    for (int i = i0; i < i1; ++i) dma16(src[i] + ((long)ks << 6), st + (wave * kPer + i) * 1024);
   };
 
-  // fragment addressing: lane reads row (base + l%32), bytes [32h, 32h + 32)
-  const int wm = wave >> 1, wn = wave & 1;
+  // fragment addressing: lane reads row (base + l%32), bytes [32h, 32h + 32);
+  // fragment bases are multiples of 32 rows, so the swizzle depends on l%32
+  const int wm = wave / WN, wn = wave % WN;
   const int l32 = lane & 31, hh = lane >> 5;
-  const int sw = (l32 >> 1) & 3;
-  const int fo0 = l32 * 64 + (((2 * hh) ^ sw) << 4);
-  const int fo1 = l32 * 64 + (((2 * hh + 1) ^ sw) << 4);
-  int chbase[4];
+  const int fo0 = l32 * 64 + (swz64(l32, 2 * hh) << 4);
+  const int fo1 = l32 * 64 + (swz64(l32, 2 * hh + 1) << 4);
+  int chbase[NF];
 #pragma unroll
-  for (int f = 0; f < 4; ++f)
-    chbase[f] = (BM + ((f < 2) ? (wn * 64 + f * 32) : (kLgCh / 2 + wn * 64 + (f - 2) * 32))) * 64;
+  for (int f = 0; f < NF; ++f)
+    chbase[f] = (BM + (f < CF ? 0 : kLgCh / 2) + wn * (128 / WN) + (f % CF) * 32) * 64;
 
-  v16f acc[4][TF];
+  v16f acc[NF][TF];
 #pragma unroll
-  for (int f = 0; f < 4; ++f)
+  for (int f = 0; f < NF; ++f)
 #pragma unroll
     for (int t = 0; t < TF; ++t)
 #pragma unroll
@@ -274,12 +304,13 @@ __global__ __launch_bounds__(256, 1) void gemm1_large_kernel(GemmParams p) {
 
 #pragma unroll
   for (int s = 0; s < STAGES - 1; ++s)
-    if (s < nk) issue(s);
+    if (s < nk) issue(s, 0, kPer);
 
+  constexpr int kDmaPerGroup = (kPer + NF - 1) / NF;
   for (int ks = 0; ks < nk; ++ks) {
     if (ks + STAGES - 2 < nk) wait_barrier<(STAGES - 2) * kPer>();
     else wait_barrier<0>();
-    if (ks + STAGES - 1 < nk) issue(ks + STAGES - 1);
+    const bool more = ks + STAGES - 1 < nk;
     const uint8_t* st = smem + (ks % STAGES) * kStage;
     v8i x[TF];
 #pragma unroll
@@ -287,44 +318,80 @@ __global__ __launch_bounds__(256, 1) void gemm1_large_kernel(GemmParams p) {
       const uint8_t* r = st + (wm * (BM / 2) + t * 32) * 64;
       x[t] = as_v8i(*reinterpret_cast<const uint4*>(r + fo0), *reinterpret_cast<const uint4*>(r + fo1));
     }
+    v8i w = as_v8i(*reinterpret_cast<const uint4*>(st + chbase[0] + fo0),
+                   *reinterpret_cast<const uint4*>(st + chbase[0] + fo1));
 #pragma unroll
-    for (int f = 0; f < 4; ++f) {
-      const uint8_t* r = st + chbase[f];
-      const v8i w = as_v8i(*reinterpret_cast<const uint4*>(r + fo0), *reinterpret_cast<const uint4*>(r + fo1));
+    for (int f = 0; f < NF; ++f) {
+      v8i wnext = w;
+      if (f + 1 < NF)
+        wnext = as_v8i(*reinterpret_cast<const uint4*>(st + chbase[f + 1] + fo0),
+                       *reinterpret_cast<const uint4*>(st + chbase[f + 1] + fo1));
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int t = 0; t < TF; ++t) acc[f][t] = mfma32_fp8(w, x[t], acc[f][t]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (more) {
+        const int i0 = f * kDmaPerGroup, i1 = (f + 1) * kDmaPerGroup < kPer ? (f + 1) * kDmaPerGroup : kPer;
+        if (i0 < i1) issue(ks + STAGES - 1, i0, i1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      w = wnext;
     }
   }
 
-  // ---- epilogue: lane holds token l%32 of each token fragment and, per
-  // group q of 4 accumulator entries, channels 8q + 4h .. +3 of the fragment
+  // ---- epilogue.  Lane holds token l%32 of each token fragment and, per
+  // group q of 4 accumulator entries, channels 8q + 4h .. +3 of the fragment.
+  // h = bf16(SiLU(g) * u) goes through a padded LDS tile [BM][128 channels]
+  // so that the global stores are whole 256-byte rows.
   const float* S1 = reinterpret_cast<const float*>(p.sa[ti.wi]) + ti.eg * p.N;
   const float* S3 = reinterpret_cast<const float*>(p.sb[ti.wi]) + ti.eg * p.N;
+  float4 s1v[CF][4], s3v[CF][4];
+#pragma unroll
+  for (int c = 0; c < CF; ++c)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int ch = n0 + wn * (128 / WN) + c * 32 + 8 * q + 4 * hh;
+      s1v[c][q] = *reinterpret_cast<const float4*>(S1 + ch);
+      s3v[c][q] = *reinterpret_cast<const float4*>(S3 + ch);
+    }
+  float xs[TF];
 #pragma unroll
   for (int t = 0; t < TF; ++t) {
-    const int grow = ti.row0 + wm * (BM / 2) + t * 32 + l32;
-    if (grow >= ti.row1) continue;
-    const float xs = p.a_scale[ti.wi][grow - (ti.wi ? p.shared_row0 : 0)];
-    uint16_t* hrow = p.h + (long)grow * p.N;
+    int grow = ti.row0 + wm * (BM / 2) + t * 32 + l32;
+    if (grow >= ti.row1) grow = ti.row1 - 1;
+    xs[t] = p.a_scale[ti.wi][grow - (ti.wi ? p.shared_row0 : 0)];
+  }
+  wait_barrier<0>();     // every wave is done reading the stage ring
 #pragma unroll
-    for (int f = 0; f < 2; ++f) {
+  for (int t = 0; t < TF; ++t) {
+    uint8_t* hrow = smem + (wm * (BM / 2) + t * 32 + l32) * kHRow;
+#pragma unroll
+    for (int c = 0; c < CF; ++c)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int ch = n0 + wn * 64 + f * 32 + 8 * q + 4 * hh;
-        const float4 s1 = *reinterpret_cast<const float4*>(S1 + ch);
-        const float4 s3 = *reinterpret_cast<const float4*>(S3 + ch);
-        const float sg[4] = {s1.x, s1.y, s1.z, s1.w};
-        const float su[4] = {s3.x, s3.y, s3.z, s3.w};
+        const float sg[4] = {s1v[c][q].x, s1v[c][q].y, s1v[c][q].z, s1v[c][q].w};
+        const float su[4] = {s3v[c][q].x, s3v[c][q].y, s3v[c][q].z, s3v[c][q].w};
         uint32_t b[4];
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const float g = acc[f][t][4 * q + v] * xs * sg[v];
-          const float u = acc[f + 2][t][4 * q + v] * xs * su[v];
-          b[v] = bf16_rne(silu(g) * u);
+          const float g = acc[c][t][4 * q + v] * xs[t] * sg[v];
+          const float u = acc[CF + c][t][4 * q + v] * xs[t] * su[v];
+          b[v] = bf16_rne(silu_fast(g) * u);
         }
-        *reinterpret_cast<uint2*>(hrow + ch) = make_uint2(b[0] | (b[1] << 16), b[2] | (b[3] << 16));
+        const int col = wn * (128 / WN) + c * 32 + 8 * q + 4 * hh;
+        *reinterpret_cast<uint2*>(hrow + col * 2) = make_uint2(b[0] | (b[1] << 16), b[2] | (b[3] << 16));
       }
-    }
+  }
+  __syncthreads();
+  // BM rows x 256 bytes: 16 threads per row, 16 bytes each
+  constexpr int kRowsPerPass = 128 * WN / 16;
+#pragma unroll
+  for (int r0 = 0; r0 < BM; r0 += kRowsPerPass) {
+    const int r = r0 + (int)(threadIdx.x >> 4), c = threadIdx.x & 15;
+    const int grow = ti.row0 + r;
+    if (grow < ti.row1)
+      *reinterpret_cast<uint4*>(p.h + (long)grow * p.N + n0 + c * 8) =
+          *reinterpret_cast<const uint4*>(smem + r * kHRow + c * 16);
   }
 }
 
@@ -332,17 +399,22 @@ __global__ __launch_bounds__(256, 1) void gemm1_large_kernel(GemmParams p) {
 // large GEMM2: bf16 h x W2 (e4m3 -> bf16) -> y (fp32)
 // ============================================================================
 //
-// LDS stage: BM h rows of 64 bf16 (128 bytes, 8 slots, slot = chunk ^ (row &
-// 7)) then 256 W2 rows of 64 e4m3 codes (64 bytes, as in GEMM1).
+// LDS stage: BM h rows of 64 bf16 (128 bytes, 8 slots, swz128) then 256 W2
+// rows of 64 e4m3 codes (64 bytes, swz64).  Waves form a 2 x WN grid: wave
+// (wm, wn) owns tokens [wm * BM/2, +BM/2) and W2 rows [wn * 256/WN, +256/WN).
+// DMA issue is interleaved with the MFMA groups as in GEMM1.
 
-template <int BM, int STAGES>
-__global__ __launch_bounds__(256, 1) void gemm2_large_kernel(GemmParams p) {
+template <int BM, int WN, int STAGES>
+__global__ __launch_bounds__(128 * WN, 1) void gemm2_large_kernel(GemmParams p) {
+  constexpr int NW = 2 * WN;
   constexpr int kTokBytes = BM * 128;
   constexpr int kStage = kTokBytes + kLgCh * 64;
   constexpr int kDmaT = BM / 8;             // dma16 for h rows (8 rows each)
   constexpr int kDmaW = kLgCh / 16;         // dma16 for W2 rows (16 rows each)
-  constexpr int kPer = (kDmaT + kDmaW) / 4;
+  constexpr int kPer = (kDmaT + kDmaW) / NW;
+  static_assert((kDmaT + kDmaW) % NW == 0, "dma split");
   constexpr int TF = BM / 64;
+  constexpr int NF = 8 / WN;                // W2 fragments per wave
   __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * kStage];
   __shared__ int s_tp[kMaxExperts + 2];
   MOE_TILE_PROLOGUE(BM);
@@ -361,43 +433,42 @@ __global__ __launch_bounds__(256, 1) void gemm2_large_kernel(GemmParams p) {
     const int q = wave * kPer + i;
     if (q < kDmaT) {
       const int row = q * 8 + (lane >> 3);
-      const int chunk = (lane & 7) ^ (row & 7);
+      const int chunk = swz128(row, lane & 7);
       int r = ti.row0 + row;
       if (r >= ti.row1) r = ti.row1 - 1;
       src[i] = row_ptr(p, ti, r, 2L * K) + chunk * 16;
       step[i] = 128;
     } else {
       const int row = (q - kDmaT) * 16 + (lane >> 2);
-      const int chunk = (lane & 3) ^ ((row >> 1) & 3);
+      const int chunk = swz64(row, lane & 3);
       src[i] = W2 + (long)(n0 + row) * K + chunk * 16;
       step[i] = 64;
     }
   }
   const uint32_t lds0 = lds_addr(smem);
-  auto issue = [&](int ks) {
+  auto issue = [&](int ks, int i0, int i1) {
     const uint32_t st = lds0 + (ks % STAGES) * kStage;
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
+    for (int i = i0; i < i1; ++i) {
       const int q = wave * kPer + i;
       const uint32_t dst = (q < kDmaT) ? st + q * 1024 : st + kTokBytes + (q - kDmaT) * 1024;
       dma16(src[i] + step[i] * ks, dst);
     }
   };
 
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WN, wn = wave % WN;
   const int l32 = lane & 31, hh = lane >> 5;
   // h fragment: row l32, bf16 elements [32h, 32h + 32) = chunks 4h .. 4h+3
   int ho[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) ho[i] = l32 * 128 + (((4 * hh + i) ^ (l32 & 7)) << 4);
+  for (int i = 0; i < 4; ++i) ho[i] = l32 * 128 + (swz128(l32, 4 * hh + i) << 4);
   // W2 fragment: row l32, codes [32h, 32h + 32) = chunks 2h, 2h+1
-  const int sw = (l32 >> 1) & 3;
-  const int wo0 = l32 * 64 + (((2 * hh) ^ sw) << 4);
-  const int wo1 = l32 * 64 + (((2 * hh + 1) ^ sw) << 4);
+  const int wo0 = l32 * 64 + (swz64(l32, 2 * hh) << 4);
+  const int wo1 = l32 * 64 + (swz64(l32, 2 * hh + 1) << 4);
 
-  v16f acc[4][TF];
+  v16f acc[NF][TF];
 #pragma unroll
-  for (int f = 0; f < 4; ++f)
+  for (int f = 0; f < NF; ++f)
 #pragma unroll
     for (int t = 0; t < TF; ++t)
 #pragma unroll
@@ -405,12 +476,13 @@ __global__ __launch_bounds__(256, 1) void gemm2_large_kernel(GemmParams p) {
 
 #pragma unroll
   for (int s = 0; s < STAGES - 1; ++s)
-    if (s < nk) issue(s);
+    if (s < nk) issue(s, 0, kPer);
 
+  constexpr int kDmaPerGroup = (kPer + NF - 1) / NF;
   for (int ks = 0; ks < nk; ++ks) {
     if (ks + STAGES - 2 < nk) wait_barrier<(STAGES - 2) * kPer>();
     else wait_barrier<0>();
-    if (ks + STAGES - 1 < nk) issue(ks + STAGES - 1);
+    const bool more = ks + STAGES - 1 < nk;
     const uint8_t* st = smem + (ks % STAGES) * kStage;
     v8bf x[TF][4];
 #pragma unroll
@@ -420,33 +492,46 @@ __global__ __launch_bounds__(256, 1) void gemm2_large_kernel(GemmParams p) {
       for (int i = 0; i < 4; ++i) x[t][i] = as_v8bf(*reinterpret_cast<const uint4*>(r + ho[i]));
     }
 #pragma unroll
-    for (int f = 0; f < 4; ++f) {
-      const uint8_t* r = st + kTokBytes + (wn * 128 + f * 32) * 64;
+    for (int f = 0; f < NF; ++f) {
+      const uint8_t* r = st + kTokBytes + (wn * (256 / WN) + f * 32) * 64;
       const uint4 c0 = *reinterpret_cast<const uint4*>(r + wo0);
       const uint4 c1 = *reinterpret_cast<const uint4*>(r + wo1);
       const uint32_t cw[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
       v8bf w[4];
       fp8x32_to_bf16(cw, w);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int t = 0; t < TF; ++t)
           acc[f][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w[i], x[t][i], acc[f][t], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (more) {
+        const int i0 = f * kDmaPerGroup, i1 = (f + 1) * kDmaPerGroup < kPer ? (f + 1) * kDmaPerGroup : kPer;
+        if (i0 < i1) issue(ks + STAGES - 1, i0, i1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
   const float* S2 = reinterpret_cast<const float*>(p.sa[ti.wi]) + ti.eg * p.N;
+  float4 s2v[NF][4];
+#pragma unroll
+  for (int f = 0; f < NF; ++f)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      s2v[f][q] = *reinterpret_cast<const float4*>(S2 + n0 + wn * (256 / WN) + f * 32 + 8 * q + 4 * hh);
 #pragma unroll
   for (int t = 0; t < TF; ++t) {
     const int grow = ti.row0 + wm * (BM / 2) + t * 32 + l32;
     if (grow >= ti.row1) continue;
     float* yrow = p.y + (long)grow * p.N;
 #pragma unroll
-    for (int f = 0; f < 4; ++f)
+    for (int f = 0; f < NF; ++f)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int ch = n0 + wn * 128 + f * 32 + 8 * q + 4 * hh;
-        const float4 s2 = *reinterpret_cast<const float4*>(S2 + ch);
+        const int ch = n0 + wn * (256 / WN) + f * 32 + 8 * q + 4 * hh;
+        const float4 s2 = s2v[f][q];
         *reinterpret_cast<float4*>(yrow + ch) =
             make_float4(acc[f][t][4 * q] * s2.x, acc[f][t][4 * q + 1] * s2.y, acc[f][t][4 * q + 2] * s2.z,
                         acc[f][t][4 * q + 3] * s2.w);
@@ -758,8 +843,8 @@ hipError_t launch_gemm1(int variant, const FfnGroups& g, const RowOperand& x, co
   } else {
     p.ntiles = g.inter / (kLgCh / 2);
     const long grid = max_row_tiles(n_rows, g.n_groups, bm) * p.ntiles;
-    if (variant == kVariantLarge256) gemm1_large_kernel<256, 4><<<(unsigned)grid, 256, 0, s>>>(p);
-    else gemm1_large_kernel<128, 4><<<(unsigned)grid, 256, 0, s>>>(p);
+    if (variant == kVariantLarge256) gemm1_large_kernel<256, kLgWN, 4><<<(unsigned)grid, 128 * kLgWN, 0, s>>>(p);
+    else gemm1_large_kernel<128, kLgWN, 4><<<(unsigned)grid, 128 * kLgWN, 0, s>>>(p);
   }
   return hipGetLastError();
 }
@@ -783,8 +868,8 @@ hipError_t launch_gemm2(int variant, const FfnGroups& g, const RowOperand& h, co
   } else {
     p.ntiles = g.hidden / kLgCh;
     const long grid = max_row_tiles(n_rows, g.n_groups, bm) * p.ntiles;
-    if (variant == kVariantLarge256) gemm2_large_kernel<256, 3><<<(unsigned)grid, 256, 0, s>>>(p);
-    else gemm2_large_kernel<128, 4><<<(unsigned)grid, 256, 0, s>>>(p);
+    if (variant == kVariantLarge256) gemm2_large_kernel<256, kLgWN, 3><<<(unsigned)grid, 128 * kLgWN, 0, s>>>(p);
+    else gemm2_large_kernel<128, kLgWN, 4><<<(unsigned)grid, 128 * kLgWN, 0, s>>>(p);
   }
   return hipGetLastError();
 }
