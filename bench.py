@@ -3,8 +3,8 @@
 Default workload: the pages' per-device prefill share (2048 tokens, hidden
 8192, intermediate 2048, 8 local experts, top-2, per-channel fp8 weights,
 plus the shared expert 8192 -> 2048 -> 8192 on every token).  One step is one
-moe_forward (route, quantise + permute, gate-up GEMM, quantise h, down GEMM,
-combine) on resident device inputs.  Weight sets are rotated across steps
+moe_forward (route, quantise + permute, gate-up GEMM with SiLU*gate, down
+GEMM, combine) on resident device inputs.  Weight sets are rotated across steps
 (--copies, default 3) so that the 256 MB last-level cache cannot hold them.
 
 Prints ONE JSON line: metric / value (fp8 TFLOP/s of the whole layer,
@@ -12,9 +12,16 @@ Prints ONE JSON line: metric / value (fp8 TFLOP/s of the whole layer,
 dominant kernel (gate-up GEMM, measured with HIP events on the library's
 stream), the decode-share weight-stream rate, and the CPU oracle timed on a
 bounded sample (reported baseline only).
+
+`roofline.traffic` (HBM bytes per launch of the dominant kernel) comes from
+the FETCH_SIZE / WRITE_SIZE counter summary under profiles/; it is reported
+only while the kernel sources still hash to the value recorded there, and is
+null otherwise.  `--copy-kernel MIB` runs only a plain device copy of that
+size (the counters' calibration) and exits.
 """
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -37,8 +44,55 @@ def parse():
     ap.add_argument("--copies", type=int, default=3)
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-share measurement")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=32)
+    ap.add_argument("--cpu-tokens", type=int, default=2048,
+                    help="tokens in the CPU oracle's sample (FFN + combine of each)")
+    ap.add_argument("--copy-kernel", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (counter calibration)")
     return ap.parse_args()
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm1_prefill_hbm_traffic.txt")
+KERNEL_SOURCES = [os.path.join(ROOT, "mixture_experts_ffn_softmax_amd", "csrc", f)
+                  for f in ("gemm.hip", "device_common.h", "internal.h")]
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per GEMM1 launch from the committed counter summary, or None
+    when the summary is absent or the kernel sources changed since it was taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    fields = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and not line.startswith("#"):
+            key, val = line.split(":", 1)
+            fields[key.strip()] = val.strip()
+    if fields.get("source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return float(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_kernel(mib):
+    """A plain elementwise device copy (negation) of `mib` MiB, five times:
+    reads and writes exactly mib MiB per launch."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    log(f"[bench] copy kernel: 5 launches of {mib} MiB read + {mib} MiB written")
 
 
 def log(*a):
@@ -126,9 +180,10 @@ def time_layer(layer, steps, warmup):
     return (t1 - t0) * 1e3 / steps, stage
 
 
-def cpu_baseline(layer, n_tokens):
+def cpu_baseline(layer, n_tokens, min_seconds=10.0):
     """The oracle, as it stands, on a bounded sample: routing of all tokens
-    plus the FFN / combine of n_tokens sampled tokens."""
+    plus quantise / FFN / combine of n_tokens sampled tokens, repeated until
+    at least min_seconds of host time have been spent."""
     import numpy as np
     import torch
     from threadpoolctl import threadpool_info
@@ -144,18 +199,23 @@ def cpu_baseline(layer, n_tokens):
     x = layer.inp["x"].view(torch.int16).cpu().numpy().view(np.uint16)
     logits = layer.inp["logits"].cpu().numpy()
     Wr, Ws = host(layer.inp["routed"]), host(layer.inp["shared"])
+    n_tokens = min(n_tokens, layer.T)
     tokens = np.sort(np.random.default_rng(0).choice(layer.T, n_tokens, replace=False))
-    t0 = time.perf_counter()
-    oracle.moe.forward_sampled(x, logits, layer.k, Wr, tokens, shared=Ws,
-                               norm_gamma=None if layer.inp["gamma"] is None else layer.inp["gamma"].cpu().numpy(),
-                               norm_eps=layer.inp["eps"])
-    dt = time.perf_counter() - t0
+    gamma = None if layer.inp["gamma"] is None else layer.inp["gamma"].cpu().numpy()
+    passes, t0 = 0, time.perf_counter()
+    while True:
+        oracle.moe.forward_sampled(x, logits, layer.k, Wr, tokens, shared=Ws, norm_gamma=gamma,
+                                   norm_eps=layer.inp["eps"])
+        passes += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
     rows = n_tokens * layer.k + (n_tokens if Ws is not None else 0)
-    flops = 6.0 * layer.H * layer.I * rows
+    flops = 6.0 * layer.H * layer.I * rows * passes
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     return dict(value=flops / dt / 1e12, unit="TFLOP/s", cores=int(threads), kind="oracle",
-                sample=f"routing of all {layer.T} tokens + quantise/permute/FFN/combine of {n_tokens} "
-                       f"sampled tokens (float64 NumPy), {dt:.1f} s wall")
+                sample=f"{passes} passes of: routing of all {layer.T} tokens + quantise/permute/FFN/combine "
+                       f"of {n_tokens} sampled tokens (float64 NumPy); {dt:.1f} s wall in total")
 
 
 def main():
@@ -166,6 +226,9 @@ def main():
         sys.exit(2)
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_kernel:
+        copy_kernel(args.copy_kernel)
+        return
 
     log(f"[bench] workload {args.config}: generating inputs ({args.copies} weight copies)")
     layer = Layer(args.config, args.copies)
@@ -201,7 +264,7 @@ def main():
         "frac_fp8_peak_layer": round(value / PEAK_FP8_TFLOPS, 4),
         "roofline": {"kernel": "gemm1 (gate-up grouped GEMM + SiLU*gate)", "bound": "mfma",
                      "achieved": round(achieved, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_FP8_TFLOPS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_FP8_TFLOPS, 4), "traffic": measured_traffic(),
                      "flops_per_launch": flops_g1, "avg_launch_us": round(g1_ms * 1e3, 2)},
     }
     del layer
