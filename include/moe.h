@@ -21,7 +21,9 @@
  *
  * Conventions for every entry point
  * ---------------------------------
- *  - Tensor pointers are DEVICE pointers to row-major, contiguous arrays.
+ *  - Tensor pointers are DEVICE pointers to row-major, contiguous arrays
+ *    (expert weights may instead use the K-blocked layout of
+ *    moe_pack_weights).
  *    bf16 is passed as uint16_t bit patterns; fp8 e4m3 (OCP E4M3FN), packed
  *    e2m1 pairs and e8m0 scales as uint8_t.  `stream` is a hipStream_t
  *    (NULL = the default stream).
@@ -70,6 +72,21 @@ typedef enum {
 } moe_wfmt_t;
 
 /*
+ * Byte layout of each expert's weight matrix [N][K] (N output channels, K
+ * contraction bytes).  ROW_MAJOR: byte k of channel n at n*K + k.  K_BLOCKED
+ * (fp8 only; written by moe_pack_weights): the matrix is cut into K chunks of
+ * C bytes, C = 64 for W1 and W3 and C = 32 for W2, stored chunk after chunk,
+ * each chunk holding all N channels: byte k of channel n at
+ * (k / C) * N * C + n * C + k % C.  One contraction step of a GEMM tile then
+ * reads one contiguous block instead of N short pieces K bytes apart.
+ * Experts stay contiguous ([E][...]); scales have one layout for both.
+ */
+typedef enum {
+  MOE_LAYOUT_ROW_MAJOR = 0,
+  MOE_LAYOUT_K_BLOCKED = 1
+} moe_wlayout_t;
+
+/*
  * A group of experts that share one shape.  Host struct holding device
  * pointers; caller-owned.  W1 is the gate projection (through SiLU), W3 the
  * up projection, W2 the down projection; the contraction index is last
@@ -77,16 +94,19 @@ typedef enum {
  *
  *   fmt = FP8:   w1, w3  uint8 [E][I][H]      s1, s3  float [E][I]
  *                w2      uint8 [E][H][I]      s2      float [E][H]
+ *                (w* in `layout`: row-major as written, or K-blocked)
  *   fmt = MXFP4: w1, w3  uint8 [E][I][H/2]    s1, s3  uint8 [E][I][H/32]
  *                w2      uint8 [E][H][I/2]    s2      uint8 [E][H][I/32]
  *                (element 2i in the low nibble of byte i; scale 255 = NaN is
- *                 not allowed)
+ *                 not allowed; row-major only)
  */
 typedef struct {
   int32_t fmt;       /* moe_wfmt_t */
   int32_t n_experts; /* E */
   int32_t hidden;    /* H: model dimension (FFN input and output width) */
   int32_t inter;     /* I: intermediate dimension */
+  int32_t layout;    /* moe_wlayout_t of w1, w3, w2 */
+  int32_t reserved;  /* must be 0 */
   const uint8_t* w1;
   const uint8_t* w3;
   const uint8_t* w2;
@@ -122,7 +142,8 @@ typedef struct {
                               rows are the extra group T*k .. T*k+T-1 */
   int32_t* pair_to_row;    /* [T][k]   */
   int32_t* row_to_pair;    /* [T*k]    */
-  uint8_t* xq_rows;        /* [T*k][H] */
+  uint8_t* xq_rows;        /* [T*k][H] row-major copy of the quantised rows (the
+                              layer itself keeps them K-blocked, 64-byte chunks) */
   float* xs_rows;          /* [T*k]    */
   void* events[MOE_N_STAGES + 1];
   char variant[96];
@@ -231,6 +252,24 @@ moe_status_t moe_forward(const uint16_t* x, const float* logits, int32_t T, int3
                          const moe_weights_t* shared, const float* norm_gamma, float norm_eps,
                          uint16_t* out, moe_debug_t* dbg, void* ws, size_t ws_bytes,
                          void* stream);
+
+/*
+ * moe_pack_weights -- copy row-major fp8 expert weights into the K-blocked
+ * layout (see moe_wlayout_t), once, when the weights are loaded.
+ *   src  fmt FP8, layout ROW_MAJOR, device pointers
+ *   dst  the same fmt, n_experts, hidden and inter, layout K_BLOCKED;
+ *        dst->w1, w3, w2 are caller buffers of the sizes of src's, disjoint
+ *        from them; dst->s1, s3, s2 are not written (scales are the same in
+ *        both layouts and may alias src's)
+ * The codes are only moved, never changed: the layer computes the same
+ * values from either layout.  The per-step weight tile of the gate-up and
+ * down GEMMs becomes one contiguous block, which the direct-to-LDS loads
+ * stream at about twice the rate of the row-major pieces.  The pages do the
+ * corresponding layout work for the TPU's vector unit inside the kernel
+ * ([Ling] §7: fp8 packing and lane shuffles remain the bottleneck); here it
+ * is paid once per weight load.
+ */
+moe_status_t moe_pack_weights(const moe_weights_t* src, const moe_weights_t* dst, void* stream);
 
 /* Static description of a status code. */
 const char* moe_status_string(moe_status_t s);

@@ -12,8 +12,8 @@ import ctypes
 import torch
 
 from . import _lib
-from ._lib import (MOE_W_FP8, MOE_W_MXFP4, MOE_N_STAGES, STAGE_NAMES, MoeDebug, MoeError,
-                   MoeWeights, check)
+from ._lib import (MOE_LAYOUT_K_BLOCKED, MOE_LAYOUT_ROW_MAJOR, MOE_N_STAGES, MOE_W_FP8, MOE_W_MXFP4,
+                   STAGE_NAMES, MoeDebug, MoeError, MoeWeights, check)
 
 __all__ = ["Weights", "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_forward",
            "forward_workspace_size", "MoeError", "lib"]
@@ -37,16 +37,30 @@ class Weights:
 
     ``d`` has w1, w3, w2, s1, s3, s2 as produced by ``moe_synth`` (uint8 codes;
     float32 per-channel scales for fp8, uint8 e8m0 block scales for mxfp4).
+    fp8 weights are repacked once into the K-blocked layout (moe_pack_weights)
+    unless ``pack`` is False; ``self.tensors`` keeps the row-major originals.
     """
 
-    def __init__(self, d, fmt):
+    def __init__(self, d, fmt, pack=True, stream=None):
         self.tensors = {k: v.contiguous() for k, v in d.items()}
         t = self.tensors
         self.fmt = MOE_W_FP8 if fmt == "fp8" else MOE_W_MXFP4
         E, I = t["w1"].shape[0], t["w1"].shape[1]
         H = t["w2"].shape[1]
         self.n_experts, self.hidden, self.inter = E, H, I
-        self.c = MoeWeights(self.fmt, E, H, I, *(t[k].data_ptr() for k in ("w1", "w3", "w2", "s1", "s3", "s2")))
+        ptrs = [t[k].data_ptr() for k in ("w1", "w3", "w2", "s1", "s3", "s2")]
+        self.c = MoeWeights(self.fmt, E, H, I, MOE_LAYOUT_ROW_MAJOR, 0, *ptrs)
+        self.packed = None
+        if pack and self.fmt == MOE_W_FP8:
+            self.packed = {k: torch.empty_like(t[k]) for k in ("w1", "w3", "w2")}
+            dst = MoeWeights(self.fmt, E, H, I, MOE_LAYOUT_K_BLOCKED, 0,
+                             *(self.packed[k].data_ptr() for k in ("w1", "w3", "w2")), *ptrs[3:])
+            check(lib().moe_pack_weights(ctypes.byref(self.c), ctypes.byref(dst), _stream(stream)))
+            self.c = dst
+
+    @property
+    def layout(self):
+        return self.c.layout
 
     def ref(self):
         return ctypes.byref(self.c)

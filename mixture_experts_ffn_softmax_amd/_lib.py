@@ -14,6 +14,7 @@ LIB_PATH = os.path.join(HERE, "libmoe.so")
 
 MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_ALIGN, MOE_ERR_WORKSPACE, MOE_ERR_UNSUPPORTED, MOE_ERR_DEVICE = range(7)
 MOE_W_FP8, MOE_W_MXFP4 = 0, 1
+MOE_LAYOUT_ROW_MAJOR, MOE_LAYOUT_K_BLOCKED = 0, 1
 (MOE_STAGE_ROUTE, MOE_STAGE_PERMUTE, MOE_STAGE_GEMM1, MOE_STAGE_GEMM2, MOE_STAGE_COMBINE,
  MOE_N_STAGES) = range(6)
 STAGE_NAMES = ["route", "permute", "gemm1", "gemm2", "combine"]
@@ -22,14 +23,14 @@ STAGE_NAMES = ["route", "permute", "gemm1", "gemm2", "combine"]
 EXPORTS = [
     "moe_route", "moe_permute_workspace_size", "moe_permute", "moe_expert_ffn_workspace_size",
     "moe_expert_ffn", "moe_combine", "moe_forward_workspace_size", "moe_forward",
-    "moe_status_string", "moe_last_error", "moe_version",
+    "moe_pack_weights", "moe_status_string", "moe_last_error", "moe_version",
 ]
 
 
 class MoeWeights(ctypes.Structure):
     _fields_ = [
         ("fmt", ctypes.c_int32), ("n_experts", ctypes.c_int32), ("hidden", ctypes.c_int32),
-        ("inter", ctypes.c_int32),
+        ("inter", ctypes.c_int32), ("layout", ctypes.c_int32), ("reserved", ctypes.c_int32),
         ("w1", ctypes.c_void_p), ("w3", ctypes.c_void_p), ("w2", ctypes.c_void_p),
         ("s1", ctypes.c_void_p), ("s3", ctypes.c_void_p), ("s2", ctypes.c_void_p),
     ]
@@ -59,6 +60,7 @@ SIGNATURES = {
     "moe_combine": (_I32, [_VP, _VP, _VP, _I32, _I32, _I32, _VP, _VP, _F32, _VP, _VP]),
     "moe_forward_workspace_size": (_SZ, [_I32, _I32, _WP, _I32]),
     "moe_forward": (_I32, [_VP, _VP, _I32, _I32, _WP, _I32, _WP, _VP, _F32, _VP, _DP, _VP, _SZ, _VP]),
+    "moe_pack_weights": (_I32, [_WP, _WP, _VP]),
     "moe_status_string": (ctypes.c_char_p, [_I32]),
     "moe_last_error": (ctypes.c_char_p, []),
     "moe_version": (ctypes.c_char_p, []),

@@ -44,6 +44,8 @@
 //          the bound; fp8 and MXFP4 weights.
 #include <math.h>
 
+#include <type_traits>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -68,13 +70,30 @@ struct GemmParams {
   const void* a[2];
   const float* a_scale[2];
   long shared_row0;
+  Operand ta[2];         // byte addressing of a[0] / a[1]
   const uint8_t* wa[2];  // GEMM1: W1 (gate), GEMM2: W2 -- [0] routed, [1] shared
   const uint8_t* wb[2];  // GEMM1: W3 (up)
   const void* sa[2];
   const void* sb[2];
-  uint16_t* h;           // GEMM1 output [rows][N] bf16
+  Operand wd[2];         // byte addressing of one expert's weight matrix (fp8)
+  uint16_t* h;           // GEMM1 output: bf16, K-blocked (kHChunk-byte chunks)
+  long h_cs;             // its chunk stride in bytes (rows * kHChunk)
   float* y;              // GEMM2 output [rows][N] fp32
 };
+
+// Byte offset of contraction byte k of row r (see Operand).
+__device__ __forceinline__ long op_off(const Operand& d, long r, long k) {
+  return r * d.row_pitch + (k >> d.kc_shift) * d.chunk_stride + (k & ((1L << d.kc_shift) - 1));
+}
+// Byte advance of every row's pointer per contraction step of `step` bytes:
+// K-blocked operands have chunks of exactly one step.
+__device__ __forceinline__ long op_step(const Operand& d, int step) {
+  return (d.kc_shift < 31) ? d.chunk_stride : step;
+}
+// Element offset (bf16 units) of channel ch of row r in the K-blocked h.
+__device__ __forceinline__ long h_off(long h_cs, long r, int ch) {
+  return (ch >> 5) * (h_cs >> 1) + r * (kHChunk >> 1) + (ch & 31);
+}
 
 // ---- MFMA wrappers ---------------------------------------------------------
 
@@ -195,9 +214,9 @@ __device__ __forceinline__ TileInfo find_tile(const GemmParams& p, const int* s_
   return ti;
 }
 
-// Row r of the row operand (bytes per row `rb`).
-__device__ __forceinline__ const uint8_t* row_ptr(const GemmParams& p, const TileInfo& ti, int r, long rb) {
-  return reinterpret_cast<const uint8_t*>(p.a[ti.wi]) + (r - (ti.wi ? p.shared_row0 : 0)) * rb;
+// Start of row r of the row operand (contraction byte 0).
+__device__ __forceinline__ const uint8_t* row_ptr(const GemmParams& p, const TileInfo& ti, int r) {
+  return reinterpret_cast<const uint8_t*>(p.a[ti.wi]) + (r - (ti.wi ? p.shared_row0 : 0)) * p.ta[ti.wi].row_pitch;
 }
 
 // Common prologue: exits surplus workgroups, loads the tile prefix, finds the tile.
@@ -208,45 +227,53 @@ __device__ __forceinline__ const uint8_t* row_ptr(const GemmParams& p, const Til
   __syncthreads();                                                               \
   const TileInfo ti = find_tile(p, s_tp, xcd_remap(blockIdx.x, total_), BMROWS)
 
-// ============================================================================
-// large GEMM1: e4m3 tokens x e4m3 W1/W3 -> h = SiLU(g) * u (bf16)
-// ============================================================================
-//
-// LDS stage: BM token rows then 256 channel rows (W1 rows n0.., then W3 rows
-// n0..), each 64 bytes of the K step, as 4 16-byte slots (swz64).  One dma16
-// fills 16 rows.  Each K step issues this stage's successor STAGES-1 steps
-// ahead, one pair of dma16 after each group of MFMAs, so the loads drain
-// while the matrix cores work instead of stalling the wave in one burst.
-
 constexpr int kLgCh = 256;    // channel rows per tile
-#ifndef MOE_LARGE_WN
-#define MOE_LARGE_WN 4
-#endif
-constexpr int kLgWN = MOE_LARGE_WN;   // waves along the channel rows (2 x kLgWN waves)
 
 // fast SiLU for the epilogue (h is rounded to bf16 afterwards): g * 1/(1 + 2^(-g log2 e))
 __device__ __forceinline__ float silu_fast(float g) {
   return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * g));
 }
 
-// Waves form a 2 x WN grid: wave (wm, wn) owns tokens [wm * BM/2, +BM/2) and,
-// of the 128 gate and 128 up channel rows, the slice [wn * 128/WN, +128/WN)
-// of each (so gate and up of one channel meet in the same lane).  WN = 4
-// gives 8 waves, two per SIMD: while one waits on its loads or the barrier,
-// the other keeps the matrix core busy.
-template <int BM, int WN, int STAGES>
-__global__ __launch_bounds__(128 * WN, 1) void gemm1_large_kernel(GemmParams p) {
-  constexpr int NW = 2 * WN;                // waves
+// ============================================================================
+// pipelined large variants: 4 waves, one per SIMD
+// ============================================================================
+//
+// LDS bandwidth (about 128 bytes per clock per CU for 16-byte reads) bounds
+// the 8-wave tiling above: a 128 x 64 wave tile re-reads 12 KB of fragments
+// per K step.  Here each wave owns a 128 x 128 tile (256 accumulator
+// registers, possible with one wave per SIMD), which cuts fragment reads per
+// K step by a third.  With one wave per SIMD nothing hides LDS latency, so
+// the fragments of step k+1 are read into a second register set while the
+// MFMAs of step k run.  The LDS ring holds the stage being read into
+// registers plus STAGES-1 stages in flight: the DMA issued during step k
+// fills step k+STAGES into the slot that step k-1's reads just released.
+
+// 32-byte LDS rows (2 slots): conflict-free for 8 or 16 lanes per cycle when
+// 32 lanes read one slot of 32 consecutive rows.
+__device__ __forceinline__ int swz32(int r, int c) { return c ^ ((r >> 2) & 1) ^ ((r >> 3) & 1); }
+
+// Wait for this wave's loads of the stage to be read next (at most N of its
+// DMAs outstanding), then barrier: that stage is complete for every wave and
+// every wave's reads of the slot about to be refilled are done.
+template <int N, int STAGES, int PER>
+__device__ __forceinline__ void pp_wait(int ks, int nk) {
+  if (ks + STAGES - 1 < nk) wait_barrier<N>();
+  else wait_barrier<0>();
+}
+
+// GEMM1: wave (wm, wn) owns tokens [wm * BM/2, +BM/2) and channels
+// [wn * 64, +64) of both the gate (fragments 0, 1) and the up rows (2, 3).
+template <int BM, int STAGES>
+__global__ __launch_bounds__(256, 1) void gemm1_pp_kernel(GemmParams p) {
   constexpr int kRows = BM + kLgCh;
   constexpr int kStage = kRows * 64;
-  constexpr int kDma = kRows / 16;          // dma16 per stage
-  constexpr int kPer = kDma / NW;           // per wave
-  static_assert(kDma % NW == 0, "dma split");
-  constexpr int TF = BM / 64;               // token fragments per wave (32 rows each)
-  constexpr int CF = 4 / WN;                // gate fragments per wave (= up fragments)
-  constexpr int NF = 2 * CF;
-  constexpr int kHRow = 128 * 2 + 16;       // padded LDS row of the h tile (bytes)
-  static_assert(STAGES * kStage >= BM * kHRow, "h staging fits in the ring");
+  constexpr int kDma = kRows / 16;
+  constexpr int kPer = kDma / 4;
+  static_assert(kDma % 4 == 0, "dma split");
+  constexpr int TF = BM / 64;
+  constexpr int NF = 4;
+  constexpr int kGrp = (kPer + NF - 1) / NF;     // DMAs issued after each MFMA group
+  static_assert((STAGES - 1) * kPer < 64, "vmcnt range");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * kStage];
   __shared__ int s_tp[kMaxExperts + 2];
   MOE_TILE_PROLOGUE(BM);
@@ -259,190 +286,25 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm1_large_kernel(GemmParams p) 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
-  // this lane's source of each of the wave's dma16 per stage
+  // this lane's source of each of the wave's dma16 per stage, advanced by one
+  // K step after every issue (stages are issued in order)
   const uint8_t* src[kPer];
+  long inc[kPer];
+  const Operand& wd = p.wd[ti.wi];
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     const int row = (wave * kPer + i) * 16 + (lane >> 2);
     const int chunk = swz64(row, lane & 3);
-    const uint8_t* base;
     if (row < BM) {
       int r = ti.row0 + row;
       if (r >= ti.row1) r = ti.row1 - 1;
-      base = row_ptr(p, ti, r, K);
+      src[i] = row_ptr(p, ti, r) + chunk * 16;
+      inc[i] = op_step(p.ta[ti.wi], 64);
     } else {
       const int c = row - BM;
-      base = (c < kLgCh / 2) ? (W1 + (long)(n0 + c) * K) : (W3 + (long)(n0 + c - kLgCh / 2) * K);
-    }
-    src[i] = base + chunk * 16;
-  }
-  const uint32_t lds0 = lds_addr(smem);
-  auto issue = [&](int ks, int i0, int i1) {
-    const uint32_t st = lds0 + (ks % STAGES) * kStage;
-#pragma unroll
-    for (int i = i0; i < i1; ++i) dma16(src[i] + ((long)ks << 6), st + (wave * kPer + i) * 1024);
-  };
-
-  // fragment addressing: lane reads row (base + l%32), bytes [32h, 32h + 32);
-  // fragment bases are multiples of 32 rows, so the swizzle depends on l%32
-  const int wm = wave / WN, wn = wave % WN;
-  const int l32 = lane & 31, hh = lane >> 5;
-  const int fo0 = l32 * 64 + (swz64(l32, 2 * hh) << 4);
-  const int fo1 = l32 * 64 + (swz64(l32, 2 * hh + 1) << 4);
-  int chbase[NF];
-#pragma unroll
-  for (int f = 0; f < NF; ++f)
-    chbase[f] = (BM + (f < CF ? 0 : kLgCh / 2) + wn * (128 / WN) + (f % CF) * 32) * 64;
-
-  v16f acc[NF][TF];
-#pragma unroll
-  for (int f = 0; f < NF; ++f)
-#pragma unroll
-    for (int t = 0; t < TF; ++t)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) acc[f][t][j] = 0.0f;
-
-#pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s)
-    if (s < nk) issue(s, 0, kPer);
-
-  constexpr int kDmaPerGroup = (kPer + NF - 1) / NF;
-  for (int ks = 0; ks < nk; ++ks) {
-    if (ks + STAGES - 2 < nk) wait_barrier<(STAGES - 2) * kPer>();
-    else wait_barrier<0>();
-    const bool more = ks + STAGES - 1 < nk;
-    const uint8_t* st = smem + (ks % STAGES) * kStage;
-    v8i x[TF];
-#pragma unroll
-    for (int t = 0; t < TF; ++t) {
-      const uint8_t* r = st + (wm * (BM / 2) + t * 32) * 64;
-      x[t] = as_v8i(*reinterpret_cast<const uint4*>(r + fo0), *reinterpret_cast<const uint4*>(r + fo1));
-    }
-    v8i w = as_v8i(*reinterpret_cast<const uint4*>(st + chbase[0] + fo0),
-                   *reinterpret_cast<const uint4*>(st + chbase[0] + fo1));
-#pragma unroll
-    for (int f = 0; f < NF; ++f) {
-      v8i wnext = w;
-      if (f + 1 < NF)
-        wnext = as_v8i(*reinterpret_cast<const uint4*>(st + chbase[f + 1] + fo0),
-                       *reinterpret_cast<const uint4*>(st + chbase[f + 1] + fo1));
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int t = 0; t < TF; ++t) acc[f][t] = mfma32_fp8(w, x[t], acc[f][t]);
-      __builtin_amdgcn_sched_barrier(0);
-      if (more) {
-        const int i0 = f * kDmaPerGroup, i1 = (f + 1) * kDmaPerGroup < kPer ? (f + 1) * kDmaPerGroup : kPer;
-        if (i0 < i1) issue(ks + STAGES - 1, i0, i1);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      w = wnext;
-    }
-  }
-
-  // ---- epilogue.  Lane holds token l%32 of each token fragment and, per
-  // group q of 4 accumulator entries, channels 8q + 4h .. +3 of the fragment.
-  // h = bf16(SiLU(g) * u) goes through a padded LDS tile [BM][128 channels]
-  // so that the global stores are whole 256-byte rows.
-  const float* S1 = reinterpret_cast<const float*>(p.sa[ti.wi]) + ti.eg * p.N;
-  const float* S3 = reinterpret_cast<const float*>(p.sb[ti.wi]) + ti.eg * p.N;
-  float4 s1v[CF][4], s3v[CF][4];
-#pragma unroll
-  for (int c = 0; c < CF; ++c)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int ch = n0 + wn * (128 / WN) + c * 32 + 8 * q + 4 * hh;
-      s1v[c][q] = *reinterpret_cast<const float4*>(S1 + ch);
-      s3v[c][q] = *reinterpret_cast<const float4*>(S3 + ch);
-    }
-  float xs[TF];
-#pragma unroll
-  for (int t = 0; t < TF; ++t) {
-    int grow = ti.row0 + wm * (BM / 2) + t * 32 + l32;
-    if (grow >= ti.row1) grow = ti.row1 - 1;
-    xs[t] = p.a_scale[ti.wi][grow - (ti.wi ? p.shared_row0 : 0)];
-  }
-  wait_barrier<0>();     // every wave is done reading the stage ring
-#pragma unroll
-  for (int t = 0; t < TF; ++t) {
-    uint8_t* hrow = smem + (wm * (BM / 2) + t * 32 + l32) * kHRow;
-#pragma unroll
-    for (int c = 0; c < CF; ++c)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float sg[4] = {s1v[c][q].x, s1v[c][q].y, s1v[c][q].z, s1v[c][q].w};
-        const float su[4] = {s3v[c][q].x, s3v[c][q].y, s3v[c][q].z, s3v[c][q].w};
-        uint32_t b[4];
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const float g = acc[c][t][4 * q + v] * xs[t] * sg[v];
-          const float u = acc[CF + c][t][4 * q + v] * xs[t] * su[v];
-          b[v] = bf16_rne(silu_fast(g) * u);
-        }
-        const int col = wn * (128 / WN) + c * 32 + 8 * q + 4 * hh;
-        *reinterpret_cast<uint2*>(hrow + col * 2) = make_uint2(b[0] | (b[1] << 16), b[2] | (b[3] << 16));
-      }
-  }
-  __syncthreads();
-  // BM rows x 256 bytes: 16 threads per row, 16 bytes each
-  constexpr int kRowsPerPass = 128 * WN / 16;
-#pragma unroll
-  for (int r0 = 0; r0 < BM; r0 += kRowsPerPass) {
-    const int r = r0 + (int)(threadIdx.x >> 4), c = threadIdx.x & 15;
-    const int grow = ti.row0 + r;
-    if (grow < ti.row1)
-      *reinterpret_cast<uint4*>(p.h + (long)grow * p.N + n0 + c * 8) =
-          *reinterpret_cast<const uint4*>(smem + r * kHRow + c * 16);
-  }
-}
-
-// ============================================================================
-// large GEMM2: bf16 h x W2 (e4m3 -> bf16) -> y (fp32)
-// ============================================================================
-//
-// LDS stage: BM h rows of 64 bf16 (128 bytes, 8 slots, swz128) then 256 W2
-// rows of 64 e4m3 codes (64 bytes, swz64).  Waves form a 2 x WN grid: wave
-// (wm, wn) owns tokens [wm * BM/2, +BM/2) and W2 rows [wn * 256/WN, +256/WN).
-// DMA issue is interleaved with the MFMA groups as in GEMM1.
-
-template <int BM, int WN, int STAGES>
-__global__ __launch_bounds__(128 * WN, 1) void gemm2_large_kernel(GemmParams p) {
-  constexpr int NW = 2 * WN;
-  constexpr int kTokBytes = BM * 128;
-  constexpr int kStage = kTokBytes + kLgCh * 64;
-  constexpr int kDmaT = BM / 8;             // dma16 for h rows (8 rows each)
-  constexpr int kDmaW = kLgCh / 16;         // dma16 for W2 rows (16 rows each)
-  constexpr int kPer = (kDmaT + kDmaW) / NW;
-  static_assert((kDmaT + kDmaW) % NW == 0, "dma split");
-  constexpr int TF = BM / 64;
-  constexpr int NF = 8 / WN;                // W2 fragments per wave
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * kStage];
-  __shared__ int s_tp[kMaxExperts + 2];
-  MOE_TILE_PROLOGUE(BM);
-
-  const int K = p.K;                        // = I
-  const int nk = K >> 6;
-  const int n0 = ti.nt * kLgCh;
-  const uint8_t* W2 = p.wa[ti.wi] + ti.eg * (long)p.N * K;
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-
-  const uint8_t* src[kPer];
-  long step[kPer];
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int q = wave * kPer + i;
-    if (q < kDmaT) {
-      const int row = q * 8 + (lane >> 3);
-      const int chunk = swz128(row, lane & 7);
-      int r = ti.row0 + row;
-      if (r >= ti.row1) r = ti.row1 - 1;
-      src[i] = row_ptr(p, ti, r, 2L * K) + chunk * 16;
-      step[i] = 128;
-    } else {
-      const int row = (q - kDmaT) * 16 + (lane >> 2);
-      const int chunk = swz64(row, lane & 3);
-      src[i] = W2 + (long)(n0 + row) * K + chunk * 16;
-      step[i] = 64;
+      const uint8_t* W = (c < kLgCh / 2) ? W1 : W3;
+      src[i] = W + (long)(n0 + (c & (kLgCh / 2 - 1))) * wd.row_pitch + chunk * 16;
+      inc[i] = op_step(wd, 64);
     }
   }
   const uint32_t lds0 = lds_addr(smem);
@@ -450,21 +312,20 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm2_large_kernel(GemmParams p) 
     const uint32_t st = lds0 + (ks % STAGES) * kStage;
 #pragma unroll
     for (int i = i0; i < i1; ++i) {
-      const int q = wave * kPer + i;
-      const uint32_t dst = (q < kDmaT) ? st + q * 1024 : st + kTokBytes + (q - kDmaT) * 1024;
-      dma16(src[i] + step[i] * ks, dst);
+      dma16(src[i], st + (wave * kPer + i) * 1024);
+      src[i] += inc[i];
     }
   };
 
-  const int wm = wave / WN, wn = wave % WN;
+  const int wm = wave >> 1, wn = wave & 1;
   const int l32 = lane & 31, hh = lane >> 5;
-  // h fragment: row l32, bf16 elements [32h, 32h + 32) = chunks 4h .. 4h+3
-  int ho[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) ho[i] = l32 * 128 + (swz128(l32, 4 * hh + i) << 4);
-  // W2 fragment: row l32, codes [32h, 32h + 32) = chunks 2h, 2h+1
-  const int wo0 = l32 * 64 + (swz64(l32, 2 * hh) << 4);
-  const int wo1 = l32 * 64 + (swz64(l32, 2 * hh + 1) << 4);
+  const int fo0 = l32 * 64 + (swz64(l32, 2 * hh) << 4);
+  const int fo1 = l32 * 64 + (swz64(l32, 2 * hh + 1) << 4);
+  const int xbase = wm * (BM / 2) * 64;
+  auto wbase = [&](int f) { return (BM + (f < 2 ? 0 : kLgCh / 2) + wn * 64 + (f & 1) * 32) * 64; };
+  auto rd = [&](const uint8_t* at) {
+    return as_v8i(*reinterpret_cast<const uint4*>(at + fo0), *reinterpret_cast<const uint4*>(at + fo1));
+  };
 
   v16f acc[NF][TF];
 #pragma unroll
@@ -475,67 +336,271 @@ __global__ __launch_bounds__(128 * WN, 1) void gemm2_large_kernel(GemmParams p) 
       for (int j = 0; j < 16; ++j) acc[f][t][j] = 0.0f;
 
 #pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s)
+  for (int s = 0; s < STAGES; ++s)
     if (s < nk) issue(s, 0, kPer);
+  if (STAGES <= nk) wait_barrier<(STAGES - 1) * kPer>();
+  else wait_barrier<0>();
 
-  constexpr int kDmaPerGroup = (kPer + NF - 1) / NF;
-  for (int ks = 0; ks < nk; ++ks) {
-    if (ks + STAGES - 2 < nk) wait_barrier<(STAGES - 2) * kPer>();
-    else wait_barrier<0>();
-    const bool more = ks + STAGES - 1 < nk;
-    const uint8_t* st = smem + (ks % STAGES) * kStage;
-    v8bf x[TF][4];
+  v8i xa[TF], wa[NF], xb[TF], wb[NF];
 #pragma unroll
-    for (int t = 0; t < TF; ++t) {
-      const uint8_t* r = st + (wm * (BM / 2) + t * 32) * 128;
+  for (int t = 0; t < TF; ++t) xa[t] = rd(smem + xbase + t * 32 * 64);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) x[t][i] = as_v8bf(*reinterpret_cast<const uint4*>(r + ho[i]));
-    }
+  for (int f = 0; f < NF; ++f) wa[f] = rd(smem + wbase(f));
+
+  // one K step on register set (xc, wc), reading step ks+1 into (xn, wn_).
+  // steady = true: step ks+1 exists and step ks+STAGES is to be loaded.
+  auto step = [&](auto steady, int ks, const v8i (&xc)[TF], const v8i (&wc)[NF], v8i (&xn)[TF],
+                  v8i (&wn_)[NF]) {
+    constexpr bool kSteady = decltype(steady)::value;
+    if (kSteady) wait_barrier<(STAGES - 2) * kPer>();
+    else pp_wait<(STAGES - 2) * kPer, STAGES, kPer>(ks, nk);
+    const bool next = kSteady || ks + 1 < nk;
+    const bool more = kSteady || ks + STAGES < nk;
+    const uint8_t* stn = smem + ((ks + 1) % STAGES) * kStage;
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
-      const uint8_t* r = st + kTokBytes + (wn * (256 / WN) + f * 32) * 64;
-      const uint4 c0 = *reinterpret_cast<const uint4*>(r + wo0);
-      const uint4 c1 = *reinterpret_cast<const uint4*>(r + wo1);
-      const uint32_t cw[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-      v8bf w[4];
-      fp8x32_to_bf16(cw, w);
       __builtin_amdgcn_sched_barrier(0);
+      if (next) {
+        wn_[f] = rd(stn + wbase(f));
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int t = 0; t < TF; ++t)
-          acc[f][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w[i], x[t][i], acc[f][t], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-      if (more) {
-        const int i0 = f * kDmaPerGroup, i1 = (f + 1) * kDmaPerGroup < kPer ? (f + 1) * kDmaPerGroup : kPer;
-        if (i0 < i1) issue(ks + STAGES - 1, i0, i1);
+        for (int t = f; t < TF; t += NF) xn[t] = rd(stn + xbase + t * 32 * 64);
       }
       __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int t = 0; t < TF; ++t) acc[f][t] = mfma32_fp8(wc[f], xc[t], acc[f][t]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (more) {
+        const int i0 = f * kGrp, i1 = (f + 1) * kGrp < kPer ? (f + 1) * kGrp : kPer;
+        if (i0 < i1) issue(ks + STAGES, i0, i1);
+      }
+    }
+  };
+  const std::true_type steady;
+  const std::false_type tail;
+  int ks = 0;
+  for (; ks + 1 + STAGES < nk; ks += 2) {
+    step(steady, ks, xa, wa, xb, wb);
+    step(steady, ks + 1, xb, wb, xa, wa);
+  }
+  for (; ks + 1 < nk; ks += 2) {
+    step(tail, ks, xa, wa, xb, wb);
+    step(tail, ks + 1, xb, wb, xa, wa);
+  }
+  if (ks < nk) step(tail, ks, xa, wa, xb, wb);
+
+  // ---- epilogue.  Lane holds token l32 of each token fragment and, per
+  // group q of 4 accumulator entries, channels 8q + 4hh .. +3 of the
+  // fragment.  h = bf16(SiLU(g) * u) goes straight to the K-blocked h: a
+  // 32-channel fragment is one 64-byte chunk row, so the four q stores of a
+  // fragment fill 32 consecutive chunk rows (2 KB).
+  const float* S1 = reinterpret_cast<const float*>(p.sa[ti.wi]) + ti.eg * p.N;
+  const float* S3 = reinterpret_cast<const float*>(p.sb[ti.wi]) + ti.eg * p.N;
+  float xs[TF];
+#pragma unroll
+  for (int t = 0; t < TF; ++t) {
+    int grow = ti.row0 + wm * (BM / 2) + t * 32 + l32;
+    if (grow >= ti.row1) grow = ti.row1 - 1;
+    xs[t] = p.a_scale[ti.wi][grow - (ti.wi ? p.shared_row0 : 0)];
+  }
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int ch0 = n0 + wn * 64 + c * 32;
+    float4 s1v[4], s3v[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      s1v[q] = *reinterpret_cast<const float4*>(S1 + ch0 + 8 * q + 4 * hh);
+      s3v[q] = *reinterpret_cast<const float4*>(S3 + ch0 + 8 * q + 4 * hh);
+    }
+#pragma unroll
+    for (int t = 0; t < TF; ++t) {
+      const int grow = ti.row0 + wm * (BM / 2) + t * 32 + l32;
+      if (grow >= ti.row1) continue;
+      uint16_t* hrow = p.h + h_off(p.h_cs, grow, ch0);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float sg[4] = {s1v[q].x, s1v[q].y, s1v[q].z, s1v[q].w};
+        const float su[4] = {s3v[q].x, s3v[q].y, s3v[q].z, s3v[q].w};
+        uint32_t b[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float g = acc[c][t][4 * q + v] * xs[t] * sg[v];
+          const float u = acc[2 + c][t][4 * q + v] * xs[t] * su[v];
+          b[v] = bf16_rne(silu_fast(g) * u);
+        }
+        *reinterpret_cast<uint2*>(hrow + 8 * q + 4 * hh) = make_uint2(b[0] | (b[1] << 16), b[2] | (b[3] << 16));
+      }
     }
   }
+}
 
-  const float* S2 = reinterpret_cast<const float*>(p.sa[ti.wi]) + ti.eg * p.N;
-  float4 s2v[NF][4];
+// GEMM2: K step of 32 elements.  LDS stage: BM h rows of 32 bf16 (64 bytes,
+// swz64) then 256 W2 rows of 32 codes (32 bytes, swz32).  Wave (wm, wn) owns
+// tokens [wm * BM/2, +BM/2) and output channels [wn * 128, +128).
+template <int BM, int STAGES>
+__global__ __launch_bounds__(256, 1) void gemm2_pp_kernel(GemmParams p) {
+  constexpr int kTokBytes = BM * 64;
+  constexpr int kStage = kTokBytes + kLgCh * 32;
+  constexpr int kDmaT = BM / 16;            // 16 h rows per dma16
+  constexpr int kDmaW = kLgCh / 32;         // 32 W2 rows per dma16
+  constexpr int kPer = (kDmaT + kDmaW) / 4;
+  static_assert((kDmaT + kDmaW) % 4 == 0, "dma split");
+  static_assert((STAGES - 1) * kPer < 64, "vmcnt range");
+  constexpr int TF = BM / 64;
+  constexpr int NF = 4;
+  constexpr int kGrp = (kPer + NF - 1) / NF;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * kStage];
+  __shared__ int s_tp[kMaxExperts + 2];
+  MOE_TILE_PROLOGUE(BM);
+
+  const int K = p.K;                        // = I
+  const int nk = K >> 5;
+  const int n0 = ti.nt * kLgCh;
+  const uint8_t* W2 = p.wa[ti.wi] + ti.eg * (long)p.N * K;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+
+  const uint8_t* src[kPer];
+  long inc[kPer];
+  uint32_t dsto[kPer];
+  const Operand& wd = p.wd[ti.wi];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int q = wave * kPer + i;
+    if (q < kDmaT) {
+      const int row = q * 16 + (lane >> 2);
+      int r = ti.row0 + row;
+      if (r >= ti.row1) r = ti.row1 - 1;
+      src[i] = row_ptr(p, ti, r) + swz64(row, lane & 3) * 16;
+      inc[i] = op_step(p.ta[ti.wi], 64);
+      dsto[i] = q * 1024;
+    } else {
+      const int row = (q - kDmaT) * 32 + (lane >> 1);
+      src[i] = W2 + (long)(n0 + row) * wd.row_pitch + swz32(row, lane & 1) * 16;
+      inc[i] = op_step(wd, 32);
+      dsto[i] = kTokBytes + (q - kDmaT) * 1024;
+    }
+  }
+  const uint32_t lds0 = lds_addr(smem);
+  auto issue = [&](int ks, int i0, int i1) {
+    const uint32_t st = lds0 + (ks % STAGES) * kStage;
+#pragma unroll
+    for (int i = i0; i < i1; ++i) {
+      dma16(src[i], st + dsto[i]);
+      src[i] += inc[i];
+    }
+  };
+
+  const int wm = wave >> 1, wn = wave & 1;
+  const int l32 = lane & 31, hh = lane >> 5;
+  // h fragment: row l32, bf16 elements [16h, 16h + 16) = 64-byte-row slots 2h, 2h+1
+  const int ho0 = l32 * 64 + (swz64(l32, 2 * hh) << 4);
+  const int ho1 = l32 * 64 + (swz64(l32, 2 * hh + 1) << 4);
+  // W2 fragment: row l32, codes [16h, 16h + 16) = 32-byte-row slot h
+  const int wo = kTokBytes + l32 * 32 + (swz32(l32, hh) << 4);
+  const int xbase = wm * (BM / 2) * 64;
+  const int wbase = wn * 128 * 32;
+
+  struct XF { v8bf a, b; };
+  auto rdx = [&](const uint8_t* at) {
+    return XF{as_v8bf(*reinterpret_cast<const uint4*>(at + ho0)), as_v8bf(*reinterpret_cast<const uint4*>(at + ho1))};
+  };
+  auto rdw = [&](const uint8_t* at) { return *reinterpret_cast<const uint4*>(at + wo); };
+
+  v16f acc[NF][TF];
 #pragma unroll
   for (int f = 0; f < NF; ++f)
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      s2v[f][q] = *reinterpret_cast<const float4*>(S2 + n0 + wn * (256 / WN) + f * 32 + 8 * q + 4 * hh);
+    for (int t = 0; t < TF; ++t)
 #pragma unroll
-  for (int t = 0; t < TF; ++t) {
-    const int grow = ti.row0 + wm * (BM / 2) + t * 32 + l32;
-    if (grow >= ti.row1) continue;
-    float* yrow = p.y + (long)grow * p.N;
+      for (int j = 0; j < 16; ++j) acc[f][t][j] = 0.0f;
+
 #pragma unroll
-    for (int f = 0; f < NF; ++f)
+  for (int s = 0; s < STAGES; ++s)
+    if (s < nk) issue(s, 0, kPer);
+  if (STAGES <= nk) wait_barrier<(STAGES - 1) * kPer>();
+  else wait_barrier<0>();
+
+  XF xa[TF], xb[TF];
+  uint4 wa[NF], wb[NF];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int ch = n0 + wn * (256 / WN) + f * 32 + 8 * q + 4 * hh;
-        const float4 s2 = s2v[f][q];
-        *reinterpret_cast<float4*>(yrow + ch) =
-            make_float4(acc[f][t][4 * q] * s2.x, acc[f][t][4 * q + 1] * s2.y, acc[f][t][4 * q + 2] * s2.z,
-                        acc[f][t][4 * q + 3] * s2.w);
+  for (int t = 0; t < TF; ++t) xa[t] = rdx(smem + xbase + t * 32 * 64);
+#pragma unroll
+  for (int f = 0; f < NF; ++f) wa[f] = rdw(smem + wbase + f * 32 * 32);
+
+  auto step = [&](auto steady, int ks, const XF (&xc)[TF], const uint4 (&wc)[NF], XF (&xn)[TF],
+                  uint4 (&wn_)[NF]) {
+    constexpr bool kSteady = decltype(steady)::value;
+    if (kSteady) wait_barrier<(STAGES - 2) * kPer>();
+    else pp_wait<(STAGES - 2) * kPer, STAGES, kPer>(ks, nk);
+    const bool next = kSteady || ks + 1 < nk;
+    const bool more = kSteady || ks + STAGES < nk;
+    const uint8_t* stn = smem + ((ks + 1) % STAGES) * kStage;
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (next) {
+        wn_[f] = rdw(stn + wbase + f * 32 * 32);
+#pragma unroll
+        for (int t = f; t < TF; t += NF) xn[t] = rdx(stn + xbase + t * 32 * 64);
       }
+      const uint32_t cw[4] = {wc[f].x, wc[f].y, wc[f].z, wc[f].w};
+      v8bf w0, w1;
+      {
+        const v2bf a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cw[0], 1.0f, false);
+        const v2bf b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cw[0], 1.0f, true);
+        const v2bf c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cw[1], 1.0f, false);
+        const v2bf d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cw[1], 1.0f, true);
+        w0 = v8bf{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+        const v2bf e = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cw[2], 1.0f, false);
+        const v2bf g = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cw[2], 1.0f, true);
+        const v2bf h = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cw[3], 1.0f, false);
+        const v2bf k = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cw[3], 1.0f, true);
+        w1 = v8bf{e[0], e[1], g[0], g[1], h[0], h[1], k[0], k[1]};
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int t = 0; t < TF; ++t) {
+        acc[f][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w0, xc[t].a, acc[f][t], 0, 0, 0);
+        acc[f][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w1, xc[t].b, acc[f][t], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (more) {
+        const int i0 = f * kGrp, i1 = (f + 1) * kGrp < kPer ? (f + 1) * kGrp : kPer;
+        if (i0 < i1) issue(ks + STAGES, i0, i1);
+      }
+    }
+  };
+  const std::true_type steady;
+  const std::false_type tail;
+  int ks = 0;
+  for (; ks + 1 + STAGES < nk; ks += 2) {
+    step(steady, ks, xa, wa, xb, wb);
+    step(steady, ks + 1, xb, wb, xa, wa);
+  }
+  for (; ks + 1 < nk; ks += 2) {
+    step(tail, ks, xa, wa, xb, wb);
+    step(tail, ks + 1, xb, wb, xa, wa);
+  }
+  if (ks < nk) step(tail, ks, xa, wa, xb, wb);
+
+  const float* S2 = reinterpret_cast<const float*>(p.sa[ti.wi]) + ti.eg * p.N;
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    float4 s2v[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      s2v[q] = *reinterpret_cast<const float4*>(S2 + n0 + wn * 128 + f * 32 + 8 * q + 4 * hh);
+#pragma unroll
+    for (int t = 0; t < TF; ++t) {
+      const int grow = ti.row0 + wm * (BM / 2) + t * 32 + l32;
+      if (grow >= ti.row1) continue;
+      float* yrow = p.y + (long)grow * p.N + n0 + wn * 128 + f * 32;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<float4*>(yrow + 8 * q + 4 * hh) =
+            make_float4(acc[f][t][4 * q] * s2v[q].x, acc[f][t][4 * q + 1] * s2v[q].y,
+                        acc[f][t][4 * q + 2] * s2v[q].z, acc[f][t][4 * q + 3] * s2v[q].w);
+    }
   }
 }
 
@@ -572,12 +637,16 @@ __global__ __launch_bounds__(256) void gemm1_small_kernel(GemmParams p) {
   // fetched from those positions to pair each product with the right K.
   const int tok_off0 = fp4 ? lg * 16 : lg * 32;
   const int tok_off1 = fp4 ? 64 + lg * 16 : lg * 32 + 16;
+  // 16-byte pieces never straddle a K chunk of either layout, so each piece
+  // is addressed through its operand's layout (op_off)
+  const Operand& td = p.ta[ti.wi];
+  const Operand& wd = p.wd[ti.wi];
   const uint8_t* tp[2];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     int r = ti.row0 + t * 16 + l16;
     if (r >= ti.row1) r = ti.row1 - 1;
-    tp[t] = row_ptr(p, ti, r, K);
+    tp[t] = row_ptr(p, ti, r);
   }
   const uint8_t* wp[4];
   const uint8_t* sp[4];
@@ -587,9 +656,15 @@ __global__ __launch_bounds__(256) void gemm1_small_kernel(GemmParams p) {
     const long crow = n0 + (f & 1) * 16 + l16;
     const uint8_t* W = m ? Wb : Wa;
     const uint8_t* S = reinterpret_cast<const uint8_t*>(m ? p.sb[ti.wi] : p.sa[ti.wi]);
-    wp[f] = W + crow * rowBytes + (fp4 ? lg * 16 : lg * 32);
+    wp[f] = fp4 ? W + crow * rowBytes + lg * 16 : W + crow * wd.row_pitch;
     sp[f] = fp4 ? (S + (ti.eg * (long)p.N + crow) * (K >> 5)) : nullptr;  // K/32 e8m0 per row
   }
+  auto tok = [&](int t, long k) {
+    return *reinterpret_cast<const uint4*>(tp[t] + ((k >> td.kc_shift) * td.chunk_stride + (k & ((1L << td.kc_shift) - 1))));
+  };
+  auto wgt = [&](int f, long k) {
+    return *reinterpret_cast<const uint4*>(wp[f] + ((k >> wd.kc_shift) * wd.chunk_stride + (k & ((1L << wd.kc_shift) - 1))));
+  };
 
   v4f acc[4][2];
 #pragma unroll
@@ -600,9 +675,7 @@ __global__ __launch_bounds__(256) void gemm1_small_kernel(GemmParams p) {
   for (int ks = wave; ks < nk; ks += 4) {
     v8i x[2];
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
-      x[t] = as_v8i(*reinterpret_cast<const uint4*>(tp[t] + ((long)ks << 7) + tok_off0),
-                    *reinterpret_cast<const uint4*>(tp[t] + ((long)ks << 7) + tok_off1));
+    for (int t = 0; t < 2; ++t) x[t] = as_v8i(tok(t, ((long)ks << 7) + tok_off0), tok(t, ((long)ks << 7) + tok_off1));
     if (fp4) {
       v8i w[4];
       int sc[4];
@@ -620,9 +693,10 @@ __global__ __launch_bounds__(256) void gemm1_small_kernel(GemmParams p) {
     } else {
       v8i w[4];
 #pragma unroll
-      for (int f = 0; f < 4; ++f)
-        w[f] = as_v8i(*reinterpret_cast<const uint4*>(wp[f] + ((long)ks << 7)),
-                      *reinterpret_cast<const uint4*>(wp[f] + ((long)ks << 7) + 16));
+      for (int f = 0; f < 4; ++f) {
+        const long k = ((long)ks << 7) + lg * 32;
+        w[f] = as_v8i(wgt(f, k), wgt(f, k + 16));
+      }
 #pragma unroll
       for (int f = 0; f < 4; ++f)
 #pragma unroll
@@ -662,7 +736,7 @@ __global__ __launch_bounds__(256) void gemm1_small_kernel(GemmParams p) {
     const float u = usum[v] * xs * su[v];
     b[v] = bf16_rne(silu(g) * u);
   }
-  *reinterpret_cast<uint2*>(p.h + (long)grow * p.N + ch) = make_uint2(b[0] | (b[1] << 16), b[2] | (b[3] << 16));
+  *reinterpret_cast<uint2*>(p.h + h_off(p.h_cs, grow, ch)) = make_uint2(b[0] | (b[1] << 16), b[2] | (b[3] << 16));
 }
 
 // GEMM2: 16x16x32 bf16 MFMA; W2 codes converted to bf16 in registers.  Lane
@@ -683,21 +757,29 @@ __global__ __launch_bounds__(256) void gemm2_small_kernel(GemmParams p) {
   const int n0 = ti.nt * kSmCh;
   const uint8_t* W2 = p.wa[ti.wi] + ti.eg * (long)p.N * rowBytes;
 
+  const Operand& td = p.ta[ti.wi];
+  const Operand& wd = p.wd[ti.wi];
   const uint8_t* tp[2];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     int r = ti.row0 + t * 16 + l16;
     if (r >= ti.row1) r = ti.row1 - 1;
-    tp[t] = row_ptr(p, ti, r, 2L * K) + lg * 64;
+    tp[t] = row_ptr(p, ti, r);
   }
   const uint8_t* wp[4];
   const uint8_t* sp[4];
 #pragma unroll
   for (int f = 0; f < 4; ++f) {
     const long crow = n0 + f * 16 + l16;
-    wp[f] = W2 + crow * rowBytes + (fp4 ? lg * 16 : lg * 32);
+    wp[f] = fp4 ? W2 + crow * rowBytes + lg * 16 : W2 + crow * wd.row_pitch;
     sp[f] = fp4 ? (reinterpret_cast<const uint8_t*>(p.sa[0]) + (ti.eg * (long)p.N + crow) * (K >> 5)) : nullptr;
   }
+  auto hpiece = [&](int t, long k) {
+    return *reinterpret_cast<const uint4*>(tp[t] + ((k >> td.kc_shift) * td.chunk_stride + (k & ((1L << td.kc_shift) - 1))));
+  };
+  auto wgt = [&](int f, long k) {
+    return *reinterpret_cast<const uint4*>(wp[f] + ((k >> wd.kc_shift) * wd.chunk_stride + (k & ((1L << wd.kc_shift) - 1))));
+  };
 
   v4f acc[4][2];
 #pragma unroll
@@ -710,7 +792,7 @@ __global__ __launch_bounds__(256) void gemm2_small_kernel(GemmParams p) {
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) x[t][i] = as_v8bf(*reinterpret_cast<const uint4*>(tp[t] + ((long)ks << 8) + 16 * i));
+      for (int i = 0; i < 4; ++i) x[t][i] = as_v8bf(hpiece(t, ((long)ks << 8) + lg * 64 + 16 * i));
     v8bf w[4][4];
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
@@ -720,8 +802,9 @@ __global__ __launch_bounds__(256) void gemm2_small_kernel(GemmParams p) {
         const uint32_t s = sp[f][ks * 4 + lg];
         fp4x32_to_bf16(cw, e8m0_to_f32(s), w[f]);
       } else {
-        const uint4 b0 = *reinterpret_cast<const uint4*>(wp[f] + ((long)ks << 7));
-        const uint4 b1 = *reinterpret_cast<const uint4*>(wp[f] + ((long)ks << 7) + 16);
+        const long k = ((long)ks << 7) + lg * 32;
+        const uint4 b0 = wgt(f, k);
+        const uint4 b1 = wgt(f, k + 16);
         const uint32_t cw[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
         fp8x32_to_bf16(cw, w[f]);
       }
@@ -782,6 +865,38 @@ __global__ __launch_bounds__(1024) void tile_prefix_kernel(const int* __restrict
 }
 
 // ============================================================================
+// weight layout
+// ============================================================================
+
+// dst[e][c][n][0 .. C) = src[e][n][c*C .. c*C + C): one thread per 16 bytes of
+// dst (consecutive threads write consecutive bytes).
+__global__ __launch_bounds__(256) void pack_kblocked_kernel(const uint8_t* __restrict__ src,
+                                                            uint8_t* __restrict__ dst, int N, int K, int C,
+                                                            long total16) {
+  const long per_e = (long)N * K, per_c = (long)N * C;
+  for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < total16; i += (long)gridDim.x * blockDim.x) {
+    const long byte = i * 16;
+    const long e = byte / per_e;
+    const long r1 = byte - e * per_e;
+    const long c = r1 / per_c;
+    const long r2 = r1 - c * per_c;
+    const long n = r2 / C;
+    const long off = r2 - n * C;
+    *reinterpret_cast<uint4*>(dst + byte) =
+        *reinterpret_cast<const uint4*>(src + e * per_e + n * K + c * C + off);
+  }
+}
+
+hipError_t launch_pack_kblocked(const uint8_t* src, uint8_t* dst, int E, int N, int K, int C, hipStream_t s) {
+  const long total16 = (long)E * N * K / 16;
+  if (total16 == 0) return hipSuccess;
+  long blocks = (total16 + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  pack_kblocked_kernel<<<(unsigned)blocks, 256, 0, s>>>(src, dst, N, K, C, total16);
+  return hipGetLastError();
+}
+
+// ============================================================================
 // launchers
 // ============================================================================
 
@@ -814,10 +929,11 @@ static GemmParams base_params(const FfnGroups& g, const RowOperand& x, const int
   p.n_routed = g.n_routed;
   p.offsets = g.offsets;
   p.tile_prefix = tile_prefix;
-  p.a[0] = x.q[0];
-  p.a[1] = x.q[1];
-  p.a_scale[0] = x.s[0];
-  p.a_scale[1] = x.s[1];
+  for (int i = 0; i < 2; ++i) {
+    p.a[i] = x.q[i];
+    p.a_scale[i] = x.s[i];
+    p.ta[i] = x.d[i];
+  }
   p.shared_row0 = x.shared_row0;
   return p;
 }
@@ -832,8 +948,10 @@ hipError_t launch_gemm1(int variant, const FfnGroups& g, const RowOperand& x, co
     p.wb[i] = g.w3[i];
     p.sa[i] = g.s1[i];
     p.sb[i] = g.s3[i];
+    p.wd[i] = g.blocked[i] ? k_blocked_operand(g.inter, kW13Chunk) : row_major_operand(g.hidden);
   }
   p.h = h;
+  p.h_cs = n_rows * kHChunk;
   const int bm = variant_rows(variant);
   if (variant == kVariantSmall) {
     p.ntiles = g.inter / (kSmCh / 2);
@@ -843,20 +961,24 @@ hipError_t launch_gemm1(int variant, const FfnGroups& g, const RowOperand& x, co
   } else {
     p.ntiles = g.inter / (kLgCh / 2);
     const long grid = max_row_tiles(n_rows, g.n_groups, bm) * p.ntiles;
-    if (variant == kVariantLarge256) gemm1_large_kernel<256, kLgWN, 4><<<(unsigned)grid, 128 * kLgWN, 0, s>>>(p);
-    else gemm1_large_kernel<128, kLgWN, 4><<<(unsigned)grid, 128 * kLgWN, 0, s>>>(p);
+    if (variant == kVariantLarge256) gemm1_pp_kernel<256, 4><<<(unsigned)grid, 256, 0, s>>>(p);
+    else gemm1_pp_kernel<128, 6><<<(unsigned)grid, 256, 0, s>>>(p);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_gemm2(int variant, const FfnGroups& g, const RowOperand& h, const int* tile_prefix,
+hipError_t launch_gemm2(int variant, const FfnGroups& g, const uint16_t* h, const int* tile_prefix,
                         long n_rows, float* y, hipStream_t s) {
-  GemmParams p = base_params(g, h, tile_prefix);
+  // every group's rows index the one K-blocked h directly
+  const Operand hd = k_blocked_operand(n_rows, kHChunk);
+  const RowOperand hr{{h, h}, {nullptr, nullptr}, 0, {hd, hd}};
+  GemmParams p = base_params(g, hr, tile_prefix);
   p.K = g.inter;
   p.N = g.hidden;
   for (int i = 0; i < 2; ++i) {
     p.wa[i] = g.w2[i];
     p.sa[i] = g.s2[i];
+    p.wd[i] = g.blocked[i] ? k_blocked_operand(g.hidden, kW2Chunk) : row_major_operand(g.inter);
   }
   p.y = y;
   const int bm = variant_rows(variant);
@@ -868,8 +990,8 @@ hipError_t launch_gemm2(int variant, const FfnGroups& g, const RowOperand& h, co
   } else {
     p.ntiles = g.hidden / kLgCh;
     const long grid = max_row_tiles(n_rows, g.n_groups, bm) * p.ntiles;
-    if (variant == kVariantLarge256) gemm2_large_kernel<256, kLgWN, 3><<<(unsigned)grid, 128 * kLgWN, 0, s>>>(p);
-    else gemm2_large_kernel<128, kLgWN, 4><<<(unsigned)grid, 128 * kLgWN, 0, s>>>(p);
+    if (variant == kVariantLarge256) gemm2_pp_kernel<256, 6><<<(unsigned)grid, 256, 0, s>>>(p);
+    else gemm2_pp_kernel<128, 8><<<(unsigned)grid, 256, 0, s>>>(p);
   }
   return hipGetLastError();
 }

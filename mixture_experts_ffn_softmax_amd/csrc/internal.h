@@ -13,6 +13,30 @@ constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 32;
 constexpr int kPermuteChunk = 1024;  // pairs per counting / ranking chunk
 
+// Byte addressing of a matrix operand with rows of K contraction bytes: byte k
+// of row r sits at r * row_pitch + (k >> kc_shift) * chunk_stride +
+// (k & ((1 << kc_shift) - 1)).  Row-major: row_pitch = K, kc_shift = 31.
+// K-blocked in C-byte chunks over R rows: row_pitch = C, kc_shift = log2 C,
+// chunk_stride = R * C (every chunk holds all R rows).
+struct Operand {
+  long row_pitch;
+  long chunk_stride;
+  int kc_shift;
+};
+inline Operand row_major_operand(long k_bytes) { return Operand{k_bytes, 0, 31}; }
+inline Operand k_blocked_operand(long rows, int chunk_bytes) {
+  int sh = 0;
+  while ((1 << sh) < chunk_bytes) ++sh;
+  return Operand{chunk_bytes, rows * chunk_bytes, sh};
+}
+// K-blocked chunk sizes: quantised tokens and W1/W3 in 64-byte chunks (one
+// gate-up MFMA step), h (bf16) in 64-byte chunks of 32 elements and W2 in
+// 32-byte chunks (one down-projection step of 32 elements).
+constexpr int kTokChunk = 64;
+constexpr int kW13Chunk = 64;
+constexpr int kHChunk = 64;
+constexpr int kW2Chunk = 32;
+
 // ---- router ---------------------------------------------------------------
 hipError_t launch_route(const float* logits, int T, int E, int k, int* ids, float* w,
                         hipStream_t s);
@@ -29,9 +53,12 @@ hipError_t launch_rank(const int* ids, int pairs, int E, const int* chunk_base, 
                        int* row_to_pair, hipStream_t s);
 // Quantise each token and write its codes / scale to rows pair_to_row[t][*]
 // (skipped when negative) and, when xq_tok is non-NULL, to xq_tok[t] / xs_tok[t].
+// blocked = false: row-major [rows][H]; true: K-blocked in kTokChunk-byte
+// chunks, xq_rows over T*k rows and xq_tok over T rows.  xq_copy, when
+// non-NULL, also receives xq_rows row-major.
 hipError_t launch_quant_scatter(const uint16_t* x, int T, int H, int k, const int* pair_to_row,
                                 uint8_t* xq_rows, float* xs_rows, uint8_t* xq_tok, float* xs_tok,
-                                hipStream_t s);
+                                bool blocked, uint8_t* xq_copy, hipStream_t s);
 
 // ---- grouped expert FFN ---------------------------------------------------
 enum WeightFormat { kFp8 = 0, kMxfp4 = 1 };
@@ -54,6 +81,7 @@ struct FfnGroups {
   const void* s1[2];
   const void* s3[2];
   const void* s2[2];
+  bool blocked[2];    // weights K-blocked (moe_pack_weights) rather than row-major
 };
 
 // Row operand of a grouped GEMM: GEMM1 reads e4m3 codes q with per-row
@@ -64,6 +92,7 @@ struct RowOperand {
   const void* q[2];
   const float* s[2];
   long shared_row0;
+  Operand d[2];       // byte addressing of q[0] / q[1]
 };
 
 enum GemmVariant { kVariantSmall = 0, kVariantLarge128 = 1, kVariantLarge256 = 2 };
@@ -75,12 +104,18 @@ long max_row_tiles(long n_rows, int n_groups, int bm);
 
 // tile_prefix[g] = sum over g' < g of ceil(rows(g') / bm), g = 0..n_groups.
 hipError_t launch_tile_prefix(const int* offsets, int n_groups, int bm, int* tile_prefix, hipStream_t s);
-// GEMM1: h[r][n] = bf16(SiLU(g) * u) for the gate/up pair of channel n.
+// GEMM1: h[r][n] = bf16(SiLU(g) * u) for the gate/up pair of channel n.  h is
+// K-blocked for GEMM2: kHChunk-byte chunks (32 channels) over n_rows rows.
 hipError_t launch_gemm1(int variant, const FfnGroups& g, const RowOperand& x, const int* tile_prefix,
                         long n_rows, uint16_t* h, hipStream_t s);
-// GEMM2: y[r][j] = (h_r . W2[j]) * s2[j] in fp32.
-hipError_t launch_gemm2(int variant, const FfnGroups& g, const RowOperand& h, const int* tile_prefix,
+// GEMM2: y[r][j] = (h_r . W2[j]) * s2[j] in fp32; h as GEMM1 writes it.
+hipError_t launch_gemm2(int variant, const FfnGroups& g, const uint16_t* h, const int* tile_prefix,
                         long n_rows, float* y, hipStream_t s);
+
+// ---- weight layout ------------------------------------------------------------
+// Copies E matrices of [N][K] bytes into the K-blocked layout with C-byte chunks.
+hipError_t launch_pack_kblocked(const uint8_t* src, uint8_t* dst, int E, int N, int K, int C,
+                                hipStream_t s);
 
 // ---- combine --------------------------------------------------------------
 hipError_t launch_combine(const float* y_rows, const int* pair_to_row, const float* w, int T,

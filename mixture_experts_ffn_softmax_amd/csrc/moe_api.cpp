@@ -82,6 +82,11 @@ moe_status_t check_weights(const moe_weights_t* w, const char* name) {
     return fail(MOE_ERR_SHAPE, "%s: n_experts = %d outside [1, %d]", name, w->n_experts, moe::kMaxExperts);
   MOE_CHECK(check_dim(w->hidden, "hidden"));
   MOE_CHECK(check_dim(w->inter, "inter"));
+  if (w->layout != MOE_LAYOUT_ROW_MAJOR && w->layout != MOE_LAYOUT_K_BLOCKED)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: unknown weight layout %d", name, w->layout);
+  if (w->layout == MOE_LAYOUT_K_BLOCKED && w->fmt != MOE_W_FP8_E4M3_PERCHANNEL)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: the K-blocked layout exists for fp8 weights only", name);
+  if (w->reserved != 0) return fail(MOE_ERR_SHAPE, "%s: reserved field must be 0", name);
   MOE_CHECK(need(w->w1, "w1"));
   MOE_CHECK(need(w->w3, "w3"));
   MOE_CHECK(need(w->w2, "w2"));
@@ -127,6 +132,7 @@ moe::FfnGroups make_groups(const moe_weights_t* r, const moe_weights_t* sh, cons
     g.s1[i] = src[i]->s1;
     g.s3[i] = src[i]->s3;
     g.s2[i] = src[i]->s2;
+    g.blocked[i] = src[i]->layout == MOE_LAYOUT_K_BLOCKED;
   }
   return g;
 }
@@ -145,8 +151,7 @@ moe_status_t run_ffn(const moe::FfnGroups& g, const moe::RowOperand& x, long n_r
   e = moe::launch_gemm1(variant, g, x, tile_prefix, n_rows, h, s);
   if (e != hipSuccess) return device_status(e, "gemm1");
   if (events && events[MOE_STAGE_GEMM2]) hipEventRecord((hipEvent_t)events[MOE_STAGE_GEMM2], s);
-  moe::RowOperand hrows{{h, h + (size_t)x.shared_row0 * g.inter}, {nullptr, nullptr}, x.shared_row0};
-  e = moe::launch_gemm2(variant, g, hrows, tile_prefix, n_rows, y, s);
+  e = moe::launch_gemm2(variant, g, h, tile_prefix, n_rows, y, s);
   if (e != hipSuccess) return device_status(e, "gemm2");
   return ok();
 }
@@ -230,7 +235,8 @@ moe_status_t moe_permute(const uint16_t* x, int32_t T, int32_t H, const int32_t*
   if (T == 0) return ok();
   e = moe::launch_rank(topk_ids, (int)pairs, E, base, pair_to_row, row_to_pair, s);
   if (e != hipSuccess) return device_status(e, "rank");
-  e = moe::launch_quant_scatter(x, T, H, top_k, pair_to_row, xq_rows, xs_rows, xq_tok, xs_tok, s);
+  e = moe::launch_quant_scatter(x, T, H, top_k, pair_to_row, xq_rows, xs_rows, xq_tok, xs_tok, false,
+                                nullptr, s);
   return device_status(e, "quant_scatter");
 }
 
@@ -262,7 +268,8 @@ moe_status_t moe_expert_ffn(const uint8_t* xq_rows, const float* xs_rows, int32_
   uint16_t* h;
   ffn_ws(c, n_rows, w->n_experts, w->inter, &tp, &h);
   const moe::FfnGroups g = make_groups(w, nullptr, expert_offsets);
-  moe::RowOperand x{{xq_rows, xq_rows}, {xs_rows, xs_rows}, (long)n_rows};
+  const moe::Operand rm = moe::row_major_operand(w->hidden);
+  moe::RowOperand x{{xq_rows, xq_rows}, {xs_rows, xs_rows}, (long)n_rows, {rm, rm}};
   return run_ffn(g, x, n_rows, y_rows, tp, h, (hipStream_t)stream, nullptr, nullptr, 0);
 }
 
@@ -376,7 +383,6 @@ moe_status_t moe_forward(const uint16_t* x, const float* logits, int32_t T, int3
     if (dbg->expert_offsets) L.offsets = dbg->expert_offsets;
     if (dbg->pair_to_row) L.p2r = dbg->pair_to_row;
     if (dbg->row_to_pair) L.r2p = dbg->row_to_pair;
-    if (dbg->xq_rows) L.xq_rows = dbg->xq_rows;
     if (dbg->xs_rows) L.xs_rows = dbg->xs_rows;
   }
   hipStream_t s = (hipStream_t)stream;
@@ -392,12 +398,18 @@ moe_status_t moe_forward(const uint16_t* x, const float* logits, int32_t T, int3
   if (e != hipSuccess) return device_status(e, "counts");
   e = moe::launch_rank(L.ids, (int)R, E, L.base, L.p2r, L.r2p, s);
   if (e != hipSuccess) return device_status(e, "rank");
-  e = moe::launch_quant_scatter(x, T, H, top_k, L.p2r, L.xq_rows, L.xs_rows, L.xq_tok, L.xs_tok, s);
+  // the layer keeps the quantised rows K-blocked (64-byte chunks); the debug
+  // capture receives a row-major copy
+  e = moe::launch_quant_scatter(x, T, H, top_k, L.p2r, L.xq_rows, L.xs_rows, L.xq_tok, L.xs_tok, true,
+                                dbg ? dbg->xq_rows : nullptr, s);
   if (e != hipSuccess) return device_status(e, "quant_scatter");
 
   const moe::FfnGroups g = make_groups(routed, sh ? shared : nullptr, L.offsets);
   const long rows = R + (sh ? T : 0);
-  moe::RowOperand xr{{L.xq_rows, sh ? L.xq_tok : L.xq_rows}, {L.xs_rows, sh ? L.xs_tok : L.xs_rows}, R};
+  const moe::Operand rows_d = moe::k_blocked_operand(R, moe::kTokChunk);
+  const moe::Operand tok_d = moe::k_blocked_operand(T, moe::kTokChunk);
+  moe::RowOperand xr{{L.xq_rows, sh ? L.xq_tok : L.xq_rows}, {L.xs_rows, sh ? L.xs_tok : L.xs_rows}, R,
+                     {rows_d, sh ? tok_d : rows_d}};
   char* vout = dbg ? dbg->variant : nullptr;
   MOE_CHECK(run_ffn(g, xr, rows, L.y_rows, L.tile_prefix, L.h, s, ev, vout,
                     dbg ? sizeof(dbg->variant) : 0));
@@ -408,6 +420,38 @@ moe_status_t moe_forward(const uint16_t* x, const float* logits, int32_t T, int3
   if (e != hipSuccess) return device_status(e, "combine");
   if (ev && ev[MOE_N_STAGES]) hipEventRecord((hipEvent_t)ev[MOE_N_STAGES], s);
   return ok();
+}
+
+// ---------------------------------------------------------------------------
+moe_status_t moe_pack_weights(const moe_weights_t* src, const moe_weights_t* dst, void* stream) {
+  MOE_CHECK(check_weights(src, "src"));
+  MOE_CHECK(check_weights(dst, "dst"));
+  if (src->fmt != MOE_W_FP8_E4M3_PERCHANNEL)
+    return fail(MOE_ERR_UNSUPPORTED, "only fp8 weights have a K-blocked layout");
+  if (src->layout != MOE_LAYOUT_ROW_MAJOR) return fail(MOE_ERR_SHAPE, "src must be row-major");
+  if (dst->layout != MOE_LAYOUT_K_BLOCKED) return fail(MOE_ERR_SHAPE, "dst must be K-blocked");
+  if (dst->fmt != src->fmt || dst->n_experts != src->n_experts || dst->hidden != src->hidden ||
+      dst->inter != src->inter)
+    return fail(MOE_ERR_SHAPE, "dst shape differs from src");
+  const size_t bytes13 = (size_t)src->n_experts * src->inter * src->hidden;
+  const uint8_t* s_[3] = {src->w1, src->w3, src->w2};
+  const uint8_t* d_[3] = {dst->w1, dst->w3, dst->w2};
+  for (int i = 0; i < 3; ++i)
+    for (int j = 0; j < 3; ++j)
+      if (d_[i] < s_[j] + bytes13 && s_[j] < d_[i] + bytes13)
+        return fail(MOE_ERR_SHAPE, "dst weight buffers overlap src's");
+  for (int i = 0; i < 3; ++i)
+    for (int j = i + 1; j < 3; ++j)
+      if (d_[i] < d_[j] + bytes13 && d_[j] < d_[i] + bytes13)
+        return fail(MOE_ERR_SHAPE, "dst weight buffers overlap each other");
+  hipStream_t s = (hipStream_t)stream;
+  const int E = src->n_experts, H = src->hidden, I = src->inter;
+  hipError_t e = moe::launch_pack_kblocked(src->w1, const_cast<uint8_t*>(dst->w1), E, I, H, moe::kW13Chunk, s);
+  if (e == hipSuccess)
+    e = moe::launch_pack_kblocked(src->w3, const_cast<uint8_t*>(dst->w3), E, I, H, moe::kW13Chunk, s);
+  if (e == hipSuccess)
+    e = moe::launch_pack_kblocked(src->w2, const_cast<uint8_t*>(dst->w2), E, H, I, moe::kW2Chunk, s);
+  return device_status(e, "pack_weights");
 }
 
 }  // extern "C"

@@ -138,14 +138,22 @@ __global__ __launch_bounds__(256) void rank_kernel(const int* __restrict__ ids, 
   }
 }
 
+// Byte offset of the 8 codes idx*8 .. idx*8+7 of row r: row-major (cs = 0)
+// or K-blocked in kTokChunk-byte chunks with chunk stride cs.
+__device__ __forceinline__ long code_offset(long r, int idx, int H, long cs) {
+  return cs ? (long)(idx >> 3) * cs + r * kTokChunk + (idx & 7) * 8 : r * H + (long)idx * 8;
+}
+
 // One block per token.  The row is nchk chunks of 8 bf16; thread i handles
 // chunks i, i + blockDim, ..., (CPT of them, some possibly past nchk).
 // blockDim is a multiple of 64 so that the wave reductions see full waves.
+// rows_cs / tok_cs: chunk strides of the K-blocked xq_rows / xq_tok (0 =
+// row-major); xq_copy: optional row-major copy of the xq_rows writes.
 template <int CPT>
 __global__ __launch_bounds__(1024) void quant_scatter_kernel(
     const uint16_t* __restrict__ x, int H, int k, const int* __restrict__ pair_to_row,
     uint8_t* __restrict__ xq_rows, float* __restrict__ xs_rows, uint8_t* __restrict__ xq_tok,
-    float* __restrict__ xs_tok) {
+    float* __restrict__ xs_tok, long rows_cs, long tok_cs, uint8_t* __restrict__ xq_copy) {
   __shared__ float red[16];
   const long t = blockIdx.x;
   const int nchk = H >> 3;
@@ -179,20 +187,21 @@ __global__ __launch_bounds__(1024) void quant_scatter_kernel(
   for (int j = 0; j < k; ++j) {
     const int r = pair_to_row[t * k + j];
     if (r < 0) continue;
-    uint2* dst = reinterpret_cast<uint2*>(xq_rows + (long)r * H);
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
       const int idx = threadIdx.x + c * blockDim.x;
-      if (idx < nchk) dst[idx] = q8[c];
+      if (idx < nchk) {
+        *reinterpret_cast<uint2*>(xq_rows + code_offset(r, idx, H, rows_cs)) = q8[c];
+        if (xq_copy) *reinterpret_cast<uint2*>(xq_copy + (long)r * H + (long)idx * 8) = q8[c];
+      }
     }
     if (threadIdx.x == 0) xs_rows[r] = s;
   }
   if (xq_tok) {
-    uint2* dst = reinterpret_cast<uint2*>(xq_tok + t * H);
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
       const int idx = threadIdx.x + c * blockDim.x;
-      if (idx < nchk) dst[idx] = q8[c];
+      if (idx < nchk) *reinterpret_cast<uint2*>(xq_tok + code_offset(t, idx, H, tok_cs)) = q8[c];
     }
     if (threadIdx.x == 0) xs_tok[t] = s;
   }
@@ -216,8 +225,10 @@ hipError_t launch_rank(const int* ids, int pairs, int E, const int* chunk_base, 
 
 hipError_t launch_quant_scatter(const uint16_t* x, int T, int H, int k, const int* pair_to_row,
                                 uint8_t* xq_rows, float* xs_rows, uint8_t* xq_tok, float* xs_tok,
-                                hipStream_t s) {
+                                bool blocked, uint8_t* xq_copy, hipStream_t s) {
   if (T == 0) return hipSuccess;
+  const long rows_cs = blocked ? (long)T * k * kTokChunk : 0;
+  const long tok_cs = blocked ? (long)T * kTokChunk : 0;
   const int chunks = H / 8;  // H is a multiple of 128: chunks is a multiple of 16
   int cpt = 1;
   while (chunks > 1024 * cpt) cpt *= 2;
@@ -225,7 +236,7 @@ hipError_t launch_quant_scatter(const uint16_t* x, int T, int H, int k, const in
   threads = ((threads + 63) / 64) * 64;
 #define MOE_QS(C)                                                                          \
   quant_scatter_kernel<C><<<T, threads, 0, s>>>(x, H, k, pair_to_row, xq_rows, xs_rows, xq_tok, \
-                                                xs_tok)
+                                                xs_tok, rows_cs, tok_cs, xq_copy)
   switch (cpt) {
     case 1: MOE_QS(1); break;
     case 2: MOE_QS(2); break;

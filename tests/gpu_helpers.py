@@ -75,14 +75,15 @@ def assert_weights_close(w_gpu, w_oracle):
     assert err.max() <= W_RTOL, err.max()
 
 
-def run_forward(inp, capture=True):
-    """moe_forward on device inputs; returns (out, captured dict, variant)."""
+def run_forward(inp, capture=True, pack=True):
+    """moe_forward on device inputs; returns (out, captured dict, variant).
+    pack=False keeps fp8 weights row-major instead of K-blocked."""
     import mixture_experts_ffn_softmax_amd as moe
 
     c = inp["cfg"]
     T, E, k, H = c["T"], c["E"], c["k"], c["H"]
-    routed = moe.Weights(inp["routed"], c["fmt"])
-    shared = moe.Weights(inp["shared"], "fp8") if inp["shared"] is not None else None
+    routed = moe.Weights(inp["routed"], c["fmt"], pack=pack)
+    shared = moe.Weights(inp["shared"], "fp8", pack=pack) if inp["shared"] is not None else None
     dbg = None
     if capture:
         z = lambda shape, dt: torch.empty(shape, dtype=dt, device=DEV)  # noqa: E731

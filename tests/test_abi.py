@@ -50,13 +50,14 @@ def test_version_and_status_strings(lib):
 
 
 def test_struct_layouts():
-    # moe_weights_t: 4 int32 then 6 pointers; moe_debug_t: 8 pointers, 6 events, 96 chars
-    assert ctypes.sizeof(MoeWeights) == 16 + 6 * 8
+    # moe_weights_t: 6 int32 then 6 pointers; moe_debug_t: 8 pointers, 6 events, 96 chars
+    assert ctypes.sizeof(MoeWeights) == 24 + 6 * 8
+    assert MoeWeights.w1.offset == 24
     assert ctypes.sizeof(MoeDebug) == 8 * 8 + 6 * 8 + 96
 
 
-def fp8_weights(E=8, H=256, I=128, fmt=0, **over):
-    w = MoeWeights(fmt, E, H, I, A, A, A, A, A, A)
+def fp8_weights(E=8, H=256, I=128, fmt=0, layout=0, **over):
+    w = MoeWeights(fmt, E, H, I, layout, 0, A, A, A, A, A, A)
     for k, v in over.items():
         setattr(w, k, v)
     return w
@@ -114,6 +115,9 @@ def test_expert_ffn_validation(lib):
     assert f(A, A, 64, A, ctypes.byref(fp8_weights(s3=MIS)), A, A, ws, None) == MOE_ERR_ALIGN
     assert f(A, A, -1, A, ctypes.byref(w), A, A, ws, None) == MOE_ERR_SHAPE
     assert f(A, A, 64, A, ctypes.byref(w), A, A, ws - 1, None) == MOE_ERR_WORKSPACE
+    assert f(A, A, 64, A, ctypes.byref(fp8_weights(layout=2)), A, A, ws, None) == MOE_ERR_UNSUPPORTED
+    assert f(A, A, 64, A, ctypes.byref(fp8_weights(fmt=1, layout=1)), A, A, ws, None) == MOE_ERR_UNSUPPORTED
+    assert f(A, A, 64, A, ctypes.byref(fp8_weights(reserved=1)), A, A, ws, None) == MOE_ERR_SHAPE
     assert f(None, None, 0, None, ctypes.byref(w), None, None, 0, None) == MOE_OK
 
 
@@ -162,3 +166,21 @@ def test_workspace_sizes_grow(lib):
     # h (bf16), y (fp32) and the xq rows dominate: ~ rows * (2I + 4H + H)
     assert b > a and b >= 4096 * (2 * 2048 + 5 * 8192)
     assert lib.moe_forward_workspace_size(-1, 2, ctypes.byref(w), 0) == 0
+
+
+def test_pack_weights_validation(lib):
+    pk = lib.moe_pack_weights
+    E, H, I = 4, 256, 128
+    n = E * H * I
+    src = fp8_weights(E, H, I, w1=0x100000, w3=0x100000 + n, w2=0x100000 + 2 * n)
+    base = 0x4000000
+    dst = fp8_weights(E, H, I, layout=1, w1=base, w3=base + n, w2=base + 2 * n)
+    call = lambda a, b: pk(ctypes.byref(a), ctypes.byref(b), None)
+    assert pk(None, ctypes.byref(dst), None) == MOE_ERR_NULL
+    assert call(fp8_weights(E, H, I, fmt=1), dst) == MOE_ERR_UNSUPPORTED
+    assert call(dst, dst) == MOE_ERR_SHAPE                      # src not row-major
+    assert call(src, src) == MOE_ERR_SHAPE                      # dst not K-blocked
+    assert call(src, fp8_weights(E, H, 256, layout=1, w1=base, w3=base + 2 * n, w2=base + 4 * n)) == MOE_ERR_SHAPE
+    assert call(src, fp8_weights(E, H, I, layout=1, w1=0x100000 + n // 2, w3=base, w2=base + n)) == MOE_ERR_SHAPE
+    assert call(src, fp8_weights(E, H, I, layout=1, w1=base, w3=base + n // 2, w2=base + 2 * n)) == MOE_ERR_SHAPE
+    assert call(src, fp8_weights(E, H, I, layout=1, w1=base + 8)) == MOE_ERR_ALIGN

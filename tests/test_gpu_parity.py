@@ -137,8 +137,13 @@ FULL_CASES = {
 }
 
 
-@pytest.mark.parametrize("case", list(FULL_CASES))
-def test_forward_full(lib, case):
+# (case, pack): fp8 weights K-blocked (the default) or left row-major
+FULL_RUNS = [(case, True) for case in FULL_CASES] + [
+    ("ragged_small_variant", False), ("large_variant_shared", False), ("one_token", False)]
+
+
+@pytest.mark.parametrize("case,pack", FULL_RUNS)
+def test_forward_full(lib, case, pack):
     spec = FULL_CASES[case]
     if spec is None:
         inp = moe_synth.make_inputs("tiny")
@@ -146,8 +151,9 @@ def test_forward_full(lib, case):
         T, H, I, E, k, fmt, shared, norm = spec
         inp = moe_synth.custom_inputs(T, H, I, E, k, fmt=fmt, seed=len(case), shared=shared, norm=norm)
     c = inp["cfg"]
-    say("forward full", case, {key: c[key] for key in ("T", "H", "I", "E", "k", "fmt", "shared", "norm")})
-    out, dbg, variant = run_forward(to_device(inp))
+    say("forward full", case, "packed" if pack else "row-major",
+        {key: c[key] for key in ("T", "H", "I", "E", "k", "fmt", "shared", "norm")})
+    out, dbg, variant = run_forward(to_device(inp), pack=pack)
     say("  variant", variant)
     ref = oracle.forward(bf16_np(inp["x"]), inp["logits"].numpy(), c["k"],
                          oracle_weights(inp["routed"], c["fmt"]),
@@ -231,18 +237,20 @@ def synthetic_rows(counts, H, seed):
     return q, s, offsets
 
 
-@pytest.mark.parametrize("counts,fmt", [
-    ([5, 0, 17, 1, 40, 0, 3, 32], "fp8"),          # small variant: ragged, empty experts
-    ([300, 0, 129, 64, 1], "fp8"),                  # large variant
-    ([9, 33, 0, 2, 16, 1, 0, 20], "mxfp4"),
+@pytest.mark.parametrize("counts,fmt,pack", [
+    ([5, 0, 17, 1, 40, 0, 3, 32], "fp8", True),    # small variant: ragged, empty experts
+    ([5, 0, 17, 1, 40, 0, 3, 32], "fp8", False),
+    ([300, 0, 129, 64, 1], "fp8", True),            # large variant
+    ([300, 0, 129, 64, 1], "fp8", False),
+    ([9, 33, 0, 2, 16, 1, 0, 20], "mxfp4", False),
 ])
-def test_expert_ffn(lib, counts, fmt):
+def test_expert_ffn(lib, counts, fmt, pack):
     E, H, I = len(counts), 256, 256
-    say("expert_ffn", counts, fmt)
+    say("expert_ffn", counts, fmt, "packed" if pack else "row-major")
     q, s, offsets = synthetic_rows(counts, H, seed=sum(counts))
     W = moe_synth.expert_weights(77, "cpu", fmt, E, H, I)
     y = lib.moe_expert_ffn(q.to(DEV), s.to(DEV), torch.as_tensor(offsets, device=DEV),
-                           lib.Weights(to_device(W), fmt))
+                           lib.Weights(to_device(W), fmt, pack=pack))
     torch.cuda.synchronize()
     y_ref = oracle.expert_ffn(q.numpy(), s.numpy(), offsets, oracle_weights(W, fmt))[0]
     ratio = tolerance_ratio(host(y), y_ref)
@@ -280,3 +288,24 @@ def test_combine_zero_weights(lib):
     out = lib.moe_combine(y, p2r, torch.zeros((20, 2), device=DEV))
     torch.cuda.synchronize()
     assert (out.float() == 0).all()
+
+
+# ----------------------------------------------------------------------------
+# weight layout
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("E,H,I", [(3, 256, 128), (2, 384, 640)])
+def test_pack_weights(lib, E, H, I):
+    """moe_pack_weights moves codes only: dst[e][c][n][0:C] == src[e][n][c*C:(c+1)*C],
+    C = 64 for W1/W3 and 32 for W2, bit for bit."""
+    say("pack_weights", E, H, I)
+    W = to_device(moe_synth.expert_weights(5, "cpu", "fp8", E, H, I))
+    w = lib.Weights(W, "fp8", pack=True)
+    torch.cuda.synchronize()
+    assert w.layout == lib.MOE_LAYOUT_K_BLOCKED
+    for name, C in (("w1", 64), ("w3", 64), ("w2", 32)):
+        src = host(W[name])
+        N, K = src.shape[1], src.shape[2]
+        want = src.reshape(E, N, K // C, C).transpose(0, 2, 1, 3).reshape(-1)
+        got = host(w.packed[name]).reshape(-1)
+        assert (got == want).all(), name
