@@ -49,6 +49,7 @@
 #include "device_common.h"
 #include "internal.h"
 
+
 namespace moe {
 
 typedef float v16f __attribute__((ext_vector_type(16)));
@@ -150,6 +151,16 @@ __device__ __forceinline__ v8i as_v8i(const uint4& a, const uint4& b) {
 }
 __device__ __forceinline__ v8bf as_v8bf(const uint4& a) { return __builtin_bit_cast(v8bf, a); }
 
+// Calls fn(std::integral_constant<int, i>) for i = I .. N-1: loop bodies whose
+// index must be a constant expression.
+template <int N, int I = 0, class Fn>
+__device__ __forceinline__ void static_for(Fn&& fn) {
+  if constexpr (I < N) {
+    fn(std::integral_constant<int, I>{});
+    static_for<N, I + 1>(fn);
+  }
+}
+
 // ---- direct-to-LDS loads, waits, barriers ---------------------------------
 // Explicit so that the compiler neither drains every outstanding load before
 // an LDS read nor moves LDS reads across a barrier.
@@ -235,18 +246,23 @@ __device__ __forceinline__ float silu_fast(float g) {
 }
 
 // ============================================================================
-// pipelined large variants: 4 waves, one per SIMD
+// large variants: 4 waves, one per SIMD, pipelined through an LDS ring
 // ============================================================================
 //
-// LDS bandwidth (about 128 bytes per clock per CU for 16-byte reads) bounds
-// the 8-wave tiling above: a 128 x 64 wave tile re-reads 12 KB of fragments
-// per K step.  Here each wave owns a 128 x 128 tile (256 accumulator
-// registers, possible with one wave per SIMD), which cuts fragment reads per
-// K step by a third.  With one wave per SIMD nothing hides LDS latency, so
-// the fragments of step k+1 are read into a second register set while the
-// MFMAs of step k run.  The LDS ring holds the stage being read into
-// registers plus STAGES-1 stages in flight: the DMA issued during step k
-// fills step k+STAGES into the slot that step k-1's reads just released.
+// Each wave owns a 128 x 128 output tile (256 accumulator registers, possible
+// with one wave per SIMD), so fragment reads per K step stay at 1/64 byte per
+// flop.  With one wave per SIMD nothing hides LDS latency, so the fragments of
+// step k+1 are read into a second register set while the MFMAs of step k run.
+// The LDS ring holds the stage being read into registers plus STAGES-1 stages
+// in flight: the DMA issued during step k fills step k+STAGES into the slot
+// that step k-1's reads released.
+//
+// Token fragments are interleaved between the two wave rows: fragment t of
+// wave row wm covers tile rows [(2t + wm) * 32, +32).  A row tile that ends
+// inside a group (the last tile of a ragged group) has a valid prefix of
+// rows; fragments wholly past it are skipped (the main loop is instantiated
+// for each count TV of valid fragments), and the interleave keeps the two wave
+// rows' shares of the remaining work equal.
 
 // 32-byte LDS rows (2 slots): conflict-free for 8 or 16 lanes per cycle when
 // 32 lanes read one slot of 32 consecutive rows.
@@ -261,22 +277,28 @@ __device__ __forceinline__ void pp_wait(int ks, int nk) {
   else wait_barrier<0>();
 }
 
-// GEMM1: wave (wm, wn) owns tokens [wm * BM/2, +BM/2) and channels
-// [wn * 64, +64) of both the gate (fragments 0, 1) and the up rows (2, 3).
-template <int BM, int STAGES>
-__global__ __launch_bounds__(256, 1) void gemm1_pp_kernel(GemmParams p) {
+// Valid token fragments of wave row wm in a tile with `vr` valid rows.
+template <int TF>
+__device__ __forceinline__ int valid_frags(int vr, int wm) {
+  const int v = (vr - wm * 32 + 63) >> 6;
+  return v < 0 ? 0 : (v > TF ? TF : v);
+}
+
+// GEMM1: wave (wm, wn) owns the interleaved token fragments of wave row wm
+// and channels [wn * 64, +64) of both the gate (fragments 0, 1) and the up
+// rows (2, 3).  LDS stage: BM token rows then 256 channel rows (W1 rows
+// n0.., then W3 rows n0..), 64 bytes of the K step each (swz64).
+template <int BM, int STAGES, int TV>
+__device__ __forceinline__ void gemm1_pp_body(const GemmParams& p, const TileInfo& ti, uint8_t* smem) {
   constexpr int kRows = BM + kLgCh;
   constexpr int kStage = kRows * 64;
   constexpr int kDma = kRows / 16;
   constexpr int kPer = kDma / 4;
   static_assert(kDma % 4 == 0, "dma split");
-  constexpr int TF = BM / 64;
   constexpr int NF = 4;
   constexpr int kGrp = (kPer + NF - 1) / NF;     // DMAs issued after each MFMA group
+  constexpr int TA = TV > 0 ? TV : 1;
   static_assert((STAGES - 1) * kPer < 64, "vmcnt range");
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * kStage];
-  __shared__ int s_tp[kMaxExperts + 2];
-  MOE_TILE_PROLOGUE(BM);
 
   const int K = p.K;
   const int nk = K >> 6;
@@ -321,17 +343,17 @@ __global__ __launch_bounds__(256, 1) void gemm1_pp_kernel(GemmParams p) {
   const int l32 = lane & 31, hh = lane >> 5;
   const int fo0 = l32 * 64 + (swz64(l32, 2 * hh) << 4);
   const int fo1 = l32 * 64 + (swz64(l32, 2 * hh + 1) << 4);
-  const int xbase = wm * (BM / 2) * 64;
-  auto wbase = [&](int f) { return (BM + (f < 2 ? 0 : kLgCh / 2) + wn * 64 + (f & 1) * 32) * 64; };
+  auto xoff = [&](int t) { return (2 * t + wm) * 32 * 64; };
+  auto woff = [&](int f) { return (BM + (f < 2 ? 0 : kLgCh / 2) + wn * 64 + (f & 1) * 32) * 64; };
   auto rd = [&](const uint8_t* at) {
     return as_v8i(*reinterpret_cast<const uint4*>(at + fo0), *reinterpret_cast<const uint4*>(at + fo1));
   };
 
-  v16f acc[NF][TF];
+  v16f acc[NF][TA];
 #pragma unroll
   for (int f = 0; f < NF; ++f)
 #pragma unroll
-    for (int t = 0; t < TF; ++t)
+    for (int t = 0; t < TA; ++t)
 #pragma unroll
       for (int j = 0; j < 16; ++j) acc[f][t][j] = 0.0f;
 
@@ -341,15 +363,17 @@ __global__ __launch_bounds__(256, 1) void gemm1_pp_kernel(GemmParams p) {
   if (STAGES <= nk) wait_barrier<(STAGES - 1) * kPer>();
   else wait_barrier<0>();
 
-  v8i xa[TF], wa[NF], xb[TF], wb[NF];
+  v8i xa[TA], wa[NF], xb[TA], wb[NF];
+  if constexpr (TV > 0) {
 #pragma unroll
-  for (int t = 0; t < TF; ++t) xa[t] = rd(smem + xbase + t * 32 * 64);
+    for (int t = 0; t < TV; ++t) xa[t] = rd(smem + xoff(t));
 #pragma unroll
-  for (int f = 0; f < NF; ++f) wa[f] = rd(smem + wbase(f));
+    for (int f = 0; f < NF; ++f) wa[f] = rd(smem + woff(f));
+  }
 
   // one K step on register set (xc, wc), reading step ks+1 into (xn, wn_).
   // steady = true: step ks+1 exists and step ks+STAGES is to be loaded.
-  auto step = [&](auto steady, int ks, const v8i (&xc)[TF], const v8i (&wc)[NF], v8i (&xn)[TF],
+  auto step = [&](auto steady, int ks, const v8i (&xc)[TA], const v8i (&wc)[NF], v8i (&xn)[TA],
                   v8i (&wn_)[NF]) {
     constexpr bool kSteady = decltype(steady)::value;
     if (kSteady) wait_barrier<(STAGES - 2) * kPer>();
@@ -357,23 +381,33 @@ __global__ __launch_bounds__(256, 1) void gemm1_pp_kernel(GemmParams p) {
     const bool next = kSteady || ks + 1 < nk;
     const bool more = kSteady || ks + STAGES < nk;
     const uint8_t* stn = smem + ((ks + 1) % STAGES) * kStage;
-#pragma unroll
-    for (int f = 0; f < NF; ++f) {
+    static_for<NF>([&](auto fc) {
+      constexpr int f = decltype(fc)::value;
       __builtin_amdgcn_sched_barrier(0);
-      if (next) {
-        wn_[f] = rd(stn + wbase(f));
-#pragma unroll
-        for (int t = f; t < TF; t += NF) xn[t] = rd(stn + xbase + t * 32 * 64);
+      // the next step's fragment reads and this group's MFMAs in one
+      // scheduling region, one read after each MFMA
+      if constexpr (TV > 0) {
+        if (next) {
+          wn_[f] = rd(stn + woff(f));
+          if (f < TV) xn[f] = rd(stn + xoff(f));
+        }
       }
-      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int t = 0; t < TF; ++t) acc[f][t] = mfma32_fp8(wc[f], xc[t], acc[f][t]);
+      for (int t = 0; t < TV; ++t) acc[f][t] = mfma32_fp8(wc[f], xc[t], acc[f][t]);
+      if constexpr (TV > 0) {
+        constexpr int kReads = 2 + (f < TV ? 2 : 0);
+        static_for<(TV > kReads ? TV : kReads)>([&](auto ic) {
+          constexpr int i = decltype(ic)::value;
+          if constexpr (i < TV) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if constexpr (i < kReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        });
+      }
       __builtin_amdgcn_sched_barrier(0);
       if (more) {
-        const int i0 = f * kGrp, i1 = (f + 1) * kGrp < kPer ? (f + 1) * kGrp : kPer;
-        if (i0 < i1) issue(ks + STAGES, i0, i1);
+        constexpr int i0 = f * kGrp, i1 = (f + 1) * kGrp < kPer ? (f + 1) * kGrp : kPer;
+        if constexpr (i0 < i1) issue(ks + STAGES, i0, i1);
       }
-    }
+    });
   };
   const std::true_type steady;
   const std::false_type tail;
@@ -393,51 +427,93 @@ __global__ __launch_bounds__(256, 1) void gemm1_pp_kernel(GemmParams p) {
   // fragment.  h = bf16(SiLU(g) * u) goes straight to the K-blocked h: a
   // 32-channel fragment is one 64-byte chunk row, so the four q stores of a
   // fragment fill 32 consecutive chunk rows (2 KB).
-  const float* S1 = reinterpret_cast<const float*>(p.sa[ti.wi]) + ti.eg * p.N;
-  const float* S3 = reinterpret_cast<const float*>(p.sb[ti.wi]) + ti.eg * p.N;
-  float xs[TF];
+  if constexpr (TV > 0) {
+    const float* S1 = reinterpret_cast<const float*>(p.sa[ti.wi]) + ti.eg * p.N;
+    const float* S3 = reinterpret_cast<const float*>(p.sb[ti.wi]) + ti.eg * p.N;
+    float xs[TV];
 #pragma unroll
-  for (int t = 0; t < TF; ++t) {
-    int grow = ti.row0 + wm * (BM / 2) + t * 32 + l32;
-    if (grow >= ti.row1) grow = ti.row1 - 1;
-    xs[t] = p.a_scale[ti.wi][grow - (ti.wi ? p.shared_row0 : 0)];
-  }
-#pragma unroll
-  for (int c = 0; c < 2; ++c) {
-    const int ch0 = n0 + wn * 64 + c * 32;
-    float4 s1v[4], s3v[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      s1v[q] = *reinterpret_cast<const float4*>(S1 + ch0 + 8 * q + 4 * hh);
-      s3v[q] = *reinterpret_cast<const float4*>(S3 + ch0 + 8 * q + 4 * hh);
+    for (int t = 0; t < TV; ++t) {
+      int grow = ti.row0 + (2 * t + wm) * 32 + l32;
+      if (grow >= ti.row1) grow = ti.row1 - 1;
+      xs[t] = p.a_scale[ti.wi][grow - (ti.wi ? p.shared_row0 : 0)];
     }
 #pragma unroll
-    for (int t = 0; t < TF; ++t) {
-      const int grow = ti.row0 + wm * (BM / 2) + t * 32 + l32;
-      if (grow >= ti.row1) continue;
-      uint16_t* hrow = p.h + h_off(p.h_cs, grow, ch0);
+    for (int c = 0; c < 2; ++c) {
+      const int ch0 = n0 + wn * 64 + c * 32;
+      float4 s1v[4], s3v[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const float sg[4] = {s1v[q].x, s1v[q].y, s1v[q].z, s1v[q].w};
-        const float su[4] = {s3v[q].x, s3v[q].y, s3v[q].z, s3v[q].w};
-        uint32_t b[4];
+        s1v[q] = *reinterpret_cast<const float4*>(S1 + ch0 + 8 * q + 4 * hh);
+        s3v[q] = *reinterpret_cast<const float4*>(S3 + ch0 + 8 * q + 4 * hh);
+      }
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const float g = acc[c][t][4 * q + v] * xs[t] * sg[v];
-          const float u = acc[2 + c][t][4 * q + v] * xs[t] * su[v];
-          b[v] = bf16_rne(silu_fast(g) * u);
+      for (int t = 0; t < TV; ++t) {
+        const int grow = ti.row0 + (2 * t + wm) * 32 + l32;
+        if (grow >= ti.row1) continue;
+        uint16_t* hrow = p.h + h_off(p.h_cs, grow, ch0);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float sg[4] = {s1v[q].x, s1v[q].y, s1v[q].z, s1v[q].w};
+          const float su[4] = {s3v[q].x, s3v[q].y, s3v[q].z, s3v[q].w};
+          uint32_t b[4];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const float g = acc[c][t][4 * q + v] * xs[t] * sg[v];
+            const float u = acc[2 + c][t][4 * q + v] * xs[t] * su[v];
+            b[v] = bf16_rne(silu_fast(g) * u);
+          }
+          *reinterpret_cast<uint2*>(hrow + 8 * q + 4 * hh) = make_uint2(b[0] | (b[1] << 16), b[2] | (b[3] << 16));
         }
-        *reinterpret_cast<uint2*>(hrow + 8 * q + 4 * hh) = make_uint2(b[0] | (b[1] << 16), b[2] | (b[3] << 16));
       }
     }
   }
 }
 
+template <int BM, int STAGES>
+__global__ __launch_bounds__(256, 1) void gemm1_pp_kernel(GemmParams p) {
+  constexpr int kStage = (BM + kLgCh) * 64;
+  constexpr int TF = BM / 64;
+  // the tile-prefix table lives in the ring until the first DMA is issued
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * kStage];
+  static_assert(STAGES * kStage >= (kMaxExperts + 2) * 4, "tile prefix fits in the ring");
+  int* s_tp = reinterpret_cast<int*>(smem);
+  MOE_TILE_PROLOGUE(BM);
+  __syncthreads();   // every thread has its tile: the ring is free
+  const int vr = min(BM, ti.row1 - ti.row0);
+  const int wm = __builtin_amdgcn_readfirstlane(threadIdx.x >> 7);
+  switch (valid_frags<TF>(vr, wm)) {
+    case 0: gemm1_pp_body<BM, STAGES, 0>(p, ti, smem); break;
+    case 1: gemm1_pp_body<BM, STAGES, 1>(p, ti, smem); break;
+    case 2: gemm1_pp_body<BM, STAGES, 2>(p, ti, smem); break;
+    case 3: if constexpr (TF >= 3) gemm1_pp_body<BM, STAGES, 3>(p, ti, smem); break;
+    default: if constexpr (TF >= 4) gemm1_pp_body<BM, STAGES, 4>(p, ti, smem); break;
+  }
+}
+
+// 32 e4m3 codes (4 words, 16 per half-lane K slice) -> the two bf16 halves
+// of a 32x32x16 fragment pair, exact.
+struct BfPair { v8bf a, b; };
+__device__ __forceinline__ BfPair fp8x16_to_bf16(const uint4& w) {
+  const v2bf a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.0f, false);
+  const v2bf b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.0f, true);
+  const v2bf c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.0f, false);
+  const v2bf d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.0f, true);
+  const v2bf e = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.z, 1.0f, false);
+  const v2bf g = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.z, 1.0f, true);
+  const v2bf h = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.w, 1.0f, false);
+  const v2bf k = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.w, 1.0f, true);
+  return BfPair{v8bf{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]},
+                v8bf{e[0], e[1], g[0], g[1], h[0], h[1], k[0], k[1]}};
+}
+
 // GEMM2: K step of 32 elements.  LDS stage: BM h rows of 32 bf16 (64 bytes,
 // swz64) then 256 W2 rows of 32 codes (32 bytes, swz32).  Wave (wm, wn) owns
-// tokens [wm * BM/2, +BM/2) and output channels [wn * 128, +128).
-template <int BM, int STAGES>
-__global__ __launch_bounds__(256, 1) void gemm2_pp_kernel(GemmParams p) {
+// the interleaved token fragments of wave row wm and output channels
+// [wn * 128, +128).  W2 fragments are widened to bf16 one step ahead: the
+// conversions of step k+1 run between the MFMAs of step k, which do not
+// depend on them, so the vector unit works while the matrix core does.
+template <int BM, int STAGES, int TV>
+__device__ __forceinline__ void gemm2_pp_body(const GemmParams& p, const TileInfo& ti, uint8_t* smem) {
   constexpr int kTokBytes = BM * 64;
   constexpr int kStage = kTokBytes + kLgCh * 32;
   constexpr int kDmaT = BM / 16;            // 16 h rows per dma16
@@ -445,12 +521,9 @@ __global__ __launch_bounds__(256, 1) void gemm2_pp_kernel(GemmParams p) {
   constexpr int kPer = (kDmaT + kDmaW) / 4;
   static_assert((kDmaT + kDmaW) % 4 == 0, "dma split");
   static_assert((STAGES - 1) * kPer < 64, "vmcnt range");
-  constexpr int TF = BM / 64;
   constexpr int NF = 4;
   constexpr int kGrp = (kPer + NF - 1) / NF;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * kStage];
-  __shared__ int s_tp[kMaxExperts + 2];
-  MOE_TILE_PROLOGUE(BM);
+  constexpr int TA = TV > 0 ? TV : 1;
 
   const int K = p.K;                        // = I
   const int nk = K >> 5;
@@ -460,9 +533,9 @@ __global__ __launch_bounds__(256, 1) void gemm2_pp_kernel(GemmParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
   const uint8_t* src[kPer];
-  long inc[kPer];
-  uint32_t dsto[kPer];
   const Operand& wd = p.wd[ti.wi];
+  const long inc_t = op_step(p.ta[ti.wi], 64);
+  const long inc_w = op_step(wd, 32);
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     const int q = wave * kPer + i;
@@ -471,13 +544,9 @@ __global__ __launch_bounds__(256, 1) void gemm2_pp_kernel(GemmParams p) {
       int r = ti.row0 + row;
       if (r >= ti.row1) r = ti.row1 - 1;
       src[i] = row_ptr(p, ti, r) + swz64(row, lane & 3) * 16;
-      inc[i] = op_step(p.ta[ti.wi], 64);
-      dsto[i] = q * 1024;
     } else {
       const int row = (q - kDmaT) * 32 + (lane >> 1);
       src[i] = W2 + (long)(n0 + row) * wd.row_pitch + swz32(row, lane & 1) * 16;
-      inc[i] = op_step(wd, 32);
-      dsto[i] = kTokBytes + (q - kDmaT) * 1024;
     }
   }
   const uint32_t lds0 = lds_addr(smem);
@@ -485,8 +554,10 @@ __global__ __launch_bounds__(256, 1) void gemm2_pp_kernel(GemmParams p) {
     const uint32_t st = lds0 + (ks % STAGES) * kStage;
 #pragma unroll
     for (int i = i0; i < i1; ++i) {
-      dma16(src[i], st + dsto[i]);
-      src[i] += inc[i];
+      const int q = wave * kPer + i;
+      const bool tok = q < kDmaT;
+      dma16(src[i], st + (tok ? q * 1024 : kTokBytes + (q - kDmaT) * 1024));
+      src[i] += tok ? inc_t : inc_w;
     }
   };
 
@@ -496,21 +567,19 @@ __global__ __launch_bounds__(256, 1) void gemm2_pp_kernel(GemmParams p) {
   const int ho0 = l32 * 64 + (swz64(l32, 2 * hh) << 4);
   const int ho1 = l32 * 64 + (swz64(l32, 2 * hh + 1) << 4);
   // W2 fragment: row l32, codes [16h, 16h + 16) = 32-byte-row slot h
-  const int wo = kTokBytes + l32 * 32 + (swz32(l32, hh) << 4);
-  const int xbase = wm * (BM / 2) * 64;
-  const int wbase = wn * 128 * 32;
+  const int wo = kTokBytes + wn * 128 * 32 + l32 * 32 + (swz32(l32, hh) << 4);
+  auto xoff = [&](int t) { return (2 * t + wm) * 32 * 64; };
 
-  struct XF { v8bf a, b; };
   auto rdx = [&](const uint8_t* at) {
-    return XF{as_v8bf(*reinterpret_cast<const uint4*>(at + ho0)), as_v8bf(*reinterpret_cast<const uint4*>(at + ho1))};
+    return BfPair{as_v8bf(*reinterpret_cast<const uint4*>(at + ho0)), as_v8bf(*reinterpret_cast<const uint4*>(at + ho1))};
   };
-  auto rdw = [&](const uint8_t* at) { return *reinterpret_cast<const uint4*>(at + wo); };
+  auto rdw = [&](const uint8_t* st, int f) { return *reinterpret_cast<const uint4*>(st + wo + f * 32 * 32); };
 
-  v16f acc[NF][TF];
+  v16f acc[NF][TA];
 #pragma unroll
   for (int f = 0; f < NF; ++f)
 #pragma unroll
-    for (int t = 0; t < TF; ++t)
+    for (int t = 0; t < TA; ++t)
 #pragma unroll
       for (int j = 0; j < 16; ++j) acc[f][t][j] = 0.0f;
 
@@ -520,55 +589,70 @@ __global__ __launch_bounds__(256, 1) void gemm2_pp_kernel(GemmParams p) {
   if (STAGES <= nk) wait_barrier<(STAGES - 1) * kPer>();
   else wait_barrier<0>();
 
-  XF xa[TF], xb[TF];
-  uint4 wa[NF], wb[NF];
+  BfPair xa[TA], xb[TA], wa[NF], wb[NF];
+  if constexpr (TV > 0) {
 #pragma unroll
-  for (int t = 0; t < TF; ++t) xa[t] = rdx(smem + xbase + t * 32 * 64);
+    for (int t = 0; t < TV; ++t) xa[t] = rdx(smem + xoff(t));
 #pragma unroll
-  for (int f = 0; f < NF; ++f) wa[f] = rdw(smem + wbase + f * 32 * 32);
+    for (int f = 0; f < NF; ++f) wa[f] = fp8x16_to_bf16(rdw(smem, f));
+  }
 
-  auto step = [&](auto steady, int ks, const XF (&xc)[TF], const uint4 (&wc)[NF], XF (&xn)[TF],
-                  uint4 (&wn_)[NF]) {
+  auto step = [&](auto steady, int ks, const BfPair (&xc)[TA], const BfPair (&wc)[NF], BfPair (&xn)[TA],
+                  BfPair (&wn_)[NF]) {
     constexpr bool kSteady = decltype(steady)::value;
     if (kSteady) wait_barrier<(STAGES - 2) * kPer>();
     else pp_wait<(STAGES - 2) * kPer, STAGES, kPer>(ks, nk);
     const bool next = kSteady || ks + 1 < nk;
     const bool more = kSteady || ks + STAGES < nk;
     const uint8_t* stn = smem + ((ks + 1) % STAGES) * kStage;
-#pragma unroll
-    for (int f = 0; f < NF; ++f) {
+    uint4 raw[NF];
+    static_for<NF>([&](auto fc) {
+      constexpr int f = decltype(fc)::value;
       __builtin_amdgcn_sched_barrier(0);
-      if (next) {
-        wn_[f] = rdw(stn + wbase + f * 32 * 32);
+      if constexpr (TV > 0) {
+        if (next) {
+          if (f == 0) {
 #pragma unroll
-        for (int t = f; t < TF; t += NF) xn[t] = rdx(stn + xbase + t * 32 * 64);
+            for (int g = 0; g < NF; ++g) raw[g] = rdw(stn, g);
+          }
+          if (f < TV) xn[f] = rdx(stn + xoff(f));
+        }
       }
-      const uint32_t cw[4] = {wc[f].x, wc[f].y, wc[f].z, wc[f].w};
-      v8bf w0, w1;
-      {
-        const v2bf a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cw[0], 1.0f, false);
-        const v2bf b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cw[0], 1.0f, true);
-        const v2bf c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cw[1], 1.0f, false);
-        const v2bf d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cw[1], 1.0f, true);
-        w0 = v8bf{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
-        const v2bf e = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cw[2], 1.0f, false);
-        const v2bf g = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cw[2], 1.0f, true);
-        const v2bf h = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cw[3], 1.0f, false);
-        const v2bf k = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cw[3], 1.0f, true);
-        w1 = v8bf{e[0], e[1], g[0], g[1], h[0], h[1], k[0], k[1]};
-      }
-      __builtin_amdgcn_sched_barrier(0);
+      // MFMAs of this group, the conversions of the next step's W2 fragments
+      // (f - 1 and, in the last group, f) and the fragment reads in one
+      // scheduling region, one read and a few conversions after each MFMA
+      // the two K halves of each accumulator TV instructions apart
 #pragma unroll
-      for (int t = 0; t < TF; ++t) {
-        acc[f][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w0, xc[t].a, acc[f][t], 0, 0, 0);
-        acc[f][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w1, xc[t].b, acc[f][t], 0, 0, 0);
+      for (int t = 0; t < TV; ++t)
+        acc[f][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wc[f].a, xc[t].a, acc[f][t], 0, 0, 0);
+#pragma unroll
+      for (int t = 0; t < TV; ++t)
+        acc[f][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wc[f].b, xc[t].b, acc[f][t], 0, 0, 0);
+      if constexpr (TV > 0) {
+        if (next && f > 0) {
+          wn_[f - 1] = fp8x16_to_bf16(raw[f - 1]);
+          if (f == NF - 1) wn_[f] = fp8x16_to_bf16(raw[f]);
+        }
+      }
+      if constexpr (TV > 0) {
+        // per group: 2*TV MFMAs; DS reads: the 4 raw W2 fragments (group 0)
+        // and one token fragment (2 reads); 8 conversions per W2 fragment
+        constexpr int kReads = (f == 0 ? NF : 0) + (f < TV ? 2 : 0);
+        constexpr int kCvt = (f == 0) ? 0 : (f == NF - 1 ? 16 : 8);
+        constexpr int kCvtPer = (kCvt + 2 * TV - 1) / (2 * TV);
+        static_for<2 * TV>([&](auto ic) {
+          constexpr int i = decltype(ic)::value;
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if constexpr (i < kReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          if constexpr (kCvtPer > 0) __builtin_amdgcn_sched_group_barrier(0x002, kCvtPer, 0);
+        });
       }
       __builtin_amdgcn_sched_barrier(0);
       if (more) {
-        const int i0 = f * kGrp, i1 = (f + 1) * kGrp < kPer ? (f + 1) * kGrp : kPer;
-        if (i0 < i1) issue(ks + STAGES, i0, i1);
+        constexpr int i0 = f * kGrp, i1 = (f + 1) * kGrp < kPer ? (f + 1) * kGrp : kPer;
+        if constexpr (i0 < i1) issue(ks + STAGES, i0, i1);
       }
-    }
+    });
   };
   const std::true_type steady;
   const std::false_type tail;
@@ -583,27 +667,50 @@ __global__ __launch_bounds__(256, 1) void gemm2_pp_kernel(GemmParams p) {
   }
   if (ks < nk) step(tail, ks, xa, wa, xb, wb);
 
-  const float* S2 = reinterpret_cast<const float*>(p.sa[ti.wi]) + ti.eg * p.N;
+  // ---- epilogue: y = acc * s2 in fp32.  Lane holds token l32 of each
+  // token fragment and channels 8q + 4hh .. +3 of each channel fragment.
+  if constexpr (TV > 0) {
+    const float* S2 = reinterpret_cast<const float*>(p.sa[ti.wi]) + ti.eg * p.N + n0 + wn * 128;
 #pragma unroll
-  for (int f = 0; f < NF; ++f) {
-    float4 s2v[4];
+    for (int f = 0; f < NF; ++f) {
+      float4 s2v[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      s2v[q] = *reinterpret_cast<const float4*>(S2 + n0 + wn * 128 + f * 32 + 8 * q + 4 * hh);
+      for (int q = 0; q < 4; ++q) s2v[q] = *reinterpret_cast<const float4*>(S2 + f * 32 + 8 * q + 4 * hh);
 #pragma unroll
-    for (int t = 0; t < TF; ++t) {
-      const int grow = ti.row0 + wm * (BM / 2) + t * 32 + l32;
-      if (grow >= ti.row1) continue;
-      float* yrow = p.y + (long)grow * p.N + n0 + wn * 128 + f * 32;
+      for (int t = 0; t < TV; ++t) {
+        const int grow = ti.row0 + (2 * t + wm) * 32 + l32;
+        if (grow >= ti.row1) continue;
+        float* yrow = p.y + (long)grow * p.N + n0 + wn * 128 + f * 32 + 4 * hh;
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        *reinterpret_cast<float4*>(yrow + 8 * q + 4 * hh) =
-            make_float4(acc[f][t][4 * q] * s2v[q].x, acc[f][t][4 * q + 1] * s2v[q].y,
-                        acc[f][t][4 * q + 2] * s2v[q].z, acc[f][t][4 * q + 3] * s2v[q].w);
+        for (int q = 0; q < 4; ++q)
+          *reinterpret_cast<float4*>(yrow + 8 * q) =
+              make_float4(acc[f][t][4 * q] * s2v[q].x, acc[f][t][4 * q + 1] * s2v[q].y,
+                          acc[f][t][4 * q + 2] * s2v[q].z, acc[f][t][4 * q + 3] * s2v[q].w);
+      }
     }
   }
 }
 
+template <int BM, int STAGES>
+__global__ __launch_bounds__(256, 1) void gemm2_pp_kernel(GemmParams p) {
+  constexpr int kStage = BM * 64 + kLgCh * 32;
+  constexpr int TF = BM / 64;
+  // the tile-prefix table lives in the ring until the first DMA is issued
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * kStage];
+  static_assert(STAGES * kStage >= (kMaxExperts + 2) * 4, "tile prefix fits in the ring");
+  int* s_tp = reinterpret_cast<int*>(smem);
+  MOE_TILE_PROLOGUE(BM);
+  __syncthreads();   // every thread has its tile: the ring is free
+  const int vr = min(BM, ti.row1 - ti.row0);
+  const int wm = __builtin_amdgcn_readfirstlane(threadIdx.x >> 7);
+  switch (valid_frags<TF>(vr, wm)) {
+    case 0: gemm2_pp_body<BM, STAGES, 0>(p, ti, smem); break;
+    case 1: gemm2_pp_body<BM, STAGES, 1>(p, ti, smem); break;
+    case 2: gemm2_pp_body<BM, STAGES, 2>(p, ti, smem); break;
+    case 3: if constexpr (TF >= 3) gemm2_pp_body<BM, STAGES, 3>(p, ti, smem); break;
+    default: if constexpr (TF >= 4) gemm2_pp_body<BM, STAGES, 4>(p, ti, smem); break;
+  }
+}
 // ============================================================================
 // small variants (decode-sized groups; fp8 or MXFP4 weights)
 // ============================================================================

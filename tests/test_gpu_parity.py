@@ -130,6 +130,7 @@ FULL_CASES = {
     "shared_small_variant": (40, 256, 256, 4, 2, "fp8", True, False),
     "large_variant": (300, 256, 256, 4, 2, "fp8", False, False),
     "large_variant_shared": (333, 512, 384, 3, 2, "fp8", True, False),
+    "large256_ragged_shared": (1000, 256, 256, 4, 2, "fp8", True, False),
     "mxfp4_rmsnorm": (48, 256, 128, 8, 2, "mxfp4", False, True),
     "mxfp4_k_equals_E": (20, 384, 256, 4, 4, "mxfp4", False, False),
     "dense_E1_k1": (70, 256, 128, 1, 1, "fp8", False, False),
@@ -242,6 +243,9 @@ def synthetic_rows(counts, H, seed):
     ([5, 0, 17, 1, 40, 0, 3, 32], "fp8", False),
     ([300, 0, 129, 64, 1], "fp8", True),            # large variant
     ([300, 0, 129, 64, 1], "fp8", False),
+    # 256-row tiles; the last tile of each group leaves 0..4 valid 32-row
+    # fragments per wave row (rows mod 256 = 188, 34, 1, 33, 232, 88, 97)
+    ([700, 0, 290, 513, 33, 1000, 600, 97], "fp8", True),
     ([9, 33, 0, 2, 16, 1, 0, 20], "mxfp4", False),
 ])
 def test_expert_ffn(lib, counts, fmt, pack):
