@@ -12,6 +12,8 @@ namespace moe {
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 32;
 constexpr int kPermuteChunk = 1024;  // pairs per counting / ranking chunk
+constexpr int kMetaMaxPairs = 2048;  // pairs handled by the single-workgroup metadata kernel
+constexpr int kMetaRouteMaxE = 32;   // experts it can also route (one lane per token)
 
 // Byte addressing of a matrix operand with rows of K contraction bytes: byte k
 // of row r sits at r * row_pitch + (k >> kc_shift) * chunk_stride +
@@ -59,6 +61,13 @@ hipError_t launch_rank(const int* ids, int pairs, int E, const int* chunk_base, 
 hipError_t launch_quant_scatter(const uint16_t* x, int T, int H, int k, const int* pair_to_row,
                                 uint8_t* xq_rows, float* xs_rows, uint8_t* xq_tok, float* xs_tok,
                                 bool blocked, uint8_t* xq_copy, hipStream_t s);
+// For T * k <= kMetaMaxPairs: counts, offsets (+ the extra group), ranks and,
+// when tile_prefix is non-NULL, the tile prefix of the groups for row tiles
+// of bm, in one launch.  logits non-NULL (E <= kMetaRouteMaxE): routes first
+// and writes ids / w; logits NULL: reads ids.
+hipError_t launch_meta(const float* logits, int T, int E, int k, int* ids, float* w, int* counts,
+                       int* offsets, int extra_rows, int* pair_to_row, int* row_to_pair, int* tile_prefix,
+                       int bm, hipStream_t s);
 
 // ---- grouped expert FFN ---------------------------------------------------
 enum WeightFormat { kFp8 = 0, kMxfp4 = 1 };

@@ -138,15 +138,20 @@ moe::FfnGroups make_groups(const moe_weights_t* r, const moe_weights_t* sh, cons
 }
 
 // GEMM1 -> GEMM2 over the groups of `g`.
+// tile_prefix_ready: the tile prefix for this variant is already in place
+// (the metadata kernel computed it).
 moe_status_t run_ffn(const moe::FfnGroups& g, const moe::RowOperand& x, long n_rows, float* y,
                      int32_t* tile_prefix, uint16_t* h, hipStream_t s, void* const* events,
-                     char* variant_out, size_t variant_len) {
+                     char* variant_out, size_t variant_len, bool tile_prefix_ready = false) {
   const int variant = moe::choose_variant(g, n_rows);
   if (variant_out)
     snprintf(variant_out, variant_len, "%s/%s", moe::variant_name(variant),
              g.fmt == moe::kMxfp4 ? "mxfp4" : "fp8");
-  hipError_t e = moe::launch_tile_prefix(g.offsets, g.n_groups, moe::variant_rows(variant), tile_prefix, s);
-  if (e != hipSuccess) return device_status(e, "tile_prefix");
+  hipError_t e = hipSuccess;
+  if (!tile_prefix_ready) {
+    e = moe::launch_tile_prefix(g.offsets, g.n_groups, moe::variant_rows(variant), tile_prefix, s);
+    if (e != hipSuccess) return device_status(e, "tile_prefix");
+  }
   if (events && events[MOE_STAGE_GEMM1]) hipEventRecord((hipEvent_t)events[MOE_STAGE_GEMM1], s);
   e = moe::launch_gemm1(variant, g, x, tile_prefix, n_rows, h, s);
   if (e != hipSuccess) return device_status(e, "gemm1");
@@ -229,12 +234,19 @@ moe_status_t moe_permute(const uint16_t* x, int32_t T, int32_t H, const int32_t*
   Carve c(ws);
   int32_t* hist = c.take<int32_t>(chunks * E);
   int32_t* base = c.take<int32_t>(chunks * E);
-  hipError_t e = moe::launch_counts(topk_ids, (int)pairs, E, hist, base, expert_counts,
-                                    expert_offsets, 0, s);
-  if (e != hipSuccess) return device_status(e, "counts");
-  if (T == 0) return ok();
-  e = moe::launch_rank(topk_ids, (int)pairs, E, base, pair_to_row, row_to_pair, s);
-  if (e != hipSuccess) return device_status(e, "rank");
+  hipError_t e;
+  if (T > 0 && pairs <= moe::kMetaMaxPairs) {
+    // reads topk_ids only (no logits): the const is not written through
+    e = moe::launch_meta(nullptr, T, E, top_k, const_cast<int32_t*>(topk_ids), nullptr, expert_counts,
+                         expert_offsets, 0, pair_to_row, row_to_pair, nullptr, 0, s);
+    if (e != hipSuccess) return device_status(e, "meta");
+  } else {
+    e = moe::launch_counts(topk_ids, (int)pairs, E, hist, base, expert_counts, expert_offsets, 0, s);
+    if (e != hipSuccess) return device_status(e, "counts");
+    if (T == 0) return ok();
+    e = moe::launch_rank(topk_ids, (int)pairs, E, base, pair_to_row, row_to_pair, s);
+    if (e != hipSuccess) return device_status(e, "rank");
+  }
   e = moe::launch_quant_scatter(x, T, H, top_k, pair_to_row, xq_rows, xs_rows, xq_tok, xs_tok, false,
                                 nullptr, s);
   return device_status(e, "quant_scatter");
@@ -389,30 +401,44 @@ moe_status_t moe_forward(const uint16_t* x, const float* logits, int32_t T, int3
   const long R = (long)T * top_k;
   hipError_t e;
 
+  const moe::FfnGroups g = make_groups(routed, sh ? shared : nullptr, L.offsets);
+  const long rows = R + (sh ? T : 0);
+  // Up to kMetaMaxPairs pairs, one workgroup computes the whole routing
+  // metadata (and routes, for at most kMetaRouteMaxE experts); beyond that,
+  // route / counts / ranks run as grid-wide kernels.
+  const bool meta = R <= moe::kMetaMaxPairs;
+  const bool fused_route = meta && E <= moe::kMetaRouteMaxE;
   if (ev && ev[MOE_STAGE_ROUTE]) hipEventRecord((hipEvent_t)ev[MOE_STAGE_ROUTE], s);
-  e = moe::launch_route(logits, T, E, top_k, L.ids, L.w, s);
-  if (e != hipSuccess) return device_status(e, "route");
+  if (!fused_route) {
+    e = moe::launch_route(logits, T, E, top_k, L.ids, L.w, s);
+    if (e != hipSuccess) return device_status(e, "route");
+  }
 
   if (ev && ev[MOE_STAGE_PERMUTE]) hipEventRecord((hipEvent_t)ev[MOE_STAGE_PERMUTE], s);
-  e = moe::launch_counts(L.ids, (int)R, E, L.hist, L.base, L.counts, L.offsets, sh ? T : 0, s);
-  if (e != hipSuccess) return device_status(e, "counts");
-  e = moe::launch_rank(L.ids, (int)R, E, L.base, L.p2r, L.r2p, s);
-  if (e != hipSuccess) return device_status(e, "rank");
+  if (meta) {
+    const int bm = moe::variant_rows(moe::choose_variant(g, rows));
+    e = moe::launch_meta(fused_route ? logits : nullptr, T, E, top_k, L.ids, L.w, L.counts, L.offsets,
+                         sh ? T : 0, L.p2r, L.r2p, L.tile_prefix, bm, s);
+    if (e != hipSuccess) return device_status(e, "meta");
+  } else {
+    e = moe::launch_counts(L.ids, (int)R, E, L.hist, L.base, L.counts, L.offsets, sh ? T : 0, s);
+    if (e != hipSuccess) return device_status(e, "counts");
+    e = moe::launch_rank(L.ids, (int)R, E, L.base, L.p2r, L.r2p, s);
+    if (e != hipSuccess) return device_status(e, "rank");
+  }
   // the layer keeps the quantised rows K-blocked (64-byte chunks); the debug
   // capture receives a row-major copy
   e = moe::launch_quant_scatter(x, T, H, top_k, L.p2r, L.xq_rows, L.xs_rows, L.xq_tok, L.xs_tok, true,
                                 dbg ? dbg->xq_rows : nullptr, s);
   if (e != hipSuccess) return device_status(e, "quant_scatter");
 
-  const moe::FfnGroups g = make_groups(routed, sh ? shared : nullptr, L.offsets);
-  const long rows = R + (sh ? T : 0);
   const moe::Operand rows_d = moe::k_blocked_operand(R, moe::kTokChunk);
   const moe::Operand tok_d = moe::k_blocked_operand(T, moe::kTokChunk);
   moe::RowOperand xr{{L.xq_rows, sh ? L.xq_tok : L.xq_rows}, {L.xs_rows, sh ? L.xs_tok : L.xs_rows}, R,
                      {rows_d, sh ? tok_d : rows_d}};
   char* vout = dbg ? dbg->variant : nullptr;
   MOE_CHECK(run_ffn(g, xr, rows, L.y_rows, L.tile_prefix, L.h, s, ev, vout,
-                    dbg ? sizeof(dbg->variant) : 0));
+                    dbg ? sizeof(dbg->variant) : 0, meta));
 
   if (ev && ev[MOE_STAGE_COMBINE]) hipEventRecord((hipEvent_t)ev[MOE_STAGE_COMBINE], s);
   e = moe::launch_combine(L.y_rows, L.p2r, L.w, T, H, top_k, sh ? L.y_rows + (size_t)R * H : nullptr,

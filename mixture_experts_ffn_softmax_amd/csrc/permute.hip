@@ -14,6 +14,11 @@
 //                  in pair order -> pair_to_row / row_to_pair
 //   quant_scatter  per token: amax, scale, e4m3 codes, written to each of the
 //                  token's rows (and optionally in token order)
+//   meta_kernel    one workgroup doing all of the above (and, for at most
+//                  kMetaRouteMaxE experts, the routing; and the grouped
+//                  GEMMs' tile prefix) when there are at most kMetaMaxPairs
+//                  pairs: one launch instead of five for decode-sized
+//                  batches, where launch latency is the cost
 // Rows are ordered by expert and, inside an expert, by pair index; this order
 // is unique, so the result is deterministic.  Expert ids outside [0, E) are
 // skipped (their pairs get row -1) so that no access leaves its buffer.
@@ -207,6 +212,134 @@ __global__ __launch_bounds__(1024) void quant_scatter_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// meta_kernel: one workgroup of 1024 threads (16 waves).
+//   1. ids: routed here (E <= kMetaRouteMaxE, one lane per token, the same
+//      selection and weight arithmetic as route_kernel) or read from `ids`;
+//      kept in LDS.
+//   2. counts (LDS atomics: counts only), exclusive offsets, the optional
+//      extra group, and the tile prefix of the groups for row tiles of bm.
+//   3. ranks, chunk by chunk of 1024 pairs in pair order: each wave ranks its
+//      64 pairs by ballots, a per-expert scan over the 16 waves turns the
+//      wave counts into starting rows.
+constexpr int kMetaWaves = 16;
+
+__global__ __launch_bounds__(1024) void meta_kernel(const float* __restrict__ logits, int T, int E, int k,
+                                                    int* __restrict__ ids, float* __restrict__ w,
+                                                    int* __restrict__ counts, int* __restrict__ offsets,
+                                                    int extra_rows, int* __restrict__ pair_to_row,
+                                                    int* __restrict__ row_to_pair, int* __restrict__ tile_prefix,
+                                                    int bm) {
+  __shared__ int s_ids[kMetaMaxPairs];
+  __shared__ int s_cnt[kMetaWaves * kMaxExperts];
+  __shared__ int s_tot[kMaxExperts + 1];
+  __shared__ int s_run[kMaxExperts];
+  __shared__ int s_tmp[16];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wv = tid >> 6;
+  const int R = T * k;
+
+  for (int e = tid; e < E; e += 1024) s_tot[e] = 0;
+  if (logits) {
+    for (int t = tid; t < T; t += 1024) {
+      float v[kMetaRouteMaxE];
+      const float* row = logits + (long)t * E;
+#pragma unroll
+      for (int i = 0; i < kMetaRouteMaxE; ++i) v[i] = (i < E) ? row[i] : 0.0f;
+      uint32_t avail = (E >= 32) ? 0xFFFFFFFFu : ((1u << E) - 1u);
+      float vmax = 0.0f, sum = 0.0f;
+      float ex[kMaxTopK];
+      for (int j = 0; j < k; ++j) {
+        float bv = -INFINITY;
+        int bi = 0x7FFFFFFF;
+#pragma unroll
+        for (int i = 0; i < kMetaRouteMaxE; ++i)
+          if (((avail >> i) & 1u) && (v[i] > bv || (v[i] == bv && i < bi))) {
+            bv = v[i];
+            bi = i;
+          }
+        avail &= ~(1u << bi);
+        if (j == 0) vmax = bv;
+        ex[j] = expf(bv - vmax);
+        sum += ex[j];
+        ids[(long)t * k + j] = bi;
+        s_ids[t * k + j] = bi;
+      }
+      for (int j = 0; j < k; ++j) w[(long)t * k + j] = ex[j] / sum;
+    }
+  } else {
+    for (int p = tid; p < R; p += 1024) s_ids[p] = ids[p];
+  }
+  __syncthreads();
+
+  // ---- counts, offsets, tile prefix
+  for (int p = tid; p < R; p += 1024) {
+    const int e = s_ids[p];
+    if ((unsigned)e < (unsigned)E) atomicAdd(&s_tot[e], 1);
+  }
+  __syncthreads();
+  const int cnt_e = (tid < E) ? s_tot[tid] : 0;
+  const int total = block_exclusive_scan_1024(s_tot, s_tmp, E);
+  if (tid < E) {
+    counts[tid] = cnt_e;
+    offsets[tid] = s_tot[tid];
+    s_run[tid] = s_tot[tid];
+  }
+  if (tid == 0) {
+    offsets[E] = total;
+    if (extra_rows > 0) offsets[E + 1] = total + extra_rows;
+  }
+  if (tile_prefix) {
+    const int G = E + (extra_rows > 0 ? 1 : 0);
+    __syncthreads();                     // s_tot is reused for the tile counts
+    const int rows = (tid < E) ? cnt_e : (tid == E ? extra_rows : 0);
+    if (tid < G) s_tot[tid] = rows > 0 ? (rows + bm - 1) / bm : 0;
+    __syncthreads();
+    const int tiles = block_exclusive_scan_1024(s_tot, s_tmp, G);
+    if (tid < G) tile_prefix[tid] = s_tot[tid];
+    if (tid == 0) tile_prefix[G] = tiles;
+  }
+  __syncthreads();
+
+  // ---- ranks
+  int* my_cnt = s_cnt + wv * E;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int c0 = 0; c0 < R; c0 += 1024) {
+    for (int e = lane; e < E; e += 64) my_cnt[e] = 0;
+    const int p = c0 + tid;
+    int e = (p < R) ? s_ids[p] : -1;
+    if ((unsigned)e >= (unsigned)E) e = -1;
+    uint64_t pending = __ballot(e >= 0);
+    int rank = 0;
+    while (pending) {
+      const int leader = __ffsll((unsigned long long)pending) - 1;
+      const int el = __builtin_amdgcn_readlane(e, leader);
+      const uint64_t same = __ballot(e == el) & pending;
+      if (e == el) rank = __popcll(same & lt_mask);
+      if (lane == leader) my_cnt[el] = __popcll(same);
+      pending &= ~same;
+    }
+    __syncthreads();
+    for (int x = tid; x < E; x += 1024) {
+      int run = s_run[x];
+#pragma unroll
+      for (int q = 0; q < kMetaWaves; ++q) {
+        const int n = s_cnt[q * E + x];
+        s_cnt[q * E + x] = run;
+        run += n;
+      }
+      s_run[x] = run;
+    }
+    __syncthreads();
+    if (p < R) {
+      const int row = e >= 0 ? my_cnt[e] + rank : -1;
+      pair_to_row[p] = row;
+      if (row >= 0) row_to_pair[row] = p;
+    }
+    __syncthreads();
+  }
+}
+
 hipError_t launch_counts(const int* ids, int pairs, int E, int* chunk_hist, int* chunk_base,
                          int* counts, int* offsets, int extra_rows, hipStream_t s) {
   const int chunks = permute_chunks(pairs);
@@ -244,6 +377,14 @@ hipError_t launch_quant_scatter(const uint16_t* x, int T, int H, int k, const in
     default: MOE_QS(8); break;
   }
 #undef MOE_QS
+  return hipGetLastError();
+}
+
+hipError_t launch_meta(const float* logits, int T, int E, int k, int* ids, float* w, int* counts,
+                       int* offsets, int extra_rows, int* pair_to_row, int* row_to_pair, int* tile_prefix,
+                       int bm, hipStream_t s) {
+  meta_kernel<<<1, 1024, 0, s>>>(logits, T, E, k, ids, w, counts, offsets, extra_rows, pair_to_row,
+                                 row_to_pair, tile_prefix, bm);
   return hipGetLastError();
 }
 

@@ -66,6 +66,7 @@ PERMUTE_CASES = [  # T, H, E, k, hot expert
     (512, 3584, 896, 16, None),
     (2048, 8192, 8, 2, None),
     (1, 128, 1024, 32, None),
+    (5000, 128, 64, 4, None),     # 20000 pairs: the grid-wide counting / ranking kernels
 ]
 
 
@@ -135,6 +136,8 @@ FULL_CASES = {
     "mxfp4_k_equals_E": (20, 384, 256, 4, 4, "mxfp4", False, False),
     "dense_E1_k1": (70, 256, 128, 1, 1, "fp8", False, False),
     "one_token": (1, 128, 128, 16, 4, "fp8", True, False),
+    # 18000 pairs: routing and metadata by the grid-wide kernels
+    "many_tokens": (9000, 128, 128, 16, 2, "fp8", False, False),
 }
 
 
@@ -166,6 +169,26 @@ def test_forward_full(lib, case, pack):
     ratio = tolerance_ratio(bits(out), ref["out_exact"])
     say("  max|err|/rms", ratio)
     assert ratio <= OUT_TOL
+
+
+@pytest.mark.parametrize("E,k", [(8, 2), (32, 5), (33, 3)])
+def test_forward_route_ties(lib, E, k):
+    """Integer logits with many ties and signed zeros through moe_forward: at
+    most 32 experts are routed inside the metadata kernel, more by the router
+    kernel; both must break ties towards the lower expert id."""
+    T = 200
+    inp = moe_synth.custom_inputs(T, 128, 128, E, k, seed=E + k)
+    g = torch.Generator().manual_seed(E * k)
+    logits = torch.randint(-2, 3, (T, E), generator=g).float()
+    logits[::7] = 0.0
+    logits[1::7, ::2] = -0.0
+    inp["logits"] = logits
+    say("forward route ties", E, k)
+    out, dbg, _ = run_forward(to_device(inp))
+    c = inp["cfg"]
+    ref = oracle.forward(bf16_np(inp["x"]), logits.numpy(), k, oracle_weights(inp["routed"], "fp8"))
+    check_metadata(dbg, ref, T, k, E, False)
+    assert tolerance_ratio(bits(out), ref["out_exact"]) <= OUT_TOL
 
 
 def test_forward_zero_tokens(lib):
