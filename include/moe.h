@@ -131,8 +131,12 @@ enum {
  * non-NULL device pointer receives the named intermediate (and is used in
  * place of the corresponding workspace slice).  events[i], when non-NULL, is
  * a hipEvent_t recorded on `stream` just before stage i; events[MOE_N_STAGES]
- * after the last stage.  `variant` receives a NUL-terminated name of the
- * kernel variants chosen.
+ * after the last stage (each such record is one more packet on the stream,
+ * a few microseconds of command-processor time).  `variant` receives a
+ * NUL-terminated name of the kernel variants chosen.  gemm1_events[0] / [1],
+ * when non-NULL, are hipEvent_t stamped by the gate-up GEMM's own dispatch
+ * (hipExtLaunchKernel) at its start and end: its duration with no extra
+ * packets on the stream.
  */
 typedef struct {
   int32_t* topk_ids;       /* [T][k]   */
@@ -147,6 +151,7 @@ typedef struct {
   float* xs_rows;          /* [T*k]    */
   void* events[MOE_N_STAGES + 1];
   char variant[96];
+  void* gemm1_events[2];
 } moe_debug_t;
 
 /* ------------------------------------------------------------------------ */

@@ -44,6 +44,7 @@ class MoeDebug(ctypes.Structure):
         ("xq_rows", ctypes.c_void_p), ("xs_rows", ctypes.c_void_p),
         ("events", ctypes.c_void_p * (MOE_N_STAGES + 1)),
         ("variant", ctypes.c_char * 96),
+        ("gemm1_events", ctypes.c_void_p * 2),
     ]
 
 

@@ -46,6 +46,8 @@
 
 #include <type_traits>
 
+#include <hip/hip_ext.h>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -1046,7 +1048,7 @@ static GemmParams base_params(const FfnGroups& g, const RowOperand& x, const int
 }
 
 hipError_t launch_gemm1(int variant, const FfnGroups& g, const RowOperand& x, const int* tile_prefix,
-                        long n_rows, uint16_t* h, hipStream_t s) {
+                        long n_rows, uint16_t* h, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop) {
   GemmParams p = base_params(g, x, tile_prefix);
   p.K = g.hidden;
   p.N = g.inter;
@@ -1063,13 +1065,17 @@ hipError_t launch_gemm1(int variant, const FfnGroups& g, const RowOperand& x, co
   if (variant == kVariantSmall) {
     p.ntiles = g.inter / (kSmCh / 2);
     const long grid = max_row_tiles(n_rows, g.n_groups, bm) * p.ntiles;
-    if (g.fmt == kMxfp4) gemm1_small_kernel<kMxfp4><<<(unsigned)grid, 256, 0, s>>>(p);
-    else gemm1_small_kernel<kFp8><<<(unsigned)grid, 256, 0, s>>>(p);
+    if (g.fmt == kMxfp4)
+      hipExtLaunchKernelGGL(gemm1_small_kernel<kMxfp4>, dim3((unsigned)grid), dim3(256), 0, s, ev_start, ev_stop, 0, p);
+    else
+      hipExtLaunchKernelGGL(gemm1_small_kernel<kFp8>, dim3((unsigned)grid), dim3(256), 0, s, ev_start, ev_stop, 0, p);
   } else {
     p.ntiles = g.inter / (kLgCh / 2);
     const long grid = max_row_tiles(n_rows, g.n_groups, bm) * p.ntiles;
-    if (variant == kVariantLarge256) gemm1_pp_kernel<256, 4><<<(unsigned)grid, 256, 0, s>>>(p);
-    else gemm1_pp_kernel<128, 6><<<(unsigned)grid, 256, 0, s>>>(p);
+    if (variant == kVariantLarge256)
+      hipExtLaunchKernelGGL(gemm1_pp_kernel<256, 4>, dim3((unsigned)grid), dim3(256), 0, s, ev_start, ev_stop, 0, p);
+    else
+      hipExtLaunchKernelGGL(gemm1_pp_kernel<128, 6>, dim3((unsigned)grid), dim3(256), 0, s, ev_start, ev_stop, 0, p);
   }
   return hipGetLastError();
 }

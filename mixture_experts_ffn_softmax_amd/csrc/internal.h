@@ -115,8 +115,10 @@ long max_row_tiles(long n_rows, int n_groups, int bm);
 hipError_t launch_tile_prefix(const int* offsets, int n_groups, int bm, int* tile_prefix, hipStream_t s);
 // GEMM1: h[r][n] = bf16(SiLU(g) * u) for the gate/up pair of channel n.  h is
 // K-blocked for GEMM2: kHChunk-byte chunks (32 channels) over n_rows rows.
+// ev_start / ev_stop (may be NULL): stamped by the GEMM1 dispatch itself.
 hipError_t launch_gemm1(int variant, const FfnGroups& g, const RowOperand& x, const int* tile_prefix,
-                        long n_rows, uint16_t* h, hipStream_t s);
+                        long n_rows, uint16_t* h, hipStream_t s, hipEvent_t ev_start = nullptr,
+                        hipEvent_t ev_stop = nullptr);
 // GEMM2: y[r][j] = (h_r . W2[j]) * s2[j] in fp32; h as GEMM1 writes it.
 hipError_t launch_gemm2(int variant, const FfnGroups& g, const uint16_t* h, const int* tile_prefix,
                         long n_rows, float* y, hipStream_t s);

@@ -9,6 +9,8 @@ import re
 
 import pytest
 
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
 from mixture_experts_ffn_softmax_amd import _lib
 from mixture_experts_ffn_softmax_amd._lib import (MOE_ERR_ALIGN, MOE_ERR_NULL, MOE_ERR_SHAPE,
                                                   MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_OK,
@@ -49,11 +51,27 @@ def test_version_and_status_strings(lib):
     assert lib.moe_status_string(99) == b"unknown status"
 
 
-def test_struct_layouts():
-    # moe_weights_t: 6 int32 then 6 pointers; moe_debug_t: 8 pointers, 6 events, 96 chars
-    assert ctypes.sizeof(MoeWeights) == 24 + 6 * 8
-    assert MoeWeights.w1.offset == 24
-    assert ctypes.sizeof(MoeDebug) == 8 * 8 + 6 * 8 + 96
+def test_struct_layouts(tmp_path):
+    """The ctypes mirrors match the C header: sizes and field offsets as a C
+    compiler lays the structs out (gcc on the header itself)."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no C compiler")
+    src = tmp_path / "layout.c"
+    src.write_text(
+        '#include <stddef.h>\n#include <stdio.h>\n#include "moe.h"\n'
+        'int main(void) { printf("%zu %zu %zu %zu %zu %zu %zu\\n", sizeof(moe_weights_t),'
+        ' offsetof(moe_weights_t, w1), offsetof(moe_weights_t, s2), sizeof(moe_debug_t),'
+        ' offsetof(moe_debug_t, events), offsetof(moe_debug_t, variant),'
+        ' offsetof(moe_debug_t, gemm1_events)); return 0; }\n')
+    exe = tmp_path / "layout"
+    subprocess.run([gcc, "-std=c99", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    got = [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
+    assert got == [ctypes.sizeof(MoeWeights), MoeWeights.w1.offset, MoeWeights.s2.offset,
+                   ctypes.sizeof(MoeDebug), MoeDebug.events.offset, MoeDebug.variant.offset,
+                   MoeDebug.gemm1_events.offset]
 
 
 def fp8_weights(E=8, H=256, I=128, fmt=0, layout=0, **over):
