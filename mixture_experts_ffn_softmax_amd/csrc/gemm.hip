@@ -716,22 +716,50 @@ __global__ __launch_bounds__(256, 1) void gemm2_pp_kernel(GemmParams p) {
 // ============================================================================
 // small variants (decode-sized groups; fp8 or MXFP4 weights)
 // ============================================================================
+//
+// The weight stream is the bound: every weight byte of a touched expert is
+// read once per row tile, and a decode-sized group fits in one row tile.  The
+// 4 waves of a workgroup take the K steps round-robin and reduce through LDS
+// at the end.  GEMM1 keeps the loads of a wave's next K step in flight (a
+// second register set) while the MFMAs of the current one run; GEMM2 (short
+// K) spends the registers on a wider channel tile instead.  A tile with at
+// most 16 valid rows skips its second token fragment (loads and MFMAs).
 
 constexpr int kSmRows = 32;   // token rows per tile: 2 fragments of 16
-constexpr int kSmCh = 64;     // channel rows per tile: 4 fragments (GEMM1: 2 gate + 2 up)
+constexpr int kSmCh = 64;     // GEMM1 channel rows per tile: 4 fragments (2 gate + 2 up)
+constexpr int kSmCh2 = 128;   // GEMM2 output channels per tile: 8 fragments
+
+// Steps ks = wave, wave + 4, ... < nk of this wave through D register sets:
+// load(ks, set) fills a set, compute(set) consumes it; the loads of the next
+// D - 1 steps are in flight while a step computes.
+template <int D, class St, class Load, class Compute>
+__device__ __forceinline__ void small_pipeline(int wave, int nk, Load&& load, Compute&& compute) {
+  const int n = nk > wave ? (nk - wave + 3) >> 2 : 0;
+  St st[D];
+  static_for<D>([&](auto jc) {
+    constexpr int j = decltype(jc)::value;
+    if (j < n) load(wave + 4 * j, st[j]);
+  });
+  for (int i = 0; i < n; i += D) {
+    static_for<D>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      if (i + j < n) {
+        compute(st[j]);
+        if (i + j + D < n) load(wave + 4 * (i + j + D), st[j]);
+      }
+    });
+  }
+}
 
 // GEMM1: 16x16x128 MFMA on e4m3 x e4m3, or e2m1 x e4m3 with block scales.
-template <int FMT>
-__global__ __launch_bounds__(256) void gemm1_small_kernel(GemmParams p) {
-  __shared__ v4f red[4][8][64];                 // per-wave partial sums
-  __shared__ int s_tp[kMaxExperts + 2];
-  MOE_TILE_PROLOGUE(kSmRows);
-
+template <bool FP4, int TV>
+__device__ __forceinline__ void gemm1_small_body(const GemmParams& p, const TileInfo& ti, v4f (*red)[8][64]) {
+  constexpr int kSmallDepth1 = 2;
   const int K = p.K;
   const int nk = K >> 7;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l16 = lane & 15, lg = lane >> 4;
-  const bool fp4 = (FMT == kMxfp4) && ti.wi == 0;   // the shared group is fp8
+  constexpr bool fp4 = FP4;
   const long rowBytes = fp4 ? (K >> 1) : K;
   const int n0 = ti.nt * (kSmCh / 2);
   const uint8_t* Wa = p.wa[ti.wi] + ti.eg * (long)p.N * rowBytes;
@@ -747,7 +775,7 @@ __global__ __launch_bounds__(256) void gemm1_small_kernel(GemmParams p) {
   const int tok_off0 = fp4 ? lg * 16 : lg * 32;
   const int tok_off1 = fp4 ? 64 + lg * 16 : lg * 32 + 16;
   // 16-byte pieces never straddle a K chunk of either layout, so each piece
-  // is addressed through its operand's layout (op_off)
+  // is addressed through its operand's layout
   const Operand& td = p.ta[ti.wi];
   const Operand& wd = p.wd[ti.wi];
   const uint8_t* tp[2];
@@ -775,52 +803,59 @@ __global__ __launch_bounds__(256) void gemm1_small_kernel(GemmParams p) {
     return *reinterpret_cast<const uint4*>(wp[f] + ((k >> wd.kc_shift) * wd.chunk_stride + (k & ((1L << wd.kc_shift) - 1))));
   };
 
-  v4f acc[4][2];
+  v4f acc[4][TV];
 #pragma unroll
   for (int f = 0; f < 4; ++f)
 #pragma unroll
-    for (int t = 0; t < 2; ++t) acc[f][t] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < TV; ++t) acc[f][t] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  for (int ks = wave; ks < nk; ks += 4) {
-    v8i x[2];
+  struct St {
+    v8i x[TV];
+    v8i w[4];
+    int sc[4];
+  };
+  auto load = [&](int ks, St& st) {
+    const long kb = (long)ks << 7;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) x[t] = as_v8i(tok(t, ((long)ks << 7) + tok_off0), tok(t, ((long)ks << 7) + tok_off1));
-    if (fp4) {
-      v8i w[4];
-      int sc[4];
+    for (int t = 0; t < TV; ++t) st.x[t] = as_v8i(tok(t, kb + tok_off0), tok(t, kb + tok_off1));
+    if constexpr (fp4) {
 #pragma unroll
       for (int f = 0; f < 4; ++f) {
         const uint4 b0 = *reinterpret_cast<const uint4*>(wp[f] + ((long)ks << 6));
-        w[f] = v8i{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, 0, 0, 0, 0};
-        const uint32_t s4 = *reinterpret_cast<const uint32_t*>(sp[f] + ks * 4);
-        sc[f] = (int)((s4 >> (8 * lg)) & 0xFFu);
+        st.w[f] = v8i{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, 0, 0, 0, 0};
+        st.sc[f] = (int)*reinterpret_cast<const uint32_t*>(sp[f] + ks * 4);
       }
-#pragma unroll
-      for (int f = 0; f < 4; ++f)
-#pragma unroll
-        for (int t = 0; t < 2; ++t) acc[f][t] = mfma16_fp4w(w[f], x[t], acc[f][t], sc[f]);
     } else {
-      v8i w[4];
+#pragma unroll
+      for (int f = 0; f < 4; ++f) st.w[f] = as_v8i(wgt(f, kb + lg * 32), wgt(f, kb + lg * 32 + 16));
+    }
+  };
+  auto compute = [&](const St& st) {
+    if constexpr (fp4) {
 #pragma unroll
       for (int f = 0; f < 4; ++f) {
-        const long k = ((long)ks << 7) + lg * 32;
-        w[f] = as_v8i(wgt(f, k), wgt(f, k + 16));
+        const int sc = (st.sc[f] >> (8 * lg)) & 0xFF;
+#pragma unroll
+        for (int t = 0; t < TV; ++t) acc[f][t] = mfma16_fp4w(st.w[f], st.x[t], acc[f][t], sc);
       }
+    } else {
 #pragma unroll
       for (int f = 0; f < 4; ++f)
 #pragma unroll
-        for (int t = 0; t < 2; ++t) acc[f][t] = mfma16_fp8(w[f], x[t], acc[f][t]);
+        for (int t = 0; t < TV; ++t) acc[f][t] = mfma16_fp8(st.w[f], st.x[t], acc[f][t]);
     }
-  }
+  };
+  small_pipeline<kSmallDepth1, St>(wave, nk, load, compute);
 
 #pragma unroll
   for (int f = 0; f < 4; ++f)
 #pragma unroll
-    for (int t = 0; t < 2; ++t) red[wave][f * 2 + t][lane] = acc[f][t];
+    for (int t = 0; t < TV; ++t) red[wave][f * 2 + t][lane] = acc[f][t];
   __syncthreads();
 
   // wave w: gate fragment f = w >> 1 (up fragment f + 2), token fragment t = w & 1
   const int f = wave >> 1, t = wave & 1;
+  if (t >= TV) return;
   v4f gsum = red[0][f * 2 + t][lane], usum = red[0][(f + 2) * 2 + t][lane];
 #pragma unroll
   for (int q = 1; q < 4; ++q) {
@@ -848,22 +883,39 @@ __global__ __launch_bounds__(256) void gemm1_small_kernel(GemmParams p) {
   *reinterpret_cast<uint2*>(p.h + h_off(p.h_cs, grow, ch)) = make_uint2(b[0] | (b[1] << 16), b[2] | (b[3] << 16));
 }
 
+template <int FMT>
+__global__ __launch_bounds__(256) void gemm1_small_kernel(GemmParams p) {
+  __shared__ v4f red[4][8][64];                 // per-wave partial sums
+  __shared__ int s_tp[kMaxExperts + 2];
+  MOE_TILE_PROLOGUE(kSmRows);
+  // MXFP4 routed weights; the shared group is always fp8
+  const bool two = ti.row1 - ti.row0 > 16;
+  if (FMT == kMxfp4 && ti.wi == 0) {
+    if (two) gemm1_small_body<true, 2>(p, ti, red);
+    else gemm1_small_body<true, 1>(p, ti, red);
+  } else {
+    if (two) gemm1_small_body<false, 2>(p, ti, red);
+    else gemm1_small_body<false, 1>(p, ti, red);
+  }
+}
+
 // GEMM2: 16x16x32 bf16 MFMA; W2 codes converted to bf16 in registers.  Lane
 // group lg takes elements [32*lg, 32*lg + 32) of the 128-wide K step on both
 // operands; sub-step i of the 4 instructions uses elements [8i, 8i + 8).
-template <int FMT>
-__global__ __launch_bounds__(256) void gemm2_small_kernel(GemmParams p) {
-  __shared__ v4f red[4][8][64];
-  __shared__ int s_tp[kMaxExperts + 2];
-  MOE_TILE_PROLOGUE(kSmRows);
-
+// A tile is kSmCh2 = 128 output channels (8 fragments): with K = I the
+// shortest contraction of the layer, wider tiles keep the launch to about
+// one workgroup per two SIMD pairs.
+template <bool FP4, int TV>
+__device__ __forceinline__ void gemm2_small_body(const GemmParams& p, const TileInfo& ti, v4f (*red)[2 * kSmCh2 / 16][64]) {
+  constexpr int kSmallDepth2 = 1;             // registers go to the 8 fragments instead
+  constexpr int NF = kSmCh2 / 16;             // channel fragments
   const int K = p.K;                          // = I
   const int nk = K >> 7;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l16 = lane & 15, lg = lane >> 4;
-  const bool fp4 = (FMT == kMxfp4) && ti.wi == 0;
+  constexpr bool fp4 = FP4;
   const long rowBytes = fp4 ? (K >> 1) : K;
-  const int n0 = ti.nt * kSmCh;
+  const int n0 = ti.nt * kSmCh2;
   const uint8_t* W2 = p.wa[ti.wi] + ti.eg * (long)p.N * rowBytes;
 
   const Operand& td = p.ta[ti.wi];
@@ -875,10 +927,10 @@ __global__ __launch_bounds__(256) void gemm2_small_kernel(GemmParams p) {
     if (r >= ti.row1) r = ti.row1 - 1;
     tp[t] = row_ptr(p, ti, r);
   }
-  const uint8_t* wp[4];
-  const uint8_t* sp[4];
+  const uint8_t* wp[NF];
+  const uint8_t* sp[NF];
 #pragma unroll
-  for (int f = 0; f < 4; ++f) {
+  for (int f = 0; f < NF; ++f) {
     const long crow = n0 + f * 16 + l16;
     wp[f] = fp4 ? W2 + crow * rowBytes + lg * 16 : W2 + crow * wd.row_pitch;
     sp[f] = fp4 ? (reinterpret_cast<const uint8_t*>(p.sa[0]) + (ti.eg * (long)p.N + crow) * (K >> 5)) : nullptr;
@@ -890,66 +942,97 @@ __global__ __launch_bounds__(256) void gemm2_small_kernel(GemmParams p) {
     return *reinterpret_cast<const uint4*>(wp[f] + ((k >> wd.kc_shift) * wd.chunk_stride + (k & ((1L << wd.kc_shift) - 1))));
   };
 
-  v4f acc[4][2];
+  v4f acc[NF][TV];
 #pragma unroll
-  for (int f = 0; f < 4; ++f)
+  for (int f = 0; f < NF; ++f)
 #pragma unroll
-    for (int t = 0; t < 2; ++t) acc[f][t] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < TV; ++t) acc[f][t] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  for (int ks = wave; ks < nk; ks += 4) {
-    v8bf x[2][4];
+  struct St {
+    uint4 x[TV][4];
+    uint4 w[NF][2];
+    uint32_t sc[NF];
+  };
+  auto load = [&](int ks, St& st) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < TV; ++t)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) x[t][i] = as_v8bf(hpiece(t, ((long)ks << 8) + lg * 64 + 16 * i));
-    v8bf w[4][4];
+      for (int i = 0; i < 4; ++i) st.x[t][i] = hpiece(t, ((long)ks << 8) + lg * 64 + 16 * i);
 #pragma unroll
-    for (int f = 0; f < 4; ++f) {
-      if (fp4) {
-        const uint4 b0 = *reinterpret_cast<const uint4*>(wp[f] + ((long)ks << 6));
-        const uint32_t cw[4] = {b0.x, b0.y, b0.z, b0.w};
-        const uint32_t s = sp[f][ks * 4 + lg];
-        fp4x32_to_bf16(cw, e8m0_to_f32(s), w[f]);
+    for (int f = 0; f < NF; ++f) {
+      if constexpr (fp4) {
+        st.w[f][0] = *reinterpret_cast<const uint4*>(wp[f] + ((long)ks << 6));
+        st.sc[f] = sp[f][ks * 4 + lg];
       } else {
         const long k = ((long)ks << 7) + lg * 32;
-        const uint4 b0 = wgt(f, k);
-        const uint4 b1 = wgt(f, k + 16);
-        const uint32_t cw[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-        fp8x32_to_bf16(cw, w[f]);
+        st.w[f][0] = wgt(f, k);
+        st.w[f][1] = wgt(f, k + 16);
       }
     }
+  };
+  auto compute = [&](const St& st) {
 #pragma unroll
-    for (int f = 0; f < 4; ++f)
+    for (int f = 0; f < NF; ++f) {
+      v8bf w[4];
+      if constexpr (fp4) {
+        const uint32_t cw[4] = {st.w[f][0].x, st.w[f][0].y, st.w[f][0].z, st.w[f][0].w};
+        fp4x32_to_bf16(cw, e8m0_to_f32(st.sc[f]), w);
+      } else {
+        const uint32_t cw[8] = {st.w[f][0].x, st.w[f][0].y, st.w[f][0].z, st.w[f][0].w,
+                                st.w[f][1].x, st.w[f][1].y, st.w[f][1].z, st.w[f][1].w};
+        fp8x32_to_bf16(cw, w);
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
-          acc[f][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w[f][i], x[t][i], acc[f][t], 0, 0, 0);
-  }
+        for (int t = 0; t < TV; ++t)
+          acc[f][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w[i], as_v8bf(st.x[t][i]), acc[f][t], 0, 0, 0);
+    }
+  };
+  small_pipeline<kSmallDepth2, St>(wave, nk, load, compute);
 
 #pragma unroll
-  for (int f = 0; f < 4; ++f)
+  for (int f = 0; f < NF; ++f)
 #pragma unroll
-    for (int t = 0; t < 2; ++t) red[wave][f * 2 + t][lane] = acc[f][t];
+    for (int t = 0; t < TV; ++t) red[wave][f * 2 + t][lane] = acc[f][t];
   __syncthreads();
 
-  // wave w: channel fragment f = w, both token fragments
-  const int f = wave;
-  const int ch = n0 + f * 16 + 4 * lg;
-  float s2v[4] = {1.f, 1.f, 1.f, 1.f};
-  if (!fp4) {
-    const float4 s2 = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(p.sa[ti.wi]) + ti.eg * p.N + ch);
-    s2v[0] = s2.x; s2v[1] = s2.y; s2v[2] = s2.z; s2v[3] = s2.w;
+  // wave w: channel fragments 2w and 2w + 1, every valid token fragment
+#pragma unroll
+  for (int ff = 0; ff < NF / 4; ++ff) {
+    const int f = wave * (NF / 4) + ff;
+    const int ch = n0 + f * 16 + 4 * lg;
+    float s2v[4] = {1.f, 1.f, 1.f, 1.f};
+    if (!fp4) {
+      const float4 s2 = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(p.sa[ti.wi]) + ti.eg * p.N + ch);
+      s2v[0] = s2.x; s2v[1] = s2.y; s2v[2] = s2.z; s2v[3] = s2.w;
+    }
+#pragma unroll
+    for (int t = 0; t < TV; ++t) {
+      v4f s = red[0][f * 2 + t][lane];
+#pragma unroll
+      for (int q = 1; q < 4; ++q) s += red[q][f * 2 + t][lane];
+      const int grow = ti.row0 + t * 16 + l16;
+      if (grow < ti.row1)
+        *reinterpret_cast<float4*>(p.y + (long)grow * p.N + ch) =
+            make_float4(s[0] * s2v[0], s[1] * s2v[1], s[2] * s2v[2], s[3] * s2v[3]);
+    }
   }
-#pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    v4f s = red[0][f * 2 + t][lane];
-#pragma unroll
-    for (int q = 1; q < 4; ++q) s += red[q][f * 2 + t][lane];
-    const int grow = ti.row0 + t * 16 + l16;
-    if (grow < ti.row1)
-      *reinterpret_cast<float4*>(p.y + (long)grow * p.N + ch) =
-          make_float4(s[0] * s2v[0], s[1] * s2v[1], s[2] * s2v[2], s[3] * s2v[3]);
+}
+
+template <int FMT>
+__global__ __launch_bounds__(256) void gemm2_small_kernel(GemmParams p) {
+  __shared__ v4f red[4][2 * kSmCh2 / 16][64];
+  __shared__ int s_tp[kMaxExperts + 2];
+  MOE_TILE_PROLOGUE(kSmRows);
+  // MXFP4 routed weights; the shared group is always fp8
+  const bool two = ti.row1 - ti.row0 > 16;
+  if (FMT == kMxfp4 && ti.wi == 0) {
+    if (two) gemm2_small_body<true, 2>(p, ti, red);
+    else gemm2_small_body<true, 1>(p, ti, red);
+  } else {
+    if (two) gemm2_small_body<false, 2>(p, ti, red);
+    else gemm2_small_body<false, 1>(p, ti, red);
   }
 }
 
@@ -1096,7 +1179,7 @@ hipError_t launch_gemm2(int variant, const FfnGroups& g, const uint16_t* h, cons
   p.y = y;
   const int bm = variant_rows(variant);
   if (variant == kVariantSmall) {
-    p.ntiles = g.hidden / kSmCh;
+    p.ntiles = g.hidden / kSmCh2;
     const long grid = max_row_tiles(n_rows, g.n_groups, bm) * p.ntiles;
     if (g.fmt == kMxfp4) gemm2_small_kernel<kMxfp4><<<(unsigned)grid, 256, 0, s>>>(p);
     else gemm2_small_kernel<kFp8><<<(unsigned)grid, 256, 0, s>>>(p);
