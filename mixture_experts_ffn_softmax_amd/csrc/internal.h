@@ -12,8 +12,9 @@ namespace moe {
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 32;
 constexpr int kPermuteChunk = 1024;  // pairs per counting / ranking chunk
-constexpr int kMetaMaxPairs = 2048;  // pairs handled by the single-workgroup metadata kernel
-constexpr int kMetaRouteMaxE = 32;   // experts it can also route (one lane per token)
+constexpr int kMetaMaxPairs = 16384; // pairs handled by the single-workgroup metadata kernel
+constexpr int kMetaRouteMaxE = 32;   // experts it can also route (one lane per token) ...
+constexpr int kMetaRouteMaxT = 256;  // ... for batches of at most this many tokens
 
 // Byte addressing of a matrix operand with rows of K contraction bytes: byte k
 // of row r sits at r * row_pitch + (k >> kc_shift) * chunk_stride +

@@ -407,10 +407,12 @@ moe_status_t moe_forward(const uint16_t* x, const float* logits, int32_t T, int3
   const moe::FfnGroups g = make_groups(routed, sh ? shared : nullptr, L.offsets);
   const long rows = R + (sh ? T : 0);
   // Up to kMetaMaxPairs pairs, one workgroup computes the whole routing
-  // metadata (and routes, for at most kMetaRouteMaxE experts); beyond that,
-  // route / counts / ranks run as grid-wide kernels.
+  // metadata (and routes, for at most kMetaRouteMaxE experts and
+  // kMetaRouteMaxT tokens: beyond that one CU's routing takes longer than a
+  // grid-wide router launch); beyond kMetaMaxPairs, route / counts / ranks
+  // run as grid-wide kernels.
   const bool meta = R <= moe::kMetaMaxPairs;
-  const bool fused_route = meta && E <= moe::kMetaRouteMaxE;
+  const bool fused_route = meta && E <= moe::kMetaRouteMaxE && T <= moe::kMetaRouteMaxT;
   if (ev && ev[MOE_STAGE_ROUTE]) hipEventRecord((hipEvent_t)ev[MOE_STAGE_ROUTE], s);
   if (!fused_route) {
     e = moe::launch_route(logits, T, E, top_k, L.ids, L.w, s);

@@ -160,9 +160,13 @@ __global__ __launch_bounds__(1024) void quant_scatter_kernel(
     uint8_t* __restrict__ xq_rows, float* __restrict__ xs_rows, uint8_t* __restrict__ xq_tok,
     float* __restrict__ xs_tok, long rows_cs, long tok_cs, uint8_t* __restrict__ xq_copy) {
   __shared__ float red[16];
+  __shared__ int s_rows[kMaxTopK];
   const long t = blockIdx.x;
   const int nchk = H >> 3;
   const uint4* src = reinterpret_cast<const uint4*>(x + t * H);
+  // the token's rows, fetched first so that their latency overlaps the row's
+  // (block_max's barrier publishes them)
+  if (threadIdx.x < k) s_rows[threadIdx.x] = pair_to_row[t * k + threadIdx.x];
   uint4 in[CPT];
   float amax = 0.0f;
 #pragma unroll
@@ -190,7 +194,7 @@ __global__ __launch_bounds__(1024) void quant_scatter_kernel(
     q8[c] = make_uint2(packed[0], packed[1]);
   }
   for (int j = 0; j < k; ++j) {
-    const int r = pair_to_row[t * k + j];
+    const int r = s_rows[j];
     if (r < 0) continue;
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
@@ -223,6 +227,93 @@ __global__ __launch_bounds__(1024) void quant_scatter_kernel(
 //      64 pairs by ballots, a per-expert scan over the 16 waves turns the
 //      wave counts into starting rows.
 constexpr int kMetaWaves = 16;
+constexpr int kMetaChunk = kMetaWaves * 256;   // pairs per rank chunk: 4 per lane
+
+// Routing inside the metadata kernel, one lane per token, for E <= NE experts:
+// the same selection (largest logit first, ties to the lower id) and weight
+// arithmetic as route_kernel.
+template <int NE>
+__device__ __forceinline__ void meta_route(const float* __restrict__ logits, int T, int E, int k,
+                                           int* __restrict__ ids, float* __restrict__ w, int* s_ids) {
+  for (int t = threadIdx.x; t < T; t += blockDim.x) {
+    float v[NE];
+    const float* row = logits + (long)t * E;
+#pragma unroll
+    for (int i = 0; i < NE; ++i) v[i] = (i < E) ? row[i] : 0.0f;
+    uint32_t avail = (E >= 32) ? 0xFFFFFFFFu : ((1u << E) - 1u);
+    float vmax = 0.0f, sum = 0.0f;
+    float ex[kMaxTopK];
+    for (int j = 0; j < k; ++j) {
+      float bv = -INFINITY;
+      int bi = 0x7FFFFFFF;
+#pragma unroll
+      for (int i = 0; i < NE; ++i)
+        if (((avail >> i) & 1u) && (v[i] > bv || (v[i] == bv && i < bi))) {
+          bv = v[i];
+          bi = i;
+        }
+      avail &= ~(1u << bi);
+      if (j == 0) vmax = bv;
+      ex[j] = expf(bv - vmax);
+      sum += ex[j];
+      ids[(long)t * k + j] = bi;
+      s_ids[t * k + j] = bi;
+    }
+    for (int j = 0; j < k; ++j) w[(long)t * k + j] = ex[j] / sum;
+  }
+}
+
+// Expert ids of pairs p0 .. p0+3 from LDS; -1 past the end or out of range.
+__device__ __forceinline__ void load_chunk_ids(const int* s_ids, int R, int E, int p0, int (&e)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    int x = (p0 + i < R) ? s_ids[p0 + i] : -1;
+    e[i] = ((unsigned)x < (unsigned)E) ? x : -1;
+  }
+}
+
+// Visits each expert present among the wave's 256 pairs (lane l holds pairs
+// 4l .. 4l+3 in order) once: fn(expert, pairs of that expert in the wave,
+// rank[4]) where rank[i] counts the wave's earlier pairs of that expert
+// (valid where e[i] is that expert).
+template <class Fn>
+__device__ __forceinline__ void wave_match4(const int (&e)[4], uint64_t lt_mask, Fn&& fn) {
+  const int lane = threadIdx.x & 63;
+  bool pend[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) pend[i] = e[i] >= 0;
+  while (true) {
+    int mine = -1;
+#pragma unroll
+    for (int i = 3; i >= 0; --i)
+      if (pend[i]) mine = e[i];
+    const uint64_t any = __ballot(mine >= 0);
+    if (!any) break;
+    const int leader = __ffsll((unsigned long long)any) - 1;
+    const int el = __builtin_amdgcn_readlane(mine, leader);
+    uint64_t m[4];
+    int n = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      m[i] = __ballot(e[i] == el);
+      n += __popcll(m[i]);
+    }
+    int before = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) before += __popcll(m[i] & lt_mask);
+    int r[4];
+    int own = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      r[i] = before + own;
+      if (e[i] == el) {
+        ++own;
+        pend[i] = false;
+      }
+    }
+    fn(el, n, r);
+  }
+}
 
 __global__ __launch_bounds__(1024) void meta_kernel(const float* __restrict__ logits, int T, int E, int k,
                                                     int* __restrict__ ids, float* __restrict__ w,
@@ -239,43 +330,25 @@ __global__ __launch_bounds__(1024) void meta_kernel(const float* __restrict__ lo
   const int lane = tid & 63, wv = tid >> 6;
   const int R = T * k;
 
-  for (int e = tid; e < E; e += 1024) s_tot[e] = 0;
+  for (int x = tid; x < E; x += 1024) s_tot[x] = 0;
   if (logits) {
-    for (int t = tid; t < T; t += 1024) {
-      float v[kMetaRouteMaxE];
-      const float* row = logits + (long)t * E;
-#pragma unroll
-      for (int i = 0; i < kMetaRouteMaxE; ++i) v[i] = (i < E) ? row[i] : 0.0f;
-      uint32_t avail = (E >= 32) ? 0xFFFFFFFFu : ((1u << E) - 1u);
-      float vmax = 0.0f, sum = 0.0f;
-      float ex[kMaxTopK];
-      for (int j = 0; j < k; ++j) {
-        float bv = -INFINITY;
-        int bi = 0x7FFFFFFF;
-#pragma unroll
-        for (int i = 0; i < kMetaRouteMaxE; ++i)
-          if (((avail >> i) & 1u) && (v[i] > bv || (v[i] == bv && i < bi))) {
-            bv = v[i];
-            bi = i;
-          }
-        avail &= ~(1u << bi);
-        if (j == 0) vmax = bv;
-        ex[j] = expf(bv - vmax);
-        sum += ex[j];
-        ids[(long)t * k + j] = bi;
-        s_ids[t * k + j] = bi;
-      }
-      for (int j = 0; j < k; ++j) w[(long)t * k + j] = ex[j] / sum;
-    }
+    if (E <= 8) meta_route<8>(logits, T, E, k, ids, w, s_ids);
+    else if (E <= 16) meta_route<16>(logits, T, E, k, ids, w, s_ids);
+    else meta_route<kMetaRouteMaxE>(logits, T, E, k, ids, w, s_ids);
   } else {
     for (int p = tid; p < R; p += 1024) s_ids[p] = ids[p];
   }
   __syncthreads();
 
-  // ---- counts, offsets, tile prefix
-  for (int p = tid; p < R; p += 1024) {
-    const int e = s_ids[p];
-    if ((unsigned)e < (unsigned)E) atomicAdd(&s_tot[e], 1);
+  // ---- counts, offsets, tile prefix.  Counts come from the same wave-level
+  // matching as the ranks (one LDS add per wave and expert present).
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int c0 = 0; c0 < R; c0 += kMetaChunk) {
+    int e[4];
+    load_chunk_ids(s_ids, R, E, c0 + wv * 256 + 4 * lane, e);
+    wave_match4(e, lt_mask, [&](int el, int n, const int*) {
+      if (lane == 0) atomicAdd(&s_tot[el], n);
+    });
   }
   __syncthreads();
   const int cnt_e = (tid < E) ? s_tot[tid] : 0;
@@ -301,40 +374,49 @@ __global__ __launch_bounds__(1024) void meta_kernel(const float* __restrict__ lo
   }
   __syncthreads();
 
-  // ---- ranks
+  // ---- ranks, chunk by chunk of kMetaChunk pairs in pair order.  Lane l of
+  // wave w owns pairs c0 + 256 w + 4 l + i (i < 4); inside the wave a pair's
+  // rank among its expert's pairs comes from ballots, the per-expert wave
+  // counts become starting rows by a scan over the 16 waves (16 lanes per
+  // expert, shuffles), carried across chunks in s_run.
   int* my_cnt = s_cnt + wv * E;
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int c0 = 0; c0 < R; c0 += 1024) {
-    for (int e = lane; e < E; e += 64) my_cnt[e] = 0;
-    const int p = c0 + tid;
-    int e = (p < R) ? s_ids[p] : -1;
-    if ((unsigned)e >= (unsigned)E) e = -1;
-    uint64_t pending = __ballot(e >= 0);
-    int rank = 0;
-    while (pending) {
-      const int leader = __ffsll((unsigned long long)pending) - 1;
-      const int el = __builtin_amdgcn_readlane(e, leader);
-      const uint64_t same = __ballot(e == el) & pending;
-      if (e == el) rank = __popcll(same & lt_mask);
-      if (lane == leader) my_cnt[el] = __popcll(same);
-      pending &= ~same;
-    }
-    __syncthreads();
-    for (int x = tid; x < E; x += 1024) {
-      int run = s_run[x];
+  for (int c0 = 0; c0 < R; c0 += kMetaChunk) {
+    for (int x = lane; x < E; x += 64) my_cnt[x] = 0;
+    const int p0 = c0 + wv * 256 + 4 * lane;
+    int e[4], rank[4] = {0, 0, 0, 0};
+    load_chunk_ids(s_ids, R, E, p0, e);
+    wave_match4(e, lt_mask, [&](int el, int n, const int* r) {
 #pragma unroll
-      for (int q = 0; q < kMetaWaves; ++q) {
-        const int n = s_cnt[q * E + x];
-        s_cnt[q * E + x] = run;
-        run += n;
+      for (int i = 0; i < 4; ++i)
+        if (e[i] == el) rank[i] = r[i];
+      if (lane == 0) my_cnt[el] = n;
+    });
+    __syncthreads();
+    for (int base = 0; base < E * kMetaWaves; base += 1024) {
+      const int idx = base + tid;
+      const int x = idx >> 4, q = idx & 15;    // expert, wave
+      const int v = (x < E) ? s_cnt[q * E + x] : 0;
+      int inc = v;
+#pragma unroll
+      for (int d = 1; d < 16; d <<= 1) {
+        const int o = __shfl_up(inc, d, 16);
+        if (q >= d) inc += o;
       }
-      s_run[x] = run;
+      if (x < E) {
+        const int run = s_run[x];
+        s_cnt[q * E + x] = run + inc - v;
+        if (q == 15) s_run[x] = run + inc;
+      }
     }
     __syncthreads();
-    if (p < R) {
-      const int row = e >= 0 ? my_cnt[e] + rank : -1;
-      pair_to_row[p] = row;
-      if (row >= 0) row_to_pair[row] = p;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int p = p0 + i;
+      if (p < R) {
+        const int row = e[i] >= 0 ? my_cnt[e[i]] + rank[i] : -1;
+        pair_to_row[p] = row;
+        if (row >= 0) row_to_pair[row] = p;
+      }
     }
     __syncthreads();
   }
