@@ -9,14 +9,15 @@ GEMM, combine) on resident device inputs.  Weight sets are rotated across steps
 
 Prints ONE JSON line: metric / value (fp8 TFLOP/s of the whole layer,
 6*H*I flops per routed row and per shared-expert token), the roofline of the
-dominant kernel (gate-up GEMM, measured with HIP events on the library's
-stream), the decode-share weight-stream rate, and the CPU oracle timed on a
-bounded sample (reported baseline only).
+dominant kernel (the down GEMM, the layer's longest; the gate-up GEMM's
+beside it), each timed by events its own dispatch stamps, the decode-share
+weight-stream rate, and the CPU oracle timed on a bounded sample (reported
+baseline only).
 
-`roofline.traffic` (HBM bytes per launch of the dominant kernel) comes from
-the FETCH_SIZE / WRITE_SIZE counter summary under profiles/; it is reported
-only while the kernel sources still hash to the value recorded there, and is
-null otherwise.  `--copy-kernel MIB` runs only a plain device copy of that
+`roofline.traffic` (HBM bytes per launch) comes from the FETCH_SIZE /
+WRITE_SIZE counter summary under profiles/; it is reported only while the
+kernel sources still hash to the value recorded there, and is null
+otherwise.  `--copy-kernel MIB` runs only a plain device copy of that
 size (the counters' calibration) and exits.
 """
 
@@ -31,6 +32,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_FP8_TFLOPS = 5000.0     # MI355X dense fp8 MFMA
+PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
 BASELINE_METRIC = "MoE layer µs & fp8 TFLOP/s (% MFMA peak); decode weight-stream GB/s (% HBM)"
 
@@ -51,7 +53,7 @@ def parse():
     return ap.parse_args()
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm1_prefill_hbm_traffic.txt")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "moe_layer_prefill_hbm_traffic.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "mixture_experts_ffn_softmax_amd", "csrc", f)
                   for f in ("gemm.hip", "device_common.h", "internal.h")]
 
@@ -64,9 +66,10 @@ def kernel_source_hash():
     return h.hexdigest()
 
 
-def measured_traffic():
-    """HBM bytes per GEMM1 launch from the committed counter summary, or None
-    when the summary is absent or the kernel sources changed since it was taken."""
+def measured_traffic(which):
+    """HBM bytes per launch of GEMM `which` ("gemm1" / "gemm2") from the
+    committed counter summary, or None when the summary is absent or the
+    kernel sources changed since it was taken."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     fields = {}
@@ -77,7 +80,7 @@ def measured_traffic():
     if fields.get("source_sha256") != kernel_source_hash():
         return None
     try:
-        return float(fields["traffic_bytes_per_launch"])
+        return float(fields[f"{which}_traffic_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
 
@@ -124,12 +127,13 @@ class Layer:
         self.ws = torch.empty((nbytes,), dtype=torch.uint8, device="cuda")
         self.moe = moe
 
-    def step(self, i, events=None, gemm1_events=None):
+    def step(self, i, events=None, gemm_events=None):
         j = i % len(self.routed)
+        g = gemm_events or (None, None)
         self.moe.moe_forward(self.inp["x"], self.inp["logits"], self.k, self.routed[j],
                              None if self.shared is None else self.shared[j], self.inp["gamma"],
                              self.inp["eps"], out=self.out, ws=self.ws, events=events,
-                             gemm1_events=gemm1_events)
+                             gemm1_events=g[0], gemm2_events=g[1])
 
     def flops(self):
         rows = self.T * self.k + (self.T if self.shared is not None else 0)
@@ -161,24 +165,25 @@ def make_events(n):
 def time_layer(layer, steps, warmup):
     """Times `steps` steps after `warmup` untimed ones.  Returns (ms per step by
     the host clock between synchronisations, ms per step by GPU events around
-    the whole region, average GEMM1 launch ms).  The only events inside the
-    region are the pair the gate-up GEMM's own dispatch stamps."""
+    the whole region, average GEMM1 and GEMM2 launch ms).  The only events
+    inside the region are the pairs the two GEMMs' own dispatches stamp."""
     import torch
     for i in range(warmup):
         layer.step(i)
     torch.cuda.synchronize()
-    g1 = [make_events(2) for _ in range(steps)]
+    ge = [(make_events(2), make_events(2)) for _ in range(steps)]
     region = make_events(2)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     region[0].record()
     for i in range(steps):
-        layer.step(i, gemm1_events=g1[i])
+        layer.step(i, gemm_events=ge[i])
     region[1].record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    g1_ms = sum(a.elapsed_time(b) for a, b in g1) / steps
-    return (t1 - t0) * 1e3 / steps, region[0].elapsed_time(region[1]) / steps, g1_ms
+    g1_ms = sum(a.elapsed_time(b) for (a, b), _ in ge) / steps
+    g2_ms = sum(a.elapsed_time(b) for _, (a, b) in ge) / steps
+    return (t1 - t0) * 1e3 / steps, region[0].elapsed_time(region[1]) / steps, g1_ms, g2_ms
 
 
 def stage_times(layer, steps):
@@ -253,14 +258,16 @@ def main():
     layer = Layer(args.config, args.copies)
     c = layer.cfg
     log(f"[bench] timing {args.steps} steps after {args.warmup} warm-up")
-    ms, gpu_ms, g1_ms = time_layer(layer, args.steps, args.warmup)
+    ms, gpu_ms, g1_ms, g2_ms = time_layer(layer, args.steps, args.warmup)
     stage = stage_times(layer, min(args.steps, 20))
     flops, flops_g1 = layer.flops()
+    flops_g2 = flops - flops_g1
     value = flops / (ms * 1e-3) / 1e12
-    achieved = flops_g1 / (g1_ms * 1e-3) / 1e12
+    achieved_g1 = flops_g1 / (g1_ms * 1e-3) / 1e12
+    achieved_g2 = flops_g2 / (g2_ms * 1e-3) / 1e12
     wbytes, io, touched = layer.weight_bytes_touched()
     log(f"[bench] {ms * 1e3:.1f} us/layer ({gpu_ms * 1e3:.1f} by GPU events), {value:.1f} TFLOP/s; "
-        f"gemm1 {g1_ms * 1e3:.1f} us; stages with events (us): "
+        f"gemm1 {g1_ms * 1e3:.1f} us, gemm2 {g2_ms * 1e3:.1f} us; stages with events (us): "
         + ", ".join(f"{n} {v * 1e3:.1f}" for n, v in stage.items()))
     result = {
         "metric": BASELINE_METRIC,
@@ -283,10 +290,15 @@ def main():
                    "flops_per_step": flops, "touched_experts": touched},
         "stage_us_with_events": {n: round(v * 1e3, 2) for n, v in stage.items()},
         "frac_fp8_peak_layer": round(value / PEAK_FP8_TFLOPS, 4),
-        "roofline": {"kernel": "gemm1 (gate-up grouped GEMM + SiLU*gate)", "bound": "mfma",
-                     "achieved": round(achieved, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_FP8_TFLOPS, 4), "traffic": measured_traffic(),
-                     "flops_per_launch": flops_g1, "avg_launch_us": round(g1_ms * 1e3, 2)},
+        "roofline": {"kernel": "gemm2 (down grouped GEMM, bf16 h x W2 widened to bf16): the layer's longest kernel",
+                     "bound": "mfma", "achieved": round(achieved_g2, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved_g2 / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic("gemm2"), "flops_per_launch": flops_g2,
+                     "avg_launch_us": round(g2_ms * 1e3, 2)},
+        "roofline_gemm1": {"kernel": "gemm1 (gate-up grouped GEMM + SiLU*gate, fp8)", "bound": "mfma",
+                           "achieved": round(achieved_g1, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                           "frac": round(achieved_g1 / PEAK_FP8_TFLOPS, 4), "traffic": measured_traffic("gemm1"),
+                           "flops_per_launch": flops_g1, "avg_launch_us": round(g1_ms * 1e3, 2)},
     }
     del layer
     torch.cuda.empty_cache()
@@ -294,7 +306,7 @@ def main():
     if not args.no_decode:
         log("[bench] decode share (weight-stream bound)")
         dl = Layer("decode", args.copies)
-        dms, dgpu_ms, _ = time_layer(dl, max(args.steps, 50), args.warmup)
+        dms, dgpu_ms, _, _ = time_layer(dl, max(args.steps, 50), args.warmup)
         dstage = stage_times(dl, 20)
         dbytes, dio, dtouched = dl.weight_bytes_touched()
         gbs = (dbytes + dio) / (dms * 1e-3) / 1e9

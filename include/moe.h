@@ -133,10 +133,10 @@ enum {
  * a hipEvent_t recorded on `stream` just before stage i; events[MOE_N_STAGES]
  * after the last stage (each such record is one more packet on the stream,
  * a few microseconds of command-processor time).  `variant` receives a
- * NUL-terminated name of the kernel variants chosen.  gemm1_events[0] / [1],
- * when non-NULL, are hipEvent_t stamped by the gate-up GEMM's own dispatch
- * (hipExtLaunchKernel) at its start and end: its duration with no extra
- * packets on the stream.
+ * NUL-terminated name of the kernel variants chosen.  gemm1_events[0] / [1]
+ * and gemm2_events[0] / [1], when non-NULL, are hipEvent_t stamped by the
+ * gate-up / down GEMM's own dispatch (hipExtLaunchKernel) at its start and
+ * end: its duration with no extra packets on the stream.
  */
 typedef struct {
   int32_t* topk_ids;       /* [T][k]   */
@@ -152,6 +152,7 @@ typedef struct {
   void* events[MOE_N_STAGES + 1];
   char variant[96];
   void* gemm1_events[2];
+  void* gemm2_events[2];
 } moe_debug_t;
 
 /* ------------------------------------------------------------------------ */

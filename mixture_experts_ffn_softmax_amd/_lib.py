@@ -45,6 +45,7 @@ class MoeDebug(ctypes.Structure):
         ("events", ctypes.c_void_p * (MOE_N_STAGES + 1)),
         ("variant", ctypes.c_char * 96),
         ("gemm1_events", ctypes.c_void_p * 2),
+        ("gemm2_events", ctypes.c_void_p * 2),
     ]
 
 

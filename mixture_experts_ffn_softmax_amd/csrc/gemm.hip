@@ -1164,7 +1164,7 @@ hipError_t launch_gemm1(int variant, const FfnGroups& g, const RowOperand& x, co
 }
 
 hipError_t launch_gemm2(int variant, const FfnGroups& g, const uint16_t* h, const int* tile_prefix,
-                        long n_rows, float* y, hipStream_t s) {
+                        long n_rows, float* y, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop) {
   // every group's rows index the one K-blocked h directly
   const Operand hd = k_blocked_operand(n_rows, kHChunk);
   const RowOperand hr{{h, h}, {nullptr, nullptr}, 0, {hd, hd}};
@@ -1181,13 +1181,17 @@ hipError_t launch_gemm2(int variant, const FfnGroups& g, const uint16_t* h, cons
   if (variant == kVariantSmall) {
     p.ntiles = g.hidden / kSmCh2;
     const long grid = max_row_tiles(n_rows, g.n_groups, bm) * p.ntiles;
-    if (g.fmt == kMxfp4) gemm2_small_kernel<kMxfp4><<<(unsigned)grid, 256, 0, s>>>(p);
-    else gemm2_small_kernel<kFp8><<<(unsigned)grid, 256, 0, s>>>(p);
+    if (g.fmt == kMxfp4)
+      hipExtLaunchKernelGGL(gemm2_small_kernel<kMxfp4>, dim3((unsigned)grid), dim3(256), 0, s, ev_start, ev_stop, 0, p);
+    else
+      hipExtLaunchKernelGGL(gemm2_small_kernel<kFp8>, dim3((unsigned)grid), dim3(256), 0, s, ev_start, ev_stop, 0, p);
   } else {
     p.ntiles = g.hidden / kLgCh;
     const long grid = max_row_tiles(n_rows, g.n_groups, bm) * p.ntiles;
-    if (variant == kVariantLarge256) gemm2_pp_kernel<256, 6><<<(unsigned)grid, 256, 0, s>>>(p);
-    else gemm2_pp_kernel<128, 8><<<(unsigned)grid, 256, 0, s>>>(p);
+    if (variant == kVariantLarge256)
+      hipExtLaunchKernelGGL(gemm2_pp_kernel<256, 6>, dim3((unsigned)grid), dim3(256), 0, s, ev_start, ev_stop, 0, p);
+    else
+      hipExtLaunchKernelGGL(gemm2_pp_kernel<128, 8>, dim3((unsigned)grid), dim3(256), 0, s, ev_start, ev_stop, 0, p);
   }
   return hipGetLastError();
 }

@@ -122,7 +122,8 @@ hipError_t launch_gemm1(int variant, const FfnGroups& g, const RowOperand& x, co
                         hipEvent_t ev_stop = nullptr);
 // GEMM2: y[r][j] = (h_r . W2[j]) * s2[j] in fp32; h as GEMM1 writes it.
 hipError_t launch_gemm2(int variant, const FfnGroups& g, const uint16_t* h, const int* tile_prefix,
-                        long n_rows, float* y, hipStream_t s);
+                        long n_rows, float* y, hipStream_t s, hipEvent_t ev_start = nullptr,
+                        hipEvent_t ev_stop = nullptr);
 
 // ---- weight layout ------------------------------------------------------------
 // Copies E matrices of [N][K] bytes into the K-blocked layout with C-byte chunks.

@@ -143,7 +143,7 @@ moe::FfnGroups make_groups(const moe_weights_t* r, const moe_weights_t* sh, cons
 moe_status_t run_ffn(const moe::FfnGroups& g, const moe::RowOperand& x, long n_rows, float* y,
                      int32_t* tile_prefix, uint16_t* h, hipStream_t s, void* const* events,
                      char* variant_out, size_t variant_len, bool tile_prefix_ready = false,
-                     void* const* gemm1_events = nullptr) {
+                     void* const* gemm1_events = nullptr, void* const* gemm2_events = nullptr) {
   const int variant = moe::choose_variant(g, n_rows);
   if (variant_out)
     snprintf(variant_out, variant_len, "%s/%s", moe::variant_name(variant),
@@ -159,7 +159,9 @@ moe_status_t run_ffn(const moe::FfnGroups& g, const moe::RowOperand& x, long n_r
                         gemm1_events ? (hipEvent_t)gemm1_events[1] : nullptr);
   if (e != hipSuccess) return device_status(e, "gemm1");
   if (events && events[MOE_STAGE_GEMM2]) hipEventRecord((hipEvent_t)events[MOE_STAGE_GEMM2], s);
-  e = moe::launch_gemm2(variant, g, h, tile_prefix, n_rows, y, s);
+  e = moe::launch_gemm2(variant, g, h, tile_prefix, n_rows, y, s,
+                        gemm2_events ? (hipEvent_t)gemm2_events[0] : nullptr,
+                        gemm2_events ? (hipEvent_t)gemm2_events[1] : nullptr);
   if (e != hipSuccess) return device_status(e, "gemm2");
   return ok();
 }
@@ -443,7 +445,8 @@ moe_status_t moe_forward(const uint16_t* x, const float* logits, int32_t T, int3
                      {rows_d, sh ? tok_d : rows_d}};
   char* vout = dbg ? dbg->variant : nullptr;
   MOE_CHECK(run_ffn(g, xr, rows, L.y_rows, L.tile_prefix, L.h, s, ev, vout,
-                    dbg ? sizeof(dbg->variant) : 0, meta, dbg ? dbg->gemm1_events : nullptr));
+                    dbg ? sizeof(dbg->variant) : 0, meta, dbg ? dbg->gemm1_events : nullptr,
+                    dbg ? dbg->gemm2_events : nullptr));
 
   if (ev && ev[MOE_STAGE_COMBINE]) hipEventRecord((hipEvent_t)ev[MOE_STAGE_COMBINE], s);
   e = moe::launch_combine(L.y_rows, L.p2r, L.w, T, H, top_k, sh ? L.y_rows + (size_t)R * H : nullptr,
