@@ -19,8 +19,8 @@ format and the LatentMoE expert shape with its RMSNorm come from the page
 of the sglang-jax reference wiki (cited as *sglang-jax gap list*).
 
 Everything is float64 except at the rounding points the method itself
-defines (the fp8 e4m3 quantisation of activations and of the intermediate,
-and the final bf16 output).
+defines (the fp8 e4m3 quantisation of the activations before the scatter,
+the bf16 intermediate h, and the final bf16 output).
 
 Pins (each checked in ``tests/test_oracle_*.py`` against something other than
 the oracle itself): codecs against the OCP definitions and against torch's

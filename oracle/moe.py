@@ -4,7 +4,7 @@ TEST INFRASTRUCTURE ONLY (see the package docstring).
 
 Steps and where the pages describe them:
 
-1. ``route``            -- softmax router, top-k, renormalised weights.
+1. ``route``            -- softmax (or sigmoid) router, top-k, renormalised weights.
    *Ling-2.6-1T on TPU*: overview (256 routed experts, top-8 plus one shared
    expert) and §1 cost model; *Kimi K3 on TPU*, §2.4 LatentMoE
    (renormalised top-k weights, routed scaling factor 1.0).
@@ -16,11 +16,11 @@ Steps and where the pages describe them:
    indices) and the scatter of token rows to experts.  *Ling-2.6-1T on TPU*,
    §1 ("scatter tokens -> local expert FFN -> gather results") and §6 (the
    metadata block).
-4. ``expert_ffn``       -- gated expert FFN: W1/W3 gate-up projection, SiLU,
-   gate multiply, scale multiply, W2 down projection, with per-channel scales
-   applied after the full-K reduction.  *Ling-2.6-1T on TPU*, §2 (table of
-   hardware units and the MoE work each does) and §5 "per-channel
-   direct_scaled_dot".
+4. ``expert_ffn``       -- gated expert FFN: W1/W3 gate-up projection, SiLU
+   (or SiTU, *Kimi K3 on TPU* §2.6), gate multiply, scale multiply, W2 down
+   projection, with per-channel scales applied after the full-K reduction.
+   *Ling-2.6-1T on TPU*, §2 (table of hardware units and the MoE work each
+   does) and §5 "per-channel direct_scaled_dot".
 5. ``combine``          -- weighted gather back into token order, optional
    per-token RMSNorm of the routed sum (*Kimi K3 on TPU*, §2.4
    routed_expert_norm), plus the shared expert's output (*Ling-2.6-1T on TPU*,
@@ -54,15 +54,20 @@ from .codecs import (
 # ----------------------------------------------------------------------------
 
 
-def route(logits, top_k):
-    """Top-k experts per token and their renormalised softmax weights.
+def route(logits, top_k, score="softmax"):
+    """Top-k experts per token and their renormalised weights.
 
     logits: float32 [T][E].  Returns (topk_ids int32 [T][k], topk_w float64
     [T][k]).  Experts are ordered by descending logit, equal logits by
     ascending expert index; that order is both the selection and the slot
-    order.  p = softmax(logits[t]) in float64 (max subtracted), and
-    w_j = p[id_j] / sum_j' p[id_j'].
+    order.  score "softmax": p = softmax(logits[t]) in float64 (max
+    subtracted); score "sigmoid" (the *Kimi K3 on TPU* router, §2.4, without
+    its selection bias, which the pages do not define): p = 1 / (1 + e^-l).
+    Both are increasing in the logit, so they select the same experts.  Then
+    w_j = p[id_j] / sum_j' p[id_j'] (renormalised, routed scaling factor 1).
     """
+    if score not in ("softmax", "sigmoid"):
+        raise ValueError(score)
     logits = np.asarray(logits, dtype=np.float32)
     T, E = logits.shape
     if not 1 <= top_k <= E:
@@ -76,8 +81,11 @@ def route(logits, top_k):
         order = np.lexsort((index, -row))
         sel = order[:top_k]
         ids[t] = sel
-        p = np.exp(row - row.max())
-        p = p / p.sum()
+        if score == "softmax":
+            p = np.exp(row - row.max())
+            p = p / p.sum()
+        else:
+            p = 1.0 / (1.0 + np.exp(-row))
         w[t] = p[sel] / p[sel].sum()
     return ids, w
 
@@ -171,12 +179,17 @@ class ExpertWeights:
     W1 is the gate projection and W3 the up projection.  The six stacks may
     be any objects with a ``shape`` whose ``[e]`` gives expert e as a NumPy
     array (so very large stacks can be fetched one expert at a time).
+    activation: "silu" (SiLU(g) * u) or "situ" (SiTU with parameter beta).
     """
 
-    def __init__(self, fmt, w1, w3, w2, s1, s3, s2):
+    def __init__(self, fmt, w1, w3, w2, s1, s3, s2, activation="silu", beta=4.0):
         if fmt not in ("fp8", "mxfp4"):
             raise ValueError(fmt)
+        if activation not in ("silu", "situ") or not beta > 0:
+            raise ValueError(activation)
         self.fmt = fmt
+        self.activation = activation
+        self.beta = float(beta)
         wrap = lambda a: a if hasattr(a, "shape") and not isinstance(a, (list, tuple)) else np.asarray(a)  # noqa: E731
         self.w1, self.w3, self.w2 = (wrap(a) for a in (w1, w3, w2))
         self.s1, self.s3, self.s2 = (wrap(a) for a in (s1, s3, s2))
@@ -205,13 +218,26 @@ def silu(z):
         return z / (1.0 + np.exp(-z))
 
 
+def situ(z, beta):
+    """SiTU(z) = beta * tanh(z / beta) * sigmoid(z) (*Kimi K3 on TPU*, §2.6,
+    with beta = 4): SiLU with its linear factor z bounded to (-beta, beta)."""
+    with np.errstate(over="ignore"):
+        return beta * np.tanh(z / beta) / (1.0 + np.exp(-z))
+
+
+def activate(g, weights):
+    """The expert group's gate activation."""
+    return silu(g) if weights.activation == "silu" else situ(g, weights.beta)
+
+
 def expert_ffn(xq_rows, xs_rows, offsets, weights):
     """Gated FFN of every routed row with its expert's weights.
 
     For row r in expert e's segment (rows offsets[e] .. offsets[e+1]-1):
       g = (sum_k q_r[k] W1[e][n][k]) * xs_r * s1[e][n]
       u = (sum_k q_r[k] W3[e][n][k]) * xs_r * s3[e][n]
-      h = bf16( SiLU(g) * u )                  (the activation dtype)
+      h = bf16( act(g) * u )                   (the activation dtype;
+                                                act = SiLU, or SiTU)
       y[r][j] = (sum_n h_r[n] W2[e][j][n]) * s2[e][j]
     The sums of fp8 (or e2m1 * 2^k) products, and of bf16 x fp8 products,
     are exact in float64.  Returns (y float64 [R][H], h uint16 bf16 bits [R][I]).
@@ -230,7 +256,7 @@ def expert_ffn(xq_rows, xs_rows, offsets, weights):
         a = e4m3_decode(xq_rows[r0:r1])
         g = (a @ W1.T) * xs_rows[r0:r1, None] * c1[None, :]
         u = (a @ W3.T) * xs_rows[r0:r1, None] * c3[None, :]
-        h = bf16_encode(silu(g) * u)
+        h = bf16_encode(activate(g, weights) * u)
         y[r0:r1] = (bf16_decode(h) @ W2.T) * c2[None, :]
         h_all[r0:r1] = h
     return y, h_all
@@ -271,14 +297,16 @@ def combine(y_rows, pair_to_row, topk_w, y_shared=None, norm_gamma=None, norm_ep
 # ----------------------------------------------------------------------------
 
 
-def forward(x_bf16, logits, top_k, routed, shared=None, norm_gamma=None, norm_eps=1e-6):
+def forward(x_bf16, logits, top_k, routed, shared=None, norm_gamma=None, norm_eps=1e-6,
+            score="softmax"):
     """Route -> quantise -> count/offset -> permute -> expert FFN -> combine.
 
     x_bf16 uint16 [T][H]; logits float32 [T][E]; routed/shared ExpertWeights
-    (shared has one expert and runs on every token in token order).  Returns a
-    dict with every intermediate and ``out`` (uint16 bf16 [T][H]).
+    (shared has one expert and runs on every token in token order); score as
+    in ``route``.  Returns a dict with every intermediate and ``out`` (uint16
+    bf16 [T][H]).
     """
-    ids, w = route(logits, top_k)
+    ids, w = route(logits, top_k, score)
     xq, xs = quantize_tokens(x_bf16)
     counts, offsets = expert_counts_offsets(ids, routed.n_experts)
     pair_to_row, row_to_pair, xq_rows, xs_rows = permute_rows(ids, offsets, xq, xs)
@@ -295,7 +323,7 @@ def forward(x_bf16, logits, top_k, routed, shared=None, norm_gamma=None, norm_ep
 
 
 def forward_sampled(x_bf16, logits, top_k, routed, tokens, shared=None,
-                    norm_gamma=None, norm_eps=1e-6, routing=None):
+                    norm_gamma=None, norm_eps=1e-6, routing=None, score="softmax"):
     """The layer's output for a subset of tokens only (rows are independent).
 
     Routing runs for all tokens (or is taken from ``routing`` = (topk_ids,
@@ -305,7 +333,7 @@ def forward_sampled(x_bf16, logits, top_k, routed, tokens, shared=None,
     tokens[i]).
     """
     tokens = np.asarray(tokens, dtype=np.int64)
-    ids, w = route(logits, top_k) if routing is None else routing
+    ids, w = route(logits, top_k, score) if routing is None else routing
     xq, xs = quantize_tokens(np.asarray(x_bf16)[tokens])
     sub_ids = ids[tokens]
     _, sub_off = expert_counts_offsets(sub_ids, routed.n_experts)
