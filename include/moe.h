@@ -87,10 +87,32 @@ typedef enum {
 } moe_wlayout_t;
 
 /*
+ * Gate activation of an expert group: h = act(g) * u.  SILU: g * sigmoid(g)
+ * (the Ling-2.6-1T page, §2: SiLU on the gate).  SITU: beta * tanh(g / beta)
+ * * sigmoid(g) (the Kimi K3 page, §2.6, with beta = 4).
+ */
+typedef enum {
+  MOE_ACT_SILU = 0,
+  MOE_ACT_SITU = 1
+} moe_act_t;
+
+/*
+ * Router score function.  SOFTMAX: p = softmax(logits[t]) (the default).
+ * SIGMOID: p = 1 / (1 + e^-l) per expert (the Kimi K3 page, §2.4; its
+ * noaux_tc selection bias is not defined there and not provided).  Both are
+ * increasing in the logit, so both select the k largest logits; the weights
+ * are p renormalised over the k chosen.
+ */
+typedef enum {
+  MOE_SCORE_SOFTMAX = 0,
+  MOE_SCORE_SIGMOID = 1
+} moe_score_t;
+
+/*
  * A group of experts that share one shape.  Host struct holding device
- * pointers; caller-owned.  W1 is the gate projection (through SiLU), W3 the
- * up projection, W2 the down projection; the contraction index is last
- * ("K contiguous").
+ * pointers; caller-owned.  W1 is the gate projection (through the
+ * activation), W3 the up projection, W2 the down projection; the contraction
+ * index is last ("K contiguous").
  *
  *   fmt = FP8:   w1, w3  uint8 [E][I][H]      s1, s3  float [E][I]
  *                w2      uint8 [E][H][I]      s2      float [E][H]
@@ -106,6 +128,8 @@ typedef struct {
   int32_t hidden;    /* H: model dimension (FFN input and output width) */
   int32_t inter;     /* I: intermediate dimension */
   int32_t layout;    /* moe_wlayout_t of w1, w3, w2 */
+  int32_t activation;/* moe_act_t (0 = SiLU) */
+  float act_beta;    /* SiTU's beta, finite and > 0; ignored for SiLU */
   int32_t reserved;  /* must be 0 */
   const uint8_t* w1;
   const uint8_t* w3;
@@ -158,17 +182,19 @@ typedef struct {
 /* ------------------------------------------------------------------------ */
 
 /*
- * moe_route -- softmax router with top-k selection.
- *   logits    float [T][E]   router logits
+ * moe_route -- router with top-k selection.
+ *   logits    float [T][E]   router logits (|l| <= 80: beyond, fp32 sigmoid
+ *                            scores underflow and the weights are undefined)
+ *   score     moe_score_t
  *   topk_ids  int32 [T][k]   out: chosen experts, slot order = descending
  *                            logit, equal logits by ascending expert index
  *                            (-0.0 equals +0.0); the raw fp32 logits decide
- *   topk_w    float [T][k]   out: w_j = p[id_j] / sum_j' p[id_j'] with
- *                            p = softmax(logits[t]) (routed scaling 1.0)
+ *   topk_w    float [T][k]   out: w_j = p[id_j] / sum_j' p[id_j'] with p the
+ *                            score (routed scaling 1.0)
  * [Ling] overview and §1 (top-8 of 256 routed experts); renormalised weights
- * as in the Kimi K3 page, §2.4.
+ * and the sigmoid score as in the Kimi K3 page, §2.4.
  */
-moe_status_t moe_route(const float* logits, int32_t T, int32_t E, int32_t top_k,
+moe_status_t moe_route(const float* logits, int32_t T, int32_t E, int32_t top_k, int32_t score,
                        int32_t* topk_ids, float* topk_w, void* stream);
 
 /*
@@ -208,7 +234,7 @@ moe_status_t moe_permute(const uint16_t* x, int32_t T, int32_t H, const int32_t*
  * For row r of expert e ([Ling] §5, per-channel direct_scaled_dot: scales
  * applied after the full-K reduction; fp32 accumulation):
  *   g = (sum_k q_r[k] W1[e][n][k]) * xs_r * s1[e][n];  u likewise with W3, s3
- *   h = bf16( SiLU(g) * u )
+ *   h = bf16( act(g) * u )   act = SiLU or SiTU (w->activation)
  *   y_r[j] = (sum_n h_r[n] W2[e][j][n]) * s2[e][j]
  * GEMM1 runs e4m3 x e4m3 on the matrix cores; GEMM2 runs bf16 h x W2 with
  * W2's codes converted exactly to bf16.
@@ -243,6 +269,7 @@ moe_status_t moe_combine(const float* y_rows, const int32_t* pair_to_row, const 
  * moe_forward -- the whole layer: route -> permute -> expert FFN (routed
  * experts and, if use_shared, the shared expert on every token) -> combine.
  *   x       bf16  [T][H]         logits float [T][E] (E = routed->n_experts)
+ *   score   moe_score_t of the router (see moe_route)
  *   routed  the routed experts; shared: one expert of the same H and I, fp8
  *           (required iff use_shared)
  *   out     bf16  [T][H]
@@ -254,7 +281,7 @@ moe_status_t moe_combine(const float* y_rows, const int32_t* pair_to_row, const 
 size_t moe_forward_workspace_size(int32_t T, int32_t top_k, const moe_weights_t* routed,
                                   int32_t use_shared);
 moe_status_t moe_forward(const uint16_t* x, const float* logits, int32_t T, int32_t top_k,
-                         const moe_weights_t* routed, int32_t use_shared,
+                         int32_t score, const moe_weights_t* routed, int32_t use_shared,
                          const moe_weights_t* shared, const float* norm_gamma, float norm_eps,
                          uint16_t* out, moe_debug_t* dbg, void* ws, size_t ws_bytes,
                          void* stream);

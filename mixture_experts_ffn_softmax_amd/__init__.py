@@ -39,9 +39,10 @@ class Weights:
     float32 per-channel scales for fp8, uint8 e8m0 block scales for mxfp4).
     fp8 weights are repacked once into the K-blocked layout (moe_pack_weights)
     unless ``pack`` is False; ``self.tensors`` keeps the row-major originals.
+    ``activation``: "silu" or "situ" (with ``beta``).
     """
 
-    def __init__(self, d, fmt, pack=True, stream=None):
+    def __init__(self, d, fmt, pack=True, stream=None, activation="silu", beta=4.0):
         self.tensors = {k: v.contiguous() for k, v in d.items()}
         t = self.tensors
         self.fmt = MOE_W_FP8 if fmt == "fp8" else MOE_W_MXFP4
@@ -49,11 +50,13 @@ class Weights:
         H = t["w2"].shape[1]
         self.n_experts, self.hidden, self.inter = E, H, I
         ptrs = [t[k].data_ptr() for k in ("w1", "w3", "w2", "s1", "s3", "s2")]
-        self.c = MoeWeights(self.fmt, E, H, I, MOE_LAYOUT_ROW_MAJOR, 0, *ptrs)
+        act = _lib.MOE_ACT_SITU if activation == "situ" else _lib.MOE_ACT_SILU
+        self.activation, self.beta = activation, beta
+        self.c = MoeWeights(self.fmt, E, H, I, MOE_LAYOUT_ROW_MAJOR, act, beta, 0, *ptrs)
         self.packed = None
         if pack and self.fmt == MOE_W_FP8:
             self.packed = {k: torch.empty_like(t[k]) for k in ("w1", "w3", "w2")}
-            dst = MoeWeights(self.fmt, E, H, I, MOE_LAYOUT_K_BLOCKED, 0,
+            dst = MoeWeights(self.fmt, E, H, I, MOE_LAYOUT_K_BLOCKED, act, beta, 0,
                              *(self.packed[k].data_ptr() for k in ("w1", "w3", "w2")), *ptrs[3:])
             check(lib().moe_pack_weights(ctypes.byref(self.c), ctypes.byref(dst), _stream(stream)))
             self.c = dst
@@ -70,12 +73,17 @@ def _empty(shape, dtype, device):
     return torch.empty(shape, dtype=dtype, device=device)
 
 
-def moe_route(logits, top_k, topk_ids=None, topk_w=None, stream=None):
+def _score(score):
+    return {"softmax": _lib.MOE_SCORE_SOFTMAX, "sigmoid": _lib.MOE_SCORE_SIGMOID}[score]
+
+
+def moe_route(logits, top_k, topk_ids=None, topk_w=None, score="softmax", stream=None):
     T, E = logits.shape
     dev = logits.device
     topk_ids = _empty((T, top_k), torch.int32, dev) if topk_ids is None else topk_ids
     topk_w = _empty((T, top_k), torch.float32, dev) if topk_w is None else topk_w
-    check(lib().moe_route(_p(logits), T, E, top_k, _p(topk_ids), _p(topk_w), _stream(stream)))
+    check(lib().moe_route(_p(logits), T, E, top_k, _score(score), _p(topk_ids), _p(topk_w),
+                          _stream(stream)))
     return topk_ids, topk_w
 
 
@@ -129,7 +137,8 @@ def forward_workspace_size(T, top_k, routed, use_shared):
 
 
 def moe_forward(x, logits, top_k, routed, shared=None, norm_gamma=None, norm_eps=1e-6, out=None,
-                ws=None, debug=None, events=None, gemm1_events=None, gemm2_events=None, stream=None):
+                ws=None, debug=None, events=None, gemm1_events=None, gemm2_events=None,
+                score="softmax", stream=None):
     """The whole layer.  ``debug``: dict of device tensors to capture
     (keys topk_ids, topk_w, expert_counts, expert_offsets, pair_to_row,
     row_to_pair, xq_rows, xs_rows).  ``events``: list of MOE_N_STAGES + 1
@@ -155,7 +164,7 @@ def moe_forward(x, logits, top_k, routed, shared=None, norm_gamma=None, norm_eps
             dbg.gemm1_events[i] = ev.cuda_event
         for i, ev in enumerate(gemm2_events or []):
             dbg.gemm2_events[i] = ev.cuda_event
-    check(lib().moe_forward(_p(x), _p(logits), T, top_k, routed.ref(), int(shared is not None),
+    check(lib().moe_forward(_p(x), _p(logits), T, top_k, _score(score), routed.ref(), int(shared is not None),
                             shared.ref() if shared is not None else None, _p(norm_gamma),
                             float(norm_eps), _p(out), ctypes.byref(dbg) if dbg is not None else None,
                             _p(ws), ws.numel(), _stream(stream)))

@@ -18,6 +18,8 @@ MOE_LAYOUT_ROW_MAJOR, MOE_LAYOUT_K_BLOCKED = 0, 1
 (MOE_STAGE_ROUTE, MOE_STAGE_PERMUTE, MOE_STAGE_GEMM1, MOE_STAGE_GEMM2, MOE_STAGE_COMBINE,
  MOE_N_STAGES) = range(6)
 STAGE_NAMES = ["route", "permute", "gemm1", "gemm2", "combine"]
+MOE_ACT_SILU, MOE_ACT_SITU = 0, 1
+MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
 
 # Every function include/moe.h declares.
 EXPORTS = [
@@ -30,7 +32,8 @@ EXPORTS = [
 class MoeWeights(ctypes.Structure):
     _fields_ = [
         ("fmt", ctypes.c_int32), ("n_experts", ctypes.c_int32), ("hidden", ctypes.c_int32),
-        ("inter", ctypes.c_int32), ("layout", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("inter", ctypes.c_int32), ("layout", ctypes.c_int32), ("activation", ctypes.c_int32),
+        ("act_beta", ctypes.c_float), ("reserved", ctypes.c_int32),
         ("w1", ctypes.c_void_p), ("w3", ctypes.c_void_p), ("w2", ctypes.c_void_p),
         ("s1", ctypes.c_void_p), ("s3", ctypes.c_void_p), ("s2", ctypes.c_void_p),
     ]
@@ -53,7 +56,7 @@ _VP, _I32, _F32, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c
 _WP, _DP = ctypes.POINTER(MoeWeights), ctypes.POINTER(MoeDebug)
 
 SIGNATURES = {
-    "moe_route": (_I32, [_VP, _I32, _I32, _I32, _VP, _VP, _VP]),
+    "moe_route": (_I32, [_VP, _I32, _I32, _I32, _I32, _VP, _VP, _VP]),
     "moe_permute_workspace_size": (_SZ, [_I32, _I32, _I32]),
     "moe_permute": (_I32, [_VP, _I32, _I32, _VP, _I32, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                            _VP, _SZ, _VP]),
@@ -61,7 +64,7 @@ SIGNATURES = {
     "moe_expert_ffn": (_I32, [_VP, _VP, _I32, _VP, _WP, _VP, _VP, _SZ, _VP]),
     "moe_combine": (_I32, [_VP, _VP, _VP, _I32, _I32, _I32, _VP, _VP, _F32, _VP, _VP]),
     "moe_forward_workspace_size": (_SZ, [_I32, _I32, _WP, _I32]),
-    "moe_forward": (_I32, [_VP, _VP, _I32, _I32, _WP, _I32, _WP, _VP, _F32, _VP, _DP, _VP, _SZ, _VP]),
+    "moe_forward": (_I32, [_VP, _VP, _I32, _I32, _I32, _WP, _I32, _WP, _VP, _F32, _VP, _DP, _VP, _SZ, _VP]),
     "moe_pack_weights": (_I32, [_WP, _WP, _VP]),
     "moe_status_string": (ctypes.c_char_p, [_I32]),
     "moe_last_error": (ctypes.c_char_p, []),

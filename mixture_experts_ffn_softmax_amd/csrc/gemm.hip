@@ -79,6 +79,8 @@ struct GemmParams {
   const void* sa[2];
   const void* sb[2];
   Operand wd[2];         // byte addressing of one expert's weight matrix (fp8)
+  int act[2];            // GEMM1: gate Activation of the routed / shared group
+  float beta[2];         // GEMM1: SiTU's beta per group
   uint16_t* h;           // GEMM1 output: bf16, K-blocked (kHChunk-byte chunks)
   long h_cs;             // its chunk stride in bytes (rows * kHChunk)
   float* y;              // GEMM2 output [rows][N] fp32
@@ -118,6 +120,10 @@ __device__ __forceinline__ v4f mfma16_fp4w(const v8i& w, const v8i& x, const v4f
 }
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
+
+// SiTU (the Kimi K3 page, §2.6): beta * tanh(g / beta) * sigmoid(g).  Its
+// linear factor saturates at +-beta, where SiLU's grows without bound.
+__device__ __forceinline__ float situ(float g, float beta) { return beta * tanhf(g / beta) / (1.0f + expf(-g)); }
 
 // 32 e4m3 codes (8 words) -> 4 x 8 bf16, exact.
 __device__ __forceinline__ void fp8x32_to_bf16(const uint32_t (&w)[8], v8bf (&out)[4]) {
@@ -246,6 +252,9 @@ constexpr int kLgCh = 256;    // channel rows per tile
 __device__ __forceinline__ float silu_fast(float g) {
   return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * g));
 }
+// The SiTU epilogue takes tanh(z) = 1 - 2 / (1 + e^(2z)), which saturates
+// cleanly at +-1 when the exponential overflows or underflows.
+
 
 // ============================================================================
 // large variants: 4 waves, one per SIMD, pipelined through an LDS ring
@@ -286,11 +295,62 @@ __device__ __forceinline__ int valid_frags(int vr, int wm) {
   return v < 0 ? 0 : (v > TF ? TF : v);
 }
 
+// GEMM1 large epilogue.  Lane holds token l32 of each token fragment and, per
+// group q of 4 accumulator entries, channels 8q + 4hh .. +3 of the fragment.
+// The gate and up sums are scaled by the token and channel scales and
+// h = bf16(act(g) * u) goes straight to the K-blocked h: a 32-channel
+// fragment is one 64-byte chunk row, so the four q stores of a fragment fill
+// 32 consecutive chunk rows (2 KB).
+template <int TV, int TA, typename Act>
+__device__ __forceinline__ void gemm1_pp_epilogue(const GemmParams& p, const TileInfo& ti, int n0, int wm, int wn,
+                                                  int l32, int hh, const v16f (&acc)[4][TA], Act act) {
+  const float* S1 = reinterpret_cast<const float*>(p.sa[ti.wi]) + ti.eg * p.N;
+  const float* S3 = reinterpret_cast<const float*>(p.sb[ti.wi]) + ti.eg * p.N;
+  float xs[TV];
+#pragma unroll
+  for (int t = 0; t < TV; ++t) {
+    int grow = ti.row0 + (2 * t + wm) * 32 + l32;
+    if (grow >= ti.row1) grow = ti.row1 - 1;
+    xs[t] = p.a_scale[ti.wi][grow - (ti.wi ? p.shared_row0 : 0)];
+  }
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int ch0 = n0 + wn * 64 + c * 32;
+    float4 s1v[4], s3v[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      s1v[q] = *reinterpret_cast<const float4*>(S1 + ch0 + 8 * q + 4 * hh);
+      s3v[q] = *reinterpret_cast<const float4*>(S3 + ch0 + 8 * q + 4 * hh);
+    }
+#pragma unroll
+    for (int t = 0; t < TV; ++t) {
+      const int grow = ti.row0 + (2 * t + wm) * 32 + l32;
+      if (grow >= ti.row1) continue;
+      uint16_t* hrow = p.h + h_off(p.h_cs, grow, ch0);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float sg[4] = {s1v[q].x, s1v[q].y, s1v[q].z, s1v[q].w};
+        const float su[4] = {s3v[q].x, s3v[q].y, s3v[q].z, s3v[q].w};
+        uint32_t b[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float g = acc[c][t][4 * q + v] * xs[t] * sg[v];
+          const float u = acc[2 + c][t][4 * q + v] * xs[t] * su[v];
+          b[v] = bf16_rne(act(g) * u);
+        }
+        *reinterpret_cast<uint2*>(hrow + 8 * q + 4 * hh) = make_uint2(b[0] | (b[1] << 16), b[2] | (b[3] << 16));
+      }
+    }
+  }
+}
+
 // GEMM1: wave (wm, wn) owns the interleaved token fragments of wave row wm
 // and channels [wn * 64, +64) of both the gate (fragments 0, 1) and the up
 // rows (2, 3).  LDS stage: BM token rows then 256 channel rows (W1 rows
-// n0.., then W3 rows n0..), 64 bytes of the K step each (swz64).
-template <int BM, int STAGES, int TV>
+// n0.., then W3 rows n0..), 64 bytes of the K step each (swz64).  SITU:
+// some group uses SiTU (a separate instantiation, so that the SiLU-only
+// kernel carries no second epilogue and its register allocation is unchanged).
+template <int BM, int STAGES, int TV, bool SITU>
 __device__ __forceinline__ void gemm1_pp_body(const GemmParams& p, const TileInfo& ti, uint8_t* smem) {
   constexpr int kRows = BM + kLgCh;
   constexpr int kStage = kRows * 64;
@@ -424,54 +484,25 @@ __device__ __forceinline__ void gemm1_pp_body(const GemmParams& p, const TileInf
   }
   if (ks < nk) step(tail, ks, xa, wa, xb, wb);
 
-  // ---- epilogue.  Lane holds token l32 of each token fragment and, per
-  // group q of 4 accumulator entries, channels 8q + 4hh .. +3 of the
-  // fragment.  h = bf16(SiLU(g) * u) goes straight to the K-blocked h: a
-  // 32-channel fragment is one 64-byte chunk row, so the four q stores of a
-  // fragment fill 32 consecutive chunk rows (2 KB).
+  // ---- epilogue
   if constexpr (TV > 0) {
-    const float* S1 = reinterpret_cast<const float*>(p.sa[ti.wi]) + ti.eg * p.N;
-    const float* S3 = reinterpret_cast<const float*>(p.sb[ti.wi]) + ti.eg * p.N;
-    float xs[TV];
-#pragma unroll
-    for (int t = 0; t < TV; ++t) {
-      int grow = ti.row0 + (2 * t + wm) * 32 + l32;
-      if (grow >= ti.row1) grow = ti.row1 - 1;
-      xs[t] = p.a_scale[ti.wi][grow - (ti.wi ? p.shared_row0 : 0)];
-    }
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const int ch0 = n0 + wn * 64 + c * 32;
-      float4 s1v[4], s3v[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        s1v[q] = *reinterpret_cast<const float4*>(S1 + ch0 + 8 * q + 4 * hh);
-        s3v[q] = *reinterpret_cast<const float4*>(S3 + ch0 + 8 * q + 4 * hh);
-      }
-#pragma unroll
-      for (int t = 0; t < TV; ++t) {
-        const int grow = ti.row0 + (2 * t + wm) * 32 + l32;
-        if (grow >= ti.row1) continue;
-        uint16_t* hrow = p.h + h_off(p.h_cs, grow, ch0);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float sg[4] = {s1v[q].x, s1v[q].y, s1v[q].z, s1v[q].w};
-          const float su[4] = {s3v[q].x, s3v[q].y, s3v[q].z, s3v[q].w};
-          uint32_t b[4];
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const float g = acc[c][t][4 * q + v] * xs[t] * sg[v];
-            const float u = acc[2 + c][t][4 * q + v] * xs[t] * su[v];
-            b[v] = bf16_rne(silu_fast(g) * u);
-          }
-          *reinterpret_cast<uint2*>(hrow + 8 * q + 4 * hh) = make_uint2(b[0] | (b[1] << 16), b[2] | (b[3] << 16));
-        }
-      }
+    if constexpr (SITU) {
+      // one epilogue for both activations (a second copy spills): SiLU is
+      // the product with the linear factor g instead of beta tanh(g / beta)
+      const bool use_situ = p.act[ti.wi] == kActSitu;
+      const float beta = p.beta[ti.wi], rbeta = 1.0f / beta;
+      gemm1_pp_epilogue<TV, TA>(p, ti, n0, wm, wn, l32, hh, acc, [=](float g) {
+        const float sig = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * g));
+        const float th = 1.0f - 2.0f * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(2.8853900817779268f * g * rbeta));
+        return (use_situ ? beta * th : g) * sig;
+      });
+    } else {
+      gemm1_pp_epilogue<TV, TA>(p, ti, n0, wm, wn, l32, hh, acc, [](float g) { return silu_fast(g); });
     }
   }
 }
 
-template <int BM, int STAGES>
+template <int BM, int STAGES, bool SITU>
 __global__ __launch_bounds__(256, 1) void gemm1_pp_kernel(GemmParams p) {
   constexpr int kStage = (BM + kLgCh) * 64;
   constexpr int TF = BM / 64;
@@ -484,11 +515,11 @@ __global__ __launch_bounds__(256, 1) void gemm1_pp_kernel(GemmParams p) {
   const int vr = min(BM, ti.row1 - ti.row0);
   const int wm = __builtin_amdgcn_readfirstlane(threadIdx.x >> 7);
   switch (valid_frags<TF>(vr, wm)) {
-    case 0: gemm1_pp_body<BM, STAGES, 0>(p, ti, smem); break;
-    case 1: gemm1_pp_body<BM, STAGES, 1>(p, ti, smem); break;
-    case 2: gemm1_pp_body<BM, STAGES, 2>(p, ti, smem); break;
-    case 3: if constexpr (TF >= 3) gemm1_pp_body<BM, STAGES, 3>(p, ti, smem); break;
-    default: if constexpr (TF >= 4) gemm1_pp_body<BM, STAGES, 4>(p, ti, smem); break;
+    case 0: gemm1_pp_body<BM, STAGES, 0, SITU>(p, ti, smem); break;
+    case 1: gemm1_pp_body<BM, STAGES, 1, SITU>(p, ti, smem); break;
+    case 2: gemm1_pp_body<BM, STAGES, 2, SITU>(p, ti, smem); break;
+    case 3: if constexpr (TF >= 3) gemm1_pp_body<BM, STAGES, 3, SITU>(p, ti, smem); break;
+    default: if constexpr (TF >= 4) gemm1_pp_body<BM, STAGES, 4, SITU>(p, ti, smem); break;
   }
 }
 
@@ -873,12 +904,14 @@ __device__ __forceinline__ void gemm1_small_body(const GemmParams& p, const Tile
     sg[0] = s1.x; sg[1] = s1.y; sg[2] = s1.z; sg[3] = s1.w;
     su[0] = s3.x; su[1] = s3.y; su[2] = s3.z; su[3] = s3.w;
   }
+  const bool use_situ = p.act[ti.wi] == kActSitu;
+  const float beta = p.beta[ti.wi];
   uint32_t b[4];
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
     const float g = gsum[v] * xs * sg[v];
     const float u = usum[v] * xs * su[v];
-    b[v] = bf16_rne(silu(g) * u);
+    b[v] = bf16_rne((use_situ ? situ(g, beta) : silu(g)) * u);
   }
   *reinterpret_cast<uint2*>(p.h + h_off(p.h_cs, grow, ch)) = make_uint2(b[0] | (b[1] << 16), b[2] | (b[3] << 16));
 }
@@ -1141,6 +1174,8 @@ hipError_t launch_gemm1(int variant, const FfnGroups& g, const RowOperand& x, co
     p.sa[i] = g.s1[i];
     p.sb[i] = g.s3[i];
     p.wd[i] = g.blocked[i] ? k_blocked_operand(g.inter, kW13Chunk) : row_major_operand(g.hidden);
+    p.act[i] = g.act[i];
+    p.beta[i] = g.beta[i];
   }
   p.h = h;
   p.h_cs = n_rows * kHChunk;
@@ -1155,10 +1190,10 @@ hipError_t launch_gemm1(int variant, const FfnGroups& g, const RowOperand& x, co
   } else {
     p.ntiles = g.inter / (kLgCh / 2);
     const long grid = max_row_tiles(n_rows, g.n_groups, bm) * p.ntiles;
-    if (variant == kVariantLarge256)
-      hipExtLaunchKernelGGL(gemm1_pp_kernel<256, 4>, dim3((unsigned)grid), dim3(256), 0, s, ev_start, ev_stop, 0, p);
-    else
-      hipExtLaunchKernelGGL(gemm1_pp_kernel<128, 6>, dim3((unsigned)grid), dim3(256), 0, s, ev_start, ev_stop, 0, p);
+    const bool situ = g.act[0] == kActSitu || (g.n_groups > g.n_routed && g.act[1] == kActSitu);
+    auto kern = variant == kVariantLarge256 ? (situ ? gemm1_pp_kernel<256, 4, true> : gemm1_pp_kernel<256, 4, false>)
+                                            : (situ ? gemm1_pp_kernel<128, 6, true> : gemm1_pp_kernel<128, 6, false>);
+    hipExtLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, s, ev_start, ev_stop, 0, p);
   }
   return hipGetLastError();
 }

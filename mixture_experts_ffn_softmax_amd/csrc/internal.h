@@ -41,7 +41,8 @@ constexpr int kHChunk = 64;
 constexpr int kW2Chunk = 32;
 
 // ---- router ---------------------------------------------------------------
-hipError_t launch_route(const float* logits, int T, int E, int k, int* ids, float* w,
+// sigmoid: scores 1 / (1 + e^-l) instead of the softmax; same selection.
+hipError_t launch_route(const float* logits, int T, int E, int k, bool sigmoid, int* ids, float* w,
                         hipStream_t s);
 
 // ---- counts, offsets, ranks, quantise + scatter ---------------------------
@@ -66,12 +67,13 @@ hipError_t launch_quant_scatter(const uint16_t* x, int T, int H, int k, const in
 // when tile_prefix is non-NULL, the tile prefix of the groups for row tiles
 // of bm, in one launch.  logits non-NULL (E <= kMetaRouteMaxE): routes first
 // and writes ids / w; logits NULL: reads ids.
-hipError_t launch_meta(const float* logits, int T, int E, int k, int* ids, float* w, int* counts,
+hipError_t launch_meta(const float* logits, bool sigmoid, int T, int E, int k, int* ids, float* w, int* counts,
                        int* offsets, int extra_rows, int* pair_to_row, int* row_to_pair, int* tile_prefix,
                        int bm, hipStream_t s);
 
 // ---- grouped expert FFN ---------------------------------------------------
 enum WeightFormat { kFp8 = 0, kMxfp4 = 1 };
+enum Activation { kActSilu = 0, kActSitu = 1 };   // gate activation of an expert group
 
 // One grouped GEMM launch covers groups 0..n_groups-1.  Rows of group g are
 // offsets[g] .. offsets[g+1]-1 of the row operand.  Groups g < n_routed take
@@ -92,6 +94,8 @@ struct FfnGroups {
   const void* s3[2];
   const void* s2[2];
   bool blocked[2];    // weights K-blocked (moe_pack_weights) rather than row-major
+  int act[2];         // Activation of the routed / shared group
+  float beta[2];      // SiTU's beta of the routed / shared group
 };
 
 // Row operand of a grouped GEMM: GEMM1 reads e4m3 codes q with per-row

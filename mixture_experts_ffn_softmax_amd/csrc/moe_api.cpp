@@ -68,6 +68,12 @@ moe_status_t check_route_shape(int32_t T, int32_t E, int32_t k) {
   return MOE_OK;
 }
 
+moe_status_t check_score(int32_t score) {
+  if (score != MOE_SCORE_SOFTMAX && score != MOE_SCORE_SIGMOID)
+    return fail(MOE_ERR_UNSUPPORTED, "unknown router score function %d", score);
+  return MOE_OK;
+}
+
 moe_status_t check_dim(int32_t v, const char* name) {
   if (v < 128 || v > kMaxDim || v % 128 != 0)
     return fail(MOE_ERR_SHAPE, "%s = %d is not a multiple of 128 in [128, %d]", name, v, kMaxDim);
@@ -87,6 +93,10 @@ moe_status_t check_weights(const moe_weights_t* w, const char* name) {
   if (w->layout == MOE_LAYOUT_K_BLOCKED && w->fmt != MOE_W_FP8_E4M3_PERCHANNEL)
     return fail(MOE_ERR_UNSUPPORTED, "%s: the K-blocked layout exists for fp8 weights only", name);
   if (w->reserved != 0) return fail(MOE_ERR_SHAPE, "%s: reserved field must be 0", name);
+  if (w->activation != MOE_ACT_SILU && w->activation != MOE_ACT_SITU)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: unknown activation %d", name, w->activation);
+  if (w->activation == MOE_ACT_SITU && !(w->act_beta > 0.0f && w->act_beta <= 3.0e38f))
+    return fail(MOE_ERR_SHAPE, "%s: SiTU needs a finite act_beta > 0", name);
   MOE_CHECK(need(w->w1, "w1"));
   MOE_CHECK(need(w->w3, "w3"));
   MOE_CHECK(need(w->w2, "w2"));
@@ -126,6 +136,8 @@ moe::FfnGroups make_groups(const moe_weights_t* r, const moe_weights_t* sh, cons
   g.offsets = offsets;
   const moe_weights_t* src[2] = {r, sh ? sh : r};
   for (int i = 0; i < 2; ++i) {
+    g.act[i] = src[i]->activation == MOE_ACT_SITU ? moe::kActSitu : moe::kActSilu;
+    g.beta[i] = src[i]->act_beta;
     g.w1[i] = src[i]->w1;
     g.w3[i] = src[i]->w3;
     g.w2[i] = src[i]->w2;
@@ -188,14 +200,16 @@ const char* moe_status_string(moe_status_t s) {
 const char* moe_last_error(void) { return g_last_error.c_str(); }
 
 // ---------------------------------------------------------------------------
-moe_status_t moe_route(const float* logits, int32_t T, int32_t E, int32_t top_k, int32_t* topk_ids,
-                       float* topk_w, void* stream) {
+moe_status_t moe_route(const float* logits, int32_t T, int32_t E, int32_t top_k, int32_t score,
+                       int32_t* topk_ids, float* topk_w, void* stream) {
   MOE_CHECK(check_route_shape(T, E, top_k));
+  MOE_CHECK(check_score(score));
   if (T == 0) return ok();
   MOE_CHECK(need(logits, "logits"));
   MOE_CHECK(need(topk_ids, "topk_ids"));
   MOE_CHECK(need(topk_w, "topk_w"));
-  return device_status(moe::launch_route(logits, T, E, top_k, topk_ids, topk_w, (hipStream_t)stream),
+  return device_status(moe::launch_route(logits, T, E, top_k, score == MOE_SCORE_SIGMOID, topk_ids, topk_w,
+                                         (hipStream_t)stream),
                        "route");
 }
 
@@ -242,7 +256,7 @@ moe_status_t moe_permute(const uint16_t* x, int32_t T, int32_t H, const int32_t*
   hipError_t e;
   if (T > 0 && pairs <= moe::kMetaMaxPairs) {
     // reads topk_ids only (no logits): the const is not written through
-    e = moe::launch_meta(nullptr, T, E, top_k, const_cast<int32_t*>(topk_ids), nullptr, expert_counts,
+    e = moe::launch_meta(nullptr, false, T, E, top_k, const_cast<int32_t*>(topk_ids), nullptr, expert_counts,
                          expert_offsets, 0, pair_to_row, row_to_pair, nullptr, 0, s);
     if (e != hipSuccess) return device_status(e, "meta");
   } else {
@@ -352,12 +366,14 @@ size_t moe_forward_workspace_size(int32_t T, int32_t top_k, const moe_weights_t*
 }
 
 moe_status_t moe_forward(const uint16_t* x, const float* logits, int32_t T, int32_t top_k,
-                         const moe_weights_t* routed, int32_t use_shared, const moe_weights_t* shared,
+                         int32_t score, const moe_weights_t* routed, int32_t use_shared, const moe_weights_t* shared,
                          const float* norm_gamma, float norm_eps, uint16_t* out, moe_debug_t* dbg,
                          void* ws, size_t ws_bytes, void* stream) {
   MOE_CHECK(check_weights(routed, "routed"));
   const int32_t E = routed->n_experts, H = routed->hidden, I = routed->inter;
   MOE_CHECK(check_route_shape(T, E, top_k));
+  MOE_CHECK(check_score(score));
+  const bool sigmoid = score == MOE_SCORE_SIGMOID;
   if (use_shared) {
     MOE_CHECK(check_weights(shared, "shared"));
     if (shared->n_experts != 1) return fail(MOE_ERR_SHAPE, "shared expert must have n_experts = 1");
@@ -417,15 +433,15 @@ moe_status_t moe_forward(const uint16_t* x, const float* logits, int32_t T, int3
   const bool fused_route = meta && E <= moe::kMetaRouteMaxE && T <= moe::kMetaRouteMaxT;
   if (ev && ev[MOE_STAGE_ROUTE]) hipEventRecord((hipEvent_t)ev[MOE_STAGE_ROUTE], s);
   if (!fused_route) {
-    e = moe::launch_route(logits, T, E, top_k, L.ids, L.w, s);
+    e = moe::launch_route(logits, T, E, top_k, sigmoid, L.ids, L.w, s);
     if (e != hipSuccess) return device_status(e, "route");
   }
 
   if (ev && ev[MOE_STAGE_PERMUTE]) hipEventRecord((hipEvent_t)ev[MOE_STAGE_PERMUTE], s);
   if (meta) {
     const int bm = moe::variant_rows(moe::choose_variant(g, rows));
-    e = moe::launch_meta(fused_route ? logits : nullptr, T, E, top_k, L.ids, L.w, L.counts, L.offsets,
-                         sh ? T : 0, L.p2r, L.r2p, L.tile_prefix, bm, s);
+    e = moe::launch_meta(fused_route ? logits : nullptr, sigmoid, T, E, top_k, L.ids, L.w, L.counts,
+                         L.offsets, sh ? T : 0, L.p2r, L.r2p, L.tile_prefix, bm, s);
     if (e != hipSuccess) return device_status(e, "meta");
   } else {
     e = moe::launch_counts(L.ids, (int)R, E, L.hist, L.base, L.counts, L.offsets, sh ? T : 0, s);

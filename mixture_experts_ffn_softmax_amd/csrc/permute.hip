@@ -233,7 +233,7 @@ constexpr int kMetaChunk = kMetaWaves * 256;   // pairs per rank chunk: 4 per la
 // the same selection (largest logit first, ties to the lower id) and weight
 // arithmetic as route_kernel.
 template <int NE>
-__device__ __forceinline__ void meta_route(const float* __restrict__ logits, int T, int E, int k,
+__device__ __forceinline__ void meta_route(const float* __restrict__ logits, bool sigmoid, int T, int E, int k,
                                            int* __restrict__ ids, float* __restrict__ w, int* s_ids) {
   for (int t = threadIdx.x; t < T; t += blockDim.x) {
     float v[NE];
@@ -254,7 +254,7 @@ __device__ __forceinline__ void meta_route(const float* __restrict__ logits, int
         }
       avail &= ~(1u << bi);
       if (j == 0) vmax = bv;
-      ex[j] = expf(bv - vmax);
+      ex[j] = sigmoid ? 1.0f / (1.0f + expf(-bv)) : expf(bv - vmax);
       sum += ex[j];
       ids[(long)t * k + j] = bi;
       s_ids[t * k + j] = bi;
@@ -315,7 +315,8 @@ __device__ __forceinline__ void wave_match4(const int (&e)[4], uint64_t lt_mask,
   }
 }
 
-__global__ __launch_bounds__(1024) void meta_kernel(const float* __restrict__ logits, int T, int E, int k,
+__global__ __launch_bounds__(1024) void meta_kernel(const float* __restrict__ logits, bool sigmoid, int T,
+                                                    int E, int k,
                                                     int* __restrict__ ids, float* __restrict__ w,
                                                     int* __restrict__ counts, int* __restrict__ offsets,
                                                     int extra_rows, int* __restrict__ pair_to_row,
@@ -332,9 +333,9 @@ __global__ __launch_bounds__(1024) void meta_kernel(const float* __restrict__ lo
 
   for (int x = tid; x < E; x += 1024) s_tot[x] = 0;
   if (logits) {
-    if (E <= 8) meta_route<8>(logits, T, E, k, ids, w, s_ids);
-    else if (E <= 16) meta_route<16>(logits, T, E, k, ids, w, s_ids);
-    else meta_route<kMetaRouteMaxE>(logits, T, E, k, ids, w, s_ids);
+    if (E <= 8) meta_route<8>(logits, sigmoid, T, E, k, ids, w, s_ids);
+    else if (E <= 16) meta_route<16>(logits, sigmoid, T, E, k, ids, w, s_ids);
+    else meta_route<kMetaRouteMaxE>(logits, sigmoid, T, E, k, ids, w, s_ids);
   } else {
     for (int p = tid; p < R; p += 1024) s_ids[p] = ids[p];
   }
@@ -462,10 +463,10 @@ hipError_t launch_quant_scatter(const uint16_t* x, int T, int H, int k, const in
   return hipGetLastError();
 }
 
-hipError_t launch_meta(const float* logits, int T, int E, int k, int* ids, float* w, int* counts,
+hipError_t launch_meta(const float* logits, bool sigmoid, int T, int E, int k, int* ids, float* w, int* counts,
                        int* offsets, int extra_rows, int* pair_to_row, int* row_to_pair, int* tile_prefix,
                        int bm, hipStream_t s) {
-  meta_kernel<<<1, 1024, 0, s>>>(logits, T, E, k, ids, w, counts, offsets, extra_rows, pair_to_row,
+  meta_kernel<<<1, 1024, 0, s>>>(logits, sigmoid, T, E, k, ids, w, counts, offsets, extra_rows, pair_to_row,
                                  row_to_pair, tile_prefix, bm);
   return hipGetLastError();
 }

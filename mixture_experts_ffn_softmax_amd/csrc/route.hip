@@ -5,7 +5,9 @@
 // to the lower index and the slots come out in descending order.  The raw
 // fp32 logits decide the selection, which therefore does not depend on the
 // rounding of exp.  Weights: w_j = exp(l_j - l_max) / sum_sel exp(l - l_max),
-// which equals p_j / sum_sel p for p = softmax over all experts.
+// which equals p_j / sum_sel p for p = softmax over all experts; with the
+// sigmoid score (the Kimi K3 page, §2.4) p_j = 1 / (1 + e^-l_j), which is
+// increasing in the logit too, so the selection is the same.
 // Top-8 of 256 routed experts on the Ling-2.6-1T page (overview, §1 cost
 // model); renormalised top-k weights on the Kimi K3 page, §2.4.
 #include <math.h>
@@ -22,7 +24,7 @@ __device__ __forceinline__ bool route_better(float va, int ia, float vb, int ib)
 }
 
 __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ logits, int T, int E,
-                                                    int k, int* __restrict__ ids,
+                                                    int k, bool sigmoid, int* __restrict__ ids,
                                                     float* __restrict__ w) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -64,7 +66,7 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
     }
     if ((bi & 63) == lane) avail &= ~(1u << (bi >> 6));
     if (j == 0) vmax = bv;
-    const float ex = expf(bv - vmax);
+    const float ex = sigmoid ? 1.0f / (1.0f + expf(-bv)) : expf(bv - vmax);
     sum += ex;
     if (lane == j) {
       my_id = bi;
@@ -77,10 +79,10 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
   }
 }
 
-hipError_t launch_route(const float* logits, int T, int E, int k, int* ids, float* w,
+hipError_t launch_route(const float* logits, int T, int E, int k, bool sigmoid, int* ids, float* w,
                         hipStream_t s) {
   if (T == 0) return hipSuccess;
-  route_kernel<<<(T + 3) / 4, 256, 0, s>>>(logits, T, E, k, ids, w);
+  route_kernel<<<(T + 3) / 4, 256, 0, s>>>(logits, T, E, k, sigmoid, ids, w);
   return hipGetLastError();
 }
 

@@ -42,11 +42,12 @@ class DeviceStack:
         return self.t[e].cpu().numpy()
 
 
-def oracle_weights(d, fmt, lazy=False):
+def oracle_weights(d, fmt, lazy=False, activation="silu", beta=4.0):
     if d is None:
         return None
     wrap = DeviceStack if lazy else host
-    return ExpertWeights(fmt, *(wrap(d[k]) for k in ("w1", "w3", "w2", "s1", "s3", "s2")))
+    return ExpertWeights(fmt, *(wrap(d[k]) for k in ("w1", "w3", "w2", "s1", "s3", "s2")),
+                         activation=activation, beta=beta)
 
 
 def tolerance_ratio(gpu, oracle_exact):
@@ -75,15 +76,17 @@ def assert_weights_close(w_gpu, w_oracle):
     assert err.max() <= W_RTOL, err.max()
 
 
-def run_forward(inp, capture=True, pack=True):
+def run_forward(inp, capture=True, pack=True, score="softmax", act=("silu", "silu"), beta=4.0):
     """moe_forward on device inputs; returns (out, captured dict, variant).
-    pack=False keeps fp8 weights row-major instead of K-blocked."""
+    pack=False keeps fp8 weights row-major instead of K-blocked; ``act``:
+    activation of the routed and of the shared experts."""
     import mixture_experts_ffn_softmax_amd as moe
 
     c = inp["cfg"]
     T, E, k, H = c["T"], c["E"], c["k"], c["H"]
-    routed = moe.Weights(inp["routed"], c["fmt"], pack=pack)
-    shared = moe.Weights(inp["shared"], "fp8", pack=pack) if inp["shared"] is not None else None
+    routed = moe.Weights(inp["routed"], c["fmt"], pack=pack, activation=act[0], beta=beta)
+    shared = (moe.Weights(inp["shared"], "fp8", pack=pack, activation=act[1], beta=beta)
+              if inp["shared"] is not None else None)
     dbg = None
     if capture:
         z = lambda shape, dt: torch.empty(shape, dtype=dt, device=DEV)  # noqa: E731
@@ -92,7 +95,8 @@ def run_forward(inp, capture=True, pack=True):
                    expert_offsets=z((E + (2 if shared else 1),), torch.int32),
                    pair_to_row=z((T, k), torch.int32), row_to_pair=z((T * k,), torch.int32),
                    xq_rows=z((T * k, H), torch.uint8), xs_rows=z((T * k,), torch.float32))
-    res = moe.moe_forward(inp["x"], inp["logits"], k, routed, shared, inp["gamma"], inp["eps"], debug=dbg)
+    res = moe.moe_forward(inp["x"], inp["logits"], k, routed, shared, inp["gamma"], inp["eps"], debug=dbg,
+                          score=score)
     out, variant = res if capture else (res, None)
     torch.cuda.synchronize()
     return out, dbg, variant

@@ -62,20 +62,21 @@ def test_struct_layouts(tmp_path):
     src = tmp_path / "layout.c"
     src.write_text(
         '#include <stddef.h>\n#include <stdio.h>\n#include "moe.h"\n'
-        'int main(void) { printf("%zu %zu %zu %zu %zu %zu %zu %zu\\n", sizeof(moe_weights_t),'
+        'int main(void) { printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu\\n", sizeof(moe_weights_t),'
         ' offsetof(moe_weights_t, w1), offsetof(moe_weights_t, s2), sizeof(moe_debug_t),'
         ' offsetof(moe_debug_t, events), offsetof(moe_debug_t, variant),'
-        ' offsetof(moe_debug_t, gemm1_events), offsetof(moe_debug_t, gemm2_events)); return 0; }\n')
+        ' offsetof(moe_debug_t, gemm1_events), offsetof(moe_debug_t, gemm2_events),'
+        ' offsetof(moe_weights_t, act_beta)); return 0; }\n')
     exe = tmp_path / "layout"
     subprocess.run([gcc, "-std=c99", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
     got = [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
     assert got == [ctypes.sizeof(MoeWeights), MoeWeights.w1.offset, MoeWeights.s2.offset,
                    ctypes.sizeof(MoeDebug), MoeDebug.events.offset, MoeDebug.variant.offset,
-                   MoeDebug.gemm1_events.offset, MoeDebug.gemm2_events.offset]
+                   MoeDebug.gemm1_events.offset, MoeDebug.gemm2_events.offset, MoeWeights.act_beta.offset]
 
 
 def fp8_weights(E=8, H=256, I=128, fmt=0, layout=0, **over):
-    w = MoeWeights(fmt, E, H, I, layout, 0, A, A, A, A, A, A)
+    w = MoeWeights(fmt, E, H, I, layout, 0, 4.0, 0, A, A, A, A, A, A)
     for k, v in over.items():
         setattr(w, k, v)
     return w
@@ -83,16 +84,17 @@ def fp8_weights(E=8, H=256, I=128, fmt=0, layout=0, **over):
 
 def test_route_validation(lib):
     r = lib.moe_route
-    assert r(A, -1, 8, 2, A, A, None) == MOE_ERR_SHAPE
-    assert r(A, 4, 0, 1, A, A, None) == MOE_ERR_SHAPE
-    assert r(A, 4, 1025, 1, A, A, None) == MOE_ERR_SHAPE
-    assert r(A, 4, 8, 9, A, A, None) == MOE_ERR_SHAPE          # k > E
-    assert r(A, 4, 64, 33, A, A, None) == MOE_ERR_SHAPE         # k > 32
-    assert r(A, 1 << 30, 8, 2, A, A, None) == MOE_ERR_SHAPE     # T*k overflows
-    assert r(None, 4, 8, 2, A, A, None) == MOE_ERR_NULL
+    assert r(A, -1, 8, 2, 0, A, A, None) == MOE_ERR_SHAPE
+    assert r(A, 4, 0, 1, 0, A, A, None) == MOE_ERR_SHAPE
+    assert r(A, 4, 1025, 1, 0, A, A, None) == MOE_ERR_SHAPE
+    assert r(A, 4, 8, 9, 0, A, A, None) == MOE_ERR_SHAPE          # k > E
+    assert r(A, 4, 64, 33, 0, A, A, None) == MOE_ERR_SHAPE         # k > 32
+    assert r(A, 1 << 30, 8, 2, 0, A, A, None) == MOE_ERR_SHAPE     # T*k overflows
+    assert r(None, 4, 8, 2, 0, A, A, None) == MOE_ERR_NULL
     assert b"logits" in lib.moe_last_error()
-    assert r(A, 4, 8, 2, MIS, A, None) == MOE_ERR_ALIGN
-    assert r(A, 0, 8, 2, None, None, None) == MOE_OK            # T = 0: nothing to do
+    assert r(A, 4, 8, 2, 0, MIS, A, None) == MOE_ERR_ALIGN
+    assert r(A, 4, 8, 2, 2, A, A, None) == MOE_ERR_UNSUPPORTED  # unknown score function
+    assert r(A, 0, 8, 2, 0, None, None, None) == MOE_OK            # T = 0: nothing to do
     assert lib.moe_last_error() == b""
 
 
@@ -136,6 +138,9 @@ def test_expert_ffn_validation(lib):
     assert f(A, A, 64, A, ctypes.byref(fp8_weights(layout=2)), A, A, ws, None) == MOE_ERR_UNSUPPORTED
     assert f(A, A, 64, A, ctypes.byref(fp8_weights(fmt=1, layout=1)), A, A, ws, None) == MOE_ERR_UNSUPPORTED
     assert f(A, A, 64, A, ctypes.byref(fp8_weights(reserved=1)), A, A, ws, None) == MOE_ERR_SHAPE
+    assert f(A, A, 64, A, ctypes.byref(fp8_weights(activation=2)), A, A, ws, None) == MOE_ERR_UNSUPPORTED
+    assert f(A, A, 64, A, ctypes.byref(fp8_weights(activation=1, act_beta=0.0)), A, A, ws, None) == MOE_ERR_SHAPE
+    assert f(A, A, 64, A, ctypes.byref(fp8_weights(activation=1, act_beta=float("inf"))), A, A, ws, None) == MOE_ERR_SHAPE
     assert f(None, None, 0, None, ctypes.byref(w), None, None, 0, None) == MOE_OK
 
 
@@ -157,8 +162,8 @@ def test_forward_validation(lib):
     ws_sh = lib.moe_forward_workspace_size(16, 2, ctypes.byref(w), 1)
     assert ws_sh > ws
 
-    def call(T=16, k=2, routed=w, use_shared=0, shared=None, out=A, dbg=None, wsb=ws, x=A):
-        return fw(x, A, T, k, ctypes.byref(routed), use_shared,
+    def call(T=16, k=2, routed=w, use_shared=0, shared=None, out=A, dbg=None, wsb=ws, x=A, score=0):
+        return fw(x, A, T, k, score, ctypes.byref(routed), use_shared,
                   ctypes.byref(shared) if shared is not None else None, None, 1e-6, out,
                   ctypes.byref(dbg) if dbg is not None else None, A, wsb, None)
 
@@ -174,6 +179,7 @@ def test_forward_validation(lib):
     d.xq_rows = MIS
     assert call(dbg=d) == MOE_ERR_ALIGN
     assert call(routed=fp8_weights(E=1024), use_shared=1, shared=sh, wsb=1 << 40) == MOE_ERR_UNSUPPORTED
+    assert call(score=5) == MOE_ERR_UNSUPPORTED
     assert call(T=0) == MOE_OK
 
 

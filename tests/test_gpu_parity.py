@@ -54,6 +54,23 @@ def test_route(lib, case):
     assert_weights_close(host(w), ref_w)
 
 
+ROUTE_SIGMOID = ["tiny", "integer_ties", "signed_zeros", "all_equal", "E1024_k32", "latent_E896_k16", "E1"]
+
+
+@pytest.mark.parametrize("case", ROUTE_SIGMOID)
+def test_route_sigmoid(lib, case):
+    """Sigmoid scores: the same selection as the softmax, weights the
+    renormalised sigmoids of the selected logits."""
+    logits = ROUTE_CASES[case]().float().contiguous()
+    k = ROUTE_K[case]
+    say("route sigmoid", case, tuple(logits.shape), k)
+    ids, w = lib.moe_route(logits.to(DEV), k, score="sigmoid")
+    torch.cuda.synchronize()
+    ref_ids, ref_w = oracle.route(logits.numpy(), k, "sigmoid")
+    assert (host(ids) == ref_ids).all()
+    assert_weights_close(host(w), ref_w)
+
+
 # ----------------------------------------------------------------------------
 # permutation and quantisation (moe_permute)
 # ----------------------------------------------------------------------------
@@ -171,8 +188,48 @@ def test_forward_full(lib, case, pack):
     assert ratio <= OUT_TOL
 
 
+# Router and activation variants (sigmoid scores; SiTU gate activation):
+# name: (T, H, I, E, k, fmt, shared, norm, score, routed act, shared act, beta)
+VARIANT_CASES = {
+    # routing fused into the metadata kernel; small GEMM variant
+    "sigmoid_situ_small": (45, 384, 256, 6, 3, "fp8", False, False, "sigmoid", "situ", "silu", 4.0),
+    # routed SiTU next to a SiLU shared expert in one grouped launch
+    "sigmoid_situ_large_shared": (333, 512, 384, 3, 2, "fp8", True, False, "sigmoid", "situ", "silu", 4.0),
+    # 256-row tiles, both groups SiTU, another beta
+    "situ_large256_shared": (1000, 256, 256, 4, 2, "fp8", True, False, "softmax", "situ", "situ", 2.5),
+    # shared SiTU, routed SiLU
+    "sigmoid_shared_situ": (300, 256, 256, 4, 2, "fp8", True, False, "sigmoid", "silu", "situ", 4.0),
+    "sigmoid_situ_mxfp4_rmsnorm": (48, 256, 128, 8, 2, "mxfp4", False, True, "sigmoid", "situ", "silu", 4.0),
+    # router kernel, then the metadata kernel (more than 32 experts)
+    "sigmoid_situ_E64": (200, 128, 128, 64, 6, "fp8", False, False, "sigmoid", "situ", "silu", 4.0),
+    # router kernel and the grid-wide metadata kernels (18000 pairs)
+    "sigmoid_situ_many_tokens": (9000, 128, 128, 16, 2, "fp8", False, False, "sigmoid", "situ", "silu", 4.0),
+}
+
+
+@pytest.mark.parametrize("case", list(VARIANT_CASES))
+def test_forward_variants(lib, case):
+    T, H, I, E, k, fmt, shared, norm, score, act_r, act_s, beta = VARIANT_CASES[case]
+    inp = moe_synth.custom_inputs(T, H, I, E, k, fmt=fmt, seed=len(case) + 100, shared=shared, norm=norm)
+    if act_r == "situ" or act_s == "situ":
+        inp["x"] = (inp["x"].float() * 4.0).to(torch.bfloat16)   # gates well past beta
+    say("forward variant", case, VARIANT_CASES[case])
+    out, dbg, variant = run_forward(to_device(inp), score=score, act=(act_r, act_s), beta=beta)
+    say("  variant", variant)
+    ref = oracle.forward(bf16_np(inp["x"]), inp["logits"].numpy(), k,
+                         oracle_weights(inp["routed"], fmt, activation=act_r, beta=beta),
+                         oracle_weights(inp["shared"], "fp8", activation=act_s, beta=beta),
+                         None if inp["gamma"] is None else inp["gamma"].numpy(), inp["eps"], score=score)
+    check_metadata(dbg, ref, T, k, E, shared)
+    assert (host(dbg["xq_rows"]) == ref["xq_rows"]).all()
+    ratio = tolerance_ratio(bits(out), ref["out_exact"])
+    say("  max|err|/rms", ratio)
+    assert ratio <= OUT_TOL
+
+
+@pytest.mark.parametrize("score", ["softmax", "sigmoid"])
 @pytest.mark.parametrize("E,k", [(8, 2), (32, 5), (33, 3)])
-def test_forward_route_ties(lib, E, k):
+def test_forward_route_ties(lib, E, k, score):
     """Integer logits with many ties and signed zeros through moe_forward: at
     most 32 experts are routed inside the metadata kernel, more by the router
     kernel; both must break ties towards the lower expert id."""
@@ -183,10 +240,9 @@ def test_forward_route_ties(lib, E, k):
     logits[::7] = 0.0
     logits[1::7, ::2] = -0.0
     inp["logits"] = logits
-    say("forward route ties", E, k)
-    out, dbg, _ = run_forward(to_device(inp))
-    c = inp["cfg"]
-    ref = oracle.forward(bf16_np(inp["x"]), logits.numpy(), k, oracle_weights(inp["routed"], "fp8"))
+    say("forward route ties", E, k, score)
+    out, dbg, _ = run_forward(to_device(inp), score=score)
+    ref = oracle.forward(bf16_np(inp["x"]), logits.numpy(), k, oracle_weights(inp["routed"], "fp8"), score=score)
     check_metadata(dbg, ref, T, k, E, False)
     assert tolerance_ratio(bits(out), ref["out_exact"]) <= OUT_TOL
 
@@ -211,15 +267,21 @@ def test_forward_deterministic(lib):
 SAMPLED = {"prefill": 24, "decode": 64, "latent": 3, "skewed": 4}
 
 
-@pytest.mark.parametrize("name", list(SAMPLED))
-def test_forward_full_size(lib, name):
+FULL_SIZE_RUNS = [(name, "softmax", "silu") for name in SAMPLED] + [
+    ("latent", "sigmoid", "situ"),      # the LatentMoE layer with its own router and activation
+    ("prefill", "sigmoid", "situ"),
+]
+
+
+@pytest.mark.parametrize("name,score,act", FULL_SIZE_RUNS)
+def test_forward_full_size(lib, name, score, act):
     inp = moe_synth.make_inputs(name, device=DEV)
     c = inp["cfg"]
     T, E, k = c["T"], c["E"], c["k"]
-    say("forward full size", name, c)
-    out, dbg, variant = run_forward(inp)
+    say("forward full size", name, score, act, c)
+    out, dbg, variant = run_forward(inp, score=score, act=(act, act))
     say("  variant", variant)
-    ids, w = oracle.route(host(inp["logits"]), k)
+    ids, w = oracle.route(host(inp["logits"]), k, score)
     counts, offsets = oracle.expert_counts_offsets(ids, E)
     p2r, r2p, _, _ = oracle.permute_rows(ids, offsets, np.zeros((T, 1), np.uint8), np.zeros(T, np.float32))
     ref = dict(topk_ids=ids, topk_w=w, counts=counts, offsets=offsets, pair_to_row=p2r, row_to_pair=r2p)
@@ -236,8 +298,8 @@ def test_forward_full_size(lib, name):
         assert (host(dbg["xq_rows"][r_d]) == xq).all()
         assert (host(dbg["xs_rows"][r_d]).view(np.uint32) == xs.view(np.uint32)).all()
     ref_out = oracle.moe.forward_sampled(
-        bits(inp["x"]), None, k, oracle_weights(inp["routed"], c["fmt"], lazy=True), tokens,
-        shared=oracle_weights(inp["shared"], "fp8", lazy=True),
+        bits(inp["x"]), None, k, oracle_weights(inp["routed"], c["fmt"], lazy=True, activation=act), tokens,
+        shared=oracle_weights(inp["shared"], "fp8", lazy=True, activation=act),
         norm_gamma=None if inp["gamma"] is None else host(inp["gamma"]), norm_eps=inp["eps"],
         routing=(ids, w))
     ratio = tolerance_ratio(bits(out[tok_d]), ref_out)
@@ -261,25 +323,30 @@ def synthetic_rows(counts, H, seed):
     return q, s, offsets
 
 
-@pytest.mark.parametrize("counts,fmt,pack", [
-    ([5, 0, 17, 1, 40, 0, 3, 32], "fp8", True),    # small variant: ragged, empty experts
-    ([5, 0, 17, 1, 40, 0, 3, 32], "fp8", False),
-    ([300, 0, 129, 64, 1], "fp8", True),            # large variant
-    ([300, 0, 129, 64, 1], "fp8", False),
+@pytest.mark.parametrize("counts,fmt,pack,act", [
+    ([5, 0, 17, 1, 40, 0, 3, 32], "fp8", True, "silu"),    # small variant: ragged, empty experts
+    ([5, 0, 17, 1, 40, 0, 3, 32], "fp8", False, "silu"),
+    ([300, 0, 129, 64, 1], "fp8", True, "silu"),            # large variant
+    ([300, 0, 129, 64, 1], "fp8", False, "silu"),
     # 256-row tiles; the last tile of each group leaves 0..4 valid 32-row
     # fragments per wave row (rows mod 256 = 188, 34, 1, 33, 232, 88, 97)
-    ([700, 0, 290, 513, 33, 1000, 600, 97], "fp8", True),
-    ([9, 33, 0, 2, 16, 1, 0, 20], "mxfp4", False),
+    ([700, 0, 290, 513, 33, 1000, 600, 97], "fp8", True, "silu"),
+    ([9, 33, 0, 2, 16, 1, 0, 20], "mxfp4", False, "silu"),
+    # SiTU in each GEMM1 variant
+    ([5, 0, 17, 1, 40, 0, 3, 32], "fp8", True, "situ"),
+    ([300, 0, 129, 64, 1], "fp8", True, "situ"),
+    ([700, 0, 290, 513, 33, 1000, 600, 97], "fp8", True, "situ"),
+    ([9, 33, 0, 2, 16, 1, 0, 20], "mxfp4", False, "situ"),
 ])
-def test_expert_ffn(lib, counts, fmt, pack):
+def test_expert_ffn(lib, counts, fmt, pack, act):
     E, H, I = len(counts), 256, 256
-    say("expert_ffn", counts, fmt, "packed" if pack else "row-major")
+    say("expert_ffn", counts, fmt, "packed" if pack else "row-major", act)
     q, s, offsets = synthetic_rows(counts, H, seed=sum(counts))
     W = moe_synth.expert_weights(77, "cpu", fmt, E, H, I)
     y = lib.moe_expert_ffn(q.to(DEV), s.to(DEV), torch.as_tensor(offsets, device=DEV),
-                           lib.Weights(to_device(W), fmt, pack=pack))
+                           lib.Weights(to_device(W), fmt, pack=pack, activation=act))
     torch.cuda.synchronize()
-    y_ref = oracle.expert_ffn(q.numpy(), s.numpy(), offsets, oracle_weights(W, fmt))[0]
+    y_ref = oracle.expert_ffn(q.numpy(), s.numpy(), offsets, oracle_weights(W, fmt, activation=act))[0]
     ratio = tolerance_ratio(host(y), y_ref)
     say("  max|err|/rms", ratio)
     assert ratio <= OUT_TOL
