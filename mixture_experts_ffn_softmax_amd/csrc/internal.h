@@ -65,8 +65,9 @@ hipError_t launch_quant_scatter(const uint16_t* x, int T, int H, int k, const in
                                 bool blocked, uint8_t* xq_copy, hipStream_t s);
 // For T * k <= kMetaMaxPairs: counts, offsets (+ the extra group), ranks and,
 // when tile_prefix is non-NULL, the tile prefix of the groups for row tiles
-// of bm, in one launch.  logits non-NULL (E <= kMetaRouteMaxE): routes first
-// and writes ids / w; logits NULL: reads ids.
+// of bm, in one launch.  logits non-NULL (T <= kMetaRouteMaxT and
+// E <= kMetaRouteMaxE, else hipErrorInvalidValue): routes first, in one wave,
+// and writes ids / w; logits NULL: reads ids (16 waves).
 hipError_t launch_meta(const float* logits, bool sigmoid, int T, int E, int k, int* ids, float* w, int* counts,
                        int* offsets, int extra_rows, int* pair_to_row, int* row_to_pair, int* tile_prefix,
                        int bm, hipStream_t s);

@@ -14,11 +14,12 @@
 //                  in pair order -> pair_to_row / row_to_pair
 //   quant_scatter  per token: amax, scale, e4m3 codes, written to each of the
 //                  token's rows (and optionally in token order)
-//   meta_kernel    one workgroup doing all of the above (and, for at most
-//                  kMetaRouteMaxE experts, the routing; and the grouped
-//                  GEMMs' tile prefix) when there are at most kMetaMaxPairs
-//                  pairs: one launch instead of five for decode-sized
-//                  batches, where launch latency is the cost
+//   meta_kernel    one workgroup doing all of the above but the quantisation
+//                  (and the grouped GEMMs' tile prefix) when there are at
+//                  most kMetaMaxPairs pairs: one launch instead of four
+//   meta_wave_kernel  the same plus the routing in a single wave, for at most
+//                  kMetaRouteMaxT tokens and kMetaRouteMaxE experts
+//                  (decode-sized batches, where latency is the cost)
 // Rows are ordered by expert and, inside an expert, by pair index; this order
 // is unique, so the result is deterministic.  Expert ids outside [0, E) are
 // skipped (their pairs get row -1) so that no access leaves its buffer.
@@ -218,9 +219,7 @@ __global__ __launch_bounds__(1024) void quant_scatter_kernel(
 
 // ---------------------------------------------------------------------------
 // meta_kernel: one workgroup of 1024 threads (16 waves).
-//   1. ids: routed here (E <= kMetaRouteMaxE, one lane per token, the same
-//      selection and weight arithmetic as route_kernel) or read from `ids`;
-//      kept in LDS.
+//   1. ids read from `ids` into LDS.
 //   2. counts (LDS atomics: counts only), exclusive offsets, the optional
 //      extra group, and the tile prefix of the groups for row tiles of bm.
 //   3. ranks, chunk by chunk of 1024 pairs in pair order: each wave ranks its
@@ -228,40 +227,6 @@ __global__ __launch_bounds__(1024) void quant_scatter_kernel(
 //      wave counts into starting rows.
 constexpr int kMetaWaves = 16;
 constexpr int kMetaChunk = kMetaWaves * 256;   // pairs per rank chunk: 4 per lane
-
-// Routing inside the metadata kernel, one lane per token, for E <= NE experts:
-// the same selection (largest logit first, ties to the lower id) and weight
-// arithmetic as route_kernel.
-template <int NE>
-__device__ __forceinline__ void meta_route(const float* __restrict__ logits, bool sigmoid, int T, int E, int k,
-                                           int* __restrict__ ids, float* __restrict__ w, int* s_ids) {
-  for (int t = threadIdx.x; t < T; t += blockDim.x) {
-    float v[NE];
-    const float* row = logits + (long)t * E;
-#pragma unroll
-    for (int i = 0; i < NE; ++i) v[i] = (i < E) ? row[i] : 0.0f;
-    uint32_t avail = (E >= 32) ? 0xFFFFFFFFu : ((1u << E) - 1u);
-    float vmax = 0.0f, sum = 0.0f;
-    float ex[kMaxTopK];
-    for (int j = 0; j < k; ++j) {
-      float bv = -INFINITY;
-      int bi = 0x7FFFFFFF;
-#pragma unroll
-      for (int i = 0; i < NE; ++i)
-        if (((avail >> i) & 1u) && (v[i] > bv || (v[i] == bv && i < bi))) {
-          bv = v[i];
-          bi = i;
-        }
-      avail &= ~(1u << bi);
-      if (j == 0) vmax = bv;
-      ex[j] = sigmoid ? 1.0f / (1.0f + expf(-bv)) : expf(bv - vmax);
-      sum += ex[j];
-      ids[(long)t * k + j] = bi;
-      s_ids[t * k + j] = bi;
-    }
-    for (int j = 0; j < k; ++j) w[(long)t * k + j] = ex[j] / sum;
-  }
-}
 
 // Expert ids of pairs p0 .. p0+3 from LDS; -1 past the end or out of range.
 __device__ __forceinline__ void load_chunk_ids(const int* s_ids, int R, int E, int p0, int (&e)[4]) {
@@ -315,9 +280,7 @@ __device__ __forceinline__ void wave_match4(const int (&e)[4], uint64_t lt_mask,
   }
 }
 
-__global__ __launch_bounds__(1024) void meta_kernel(const float* __restrict__ logits, bool sigmoid, int T,
-                                                    int E, int k,
-                                                    int* __restrict__ ids, float* __restrict__ w,
+__global__ __launch_bounds__(1024) void meta_kernel(int T, int E, int k, const int* __restrict__ ids,
                                                     int* __restrict__ counts, int* __restrict__ offsets,
                                                     int extra_rows, int* __restrict__ pair_to_row,
                                                     int* __restrict__ row_to_pair, int* __restrict__ tile_prefix,
@@ -332,13 +295,7 @@ __global__ __launch_bounds__(1024) void meta_kernel(const float* __restrict__ lo
   const int R = T * k;
 
   for (int x = tid; x < E; x += 1024) s_tot[x] = 0;
-  if (logits) {
-    if (E <= 8) meta_route<8>(logits, sigmoid, T, E, k, ids, w, s_ids);
-    else if (E <= 16) meta_route<16>(logits, sigmoid, T, E, k, ids, w, s_ids);
-    else meta_route<kMetaRouteMaxE>(logits, sigmoid, T, E, k, ids, w, s_ids);
-  } else {
-    for (int p = tid; p < R; p += 1024) s_ids[p] = ids[p];
-  }
+  for (int p = tid; p < R; p += 1024) s_ids[p] = ids[p];
   __syncthreads();
 
   // ---- counts, offsets, tile prefix.  Counts come from the same wave-level
@@ -423,6 +380,146 @@ __global__ __launch_bounds__(1024) void meta_kernel(const float* __restrict__ lo
   }
 }
 
+// meta_wave_kernel: the same results as meta_kernel with routing, for at
+// most kMetaRouteMaxT tokens and kMetaRouteMaxE experts, in ONE wave with no
+// workgroup barrier between its phases (decode-sized batches, where each
+// phase of the 16-wave kernel costs a barrier and a memory round trip).
+// Lane l routes tokens l, l + 64, ... (chunk i = t / 64) and keeps each
+// token's expert set as a bit mask.  A token picks distinct experts, so the
+// rank of pair (t, j) among the pairs of its expert e is the number of
+// earlier tokens that picked e: the pairs of chunks before i plus a popcount
+// of the ballot of e over chunk i below lane t % 64.
+constexpr int kWaveChunks = kMetaRouteMaxT / 64;
+
+template <int NE>
+__device__ __forceinline__ uint32_t wave_route_token(const float* __restrict__ logits, bool sigmoid, int t,
+                                                     int E, int k, int* __restrict__ ids,
+                                                     float* __restrict__ w, int* s_ids) {
+  float v[NE];
+  const float* row = logits + (long)t * E;
+#pragma unroll
+  for (int i = 0; i < NE; ++i) v[i] = (i < E) ? row[i] : 0.0f;
+  uint32_t avail = (E >= 32) ? 0xFFFFFFFFu : ((1u << E) - 1u);
+  const uint32_t all = avail;
+  float vmax = 0.0f, sum = 0.0f;
+  float ex[kMaxTopK];
+  for (int j = 0; j < k; ++j) {
+    float bv = -INFINITY;
+    int bi = 0x7FFFFFFF;
+#pragma unroll
+    for (int i = 0; i < NE; ++i)
+      if (((avail >> i) & 1u) && (v[i] > bv || (v[i] == bv && i < bi))) {
+        bv = v[i];
+        bi = i;
+      }
+    avail &= ~(1u << bi);
+    if (j == 0) vmax = bv;
+    ex[j] = sigmoid ? 1.0f / (1.0f + expf(-bv)) : expf(bv - vmax);
+    sum += ex[j];
+    ids[(long)t * k + j] = bi;
+    s_ids[t * k + j] = bi;
+  }
+  for (int j = 0; j < k; ++j) w[(long)t * k + j] = ex[j] / sum;
+  return all & ~avail;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(v, d, 64);
+    if (lane >= d) v += o;
+  }
+  return v;
+}
+
+__global__ __launch_bounds__(64) void meta_wave_kernel(const float* __restrict__ logits, bool sigmoid, int T,
+                                                       int E, int k, int* __restrict__ ids,
+                                                       float* __restrict__ w, int* __restrict__ counts,
+                                                       int* __restrict__ offsets, int extra_rows,
+                                                       int* __restrict__ pair_to_row,
+                                                       int* __restrict__ row_to_pair,
+                                                       int* __restrict__ tile_prefix, int bm) {
+  __shared__ int s_ids[kMetaRouteMaxT * kMaxTopK];
+  __shared__ uint64_t s_m[kMetaRouteMaxE * kWaveChunks];   // ballot of expert e over chunk i
+  __shared__ int s_base[kMetaRouteMaxE * kWaveChunks];     // first row of chunk i's pairs of e
+  const int lane = threadIdx.x;
+  const int nch = (T + 63) >> 6;
+
+  // ---- route; the expert set of each of this lane's tokens
+  uint32_t set[kWaveChunks];
+#pragma unroll
+  for (int i = 0; i < kWaveChunks; ++i) {
+    const int t = i * 64 + lane;
+    set[i] = 0;
+    if (t < T) {
+      if (E <= 8) set[i] = wave_route_token<8>(logits, sigmoid, t, E, k, ids, w, s_ids);
+      else if (E <= 16) set[i] = wave_route_token<16>(logits, sigmoid, t, E, k, ids, w, s_ids);
+      else set[i] = wave_route_token<kMetaRouteMaxE>(logits, sigmoid, t, E, k, ids, w, s_ids);
+    }
+  }
+
+  // ---- per expert and chunk: the ballot of the tokens that picked it
+  for (int e = 0; e < E; ++e) {
+#pragma unroll
+    for (int i = 0; i < kWaveChunks; ++i) {
+      if (i < nch) {
+        const uint64_t m = __ballot((set[i] >> e) & 1u);
+        if (lane == 0) s_m[e * kWaveChunks + i] = m;
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- lane e: count, offset (scan over the lanes), chunk bases
+  int c[kWaveChunks];
+  int cnt = 0;
+#pragma unroll
+  for (int i = 0; i < kWaveChunks; ++i) {
+    c[i] = (lane < E && i < nch) ? (int)__popcll(s_m[lane * kWaveChunks + i]) : 0;
+    cnt += c[i];
+  }
+  const int incl = wave_inclusive_scan(cnt);
+  const int total = __shfl(incl, E - 1, 64);
+  const int off = incl - cnt;
+  if (lane < E) {
+    counts[lane] = cnt;
+    offsets[lane] = off;
+    int run = off;
+#pragma unroll
+    for (int i = 0; i < kWaveChunks; ++i) {
+      s_base[lane * kWaveChunks + i] = run;
+      run += c[i];
+    }
+  }
+  if (lane == 0) {
+    offsets[E] = total;
+    if (extra_rows > 0) offsets[E + 1] = total + extra_rows;
+  }
+  if (tile_prefix) {
+    const int G = E + (extra_rows > 0 ? 1 : 0);
+    const int rows = (lane < E) ? cnt : (lane == E ? extra_rows : 0);
+    const int tiles = (lane < G && rows > 0) ? (rows + bm - 1) / bm : 0;
+    const int tincl = wave_inclusive_scan(tiles);
+    if (lane < G) tile_prefix[lane] = tincl - tiles;
+    if (lane == G - 1) tile_prefix[G] = tincl;
+  }
+  __syncthreads();
+
+  // ---- rows, in pair order (coalesced pair_to_row)
+  const int R = T * k;
+  for (int p = lane; p < R; p += 64) {
+    const int t = p / k;
+    const int e = s_ids[p];
+    const int i = t >> 6, tl = t & 63;
+    const uint64_t below = (tl == 0) ? 0ull : (~0ull >> (64 - tl));
+    const int row = s_base[e * kWaveChunks + i] + (int)__popcll(s_m[e * kWaveChunks + i] & below);
+    pair_to_row[p] = row;
+    row_to_pair[row] = p;
+  }
+}
+
 hipError_t launch_counts(const int* ids, int pairs, int E, int* chunk_hist, int* chunk_base,
                          int* counts, int* offsets, int extra_rows, hipStream_t s) {
   const int chunks = permute_chunks(pairs);
@@ -466,8 +563,14 @@ hipError_t launch_quant_scatter(const uint16_t* x, int T, int H, int k, const in
 hipError_t launch_meta(const float* logits, bool sigmoid, int T, int E, int k, int* ids, float* w, int* counts,
                        int* offsets, int extra_rows, int* pair_to_row, int* row_to_pair, int* tile_prefix,
                        int bm, hipStream_t s) {
-  meta_kernel<<<1, 1024, 0, s>>>(logits, sigmoid, T, E, k, ids, w, counts, offsets, extra_rows, pair_to_row,
-                                 row_to_pair, tile_prefix, bm);
+  if (logits && T <= kMetaRouteMaxT && E <= kMetaRouteMaxE) {
+    meta_wave_kernel<<<1, 64, 0, s>>>(logits, sigmoid, T, E, k, ids, w, counts, offsets, extra_rows, pair_to_row,
+                                      row_to_pair, tile_prefix, bm);
+    return hipGetLastError();
+  }
+  if (logits) return hipErrorInvalidValue;   // routing needs T <= kMetaRouteMaxT, E <= kMetaRouteMaxE
+  meta_kernel<<<1, 1024, 0, s>>>(T, E, k, ids, counts, offsets, extra_rows, pair_to_row, row_to_pair,
+                                 tile_prefix, bm);
   return hipGetLastError();
 }
 

@@ -155,6 +155,10 @@ FULL_CASES = {
     "one_token": (1, 128, 128, 16, 4, "fp8", True, False),
     # 18000 pairs: routing and metadata by the grid-wide kernels
     "many_tokens": (9000, 128, 128, 16, 2, "fp8", False, False),
+    # single-wave routing + metadata: its largest batch (4 token chunks, 32
+    # experts, 8 slots) and a second chunk holding one token
+    "meta_wave_T256_E32_k8": (256, 128, 128, 32, 8, "fp8", True, False),
+    "meta_wave_T65": (65, 128, 128, 5, 2, "fp8", False, False),
 }
 
 
