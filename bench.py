@@ -127,13 +127,13 @@ class Layer:
         self.ws = torch.empty((nbytes,), dtype=torch.uint8, device="cuda")
         self.moe = moe
 
-    def step(self, i, events=None, gemm_events=None):
+    def step(self, i, events=None, gemm_events=None, layer_events=None):
         j = i % len(self.routed)
         g = gemm_events or (None, None)
         self.moe.moe_forward(self.inp["x"], self.inp["logits"], self.k, self.routed[j],
                              None if self.shared is None else self.shared[j], self.inp["gamma"],
                              self.inp["eps"], out=self.out, ws=self.ws, events=events,
-                             gemm1_events=g[0], gemm2_events=g[1])
+                             gemm1_events=g[0], gemm2_events=g[1], layer_events=layer_events)
 
     def flops(self):
         rows = self.T * self.k + (self.T if self.shared is not None else 0)
@@ -163,27 +163,40 @@ def make_events(n):
 
 
 def time_layer(layer, steps, warmup):
-    """Times `steps` steps after `warmup` untimed ones.  Returns (ms per step by
-    the host clock between synchronisations, ms per step by GPU events around
-    the whole region, average GEMM1 and GEMM2 launch ms).  The only events
-    inside the region are the pairs the two GEMMs' own dispatches stamp."""
+    """Times `steps` steps after `warmup` untimed ones.  Returns a dict: ms per
+    step by the host clock between synchronisations (`ms`), by GPU events
+    around the whole region (`gpu_ms`), the per-layer durations (`layer_ms`,
+    a list) from the start/stop events the layer's own first and last
+    dispatches stamp, and the average GEMM1 / GEMM2 launch ms (`g1_ms`,
+    `g2_ms`) from the events their dispatches stamp.  Dispatch-stamped events
+    add no packets to the stream; the region's two records are outside the
+    layers."""
     import torch
     for i in range(warmup):
         layer.step(i)
     torch.cuda.synchronize()
-    ge = [(make_events(2), make_events(2)) for _ in range(steps)]
+    ge = [(make_events(2), make_events(2), make_events(2)) for _ in range(steps)]
     region = make_events(2)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     region[0].record()
     for i in range(steps):
-        layer.step(i, gemm_events=ge[i])
+        layer.step(i, gemm_events=ge[i][:2], layer_events=ge[i][2])
     region[1].record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    g1_ms = sum(a.elapsed_time(b) for (a, b), _ in ge) / steps
-    g2_ms = sum(a.elapsed_time(b) for _, (a, b) in ge) / steps
-    return (t1 - t0) * 1e3 / steps, region[0].elapsed_time(region[1]) / steps, g1_ms, g2_ms
+    return dict(ms=(t1 - t0) * 1e3 / steps, gpu_ms=region[0].elapsed_time(region[1]) / steps,
+                layer_ms=[c[0].elapsed_time(c[1]) for _, _, c in ge],
+                g1_ms=sum(a.elapsed_time(b) for (a, b), _, _ in ge) / steps,
+                g2_ms=sum(a.elapsed_time(b) for _, (a, b), _ in ge) / steps)
+
+
+def percentiles_us(ms_list):
+    """Median, p10 and p90 of per-layer durations, in microseconds."""
+    import numpy as np
+    a = np.asarray(ms_list) * 1e3
+    return {"median": round(float(np.median(a)), 1), "p10": round(float(np.percentile(a, 10)), 1),
+            "p90": round(float(np.percentile(a, 90)), 1)}
 
 
 def stage_times(layer, steps):
@@ -258,7 +271,8 @@ def main():
     layer = Layer(args.config, args.copies)
     c = layer.cfg
     log(f"[bench] timing {args.steps} steps after {args.warmup} warm-up")
-    ms, gpu_ms, g1_ms, g2_ms = time_layer(layer, args.steps, args.warmup)
+    tl = time_layer(layer, args.steps, args.warmup)
+    ms, gpu_ms, g1_ms, g2_ms = tl["ms"], tl["gpu_ms"], tl["g1_ms"], tl["g2_ms"]
     stage = stage_times(layer, min(args.steps, 20))
     flops, flops_g1 = layer.flops()
     flops_g2 = flops - flops_g1
@@ -279,6 +293,7 @@ def main():
         "ms_per_step": round(ms, 4),
         "us_per_layer": round(ms * 1e3, 1),
         "us_per_layer_gpu_events": round(gpu_ms * 1e3, 1),
+        "us_per_layer_dispatch_events": percentiles_us(tl["layer_ms"]),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -306,12 +321,14 @@ def main():
     if not args.no_decode:
         log("[bench] decode share (weight-stream bound)")
         dl = Layer("decode", args.copies)
-        dms, dgpu_ms, _, _ = time_layer(dl, max(args.steps, 50), args.warmup)
+        dtl = time_layer(dl, max(args.steps, 50), args.warmup)
+        dms, dgpu_ms = dtl["ms"], dtl["gpu_ms"]
         dstage = stage_times(dl, 20)
         dbytes, dio, dtouched = dl.weight_bytes_touched()
         gbs = (dbytes + dio) / (dms * 1e-3) / 1e9
         result["decode"] = {"workload": "decode: T=64 H=8192 I=2048 E=8 top_k=2 fp8",
                             "us_per_layer": round(dms * 1e3, 1), "us_per_layer_gpu_events": round(dgpu_ms * 1e3, 1),
+                            "us_per_layer_dispatch_events": percentiles_us(dtl["layer_ms"]),
                             "GB_per_s": round(gbs, 1),
                             "frac_hbm": round(gbs / PEAK_HBM_GBS, 4), "algorithmic_bytes": dbytes + dio,
                             "stage_us_with_events": {n: round(v * 1e3, 2) for n, v in dstage.items()}}

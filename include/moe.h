@@ -160,7 +160,10 @@ enum {
  * NUL-terminated name of the kernel variants chosen.  gemm1_events[0] / [1]
  * and gemm2_events[0] / [1], when non-NULL, are hipEvent_t stamped by the
  * gate-up / down GEMM's own dispatch (hipExtLaunchKernel) at its start and
- * end: its duration with no extra packets on the stream.
+ * end: its duration with no extra packets on the stream.  layer_events[0] /
+ * [1], when non-NULL, are stamped the same way by the layer's first dispatch
+ * (the router or the routing metadata kernel) at its start and by its last
+ * (the combine) at its end: the whole layer's duration (moe_forward only).
  */
 typedef struct {
   int32_t* topk_ids;       /* [T][k]   */
@@ -177,6 +180,7 @@ typedef struct {
   char variant[96];
   void* gemm1_events[2];
   void* gemm2_events[2];
+  void* layer_events[2];
 } moe_debug_t;
 
 /* ------------------------------------------------------------------------ */

@@ -138,14 +138,15 @@ def forward_workspace_size(T, top_k, routed, use_shared):
 
 def moe_forward(x, logits, top_k, routed, shared=None, norm_gamma=None, norm_eps=1e-6, out=None,
                 ws=None, debug=None, events=None, gemm1_events=None, gemm2_events=None,
-                score="softmax", stream=None):
+                layer_events=None, score="softmax", stream=None):
     """The whole layer.  ``debug``: dict of device tensors to capture
     (keys topk_ids, topk_w, expert_counts, expert_offsets, pair_to_row,
     row_to_pair, xq_rows, xs_rows).  ``events``: list of MOE_N_STAGES + 1
     torch.cuda.Event (or None) recorded at the stage boundaries.
     ``gemm1_events`` / ``gemm2_events``: (start, stop) torch.cuda.Event stamped
-    by the gate-up / down GEMM's dispatch.  Returns ``out`` (and the chosen kernel variant string
-    when debug is given)."""
+    by the gate-up / down GEMM's dispatch; ``layer_events``: (start, stop)
+    stamped by the layer's first and last dispatch.  Returns ``out`` (and the
+    chosen kernel variant string when debug is given)."""
     T, H = x.shape
     dev = x.device
     out = _empty((T, H), torch.bfloat16, dev) if out is None else out
@@ -153,7 +154,7 @@ def moe_forward(x, logits, top_k, routed, shared=None, norm_gamma=None, norm_eps
     if ws is None:
         ws = _empty((nbytes,), torch.uint8, dev)
     dbg = None
-    if debug is not None or events is not None or gemm1_events is not None or gemm2_events is not None:
+    if debug is not None or any(v is not None for v in (events, gemm1_events, gemm2_events, layer_events)):
         dbg = MoeDebug()
         for key, t in (debug or {}).items():
             setattr(dbg, key, t.data_ptr())
@@ -164,6 +165,8 @@ def moe_forward(x, logits, top_k, routed, shared=None, norm_gamma=None, norm_eps
             dbg.gemm1_events[i] = ev.cuda_event
         for i, ev in enumerate(gemm2_events or []):
             dbg.gemm2_events[i] = ev.cuda_event
+        for i, ev in enumerate(layer_events or []):
+            dbg.layer_events[i] = ev.cuda_event
     check(lib().moe_forward(_p(x), _p(logits), T, top_k, _score(score), routed.ref(), int(shared is not None),
                             shared.ref() if shared is not None else None, _p(norm_gamma),
                             float(norm_eps), _p(out), ctypes.byref(dbg) if dbg is not None else None,

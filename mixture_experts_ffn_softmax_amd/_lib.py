@@ -49,6 +49,7 @@ class MoeDebug(ctypes.Structure):
         ("variant", ctypes.c_char * 96),
         ("gemm1_events", ctypes.c_void_p * 2),
         ("gemm2_events", ctypes.c_void_p * 2),
+        ("layer_events", ctypes.c_void_p * 2),
     ]
 
 

@@ -14,6 +14,8 @@
 // once.
 #include <math.h>
 
+#include <hip/hip_ext.h>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -91,15 +93,16 @@ __global__ __launch_bounds__(1024) void combine_kernel(const float* __restrict__
 
 hipError_t launch_combine(const float* y_rows, const int* pair_to_row, const float* w, int T,
                           int H, int k, const float* y_shared, const float* gamma, float eps,
-                          uint16_t* out, hipStream_t s) {
+                          uint16_t* out, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop) {
   if (T == 0) return hipSuccess;
   const int chunks = H / 8;
   int cpt = 1;
   while (chunks > 1024 * cpt) cpt *= 2;
   int threads = (chunks + cpt - 1) / cpt;
   threads = ((threads + 63) / 64) * 64;
-#define MOE_CB(C) \
-  combine_kernel<C><<<T, threads, 0, s>>>(y_rows, pair_to_row, w, H, k, y_shared, gamma, eps, out)
+#define MOE_CB(C)                                                                               \
+  hipExtLaunchKernelGGL(combine_kernel<C>, dim3(T), dim3(threads), 0, s, ev_start, ev_stop, 0, y_rows, \
+                        pair_to_row, w, H, k, y_shared, gamma, eps, out)
   switch (cpt) {
     case 1: MOE_CB(1); break;
     case 2: MOE_CB(2); break;

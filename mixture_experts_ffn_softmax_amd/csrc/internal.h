@@ -42,8 +42,9 @@ constexpr int kW2Chunk = 32;
 
 // ---- router ---------------------------------------------------------------
 // sigmoid: scores 1 / (1 + e^-l) instead of the softmax; same selection.
+// ev_start (optional): stamped by the router's dispatch when it begins.
 hipError_t launch_route(const float* logits, int T, int E, int k, bool sigmoid, int* ids, float* w,
-                        hipStream_t s);
+                        hipStream_t s, hipEvent_t ev_start = nullptr);
 
 // ---- counts, offsets, ranks, quantise + scatter ---------------------------
 inline int permute_chunks(long pairs) { return (int)((pairs + kPermuteChunk - 1) / kPermuteChunk); }
@@ -70,7 +71,7 @@ hipError_t launch_quant_scatter(const uint16_t* x, int T, int H, int k, const in
 // and writes ids / w; logits NULL: reads ids (16 waves).
 hipError_t launch_meta(const float* logits, bool sigmoid, int T, int E, int k, int* ids, float* w, int* counts,
                        int* offsets, int extra_rows, int* pair_to_row, int* row_to_pair, int* tile_prefix,
-                       int bm, hipStream_t s);
+                       int bm, hipStream_t s, hipEvent_t ev_start = nullptr);
 
 // ---- grouped expert FFN ---------------------------------------------------
 enum WeightFormat { kFp8 = 0, kMxfp4 = 1 };
@@ -138,6 +139,7 @@ hipError_t launch_pack_kblocked(const uint8_t* src, uint8_t* dst, int E, int N, 
 // ---- combine --------------------------------------------------------------
 hipError_t launch_combine(const float* y_rows, const int* pair_to_row, const float* w, int T,
                           int H, int k, const float* y_shared, const float* gamma, float eps,
-                          uint16_t* out, hipStream_t s);
+                          uint16_t* out, hipStream_t s, hipEvent_t ev_start = nullptr,
+                          hipEvent_t ev_stop = nullptr);
 
 }  // namespace moe

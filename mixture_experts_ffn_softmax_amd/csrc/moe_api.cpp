@@ -432,8 +432,12 @@ moe_status_t moe_forward(const uint16_t* x, const float* logits, int32_t T, int3
   const bool meta = R <= moe::kMetaMaxPairs;
   const bool fused_route = meta && E <= moe::kMetaRouteMaxE && T <= moe::kMetaRouteMaxT;
   if (ev && ev[MOE_STAGE_ROUTE]) hipEventRecord((hipEvent_t)ev[MOE_STAGE_ROUTE], s);
+  // the layer's first dispatch (router, or the routing metadata kernel) and
+  // its last (combine) stamp the optional layer events
+  const hipEvent_t lev0 = dbg ? (hipEvent_t)dbg->layer_events[0] : nullptr;
+  const hipEvent_t lev1 = dbg ? (hipEvent_t)dbg->layer_events[1] : nullptr;
   if (!fused_route) {
-    e = moe::launch_route(logits, T, E, top_k, sigmoid, L.ids, L.w, s);
+    e = moe::launch_route(logits, T, E, top_k, sigmoid, L.ids, L.w, s, lev0);
     if (e != hipSuccess) return device_status(e, "route");
   }
 
@@ -441,7 +445,8 @@ moe_status_t moe_forward(const uint16_t* x, const float* logits, int32_t T, int3
   if (meta) {
     const int bm = moe::variant_rows(moe::choose_variant(g, rows));
     e = moe::launch_meta(fused_route ? logits : nullptr, sigmoid, T, E, top_k, L.ids, L.w, L.counts,
-                         L.offsets, sh ? T : 0, L.p2r, L.r2p, L.tile_prefix, bm, s);
+                         L.offsets, sh ? T : 0, L.p2r, L.r2p, L.tile_prefix, bm, s,
+                         fused_route ? lev0 : nullptr);
     if (e != hipSuccess) return device_status(e, "meta");
   } else {
     e = moe::launch_counts(L.ids, (int)R, E, L.hist, L.base, L.counts, L.offsets, sh ? T : 0, s);
@@ -466,7 +471,7 @@ moe_status_t moe_forward(const uint16_t* x, const float* logits, int32_t T, int3
 
   if (ev && ev[MOE_STAGE_COMBINE]) hipEventRecord((hipEvent_t)ev[MOE_STAGE_COMBINE], s);
   e = moe::launch_combine(L.y_rows, L.p2r, L.w, T, H, top_k, sh ? L.y_rows + (size_t)R * H : nullptr,
-                          norm_gamma, norm_eps, out, s);
+                          norm_gamma, norm_eps, out, s, nullptr, lev1);
   if (e != hipSuccess) return device_status(e, "combine");
   if (ev && ev[MOE_N_STAGES]) hipEventRecord((hipEvent_t)ev[MOE_N_STAGES], s);
   return ok();

@@ -23,6 +23,8 @@
 // Rows are ordered by expert and, inside an expert, by pair index; this order
 // is unique, so the result is deterministic.  Expert ids outside [0, E) are
 // skipped (their pairs get row -1) so that no access leaves its buffer.
+#include <hip/hip_ext.h>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -562,10 +564,10 @@ hipError_t launch_quant_scatter(const uint16_t* x, int T, int H, int k, const in
 
 hipError_t launch_meta(const float* logits, bool sigmoid, int T, int E, int k, int* ids, float* w, int* counts,
                        int* offsets, int extra_rows, int* pair_to_row, int* row_to_pair, int* tile_prefix,
-                       int bm, hipStream_t s) {
+                       int bm, hipStream_t s, hipEvent_t ev_start) {
   if (logits && T <= kMetaRouteMaxT && E <= kMetaRouteMaxE) {
-    meta_wave_kernel<<<1, 64, 0, s>>>(logits, sigmoid, T, E, k, ids, w, counts, offsets, extra_rows, pair_to_row,
-                                      row_to_pair, tile_prefix, bm);
+    hipExtLaunchKernelGGL(meta_wave_kernel, dim3(1), dim3(64), 0, s, ev_start, nullptr, 0, logits, sigmoid, T, E, k,
+                          ids, w, counts, offsets, extra_rows, pair_to_row, row_to_pair, tile_prefix, bm);
     return hipGetLastError();
   }
   if (logits) return hipErrorInvalidValue;   // routing needs T <= kMetaRouteMaxT, E <= kMetaRouteMaxE

@@ -12,6 +12,8 @@
 // model); renormalised top-k weights on the Kimi K3 page, §2.4.
 #include <math.h>
 
+#include <hip/hip_ext.h>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -80,9 +82,10 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
 }
 
 hipError_t launch_route(const float* logits, int T, int E, int k, bool sigmoid, int* ids, float* w,
-                        hipStream_t s) {
+                        hipStream_t s, hipEvent_t ev_start) {
   if (T == 0) return hipSuccess;
-  route_kernel<<<(T + 3) / 4, 256, 0, s>>>(logits, T, E, k, sigmoid, ids, w);
+  hipExtLaunchKernelGGL(route_kernel, dim3((T + 3) / 4), dim3(256), 0, s, ev_start, nullptr, 0, logits, T, E, k,
+                        sigmoid, ids, w);
   return hipGetLastError();
 }
 

@@ -62,17 +62,18 @@ def test_struct_layouts(tmp_path):
     src = tmp_path / "layout.c"
     src.write_text(
         '#include <stddef.h>\n#include <stdio.h>\n#include "moe.h"\n'
-        'int main(void) { printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu\\n", sizeof(moe_weights_t),'
+        'int main(void) { printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu %zu\\n", sizeof(moe_weights_t),'
         ' offsetof(moe_weights_t, w1), offsetof(moe_weights_t, s2), sizeof(moe_debug_t),'
         ' offsetof(moe_debug_t, events), offsetof(moe_debug_t, variant),'
         ' offsetof(moe_debug_t, gemm1_events), offsetof(moe_debug_t, gemm2_events),'
-        ' offsetof(moe_weights_t, act_beta)); return 0; }\n')
+        ' offsetof(moe_weights_t, act_beta), offsetof(moe_debug_t, layer_events)); return 0; }\n')
     exe = tmp_path / "layout"
     subprocess.run([gcc, "-std=c99", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
     got = [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
     assert got == [ctypes.sizeof(MoeWeights), MoeWeights.w1.offset, MoeWeights.s2.offset,
                    ctypes.sizeof(MoeDebug), MoeDebug.events.offset, MoeDebug.variant.offset,
-                   MoeDebug.gemm1_events.offset, MoeDebug.gemm2_events.offset, MoeWeights.act_beta.offset]
+                   MoeDebug.gemm1_events.offset, MoeDebug.gemm2_events.offset, MoeWeights.act_beta.offset,
+                   MoeDebug.layer_events.offset]
 
 
 def fp8_weights(E=8, H=256, I=128, fmt=0, layout=0, **over):

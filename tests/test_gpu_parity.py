@@ -257,6 +257,31 @@ def test_forward_zero_tokens(lib):
     assert out.shape == (0, 256)
 
 
+@pytest.mark.parametrize("T", [64, 300])
+def test_forward_dispatch_events(lib, T):
+    """The layer events stamped by the first (routing metadata kernel at T=64,
+    router at T=300) and last dispatch bracket the GEMMs' own events, and the
+    output is the same as without events."""
+    inp = to_device(moe_synth.custom_inputs(T, 256, 256, 4, 2, seed=5, shared=True))
+    ref, _, _ = run_forward(inp, capture=False)
+    routed = lib.Weights(inp["routed"], "fp8")
+    shared = lib.Weights(inp["shared"], "fp8")
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    for e in evs:
+        e.record()
+    torch.cuda.synchronize()
+    say("forward dispatch events", T)
+    out = lib.moe_forward(inp["x"], inp["logits"], 2, routed, shared, gemm1_events=evs[0:2],
+                          gemm2_events=evs[2:4], layer_events=evs[4:6])
+    torch.cuda.synchronize()
+    layer = evs[4].elapsed_time(evs[5])
+    g1, g2 = evs[0].elapsed_time(evs[1]), evs[2].elapsed_time(evs[3])
+    say("  layer ms", layer, "gemm1", g1, "gemm2", g2)
+    assert 0 < g1 and 0 < g2 and g1 + g2 <= layer
+    assert evs[4].elapsed_time(evs[0]) >= 0 and evs[3].elapsed_time(evs[5]) >= 0
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+
+
 def test_forward_deterministic(lib):
     inp = to_device(moe_synth.custom_inputs(300, 256, 256, 4, 2, seed=3, shared=True))
     a, _, _ = run_forward(inp, capture=False)
