@@ -17,6 +17,11 @@ latent 512     3584   3072   896   16   mxfp4   RMSNorm (gamma = 1, eps = 1e-6)
 skewed 16384   8192   2048   256   8    fp8     Zipf-biased logits, hottest ~5x
 =====  ======  =====  =====  ====  ===  ======  ================================
 
+``latent_block_inputs`` draws the whole LatentMoE block (hidden 7168, the
+``latent`` core over 3584, MXFP4 down/up projections, bf16 shared experts
+7168 -> 6144 -> 7168) with the same recipe (projection weights quantised per
+32-element block to MXFP4, shared weights rounded to bf16).
+
 Recipe: activations ~ N(0,1) rounded to bf16; router logits ~ N(0,1) in fp32
 (plus, for ``skewed``, a per-expert bias -alpha*1.1*ln(rank) over a seeded
 rank permutation, alpha bisected so the hottest expert gets 4.9-5.1x the mean
@@ -40,7 +45,7 @@ CONFIGS = {
     "skewed":  dict(cfg=5, T=16384, H=8192, I=2048, E=256, k=8,  fmt="fp8",   shared=False, norm=False, skew=True),
 }
 
-T_LOGITS, T_X, T_W1, T_W3, T_W2, T_SW1, T_SW3, T_SW2, T_RANK = range(9)
+T_LOGITS, T_X, T_W1, T_W3, T_W2, T_SW1, T_SW3, T_SW2, T_RANK, T_DOWN, T_UP = range(11)
 NORM_EPS = 1e-6
 WEIGHT_STD = 0.02
 
@@ -181,6 +186,35 @@ def custom_inputs(T, H, I, E, k, fmt="fp8", seed=7, device="cpu", shared=False, 
     gamma = torch.ones(H, dtype=torch.float32, device=device) if norm else None
     c = dict(cfg=cfg, T=T, H=H, I=I, E=E, k=k, fmt=fmt, shared=shared, norm=norm, skew=False, alpha=None)
     return dict(cfg=c, x=x, logits=logits, routed=routed, shared=sh, gamma=gamma, eps=NORM_EPS)
+
+
+# The LatentMoE block (the routed core of ``latent`` plus its projections and
+# shared experts): hidden 7168 -> latent 3584 -> 896 experts top-16 -> RMSNorm
+# -> 7168, shared experts 7168 -> 6144 -> 7168 on the hidden stream.
+LATENT_BLOCK = dict(cfg=6, T=512, Hm=7168, L=3584, I=3072, E=896, k=16, Is=6144)
+
+
+def latent_block_inputs(T, Hm, L, I, E, k, Is, cfg=6, device="cpu", weights=True):
+    """Inputs of the LatentMoE block, same recipe: x bf16 [T][Hm], logits
+    float32 [T][E]; down {w, s} MXFP4 [L][Hm/2] + [L][Hm/32]; up {w, s} MXFP4
+    [Hm][L/2] + [Hm][L/32]; routed MXFP4 experts over L; shared bf16
+    {w1, w3} [Is][Hm], {w2} [Hm][Is] (Is = 0: none); gamma ones [L]."""
+    x = randn((T, Hm), device, seed_of(cfg, T_X)).to(torch.bfloat16)
+    logits = randn((T, E), device, seed_of(cfg, T_LOGITS))
+    c = dict(cfg=cfg, T=T, Hm=Hm, L=L, I=I, E=E, k=k, Is=Is, fmt="mxfp4")
+    out = dict(cfg=c, x=x, logits=logits, down=None, up=None, routed=None, shared=None,
+               gamma=torch.ones(L, dtype=torch.float32, device=device), eps=NORM_EPS)
+    if not weights:
+        return out
+    for name, tid, shape in (("down", T_DOWN, (L, Hm)), ("up", T_UP, (Hm, L))):
+        w, sc = mxfp4_rows(randn(shape, device, seed_of(cfg, tid), WEIGHT_STD))
+        out[name] = dict(w=w, s=sc)
+    out["routed"] = expert_weights(cfg, device, "mxfp4", E, L, I)
+    if Is > 0:
+        out["shared"] = {n: randn(shape, device, seed_of(cfg, tid), WEIGHT_STD).to(torch.bfloat16).contiguous()
+                         for n, tid, shape in (("w1", T_SW1, (Is, Hm)), ("w3", T_SW3, (Is, Hm)),
+                                               ("w2", T_SW2, (Hm, Is)))}
+    return out
 
 
 def random_topk_ids(T, E, k, seed, device="cpu", hot=None):

@@ -29,12 +29,17 @@ cases; permutation against NumPy's stable argsort; the FFN against a dense
 gated FFN (one expert, top-1), token-permutation invariance, zero routing
 weights, power-of-two linearity, a per-token brute-force loop, hand-computed
 closed-form examples and an MXFP4 / fp8 cross-check; the FLOP and byte
-accounting against the worked figures the pages print.  The numerical MoE
+accounting against the worked figures the pages print; the LatentMoE block
+(``latent``: MXFP4 down/up projections around the routed core, bf16 shared
+experts on the hidden stream, *Kimi K3 on TPU* §2.4-2.5) against exact
+products of representable weights, selection-matrix wiring through the
+pinned core, a closed form of the shared path, torch's float64 linear and
+exact power-of-two scalings.  The numerical MoE
 output as a whole is otherwise "parity unpinned": the pages print no worked
 example of it.
 """
 
-from . import codecs, moe, accounting  # noqa: F401
+from . import codecs, moe, accounting, latent  # noqa: F401
 from .moe import (  # noqa: F401
     route,
     quantize_tokens,
