@@ -181,6 +181,8 @@ typedef struct {
   void* gemm1_events[2];
   void* gemm2_events[2];
   void* layer_events[2];
+  uint16_t* latent;     /* moe_latent_forward: bf16 [T][L] down-projection output */
+  uint16_t* core_out;   /* moe_latent_forward: bf16 [T][L] routed core output */
 } moe_debug_t;
 
 /* ------------------------------------------------------------------------ */
@@ -307,6 +309,74 @@ moe_status_t moe_forward(const uint16_t* x, const float* logits, int32_t T, int3
  * is paid once per weight load.
  */
 moe_status_t moe_pack_weights(const moe_weights_t* src, const moe_weights_t* dst, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* The LatentMoE block ([K3] §2.4: down-projection hidden -> latent before the
+ * routed experts, their RMSNorm, up-projection latent -> hidden, shared
+ * experts on the hidden stream; §2.5: the projections are MXFP4, the shared
+ * experts keep bf16 weights).  All pointers are caller-owned device memory. */
+
+typedef enum { MOE_LIN_MXFP4 = 0, MOE_LIN_BF16 = 1 } moe_lin_fmt_t;
+
+/* One dense projection y = a W^T with W [n_out][n_in].
+ *   MXFP4: w uint8 [n_out][n_in/2] (two e2m1 per byte, element 2i in the low
+ *          nibble), s uint8 e8m0 [n_out][n_in/32]
+ *   BF16:  w uint16 bf16 [n_out][n_in], s NULL
+ * n_out a multiple of 128, n_in of 64. */
+typedef struct {
+  int32_t fmt;     /* moe_lin_fmt_t */
+  int32_t n_out;
+  int32_t n_in;
+  int32_t reserved;  /* must be 0 */
+  const void* w;
+  const void* s;
+} moe_linear_t;
+
+/* The block's own weights around the routed experts (hidden Hm, latent L). */
+typedef struct {
+  moe_linear_t down;        /* Hm -> L, MXFP4 */
+  moe_linear_t up;          /* L -> Hm, MXFP4 */
+  int32_t shared_inter;     /* Is of the shared experts (a multiple of 64); 0 = none */
+  int32_t shared_activation;/* moe_act_t of the shared experts */
+  float shared_beta;        /* SiTU's beta (shared_activation == MOE_ACT_SITU) */
+  int32_t reserved;         /* must be 0 */
+  const uint16_t* sw1;      /* bf16 [Is][Hm] gate */
+  const uint16_t* sw3;      /* bf16 [Is][Hm] up */
+  const uint16_t* sw2;      /* bf16 [Hm][Is] down */
+} moe_latent_t;
+
+/*
+ * moe_linear -- out = a W^T on the bf16 MFMA, fp32 accumulation.
+ *   a       bf16  [M][n_in] row-major
+ *   out_bf16 bf16 [M][n_out] (rounded to nearest even), or NULL
+ *   out_f32  float [M][n_out], or NULL (exactly one of the two)
+ *   addend  optional float [M][n_out] added before the bf16 rounding
+ *           (only with out_bf16)
+ * The MXFP4 weights are widened exactly to bf16 inside the kernel.
+ */
+moe_status_t moe_linear(const uint16_t* a, int32_t M, const moe_linear_t* w, const float* addend,
+                        uint16_t* out_bf16, float* out_f32, void* stream);
+
+/*
+ * moe_latent_forward -- the LatentMoE block:
+ *   lat  = bf16( x down^T )                      [T][L]
+ *   core = moe_forward(lat, logits, routed experts over L, RMSNorm(norm_gamma,
+ *          norm_eps), no shared expert)          bf16 [T][L]
+ *   out  = bf16( core up^T + shared(x) )         [T][Hm]
+ *   shared(x) = bf16( act(x sw1^T) * (x sw3^T) ) sw2^T   (absent if Is = 0)
+ * x bf16 [T][Hm]; logits float [T][E]; routed->hidden == L.  dbg: as for
+ * moe_forward (its routing captures describe the core); dbg->latent and
+ * dbg->core_out (bf16 [T][L]) receive the two intermediates; layer_events
+ * bracket the whole block.  The latent and the core's output are rounded to
+ * bf16 (the activation dtype between steps); the up-projection and the
+ * shared experts' output are summed in fp32 and rounded once.
+ */
+size_t moe_latent_forward_workspace_size(int32_t T, int32_t top_k, const moe_weights_t* routed,
+                                         const moe_latent_t* lw);
+moe_status_t moe_latent_forward(const uint16_t* x, const float* logits, int32_t T, int32_t top_k,
+                                int32_t score, const moe_latent_t* lw, const moe_weights_t* routed,
+                                const float* norm_gamma, float norm_eps, uint16_t* out, moe_debug_t* dbg,
+                                void* ws, size_t ws_bytes, void* stream);
 
 /* Static description of a status code. */
 const char* moe_status_string(moe_status_t s);

@@ -12,11 +12,13 @@ import ctypes
 import torch
 
 from . import _lib
-from ._lib import (MOE_LAYOUT_K_BLOCKED, MOE_LAYOUT_ROW_MAJOR, MOE_N_STAGES, MOE_W_FP8, MOE_W_MXFP4,
-                   STAGE_NAMES, MoeDebug, MoeError, MoeWeights, check)
+from ._lib import (MOE_LAYOUT_K_BLOCKED, MOE_LAYOUT_ROW_MAJOR, MOE_LIN_BF16, MOE_LIN_MXFP4, MOE_N_STAGES,
+                   MOE_W_FP8, MOE_W_MXFP4, STAGE_NAMES, MoeDebug, MoeError, MoeLatent, MoeLinear, MoeWeights,
+                   check)
 
-__all__ = ["Weights", "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_forward",
-           "forward_workspace_size", "MoeError", "lib"]
+__all__ = ["Weights", "Linear", "LatentWeights", "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine",
+           "moe_forward", "forward_workspace_size", "moe_linear", "moe_latent_forward",
+           "latent_forward_workspace_size", "MoeError", "lib"]
 
 
 def lib():
@@ -171,6 +173,85 @@ def moe_forward(x, logits, top_k, routed, shared=None, norm_gamma=None, norm_eps
                             shared.ref() if shared is not None else None, _p(norm_gamma),
                             float(norm_eps), _p(out), ctypes.byref(dbg) if dbg is not None else None,
                             _p(ws), ws.numel(), _stream(stream)))
+    if debug is not None:
+        return out, dbg.variant.decode()
+    return out
+
+
+# ----------------------------------------------------------------------------
+# LatentMoE block
+# ----------------------------------------------------------------------------
+
+
+class Linear:
+    """One dense projection W [n_out][n_in]: ``w`` uint8 MXFP4 codes [n_out][n_in/2]
+    with ``s`` uint8 e8m0 [n_out][n_in/32], or ``w`` bf16 [n_out][n_in] (s None)."""
+
+    def __init__(self, w, s=None):
+        self.w = w.contiguous()
+        self.s = None if s is None else s.contiguous()
+        mx = self.s is not None
+        n_in = self.w.shape[1] * (2 if mx else 1)
+        self.c = MoeLinear(MOE_LIN_MXFP4 if mx else MOE_LIN_BF16, self.w.shape[0], n_in, 0,
+                           self.w.data_ptr(), self.s.data_ptr() if mx else None)
+
+    def ref(self):
+        return ctypes.byref(self.c)
+
+
+class LatentWeights:
+    """The block's weights around the routed experts: ``down`` / ``up`` dicts
+    {w, s} (MXFP4), ``shared`` dict {w1, w3, w2} of bf16 tensors or None."""
+
+    def __init__(self, down, up, shared=None, activation="silu", beta=4.0):
+        self.down, self.up = Linear(down["w"], down["s"]), Linear(up["w"], up["s"])
+        self.shared = None if shared is None else {k: v.contiguous() for k, v in shared.items()}
+        sh = self.shared
+        act = _lib.MOE_ACT_SITU if activation == "situ" else _lib.MOE_ACT_SILU
+        self.hidden, self.latent = self.down.c.n_in, self.down.c.n_out
+        self.c = MoeLatent(self.down.c, self.up.c, 0 if sh is None else sh["w1"].shape[0], act, beta, 0,
+                           *((None, None, None) if sh is None else (sh[k].data_ptr() for k in ("w1", "w3", "w2"))))
+
+    def ref(self):
+        return ctypes.byref(self.c)
+
+
+def moe_linear(a, weights, addend=None, out_dtype=torch.bfloat16, out=None, stream=None):
+    """out = a W^T (+ addend before the bf16 rounding)."""
+    M = a.shape[0]
+    if out is None:
+        out = _empty((M, weights.c.n_out), out_dtype, a.device)
+    bf = out.dtype == torch.bfloat16
+    check(lib().moe_linear(_p(a), M, weights.ref(), _p(addend), _p(out) if bf else None,
+                           None if bf else _p(out), _stream(stream)))
+    return out
+
+
+def latent_forward_workspace_size(T, top_k, latent, routed):
+    return lib().moe_latent_forward_workspace_size(T, top_k, routed.ref(), latent.ref())
+
+
+def moe_latent_forward(x, logits, top_k, latent, routed, norm_gamma=None, norm_eps=1e-6, out=None, ws=None,
+                       debug=None, layer_events=None, score="softmax", stream=None):
+    """The LatentMoE block.  ``debug``: dict of device tensors as for
+    moe_forward plus ``latent`` and ``core_out`` (bf16 [T][L]).  Returns
+    ``out`` (and the core's kernel variant string when debug is given)."""
+    T = x.shape[0]
+    out = _empty((T, latent.hidden), torch.bfloat16, x.device) if out is None else out
+    nbytes = latent_forward_workspace_size(T, top_k, latent, routed)
+    if ws is None:
+        ws = _empty((max(nbytes, 1),), torch.uint8, x.device)
+    dbg = None
+    if debug is not None or layer_events is not None:
+        dbg = MoeDebug()
+        for key, t in (debug or {}).items():
+            setattr(dbg, key, t.data_ptr())
+        for i, ev in enumerate(layer_events or []):
+            dbg.layer_events[i] = ev.cuda_event
+    check(lib().moe_latent_forward(_p(x), _p(logits), T, top_k, _score(score), latent.ref(), routed.ref(),
+                                   _p(norm_gamma), float(norm_eps), _p(out),
+                                   ctypes.byref(dbg) if dbg is not None else None, _p(ws), ws.numel(),
+                                   _stream(stream)))
     if debug is not None:
         return out, dbg.variant.decode()
     return out

@@ -20,12 +20,14 @@ MOE_LAYOUT_ROW_MAJOR, MOE_LAYOUT_K_BLOCKED = 0, 1
 STAGE_NAMES = ["route", "permute", "gemm1", "gemm2", "combine"]
 MOE_ACT_SILU, MOE_ACT_SITU = 0, 1
 MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
+MOE_LIN_MXFP4, MOE_LIN_BF16 = 0, 1
 
 # Every function include/moe.h declares.
 EXPORTS = [
     "moe_route", "moe_permute_workspace_size", "moe_permute", "moe_expert_ffn_workspace_size",
     "moe_expert_ffn", "moe_combine", "moe_forward_workspace_size", "moe_forward",
-    "moe_pack_weights", "moe_status_string", "moe_last_error", "moe_version",
+    "moe_pack_weights", "moe_linear", "moe_latent_forward_workspace_size", "moe_latent_forward",
+    "moe_status_string", "moe_last_error", "moe_version",
 ]
 
 
@@ -50,11 +52,29 @@ class MoeDebug(ctypes.Structure):
         ("gemm1_events", ctypes.c_void_p * 2),
         ("gemm2_events", ctypes.c_void_p * 2),
         ("layer_events", ctypes.c_void_p * 2),
+        ("latent", ctypes.c_void_p), ("core_out", ctypes.c_void_p),
+    ]
+
+
+class MoeLinear(ctypes.Structure):
+    _fields_ = [
+        ("fmt", ctypes.c_int32), ("n_out", ctypes.c_int32), ("n_in", ctypes.c_int32),
+        ("reserved", ctypes.c_int32), ("w", ctypes.c_void_p), ("s", ctypes.c_void_p),
+    ]
+
+
+class MoeLatent(ctypes.Structure):
+    _fields_ = [
+        ("down", MoeLinear), ("up", MoeLinear),
+        ("shared_inter", ctypes.c_int32), ("shared_activation", ctypes.c_int32),
+        ("shared_beta", ctypes.c_float), ("reserved", ctypes.c_int32),
+        ("sw1", ctypes.c_void_p), ("sw3", ctypes.c_void_p), ("sw2", ctypes.c_void_p),
     ]
 
 
 _VP, _I32, _F32, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
 _WP, _DP = ctypes.POINTER(MoeWeights), ctypes.POINTER(MoeDebug)
+_LP, _LTP = ctypes.POINTER(MoeLinear), ctypes.POINTER(MoeLatent)
 
 SIGNATURES = {
     "moe_route": (_I32, [_VP, _I32, _I32, _I32, _I32, _VP, _VP, _VP]),
@@ -67,6 +87,9 @@ SIGNATURES = {
     "moe_forward_workspace_size": (_SZ, [_I32, _I32, _WP, _I32]),
     "moe_forward": (_I32, [_VP, _VP, _I32, _I32, _I32, _WP, _I32, _WP, _VP, _F32, _VP, _DP, _VP, _SZ, _VP]),
     "moe_pack_weights": (_I32, [_WP, _WP, _VP]),
+    "moe_linear": (_I32, [_VP, _I32, _LP, _VP, _VP, _VP, _VP]),
+    "moe_latent_forward_workspace_size": (_SZ, [_I32, _I32, _WP, _LTP]),
+    "moe_latent_forward": (_I32, [_VP, _VP, _I32, _I32, _I32, _LTP, _WP, _VP, _F32, _VP, _DP, _VP, _SZ, _VP]),
     "moe_status_string": (ctypes.c_char_p, [_I32]),
     "moe_last_error": (ctypes.c_char_p, []),
     "moe_version": (ctypes.c_char_p, []),

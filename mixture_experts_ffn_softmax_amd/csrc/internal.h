@@ -142,4 +142,31 @@ hipError_t launch_combine(const float* y_rows, const int* pair_to_row, const flo
                           uint16_t* out, hipStream_t s, hipEvent_t ev_start = nullptr,
                           hipEvent_t ev_stop = nullptr);
 
+// ---- dense GEMMs (LatentMoE projections and shared experts) --------------
+// C[M][N] = epilogue(A[M][K] x B[N][K]^T): A bf16 row-major with row pitch
+// lda elements; B bf16 [N][K] (bfmt kBf16W) or MXFP4 codes [N][K/2] + e8m0
+// [N][K/32] (bfmt kMxfp4).  K % 64 == 0; N % 128 == 0 (N % 64 in kDnGateUp,
+// where b is W1 and b3 is W3, and the output h[m][n] = bf16(act(g) * u)).
+enum DenseMode { kDnStoreBf16 = 0, kDnStoreF32 = 1, kDnAddBf16 = 2, kDnGateUp = 3 };
+constexpr int kBf16W = 2;   // bf16 weights (beside kFp8 / kMxfp4)
+struct DenseParams {
+  const uint16_t* a;
+  long lda;
+  int M, N, K;
+  int bfmt;
+  const void* b;        // W (or W1 in kDnGateUp)
+  const uint8_t* bs;    // its e8m0 scales (MXFP4)
+  const void* b3;       // W3 (kDnGateUp)
+  const uint8_t* bs3;
+  int mode;             // DenseMode
+  const float* addend;  // kDnAddBf16: fp32 [M][ldc], added before the rounding
+  void* c;              // bf16 or fp32 [M][ldc]
+  long ldc;
+  int act;              // kDnGateUp: Activation and beta
+  float beta;
+  int tiles_n;          // set by launch_dense
+};
+hipError_t launch_dense(const DenseParams& p, hipStream_t s, hipEvent_t ev_start = nullptr,
+                        hipEvent_t ev_stop = nullptr);
+
 }  // namespace moe

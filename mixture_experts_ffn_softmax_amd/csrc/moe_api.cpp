@@ -509,4 +509,197 @@ moe_status_t moe_pack_weights(const moe_weights_t* src, const moe_weights_t* dst
   return device_status(e, "pack_weights");
 }
 
+// ---------------------------------------------------------------------------
+// LatentMoE block
+// ---------------------------------------------------------------------------
+
+}  // extern "C"
+
+namespace {
+
+moe_status_t check_linear(const moe_linear_t* w, const char* name) {
+  if (!w) return fail(MOE_ERR_NULL, "%s is NULL", name);
+  if (w->fmt != MOE_LIN_MXFP4 && w->fmt != MOE_LIN_BF16)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: unknown projection format %d", name, w->fmt);
+  if (w->reserved != 0) return fail(MOE_ERR_SHAPE, "%s: reserved field must be 0", name);
+  MOE_CHECK(check_dim(w->n_out, "n_out"));
+  if (w->n_in < 64 || w->n_in > kMaxDim || w->n_in % 64 != 0)
+    return fail(MOE_ERR_SHAPE, "%s: n_in = %d is not a multiple of 64 in [64, %d]", name, w->n_in, kMaxDim);
+  MOE_CHECK(need(w->w, "w"));
+  if (w->fmt == MOE_LIN_MXFP4) {
+    if (!w->s) return fail(MOE_ERR_NULL, "%s: MXFP4 scales are NULL", name);
+  } else if (w->s) {
+    return fail(MOE_ERR_SHAPE, "%s: bf16 weights take no scales", name);
+  }
+  return MOE_OK;
+}
+
+moe::DenseParams dense_params(const uint16_t* a, int M, const moe_linear_t* w) {
+  moe::DenseParams p{};
+  p.a = a;
+  p.lda = w->n_in;
+  p.M = M;
+  p.N = w->n_out;
+  p.K = w->n_in;
+  p.bfmt = w->fmt == MOE_LIN_MXFP4 ? moe::kMxfp4 : moe::kBf16W;
+  p.b = w->w;
+  p.bs = static_cast<const uint8_t*>(w->s);
+  return p;
+}
+
+moe_status_t check_latent(const moe_latent_t* lw, const moe_weights_t* routed) {
+  if (!lw) return fail(MOE_ERR_NULL, "latent weights are NULL");
+  MOE_CHECK(check_linear(&lw->down, "down"));
+  MOE_CHECK(check_linear(&lw->up, "up"));
+  const int32_t Hm = lw->down.n_in, L = lw->down.n_out;
+  if (lw->up.n_in != L || lw->up.n_out != Hm)
+    return fail(MOE_ERR_SHAPE, "up-projection %d -> %d does not invert down-projection %d -> %d", lw->up.n_in,
+                lw->up.n_out, Hm, L);
+  if (routed->hidden != L)
+    return fail(MOE_ERR_SHAPE, "routed experts' hidden %d differs from the latent %d", routed->hidden, L);
+  if (lw->reserved != 0) return fail(MOE_ERR_SHAPE, "latent: reserved field must be 0");
+  if (lw->shared_inter != 0) {
+    MOE_CHECK(check_dim(lw->shared_inter, "shared_inter"));
+    if (lw->shared_activation != MOE_ACT_SILU && lw->shared_activation != MOE_ACT_SITU)
+      return fail(MOE_ERR_UNSUPPORTED, "shared experts: unknown activation %d", lw->shared_activation);
+    if (lw->shared_activation == MOE_ACT_SITU && !(lw->shared_beta > 0.0f && lw->shared_beta <= 3.0e38f))
+      return fail(MOE_ERR_SHAPE, "shared experts: SiTU needs a finite beta > 0");
+    MOE_CHECK(need(lw->sw1, "sw1"));
+    MOE_CHECK(need(lw->sw3, "sw3"));
+    MOE_CHECK(need(lw->sw2, "sw2"));
+  }
+  return MOE_OK;
+}
+
+struct LatentLayout {
+  uint16_t *lat, *core, *h;
+  float* up;
+  void* core_ws;
+  size_t core_bytes, bytes;
+};
+
+LatentLayout latent_layout(void* ws, int32_t T, int32_t k, const moe_weights_t* routed, const moe_latent_t* lw) {
+  LatentLayout L{};
+  Carve c(ws);
+  const int32_t Hm = lw->down.n_in, Lt = lw->down.n_out, Is = lw->shared_inter;
+  L.lat = c.take<uint16_t>((size_t)T * Lt);
+  L.core = c.take<uint16_t>((size_t)T * Lt);
+  L.up = Is ? c.take<float>((size_t)T * Hm) : nullptr;
+  L.h = Is ? c.take<uint16_t>((size_t)T * Is) : nullptr;
+  L.core_bytes = moe_forward_workspace_size(T, k, routed, 0);
+  L.core_ws = c.take<uint8_t>(L.core_bytes);
+  L.bytes = c.used + 256;
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status_t moe_linear(const uint16_t* a, int32_t M, const moe_linear_t* w, const float* addend,
+                        uint16_t* out_bf16, float* out_f32, void* stream) {
+  MOE_CHECK(check_linear(w, "w"));
+  if (M < 0) return fail(MOE_ERR_SHAPE, "M = %d < 0", M);
+  if ((out_bf16 != nullptr) == (out_f32 != nullptr))
+    return fail(MOE_ERR_SHAPE, "exactly one of out_bf16 and out_f32 must be given");
+  if (addend && !out_bf16) return fail(MOE_ERR_SHAPE, "addend needs out_bf16");
+  if (M == 0) return ok();
+  MOE_CHECK(need(a, "a"));
+  MOE_CHECK(opt(addend, "addend"));
+  MOE_CHECK(opt(out_bf16, "out_bf16"));
+  MOE_CHECK(opt(out_f32, "out_f32"));
+  moe::DenseParams p = dense_params(a, M, w);
+  p.mode = out_f32 ? moe::kDnStoreF32 : (addend ? moe::kDnAddBf16 : moe::kDnStoreBf16);
+  p.addend = addend;
+  p.c = out_f32 ? static_cast<void*>(out_f32) : static_cast<void*>(out_bf16);
+  p.ldc = w->n_out;
+  return device_status(moe::launch_dense(p, (hipStream_t)stream), "linear");
+}
+
+size_t moe_latent_forward_workspace_size(int32_t T, int32_t top_k, const moe_weights_t* routed,
+                                         const moe_latent_t* lw) {
+  if (!routed || !lw || T < 0 || top_k < 1 || routed->n_experts < 1) return 0;
+  return latent_layout(nullptr, T, top_k, routed, lw).bytes;
+}
+
+moe_status_t moe_latent_forward(const uint16_t* x, const float* logits, int32_t T, int32_t top_k,
+                                int32_t score, const moe_latent_t* lw, const moe_weights_t* routed,
+                                const float* norm_gamma, float norm_eps, uint16_t* out, moe_debug_t* dbg,
+                                void* ws, size_t ws_bytes, void* stream) {
+  MOE_CHECK(check_weights(routed, "routed"));
+  MOE_CHECK(check_latent(lw, routed));
+  MOE_CHECK(check_route_shape(T, routed->n_experts, top_k));
+  MOE_CHECK(check_score(score));
+  if (norm_gamma && !(norm_eps >= 0.0f)) return fail(MOE_ERR_SHAPE, "norm_eps must be >= 0");
+  if (T == 0) return ok();
+  MOE_CHECK(need(x, "x"));
+  MOE_CHECK(need(logits, "logits"));
+  MOE_CHECK(need(out, "out"));
+  if (dbg) {
+    MOE_CHECK(opt(dbg->latent, "dbg.latent"));
+    MOE_CHECK(opt(dbg->core_out, "dbg.core_out"));
+  }
+  const size_t need_ws = moe_latent_forward_workspace_size(T, top_k, routed, lw);
+  if (!ws || ws_bytes < need_ws)
+    return fail(MOE_ERR_WORKSPACE, "workspace %zu B < %zu B", ws ? ws_bytes : 0, need_ws);
+  MOE_CHECK(need(ws, "ws"));
+  const LatentLayout L = latent_layout(ws, T, top_k, routed, lw);
+  hipStream_t s = (hipStream_t)stream;
+  const int32_t Hm = lw->down.n_in, Lt = lw->down.n_out, Is = lw->shared_inter;
+  const hipEvent_t lev0 = dbg ? (hipEvent_t)dbg->layer_events[0] : nullptr;
+  const hipEvent_t lev1 = dbg ? (hipEvent_t)dbg->layer_events[1] : nullptr;
+  uint16_t* lat = (dbg && dbg->latent) ? dbg->latent : L.lat;
+  uint16_t* core = (dbg && dbg->core_out) ? dbg->core_out : L.core;
+
+  // down-projection -> latent (bf16)
+  moe::DenseParams dp = dense_params(x, T, &lw->down);
+  dp.mode = moe::kDnStoreBf16;
+  dp.c = lat;
+  dp.ldc = Lt;
+  hipError_t e = moe::launch_dense(dp, s, lev0, nullptr);
+  if (e != hipSuccess) return device_status(e, "down-projection");
+
+  // the routed core over the latent, with its RMSNorm, no shared expert
+  moe_debug_t inner{};
+  if (dbg) {
+    inner = *dbg;
+    inner.layer_events[0] = inner.layer_events[1] = nullptr;
+  }
+  MOE_CHECK(moe_forward(lat, logits, T, top_k, score, routed, 0, nullptr, norm_gamma, norm_eps, core,
+                        dbg ? &inner : nullptr, L.core_ws, L.core_bytes, stream));
+  if (dbg) std::memcpy(dbg->variant, inner.variant, sizeof(dbg->variant));
+
+  // up-projection (+ shared experts on the hidden stream)
+  moe::DenseParams up = dense_params(core, T, &lw->up);
+  up.ldc = Hm;
+  if (Is == 0) {
+    up.mode = moe::kDnStoreBf16;
+    up.c = out;
+    e = moe::launch_dense(up, s, nullptr, lev1);
+    return device_status(e, "up-projection");
+  }
+  up.mode = moe::kDnStoreF32;
+  up.c = L.up;
+  e = moe::launch_dense(up, s);
+  if (e != hipSuccess) return device_status(e, "up-projection");
+  const moe_linear_t w13{MOE_LIN_BF16, Is, Hm, 0, lw->sw1, nullptr};
+  moe::DenseParams gu = dense_params(x, T, &w13);
+  gu.mode = moe::kDnGateUp;
+  gu.b3 = lw->sw3;
+  gu.c = L.h;
+  gu.ldc = Is;
+  gu.act = lw->shared_activation == MOE_ACT_SITU ? moe::kActSitu : moe::kActSilu;
+  gu.beta = lw->shared_beta;
+  e = moe::launch_dense(gu, s);
+  if (e != hipSuccess) return device_status(e, "shared gate-up");
+  const moe_linear_t w2{MOE_LIN_BF16, Hm, Is, 0, lw->sw2, nullptr};
+  moe::DenseParams dn = dense_params(L.h, T, &w2);
+  dn.mode = moe::kDnAddBf16;
+  dn.addend = L.up;
+  dn.c = out;
+  dn.ldc = Hm;
+  e = moe::launch_dense(dn, s, nullptr, lev1);
+  return device_status(e, "shared down");
+}
+
 }  // extern "C"

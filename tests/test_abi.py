@@ -14,7 +14,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 from mixture_experts_ffn_softmax_amd import _lib
 from mixture_experts_ffn_softmax_amd._lib import (MOE_ERR_ALIGN, MOE_ERR_NULL, MOE_ERR_SHAPE,
                                                   MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_OK,
-                                                  MoeDebug, MoeWeights)
+                                                  MoeDebug, MoeLatent, MoeLinear, MoeWeights)
 
 HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "moe.h")
 
@@ -62,18 +62,21 @@ def test_struct_layouts(tmp_path):
     src = tmp_path / "layout.c"
     src.write_text(
         '#include <stddef.h>\n#include <stdio.h>\n#include "moe.h"\n'
-        'int main(void) { printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu %zu\\n", sizeof(moe_weights_t),'
+        'int main(void) { printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu\\n", sizeof(moe_weights_t),'
         ' offsetof(moe_weights_t, w1), offsetof(moe_weights_t, s2), sizeof(moe_debug_t),'
         ' offsetof(moe_debug_t, events), offsetof(moe_debug_t, variant),'
         ' offsetof(moe_debug_t, gemm1_events), offsetof(moe_debug_t, gemm2_events),'
-        ' offsetof(moe_weights_t, act_beta), offsetof(moe_debug_t, layer_events)); return 0; }\n')
+        ' offsetof(moe_weights_t, act_beta), offsetof(moe_debug_t, layer_events),'
+        ' offsetof(moe_debug_t, core_out), sizeof(moe_linear_t), offsetof(moe_linear_t, s),'
+        ' sizeof(moe_latent_t), offsetof(moe_latent_t, sw2)); return 0; }\n')
     exe = tmp_path / "layout"
     subprocess.run([gcc, "-std=c99", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
     got = [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
     assert got == [ctypes.sizeof(MoeWeights), MoeWeights.w1.offset, MoeWeights.s2.offset,
                    ctypes.sizeof(MoeDebug), MoeDebug.events.offset, MoeDebug.variant.offset,
                    MoeDebug.gemm1_events.offset, MoeDebug.gemm2_events.offset, MoeWeights.act_beta.offset,
-                   MoeDebug.layer_events.offset]
+                   MoeDebug.layer_events.offset, MoeDebug.core_out.offset, ctypes.sizeof(MoeLinear),
+                   MoeLinear.s.offset, ctypes.sizeof(MoeLatent), MoeLatent.sw2.offset]
 
 
 def fp8_weights(E=8, H=256, I=128, fmt=0, layout=0, **over):
@@ -209,3 +212,72 @@ def test_pack_weights_validation(lib):
     assert call(src, fp8_weights(E, H, I, layout=1, w1=0x100000 + n // 2, w3=base, w2=base + n)) == MOE_ERR_SHAPE
     assert call(src, fp8_weights(E, H, I, layout=1, w1=base, w3=base + n // 2, w2=base + 2 * n)) == MOE_ERR_SHAPE
     assert call(src, fp8_weights(E, H, I, layout=1, w1=base + 8)) == MOE_ERR_ALIGN
+
+
+def linear_w(fmt=0, n_out=256, n_in=128, w=A, s=A, reserved=0):
+    return MoeLinear(fmt, n_out, n_in, reserved, w, s if fmt == 0 else None)
+
+
+def test_linear_validation(lib):
+    f = lib.moe_linear
+    w = linear_w()
+    assert f(A, 8, None, None, A, None, None) == MOE_ERR_NULL
+    assert f(A, 8, ctypes.byref(linear_w(fmt=2)), None, A, None, None) == MOE_ERR_UNSUPPORTED
+    assert f(A, 8, ctypes.byref(linear_w(n_out=200)), None, A, None, None) == MOE_ERR_SHAPE
+    assert f(A, 8, ctypes.byref(linear_w(n_in=96)), None, A, None, None) == MOE_ERR_SHAPE
+    assert f(A, 8, ctypes.byref(linear_w(s=None)), None, A, None, None) == MOE_ERR_NULL      # MXFP4 scales
+    bf = MoeLinear(1, 256, 128, 0, A, A)
+    assert f(A, 8, ctypes.byref(bf), None, A, None, None) == MOE_ERR_SHAPE                 # bf16 with scales
+    assert f(A, 8, ctypes.byref(linear_w(reserved=1)), None, A, None, None) == MOE_ERR_SHAPE
+    assert f(A, 8, ctypes.byref(linear_w(w=MIS)), None, A, None, None) == MOE_ERR_ALIGN
+    assert f(A, 8, ctypes.byref(w), None, A, A, None) == MOE_ERR_SHAPE                     # two outputs
+    assert f(A, 8, ctypes.byref(w), None, None, None, None) == MOE_ERR_SHAPE               # no output
+    assert f(A, 8, ctypes.byref(w), A, None, A, None) == MOE_ERR_SHAPE                     # addend with f32 out
+    assert f(A, -1, ctypes.byref(w), None, A, None, None) == MOE_ERR_SHAPE
+    assert f(None, 8, ctypes.byref(w), None, A, None, None) == MOE_ERR_NULL
+    assert f(A, 8, ctypes.byref(w), None, MIS, None, None) == MOE_ERR_ALIGN
+    assert f(None, 0, ctypes.byref(w), None, A, None, None) == MOE_OK
+
+
+def latent_w(Hm=512, L=256, Is=384, **over):
+    lw = MoeLatent(linear_w(0, L, Hm), linear_w(0, Hm, L), Is, 0, 4.0, 0, A, A, A)
+    for k, v in over.items():
+        setattr(lw, k, v)
+    return lw
+
+
+def test_latent_forward_validation(lib):
+    fw = lib.moe_latent_forward
+    routed = fp8_weights(E=8, H=256, I=128, fmt=1)
+    lw = latent_w()
+    ws = lib.moe_latent_forward_workspace_size(16, 2, ctypes.byref(routed), ctypes.byref(lw))
+    core = lib.moe_forward_workspace_size(16, 2, ctypes.byref(routed), 0)
+    assert ws > core + 16 * (2 * 256 * 2 + 512 * 4 + 384 * 2)
+
+    def call(T=16, k=2, latent=lw, r=routed, wsb=ws, score=0, out=A, dbg=None, eps=1e-6, gamma=None):
+        return fw(A, A, T, k, score, ctypes.byref(latent) if latent is not None else None, ctypes.byref(r),
+                  gamma, eps, out, ctypes.byref(dbg) if dbg is not None else None, A, wsb, None)
+
+    assert call(latent=None) == MOE_ERR_NULL
+    assert call(latent=latent_w(L=384)) == MOE_ERR_SHAPE                    # routed hidden != latent
+    bad_up = latent_w()
+    bad_up.up = linear_w(0, 512, 384)
+    assert call(latent=bad_up) == MOE_ERR_SHAPE                              # up does not invert down
+    assert call(latent=latent_w(Is=100)) == MOE_ERR_SHAPE
+    assert call(latent=latent_w(shared_activation=3)) == MOE_ERR_UNSUPPORTED
+    assert call(latent=latent_w(shared_activation=1, shared_beta=0.0)) == MOE_ERR_SHAPE
+    assert call(latent=latent_w(sw2=None)) == MOE_ERR_NULL
+    no_shared = latent_w(Is=0, sw1=None, sw3=None, sw2=None)
+    ws0 = lib.moe_latent_forward_workspace_size(16, 2, ctypes.byref(routed), ctypes.byref(no_shared))
+    assert core < ws0 < ws                                                   # no shared buffers
+    assert call(latent=no_shared, wsb=ws0 - 1) == MOE_ERR_WORKSPACE
+    assert call(latent=latent_w(reserved=2)) == MOE_ERR_SHAPE
+    assert call(k=9) == MOE_ERR_SHAPE
+    assert call(score=3) == MOE_ERR_UNSUPPORTED
+    assert call(eps=-1.0, gamma=A) == MOE_ERR_SHAPE
+    assert call(wsb=ws - 1) == MOE_ERR_WORKSPACE
+    assert call(out=None) == MOE_ERR_NULL
+    d = MoeDebug()
+    d.latent = MIS
+    assert call(dbg=d) == MOE_ERR_ALIGN
+    assert call(T=0) == MOE_OK
