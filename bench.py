@@ -45,6 +45,7 @@ def parse():
     ap.add_argument("--config", default="prefill")
     ap.add_argument("--copies", type=int, default=3)
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-share measurement")
+    ap.add_argument("--no-latent", action="store_true", help="skip the LatentMoE block measurement")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=2048,
                     help="tokens in the CPU oracle's sample (FFN + combine of each)")
@@ -152,6 +153,79 @@ class Layer:
             total += 3 * self.H * self.I + 4 * (2 * self.I + self.H)
         io = self.T * self.H * 2 * 2 + self.T * self.E * 4
         return total, io, touched
+
+
+class LatentBlock:
+    """The LatentMoE block (hidden 7168 -> latent 3584 -> 896 MXFP4 experts
+    top-16 + RMSNorm -> 7168, bf16 shared experts 7168 -> 6144 -> 7168) on
+    512 tokens.  Its 15.7 GB of expert weights are far beyond the last-level
+    cache, so one weight copy suffices."""
+
+    def __init__(self):
+        import torch
+
+        import mixture_experts_ffn_softmax_amd as moe
+        import moe_synth
+        self.moe = moe
+        self.blk = b = moe_synth.latent_block_inputs(**moe_synth.LATENT_BLOCK, device="cuda")
+        c = self.cfg = b["cfg"]
+        self.lw = moe.LatentWeights(b["down"], b["up"], b["shared"])
+        self.routed = moe.Weights(b["routed"], "mxfp4")
+        self.out = torch.empty((c["T"], c["Hm"]), dtype=torch.bfloat16, device="cuda")
+        n = moe.latent_forward_workspace_size(c["T"], c["k"], self.lw, self.routed)
+        self.ws = torch.empty((n,), dtype=torch.uint8, device="cuda")
+
+    def step(self, i, events=None, gemm_events=None, layer_events=None):
+        b, c = self.blk, self.cfg
+        g = gemm_events or (None, None)
+        self.moe.moe_latent_forward(b["x"], b["logits"], c["k"], self.lw, self.routed, b["gamma"], b["eps"],
+                                    out=self.out, ws=self.ws, layer_events=layer_events, gemm1_events=g[0],
+                                    gemm2_events=g[1])
+
+    def accounting(self):
+        """(algorithmic bytes, flops, routed gate-up weight bytes) of one block."""
+        import torch
+
+        import moe_synth
+        c = self.cfg
+        T, Hm, L, I, E, k, Is = (c[n] for n in ("T", "Hm", "L", "I", "E", "k", "Is"))
+        touched = int(torch.unique(torch.topk(self.blk["logits"], k, dim=1).indices).numel())
+        expert = moe_synth.weight_bytes_per_expert(L, I, "mxfp4")
+        proj = 2 * (Hm * L // 2 + Hm * L // 32)
+        shared = 3 * Hm * Is * 2
+        io = T * Hm * 2 * 2 + T * E * 4
+        flops = 6.0 * L * I * T * k + 4.0 * T * Hm * L + 6.0 * T * Hm * Is
+        gate_up = touched * 2 * (L * I // 2 + L * I // 32)
+        return touched * expert + proj + shared + io, flops, gate_up, touched
+
+
+def dense_rates(block, reps=20):
+    """Standalone TFLOP/s of the block's projections and of the shared
+    experts' down GEMM (moe_linear, back-to-back launches between two events)."""
+    import torch
+    moe, b, c = block.moe, block.blk, block.cfg
+    T = c["T"]
+    cases = {"down_proj_mxfp4": (b["x"], block.lw.down),
+             "up_proj_mxfp4": (torch.zeros((T, c["L"]), dtype=torch.bfloat16, device="cuda"), block.lw.up),
+             "shared_down_bf16": (torch.zeros((T, c["Is"]), dtype=torch.bfloat16, device="cuda"),
+                                  moe.Linear(b["shared"]["w2"]))}
+    res = {}
+    for name, (a, w) in cases.items():
+        out = torch.empty((T, w.c.n_out), dtype=torch.bfloat16, device="cuda")
+        for _ in range(3):
+            moe.moe_linear(a, w, out=out)
+        ev = make_events(2)
+        torch.cuda.synchronize()
+        ev[0].record()
+        for _ in range(reps):
+            moe.moe_linear(a, w, out=out)
+        ev[1].record()
+        torch.cuda.synchronize()
+        us = ev[0].elapsed_time(ev[1]) / reps * 1e3
+        flops = 2.0 * T * w.c.n_out * w.c.n_in
+        res[name] = {"us": round(us, 2), "TFLOP/s": round(flops / (us * 1e-6) / 1e12, 1),
+                     "frac_bf16_peak": round(flops / (us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    return res
 
 
 def make_events(n):
@@ -333,6 +407,33 @@ def main():
                             "frac_hbm": round(gbs / PEAK_HBM_GBS, 4), "algorithmic_bytes": dbytes + dio,
                             "stage_us_with_events": {n: round(v * 1e3, 2) for n, v in dstage.items()}}
         del dl
+        torch.cuda.empty_cache()
+
+    if not args.no_latent:
+        log("[bench] LatentMoE block (512 tokens, hidden 7168, latent 3584, 896 MXFP4 experts top-16, "
+            "bf16 shared experts 7168->6144->7168)")
+        lb = LatentBlock()
+        ltl = time_layer(lb, 10, 2)
+        lbytes, lflops, gate_up_bytes, ltouched = lb.accounting()
+        lus = percentiles_us(ltl["layer_ms"])
+        g1_us = ltl["g1_ms"] * 1e3
+        result["latent_block"] = {
+            "workload": "LatentMoE block: T=512 hidden=7168 latent=3584 I=3072 E=896 top_k=16 mxfp4, "
+                        "shared 7168->6144->7168 bf16",
+            "us_per_block_dispatch_events": lus, "us_per_block": round(ltl["ms"] * 1e3, 1),
+            "algorithmic_bytes": lbytes, "touched_experts": ltouched,
+            "GB_per_s": round(lbytes / (lus["median"] * 1e-6) / 1e9, 1),
+            "frac_hbm": round(lbytes / (lus["median"] * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+            "TFLOP/s": round(lflops / (lus["median"] * 1e-6) / 1e12, 1),
+            "roofline": {"kernel": "routed gate-up GEMM (MXFP4 weights streamed once)", "bound": "hbm",
+                         "achieved": round(gate_up_bytes / (g1_us * 1e-6) / 1e9, 1), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(gate_up_bytes / (g1_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                         "traffic": None, "avg_launch_us": round(g1_us, 2),
+                         "bytes_per_launch": gate_up_bytes},
+            "core_gemm_us": {"gemm1": round(g1_us, 2), "gemm2": round(ltl["g2_ms"] * 1e3, 2)},
+            "dense": dense_rates(lb),
+        }
+        del lb
         torch.cuda.empty_cache()
 
     if not args.no_cpu_baseline:

@@ -232,22 +232,27 @@ def latent_forward_workspace_size(T, top_k, latent, routed):
 
 
 def moe_latent_forward(x, logits, top_k, latent, routed, norm_gamma=None, norm_eps=1e-6, out=None, ws=None,
-                       debug=None, layer_events=None, score="softmax", stream=None):
+                       debug=None, layer_events=None, gemm1_events=None, gemm2_events=None, score="softmax",
+                       stream=None):
     """The LatentMoE block.  ``debug``: dict of device tensors as for
-    moe_forward plus ``latent`` and ``core_out`` (bf16 [T][L]).  Returns
-    ``out`` (and the core's kernel variant string when debug is given)."""
+    moe_forward plus ``latent`` and ``core_out`` (bf16 [T][L]);
+    ``layer_events`` bracket the block, ``gemm1_events`` / ``gemm2_events``
+    the routed core's GEMMs.  Returns ``out`` (and the core's kernel variant
+    string when debug is given)."""
     T = x.shape[0]
     out = _empty((T, latent.hidden), torch.bfloat16, x.device) if out is None else out
     nbytes = latent_forward_workspace_size(T, top_k, latent, routed)
     if ws is None:
         ws = _empty((max(nbytes, 1),), torch.uint8, x.device)
     dbg = None
-    if debug is not None or layer_events is not None:
+    if debug is not None or any(v is not None for v in (layer_events, gemm1_events, gemm2_events)):
         dbg = MoeDebug()
         for key, t in (debug or {}).items():
             setattr(dbg, key, t.data_ptr())
-        for i, ev in enumerate(layer_events or []):
-            dbg.layer_events[i] = ev.cuda_event
+        for name, evs in (("layer_events", layer_events), ("gemm1_events", gemm1_events),
+                          ("gemm2_events", gemm2_events)):
+            for i, ev in enumerate(evs or []):
+                getattr(dbg, name)[i] = ev.cuda_event
     check(lib().moe_latent_forward(_p(x), _p(logits), T, top_k, _score(score), latent.ref(), routed.ref(),
                                    _p(norm_gamma), float(norm_eps), _p(out),
                                    ctypes.byref(dbg) if dbg is not None else None, _p(ws), ws.numel(),
