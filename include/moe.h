@@ -74,12 +74,14 @@ typedef enum {
 /*
  * Byte layout of each expert's weight matrix [N][K] (N output channels, K
  * contraction bytes).  ROW_MAJOR: byte k of channel n at n*K + k.  K_BLOCKED
- * (fp8 only; written by moe_pack_weights): the matrix is cut into K chunks of
- * C bytes, C = 64 for W1 and W3 and C = 32 for W2, stored chunk after chunk,
- * each chunk holding all N channels: byte k of channel n at
- * (k / C) * N * C + n * C + k % C.  One contraction step of a GEMM tile then
- * reads one contiguous block instead of N short pieces K bytes apart.
- * Experts stay contiguous ([E][...]); scales have one layout for both.
+ * (written by moe_pack_weights): the matrix is cut into K chunks of C bytes,
+ * stored chunk after chunk, each chunk holding all N channels: byte k of
+ * channel n at (k / C) * N * C + n * C + k % C.  FP8: C = 64 for W1 and W3,
+ * C = 32 for W2, the per-channel scales unchanged.  MXFP4: C = 64 for the
+ * codes of W1, W3 and W2 (128 elements) and the e8m0 scales K-blocked too,
+ * with C = 4 (the 4 scales of the same 128 elements).  One contraction step
+ * of a GEMM tile then reads one contiguous block instead of N short pieces
+ * K bytes apart.  Experts stay contiguous ([E][...]).
  */
 typedef enum {
   MOE_LAYOUT_ROW_MAJOR = 0,
@@ -120,7 +122,7 @@ typedef enum {
  *   fmt = MXFP4: w1, w3  uint8 [E][I][H/2]    s1, s3  uint8 [E][I][H/32]
  *                w2      uint8 [E][H][I/2]    s2      uint8 [E][H][I/32]
  *                (element 2i in the low nibble of byte i; scale 255 = NaN is
- *                 not allowed; row-major only)
+ *                 not allowed; w* and s* in `layout`)
  */
 typedef struct {
   int32_t fmt;       /* moe_wfmt_t */
@@ -293,13 +295,15 @@ moe_status_t moe_forward(const uint16_t* x, const float* logits, int32_t T, int3
                          void* stream);
 
 /*
- * moe_pack_weights -- copy row-major fp8 expert weights into the K-blocked
+ * moe_pack_weights -- copy row-major expert weights into the K-blocked
  * layout (see moe_wlayout_t), once, when the weights are loaded.
- *   src  fmt FP8, layout ROW_MAJOR, device pointers
+ *   src  layout ROW_MAJOR, device pointers
  *   dst  the same fmt, n_experts, hidden and inter, layout K_BLOCKED;
  *        dst->w1, w3, w2 are caller buffers of the sizes of src's, disjoint
- *        from them; dst->s1, s3, s2 are not written (scales are the same in
- *        both layouts and may alias src's)
+ *        from them and from each other.  FP8: dst->s1, s3, s2 are not
+ *        written (the per-channel scales are the same in both layouts and may
+ *        alias src's).  MXFP4: dst->s1, s3, s2 receive the K-blocked scales
+ *        (caller buffers of the sizes of src's, disjoint like the codes)
  * The codes are only moved, never changed: the layer computes the same
  * values from either layout.  The per-step weight tile of the gate-up and
  * down GEMMs becomes one contiguous block, which the direct-to-LDS loads

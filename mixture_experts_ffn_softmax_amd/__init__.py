@@ -39,8 +39,9 @@ class Weights:
 
     ``d`` has w1, w3, w2, s1, s3, s2 as produced by ``moe_synth`` (uint8 codes;
     float32 per-channel scales for fp8, uint8 e8m0 block scales for mxfp4).
-    fp8 weights are repacked once into the K-blocked layout (moe_pack_weights)
-    unless ``pack`` is False; ``self.tensors`` keeps the row-major originals.
+    The weights are repacked once into the K-blocked layout (moe_pack_weights;
+    for MXFP4 the block scales too) unless ``pack`` is False; ``self.tensors``
+    keeps the row-major originals.
     ``activation``: "silu" or "situ" (with ``beta``).
     """
 
@@ -56,10 +57,12 @@ class Weights:
         self.activation, self.beta = activation, beta
         self.c = MoeWeights(self.fmt, E, H, I, MOE_LAYOUT_ROW_MAJOR, act, beta, 0, *ptrs)
         self.packed = None
-        if pack and self.fmt == MOE_W_FP8:
-            self.packed = {k: torch.empty_like(t[k]) for k in ("w1", "w3", "w2")}
-            dst = MoeWeights(self.fmt, E, H, I, MOE_LAYOUT_K_BLOCKED, act, beta, 0,
-                             *(self.packed[k].data_ptr() for k in ("w1", "w3", "w2")), *ptrs[3:])
+        if pack:
+            moved = ("w1", "w3", "w2") + (("s1", "s3", "s2") if self.fmt == MOE_W_MXFP4 else ())
+            self.packed = {k: torch.empty_like(t[k]) for k in moved}
+            dst_ptrs = [(self.packed[k] if k in self.packed else t[k]).data_ptr()
+                        for k in ("w1", "w3", "w2", "s1", "s3", "s2")]
+            dst = MoeWeights(self.fmt, E, H, I, MOE_LAYOUT_K_BLOCKED, act, beta, 0, *dst_ptrs)
             check(lib().moe_pack_weights(ctypes.byref(self.c), ctypes.byref(dst), _stream(stream)))
             self.c = dst
 

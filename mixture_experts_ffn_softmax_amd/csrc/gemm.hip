@@ -76,7 +76,8 @@ struct GemmParams {
   const uint8_t* wb[2];  // GEMM1: W3 (up)
   const void* sa[2];
   const void* sb[2];
-  Operand wd[2];         // byte addressing of one expert's weight matrix (fp8)
+  Operand wd[2];         // byte addressing of one expert's weight matrix (codes)
+  Operand sd[2];         // byte addressing of one expert's e8m0 scales (MXFP4)
   int act[2];            // GEMM1: gate Activation of the routed / shared group
   float beta[2];         // GEMM1: SiTU's beta per group
   uint16_t* h;           // GEMM1 output: bf16, K-blocked (kHChunk-byte chunks)
@@ -753,8 +754,10 @@ __device__ __forceinline__ void gemm1_small_body(const GemmParams& p, const Tile
     const long crow = n0 + (f & 1) * 16 + l16;
     const uint8_t* W = m ? Wb : Wa;
     const uint8_t* S = reinterpret_cast<const uint8_t*>(m ? p.sb[ti.wi] : p.sa[ti.wi]);
-    wp[f] = fp4 ? W + crow * rowBytes + lg * 16 : W + crow * wd.row_pitch;
-    sp[f] = fp4 ? (S + (ti.eg * (long)p.N + crow) * (K >> 5)) : nullptr;  // K/32 e8m0 per row
+    // MXFP4: this lane's codes [16*lg, 16*lg + 16) and the 4 scales of a K
+    // step, addressed through the (row-major or K-blocked) operands
+    wp[f] = fp4 ? W + op_off(wd, crow, lg * 16) : W + crow * wd.row_pitch;
+    sp[f] = fp4 ? S + ti.eg * (long)p.N * (K >> 5) + op_off(p.sd[ti.wi], crow, 0) : nullptr;
   }
   auto tok = [&](int t, long k) {
     return *reinterpret_cast<const uint4*>(tp[t] + ((k >> td.kc_shift) * td.chunk_stride + (k & ((1L << td.kc_shift) - 1))));
@@ -781,9 +784,9 @@ __device__ __forceinline__ void gemm1_small_body(const GemmParams& p, const Tile
     if constexpr (fp4) {
 #pragma unroll
       for (int f = 0; f < 4; ++f) {
-        const uint4 b0 = *reinterpret_cast<const uint4*>(wp[f] + ((long)ks << 6));
+        const uint4 b0 = *reinterpret_cast<const uint4*>(wp[f] + (long)ks * op_step(wd, 64));
         st.w[f] = v8i{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, 0, 0, 0, 0};
-        st.sc[f] = (int)*reinterpret_cast<const uint32_t*>(sp[f] + ks * 4);
+        st.sc[f] = (int)*reinterpret_cast<const uint32_t*>(sp[f] + (long)ks * op_step(p.sd[ti.wi], 4));
       }
     } else {
 #pragma unroll
@@ -894,8 +897,10 @@ __device__ __forceinline__ void gemm2_small_body(const GemmParams& p, const Tile
 #pragma unroll
   for (int f = 0; f < NF; ++f) {
     const long crow = n0 + f * 16 + l16;
-    wp[f] = fp4 ? W2 + crow * rowBytes + lg * 16 : W2 + crow * wd.row_pitch;
-    sp[f] = fp4 ? (reinterpret_cast<const uint8_t*>(p.sa[0]) + (ti.eg * (long)p.N + crow) * (K >> 5)) : nullptr;
+    wp[f] = fp4 ? W2 + op_off(wd, crow, lg * 16) : W2 + crow * wd.row_pitch;
+    sp[f] = fp4 ? (reinterpret_cast<const uint8_t*>(p.sa[0]) + ti.eg * (long)p.N * (K >> 5) +
+                   op_off(p.sd[0], crow, lg))
+                : nullptr;
   }
   auto hpiece = [&](int t, long k) {
     return *reinterpret_cast<const uint4*>(tp[t] + ((k >> td.kc_shift) * td.chunk_stride + (k & ((1L << td.kc_shift) - 1))));
@@ -923,8 +928,8 @@ __device__ __forceinline__ void gemm2_small_body(const GemmParams& p, const Tile
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
       if constexpr (fp4) {
-        st.w[f][0] = *reinterpret_cast<const uint4*>(wp[f] + ((long)ks << 6));
-        st.sc[f] = sp[f][ks * 4 + lg];
+        st.w[f][0] = *reinterpret_cast<const uint4*>(wp[f] + (long)ks * op_step(wd, 64));
+        st.sc[f] = sp[f][(long)ks * op_step(p.sd[0], 4)];
       } else {
         const long k = ((long)ks << 7) + lg * 32;
         st.w[f][0] = wgt(f, k);
@@ -1041,6 +1046,30 @@ __global__ __launch_bounds__(256) void pack_kblocked_kernel(const uint8_t* __res
   }
 }
 
+// The same with chunks of 4 bytes: one thread per 4 bytes of dst.
+__global__ __launch_bounds__(256) void pack_kblocked4_kernel(const uint32_t* __restrict__ src,
+                                                             uint32_t* __restrict__ dst, int N, int K4,
+                                                             long total4) {
+  const long per_e = (long)N * K4;
+  for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < total4; i += (long)gridDim.x * blockDim.x) {
+    const long e = i / per_e;
+    const long r1 = i - e * per_e;
+    const long c = r1 / N;
+    const long n = r1 - c * N;
+    dst[i] = src[e * per_e + n * K4 + c];
+  }
+}
+
+hipError_t launch_pack_kblocked4(const uint8_t* src, uint8_t* dst, int E, int N, int K, hipStream_t s) {
+  const long total4 = (long)E * N * (K / 4);
+  if (total4 == 0) return hipSuccess;
+  long blocks = (total4 + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  pack_kblocked4_kernel<<<(unsigned)blocks, 256, 0, s>>>(reinterpret_cast<const uint32_t*>(src),
+                                                         reinterpret_cast<uint32_t*>(dst), N, K / 4, total4);
+  return hipGetLastError();
+}
+
 hipError_t launch_pack_kblocked(const uint8_t* src, uint8_t* dst, int E, int N, int K, int C, hipStream_t s) {
   const long total16 = (long)E * N * K / 16;
   if (total16 == 0) return hipSuccess;
@@ -1102,7 +1131,10 @@ hipError_t launch_gemm1(int variant, const FfnGroups& g, const RowOperand& x, co
     p.wb[i] = g.w3[i];
     p.sa[i] = g.s1[i];
     p.sb[i] = g.s3[i];
-    p.wd[i] = g.blocked[i] ? k_blocked_operand(g.inter, kW13Chunk) : row_major_operand(g.hidden);
+    const bool fp4 = i == 0 && g.fmt == kMxfp4;
+    p.wd[i] = g.blocked[i] ? k_blocked_operand(g.inter, fp4 ? kFp4Chunk : kW13Chunk)
+                           : row_major_operand(fp4 ? g.hidden / 2 : g.hidden);
+    p.sd[i] = g.blocked[i] ? k_blocked_operand(g.inter, kFp4ScaleChunk) : row_major_operand(g.hidden / 32);
     p.act[i] = g.act[i];
     p.beta[i] = g.beta[i];
   }
@@ -1138,7 +1170,10 @@ hipError_t launch_gemm2(int variant, const FfnGroups& g, const uint16_t* h, cons
   for (int i = 0; i < 2; ++i) {
     p.wa[i] = g.w2[i];
     p.sa[i] = g.s2[i];
-    p.wd[i] = g.blocked[i] ? k_blocked_operand(g.hidden, kW2Chunk) : row_major_operand(g.inter);
+    const bool fp4 = i == 0 && g.fmt == kMxfp4;
+    p.wd[i] = g.blocked[i] ? k_blocked_operand(g.hidden, fp4 ? kFp4Chunk : kW2Chunk)
+                           : row_major_operand(fp4 ? g.inter / 2 : g.inter);
+    p.sd[i] = g.blocked[i] ? k_blocked_operand(g.hidden, kFp4ScaleChunk) : row_major_operand(g.inter / 32);
   }
   p.y = y;
   const int bm = variant_rows(variant);

@@ -39,6 +39,10 @@ constexpr int kTokChunk = 64;
 constexpr int kW13Chunk = 64;
 constexpr int kHChunk = 64;
 constexpr int kW2Chunk = 32;
+// MXFP4 weights K-blocked: codes in 64-byte chunks (128 elements, one MFMA
+// step of either GEMM) and e8m0 scales in 4-byte chunks (the same 128).
+constexpr int kFp4Chunk = 64;
+constexpr int kFp4ScaleChunk = 4;
 
 // ---- router ---------------------------------------------------------------
 // sigmoid: scores 1 / (1 + e^-l) instead of the softmax; same selection.
@@ -135,6 +139,8 @@ hipError_t launch_gemm2(int variant, const FfnGroups& g, const uint16_t* h, cons
 // Copies E matrices of [N][K] bytes into the K-blocked layout with C-byte chunks.
 hipError_t launch_pack_kblocked(const uint8_t* src, uint8_t* dst, int E, int N, int K, int C,
                                 hipStream_t s);
+// The same for chunks of 4 bytes (C = 4; K a multiple of 4).
+hipError_t launch_pack_kblocked4(const uint8_t* src, uint8_t* dst, int E, int N, int K, hipStream_t s);
 
 // ---- combine --------------------------------------------------------------
 hipError_t launch_combine(const float* y_rows, const int* pair_to_row, const float* w, int T,

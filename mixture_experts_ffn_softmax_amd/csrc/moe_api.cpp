@@ -90,8 +90,6 @@ moe_status_t check_weights(const moe_weights_t* w, const char* name) {
   MOE_CHECK(check_dim(w->inter, "inter"));
   if (w->layout != MOE_LAYOUT_ROW_MAJOR && w->layout != MOE_LAYOUT_K_BLOCKED)
     return fail(MOE_ERR_UNSUPPORTED, "%s: unknown weight layout %d", name, w->layout);
-  if (w->layout == MOE_LAYOUT_K_BLOCKED && w->fmt != MOE_W_FP8_E4M3_PERCHANNEL)
-    return fail(MOE_ERR_UNSUPPORTED, "%s: the K-blocked layout exists for fp8 weights only", name);
   if (w->reserved != 0) return fail(MOE_ERR_SHAPE, "%s: reserved field must be 0", name);
   if (w->activation != MOE_ACT_SILU && w->activation != MOE_ACT_SITU)
     return fail(MOE_ERR_UNSUPPORTED, "%s: unknown activation %d", name, w->activation);
@@ -481,31 +479,50 @@ moe_status_t moe_forward(const uint16_t* x, const float* logits, int32_t T, int3
 moe_status_t moe_pack_weights(const moe_weights_t* src, const moe_weights_t* dst, void* stream) {
   MOE_CHECK(check_weights(src, "src"));
   MOE_CHECK(check_weights(dst, "dst"));
-  if (src->fmt != MOE_W_FP8_E4M3_PERCHANNEL)
-    return fail(MOE_ERR_UNSUPPORTED, "only fp8 weights have a K-blocked layout");
   if (src->layout != MOE_LAYOUT_ROW_MAJOR) return fail(MOE_ERR_SHAPE, "src must be row-major");
   if (dst->layout != MOE_LAYOUT_K_BLOCKED) return fail(MOE_ERR_SHAPE, "dst must be K-blocked");
   if (dst->fmt != src->fmt || dst->n_experts != src->n_experts || dst->hidden != src->hidden ||
       dst->inter != src->inter)
     return fail(MOE_ERR_SHAPE, "dst shape differs from src");
-  const size_t bytes13 = (size_t)src->n_experts * src->inter * src->hidden;
-  const uint8_t* s_[3] = {src->w1, src->w3, src->w2};
-  const uint8_t* d_[3] = {dst->w1, dst->w3, dst->w2};
-  for (int i = 0; i < 3; ++i)
-    for (int j = 0; j < 3; ++j)
-      if (d_[i] < s_[j] + bytes13 && s_[j] < d_[i] + bytes13)
-        return fail(MOE_ERR_SHAPE, "dst weight buffers overlap src's");
-  for (int i = 0; i < 3; ++i)
-    for (int j = i + 1; j < 3; ++j)
-      if (d_[i] < d_[j] + bytes13 && d_[j] < d_[i] + bytes13)
-        return fail(MOE_ERR_SHAPE, "dst weight buffers overlap each other");
-  hipStream_t s = (hipStream_t)stream;
+  const bool fp4 = src->fmt == MOE_W_MXFP4_E2M1_E8M0_G32;
   const int E = src->n_experts, H = src->hidden, I = src->inter;
-  hipError_t e = moe::launch_pack_kblocked(src->w1, const_cast<uint8_t*>(dst->w1), E, I, H, moe::kW13Chunk, s);
-  if (e == hipSuccess)
-    e = moe::launch_pack_kblocked(src->w3, const_cast<uint8_t*>(dst->w3), E, I, H, moe::kW13Chunk, s);
-  if (e == hipSuccess)
-    e = moe::launch_pack_kblocked(src->w2, const_cast<uint8_t*>(dst->w2), E, H, I, moe::kW2Chunk, s);
+  // the buffers written (codes, and the scales for MXFP4) must not overlap
+  // what is read or each other
+  const size_t code_bytes = (size_t)E * I * H / (fp4 ? 2 : 1);
+  const size_t scale_bytes = (size_t)E * I * H / 32;
+  struct Buf { const void* p; size_t n; };
+  const Buf rd[6] = {{src->w1, code_bytes}, {src->w3, code_bytes}, {src->w2, code_bytes},
+                     {src->s1, fp4 ? scale_bytes : 0}, {src->s3, fp4 ? scale_bytes : 0},
+                     {src->s2, fp4 ? scale_bytes : 0}};
+  const Buf wr[6] = {{dst->w1, code_bytes}, {dst->w3, code_bytes}, {dst->w2, code_bytes},
+                     {dst->s1, fp4 ? scale_bytes : 0}, {dst->s3, fp4 ? scale_bytes : 0},
+                     {dst->s2, fp4 ? scale_bytes : 0}};
+  auto overlap = [](const Buf& a, const Buf& b) {
+    const uint8_t* pa = static_cast<const uint8_t*>(a.p);
+    const uint8_t* pb = static_cast<const uint8_t*>(b.p);
+    return a.n && b.n && pa < pb + b.n && pb < pa + a.n;
+  };
+  for (int i = 0; i < 6; ++i) {
+    for (int j = 0; j < 6; ++j)
+      if (overlap(wr[i], rd[j])) return fail(MOE_ERR_SHAPE, "dst weight buffers overlap src's");
+    for (int j = i + 1; j < 6; ++j)
+      if (overlap(wr[i], wr[j])) return fail(MOE_ERR_SHAPE, "dst weight buffers overlap each other");
+  }
+  hipStream_t s = (hipStream_t)stream;
+  auto u8 = [](const void* p) { return const_cast<uint8_t*>(static_cast<const uint8_t*>(p)); };
+  hipError_t e;
+  if (!fp4) {
+    e = moe::launch_pack_kblocked(src->w1, u8(dst->w1), E, I, H, moe::kW13Chunk, s);
+    if (e == hipSuccess) e = moe::launch_pack_kblocked(src->w3, u8(dst->w3), E, I, H, moe::kW13Chunk, s);
+    if (e == hipSuccess) e = moe::launch_pack_kblocked(src->w2, u8(dst->w2), E, H, I, moe::kW2Chunk, s);
+    return device_status(e, "pack_weights");
+  }
+  e = moe::launch_pack_kblocked(src->w1, u8(dst->w1), E, I, H / 2, moe::kFp4Chunk, s);
+  if (e == hipSuccess) e = moe::launch_pack_kblocked(src->w3, u8(dst->w3), E, I, H / 2, moe::kFp4Chunk, s);
+  if (e == hipSuccess) e = moe::launch_pack_kblocked(src->w2, u8(dst->w2), E, H, I / 2, moe::kFp4Chunk, s);
+  if (e == hipSuccess) e = moe::launch_pack_kblocked4(u8(src->s1), u8(dst->s1), E, I, H / 32, s);
+  if (e == hipSuccess) e = moe::launch_pack_kblocked4(u8(src->s3), u8(dst->s3), E, I, H / 32, s);
+  if (e == hipSuccess) e = moe::launch_pack_kblocked4(u8(src->s2), u8(dst->s2), E, H, I / 32, s);
   return device_status(e, "pack_weights");
 }
 

@@ -140,7 +140,6 @@ def test_expert_ffn_validation(lib):
     assert f(A, A, -1, A, ctypes.byref(w), A, A, ws, None) == MOE_ERR_SHAPE
     assert f(A, A, 64, A, ctypes.byref(w), A, A, ws - 1, None) == MOE_ERR_WORKSPACE
     assert f(A, A, 64, A, ctypes.byref(fp8_weights(layout=2)), A, A, ws, None) == MOE_ERR_UNSUPPORTED
-    assert f(A, A, 64, A, ctypes.byref(fp8_weights(fmt=1, layout=1)), A, A, ws, None) == MOE_ERR_UNSUPPORTED
     assert f(A, A, 64, A, ctypes.byref(fp8_weights(reserved=1)), A, A, ws, None) == MOE_ERR_SHAPE
     assert f(A, A, 64, A, ctypes.byref(fp8_weights(activation=2)), A, A, ws, None) == MOE_ERR_UNSUPPORTED
     assert f(A, A, 64, A, ctypes.byref(fp8_weights(activation=1, act_beta=0.0)), A, A, ws, None) == MOE_ERR_SHAPE
@@ -205,7 +204,16 @@ def test_pack_weights_validation(lib):
     dst = fp8_weights(E, H, I, layout=1, w1=base, w3=base + n, w2=base + 2 * n)
     call = lambda a, b: pk(ctypes.byref(a), ctypes.byref(b), None)
     assert pk(None, ctypes.byref(dst), None) == MOE_ERR_NULL
-    assert call(fp8_weights(E, H, I, fmt=1), dst) == MOE_ERR_UNSUPPORTED
+    assert call(fp8_weights(E, H, I, fmt=1), dst) == MOE_ERR_SHAPE          # formats differ
+    # MXFP4: the scales are written too, so they must not overlap src's
+    n4, s4 = n // 2, n // 32
+    msrc = fp8_weights(E, H, I, fmt=1, w1=0x100000, w3=0x100000 + n4, w2=0x100000 + 2 * n4,
+                       s1=0x200000, s3=0x200000 + s4, s2=0x200000 + 2 * s4)
+    mdst = dict(fmt=1, layout=1, w1=base, w3=base + n4, w2=base + 2 * n4)
+    assert call(msrc, fp8_weights(E, H, I, s1=0x200000 + s4 // 2, s3=base + 3 * n4, s2=base + 4 * n4,
+                                  **mdst)) == MOE_ERR_SHAPE
+    assert call(msrc, fp8_weights(E, H, I, s1=base + 3 * n4, s3=base + 3 * n4 + s4 // 2, s2=base + 4 * n4,
+                                  **mdst)) == MOE_ERR_SHAPE
     assert call(dst, dst) == MOE_ERR_SHAPE                      # src not row-major
     assert call(src, src) == MOE_ERR_SHAPE                      # dst not K-blocked
     assert call(src, fp8_weights(E, H, 256, layout=1, w1=base, w3=base + 2 * n, w2=base + 4 * n)) == MOE_ERR_SHAPE

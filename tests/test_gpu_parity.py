@@ -164,7 +164,8 @@ FULL_CASES = {
 
 # (case, pack): fp8 weights K-blocked (the default) or left row-major
 FULL_RUNS = [(case, True) for case in FULL_CASES] + [
-    ("ragged_small_variant", False), ("large_variant_shared", False), ("one_token", False)]
+    ("ragged_small_variant", False), ("large_variant_shared", False), ("one_token", False),
+    ("mxfp4_rmsnorm", False), ("mxfp4_k_equals_E", False)]
 
 
 @pytest.mark.parametrize("case,pack", FULL_RUNS)
@@ -361,6 +362,7 @@ def synthetic_rows(counts, H, seed):
     # fragments per wave row (rows mod 256 = 188, 34, 1, 33, 232, 88, 97)
     ([700, 0, 290, 513, 33, 1000, 600, 97], "fp8", True, "silu"),
     ([9, 33, 0, 2, 16, 1, 0, 20], "mxfp4", False, "silu"),
+    ([9, 33, 0, 2, 16, 1, 0, 20], "mxfp4", True, "silu"),
     # SiTU in each GEMM1 variant
     ([5, 0, 17, 1, 40, 0, 3, 32], "fp8", True, "situ"),
     ([300, 0, 129, 64, 1], "fp8", True, "situ"),
@@ -426,9 +428,27 @@ def test_pack_weights(lib, E, H, I):
     w = lib.Weights(W, "fp8", pack=True)
     torch.cuda.synchronize()
     assert w.layout == lib.MOE_LAYOUT_K_BLOCKED
+    assert set(w.packed) == {"w1", "w3", "w2"}          # per-channel scales stay as they are
     for name, C in (("w1", 64), ("w3", 64), ("w2", 32)):
         src = host(W[name])
         N, K = src.shape[1], src.shape[2]
         want = src.reshape(E, N, K // C, C).transpose(0, 2, 1, 3).reshape(-1)
         got = host(w.packed[name]).reshape(-1)
         assert (got == want).all(), name
+
+
+
+@pytest.mark.parametrize("E,H,I", [(3, 256, 128), (2, 384, 640)])
+def test_pack_weights_mxfp4(lib, E, H, I):
+    """MXFP4: codes in 64-byte chunks and e8m0 scales in 4-byte chunks, both
+    dst[e][c][n][0:C] == src[e][n][c*C:(c+1)*C], bit for bit."""
+    say("pack_weights mxfp4", E, H, I)
+    W = to_device(moe_synth.expert_weights(6, "cpu", "mxfp4", E, H, I))
+    w = lib.Weights(W, "mxfp4", pack=True)
+    torch.cuda.synchronize()
+    assert w.layout == lib.MOE_LAYOUT_K_BLOCKED
+    for name, C in (("w1", 64), ("w3", 64), ("w2", 64), ("s1", 4), ("s3", 4), ("s2", 4)):
+        src = host(W[name])
+        N, K = src.shape[1], src.shape[2]
+        want = src.reshape(E, N, K // C, C).transpose(0, 2, 1, 3).reshape(-1)
+        assert (host(w.packed[name]).reshape(-1) == want).all(), name
