@@ -733,8 +733,15 @@ __device__ __forceinline__ void gemm1_small_body(const GemmParams& p, const Tile
   // e4m3 lane group holds K [16*lg, 16*lg + 16) in its first 16 bytes and
   // K [64 + 16*lg, 64 + 16*lg + 16) in its last 16, so the token bytes are
   // fetched from those positions to pair each product with the right K.
-  const int tok_off0 = fp4 ? lg * 16 : lg * 32;
-  const int tok_off1 = fp4 ? 64 + lg * 16 : lg * 32 + 16;
+  //
+  // The contraction is a sum over K, so any assignment of K elements to lane
+  // groups serves as long as both operands use the same one.  Against e4m3
+  // weights lane group lg takes K [16*lg, +16) and [64 + 16*lg, +16) of the
+  // step as well: one load instruction then reads 16 weight rows x 64
+  // contiguous bytes, a whole K-blocked chunk row block, instead of half of
+  // two.
+  const int tok_off0 = lg * 16;
+  const int tok_off1 = 64 + lg * 16;
   // 16-byte pieces never straddle a K chunk of either layout, so each piece
   // is addressed through its operand's layout
   const Operand& td = p.ta[ti.wi];
@@ -790,7 +797,7 @@ __device__ __forceinline__ void gemm1_small_body(const GemmParams& p, const Tile
       }
     } else {
 #pragma unroll
-      for (int f = 0; f < 4; ++f) st.w[f] = as_v8i(wgt(f, kb + lg * 32), wgt(f, kb + lg * 32 + 16));
+      for (int f = 0; f < 4; ++f) st.w[f] = as_v8i(wgt(f, kb + tok_off0), wgt(f, kb + tok_off1));
     }
   };
   auto compute = [&](const St& st) {
@@ -865,8 +872,13 @@ __global__ __launch_bounds__(256) void gemm1_small_kernel(GemmParams p) {
 }
 
 // GEMM2: 16x16x32 bf16 MFMA; W2 codes converted to bf16 in registers.  Lane
-// group lg takes elements [32*lg, 32*lg + 32) of the 128-wide K step on both
-// operands; sub-step i of the 4 instructions uses elements [8i, 8i + 8).
+// group lg takes 32 elements of the 128-wide K step on both operands (the
+// sum over K does not care which, as long as both agree); sub-step i of the 4
+// instructions uses 8 of them.  MXFP4: elements [32*lg, +32) (16 bytes of a
+// 64-byte chunk, so a load reads 16 rows x 64 contiguous bytes); sub-step i:
+// [32*lg + 8i, +8).  e4m3: [16*lg, +16) and [64 + 16*lg, +16), so each of the
+// two loads reads 16 rows of two adjacent 32-byte chunks whole; sub-step i:
+// [64*(i/2) + 16*lg + 8*(i%2), +8).
 // A tile is kSmCh2 = 128 output channels (8 fragments): with K = I the
 // shortest contraction of the layer, wider tiles keep the launch to about
 // one workgroup per two SIMD pairs.
@@ -924,16 +936,17 @@ __device__ __forceinline__ void gemm2_small_body(const GemmParams& p, const Tile
 #pragma unroll
     for (int t = 0; t < TV; ++t)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) st.x[t][i] = hpiece(t, ((long)ks << 8) + lg * 64 + 16 * i);
+      for (int i = 0; i < 4; ++i)   // byte offsets of the bf16 elements of sub-step i
+        st.x[t][i] = hpiece(t, ((long)ks << 8) + (fp4 ? lg * 64 + 16 * i : 128 * (i >> 1) + 32 * lg + 16 * (i & 1)));
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
       if constexpr (fp4) {
         st.w[f][0] = *reinterpret_cast<const uint4*>(wp[f] + (long)ks * op_step(wd, 64));
         st.sc[f] = sp[f][(long)ks * op_step(p.sd[0], 4)];
       } else {
-        const long k = ((long)ks << 7) + lg * 32;
+        const long k = ((long)ks << 7) + lg * 16;
         st.w[f][0] = wgt(f, k);
-        st.w[f][1] = wgt(f, k + 16);
+        st.w[f][1] = wgt(f, k + 64);
       }
     }
   };
