@@ -26,8 +26,9 @@ Recipe: activations ~ N(0,1) rounded to bf16; router logits ~ N(0,1) in fp32
 (plus, for ``skewed``, a per-expert bias -alpha*1.1*ln(rank) over a seeded
 rank permutation, alpha bisected so the hottest expert gets 4.9-5.1x the mean
 row count); weights ~ 0.02*N(0,1) in fp32, quantised per output row to fp8
-e4m3 with scale amax/448 (torch's float8_e4m3fn cast) or per 32-element block
-to MXFP4 (e2m1 codes, e8m0 scale 2^(floor(log2 amax) - 2)).
+e4m3 with scale amax/448 (torch's float8_e4m3fn cast), per 128 x 128 tile to
+fp8 with one fp32 scale amax/448 per tile ("fp8_block"), or per 32-element
+block to MXFP4 (e2m1 codes, e8m0 scale 2^(floor(log2 amax) - 2)).
 
 Every tensor comes from its own torch.Generator seeded by
 (2026, workload, tensor, expert), so any expert can be regenerated alone.
@@ -78,6 +79,17 @@ def fp8_rows(w):
     return q.contiguous(), s.contiguous()
 
 
+def fp8_blocks(w, block=128):
+    """float32 [N][K] -> (e4m3 codes uint8 [N][K], one scale float32 per
+    block x block tile [N/block][K/block], amax/448 of the tile)."""
+    N, K = w.shape
+    t = w.reshape(N // block, block, K // block, block)
+    amax = t.abs().amax(dim=(1, 3))
+    s = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+    q = (t / s[:, None, :, None]).clamp(-448.0, 448.0).to(torch.float8_e4m3fn)
+    return q.view(torch.uint8).reshape(N, K).contiguous(), s.contiguous()
+
+
 _E2M1_MIDS_DOWN = (0.25, 1.25, 2.5, 5.0)   # a tie here goes to the lower (even) code
 _E2M1_MIDS_UP = (0.75, 1.75, 3.5)          # a tie here goes to the upper (even) code
 
@@ -111,7 +123,7 @@ def expert_weights(cfg, device, fmt, n_experts, hidden, inter, tensors=(T_W1, T_
         codes, scales = [], []
         for e in range(n_experts):
             w = randn(shapes[tid], device, seed_of(cfg, tid, e), WEIGHT_STD)
-            q, s = fp8_rows(w) if fmt == "fp8" else mxfp4_rows(w)
+            q, s = fp8_rows(w) if fmt == "fp8" else fp8_blocks(w) if fmt == "fp8_block" else mxfp4_rows(w)
             codes.append(q)
             scales.append(s)
         out["w" + name] = torch.stack(codes).contiguous()

@@ -34,7 +34,9 @@ accounting against the worked figures the pages print; the LatentMoE block
 experts on the hidden stream, *Kimi K3 on TPU* §2.4-2.5) against exact
 products of representable weights, selection-matrix wiring through the
 pinned core, a closed form of the shared path, torch's float64 linear and
-exact power-of-two scalings.  The numerical MoE
+exact power-of-two scalings; per-block fp8 weights (``fmt="fp8_block"``, one
+scale per 128 x 128 tile, *Ling-2.6-1T on TPU* §5) against a hand-worked
+closed form, the per-channel special case and a brute-force loop.  The numerical MoE
 output as a whole is otherwise "parity unpinned": the pages print no worked
 example of it.
 """

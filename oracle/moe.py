@@ -176,6 +176,14 @@ class ExpertWeights:
                  byte, element 2i in the low nibble); s1, s3 uint8
                  [E][I][H/32], s2 uint8 [E][H][I/32] (e8m0 per 32 consecutive
                  contraction elements of one output channel).
+    fmt "fp8_block": w1, w3, w2 as for "fp8"; s1, s3 float32 [E][I/128][H/128],
+                 s2 float32 [E][H/128][I/128]: one scale per block of 128
+                 output channels x 128 contraction elements, so that
+                 out[n] = sum_k a[k] W[n][k] scale[n // 128][k // 128]
+                 (*Ling-2.6-1T on TPU*, §5, per-block scaling: the scale
+                 depends on the K block and cannot leave the reduction; the
+                 [128, 128] block shape is the block-wise fp8 format the
+                 *Kimi K3 on TPU* page, §3.7, names).
     W1 is the gate projection and W3 the up projection.  The six stacks may
     be any objects with a ``shape`` whose ``[e]`` gives expert e as a NumPy
     array (so very large stacks can be fetched one expert at a time).
@@ -183,7 +191,7 @@ class ExpertWeights:
     """
 
     def __init__(self, fmt, w1, w3, w2, s1, s3, s2, activation="silu", beta=4.0):
-        if fmt not in ("fp8", "mxfp4"):
+        if fmt not in ("fp8", "mxfp4", "fp8_block"):
             raise ValueError(fmt)
         if activation not in ("silu", "situ") or not beta > 0:
             raise ValueError(activation)
@@ -206,10 +214,23 @@ class ExpertWeights:
                     np.asarray(self.s1[e], dtype=np.float64), np.asarray(self.s3[e], dtype=np.float64),
                     np.asarray(self.s2[e], dtype=np.float64))
         ones_i = np.ones(self.inter)
+        if self.fmt == "fp8_block":
+            return (block_scaled(e4m3_decode(self.w1[e]), self.s1[e]),
+                    block_scaled(e4m3_decode(self.w3[e]), self.s3[e]),
+                    block_scaled(e4m3_decode(self.w2[e]), self.s2[e]),
+                    ones_i, ones_i, np.ones(self.hidden))
         return (mxfp4_decode(self.w1[e], self.s1[e]),
                 mxfp4_decode(self.w3[e], self.s3[e]),
                 mxfp4_decode(self.w2[e], self.s2[e]),
                 ones_i, ones_i, np.ones(self.hidden))
+
+
+def block_scaled(W, scales, block=128):
+    """W [N][K] times scale[n // block][k // block] for every element: the
+    per-block weights as the float64 matrix whose plain product with a row
+    gives sum over K blocks of (block dot product) x (block scale), exactly."""
+    sc = np.asarray(scales, dtype=np.float64)
+    return W * np.repeat(np.repeat(sc, block, axis=0), block, axis=1)
 
 
 def silu(z):
