@@ -68,7 +68,8 @@ typedef enum {
 
 typedef enum {
   MOE_W_FP8_E4M3_PERCHANNEL = 0, /* e4m3 codes + one fp32 scale per output channel */
-  MOE_W_MXFP4_E2M1_E8M0_G32 = 1  /* e2m1 pairs + one e8m0 scale per 32 K-elements   */
+  MOE_W_MXFP4_E2M1_E8M0_G32 = 1, /* e2m1 pairs + one e8m0 scale per 32 K-elements   */
+  MOE_W_FP8_E4M3_BLOCK128 = 2    /* e4m3 codes + one fp32 scale per 128x128 tile    */
 } moe_wfmt_t;
 
 /*
@@ -119,6 +120,14 @@ typedef enum {
  *   fmt = FP8:   w1, w3  uint8 [E][I][H]      s1, s3  float [E][I]
  *                w2      uint8 [E][H][I]      s2      float [E][H]
  *                (w* in `layout`: row-major as written, or K-blocked)
+ *   fmt = FP8 BLOCK128: w1, w3, w2 as for FP8;  s1, s3  float [E][I/128][H/128]
+ *                                               s2      float [E][H/128][I/128]
+ *                one scale per tile of 128 output channels x 128 K elements,
+ *                applied to that tile's partial sum inside the reduction:
+ *                out[n] = sum_kb s[n/128][kb] * sum_{k in kb} a[k] W[n][k]
+ *                ([Ling] §5, per-block scaling; the [128, 128] block-wise
+ *                format of the Kimi K3 page, §3.7).  Routed experts only;
+ *                runs on the weight-streaming (small) GEMM variant.
  *   fmt = MXFP4: w1, w3  uint8 [E][I][H/2]    s1, s3  uint8 [E][I][H/32]
  *                w2      uint8 [E][H][I/2]    s2      uint8 [E][H][I/32]
  *                (element 2i in the low nibble of byte i; scale 255 = NaN is

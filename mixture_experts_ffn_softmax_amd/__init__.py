@@ -48,7 +48,7 @@ class Weights:
     def __init__(self, d, fmt, pack=True, stream=None, activation="silu", beta=4.0):
         self.tensors = {k: v.contiguous() for k, v in d.items()}
         t = self.tensors
-        self.fmt = MOE_W_FP8 if fmt == "fp8" else MOE_W_MXFP4
+        self.fmt = {"fp8": MOE_W_FP8, "mxfp4": MOE_W_MXFP4, "fp8_block": _lib.MOE_W_FP8_BLOCK}[fmt]
         E, I = t["w1"].shape[0], t["w1"].shape[1]
         H = t["w2"].shape[1]
         self.n_experts, self.hidden, self.inter = E, H, I

@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmoe.so")
 
 MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_ALIGN, MOE_ERR_WORKSPACE, MOE_ERR_UNSUPPORTED, MOE_ERR_DEVICE = range(7)
-MOE_W_FP8, MOE_W_MXFP4 = 0, 1
+MOE_W_FP8, MOE_W_MXFP4, MOE_W_FP8_BLOCK = 0, 1, 2
 MOE_LAYOUT_ROW_MAJOR, MOE_LAYOUT_K_BLOCKED = 0, 1
 (MOE_STAGE_ROUTE, MOE_STAGE_PERMUTE, MOE_STAGE_GEMM1, MOE_STAGE_GEMM2, MOE_STAGE_COMBINE,
  MOE_N_STAGES) = range(6)

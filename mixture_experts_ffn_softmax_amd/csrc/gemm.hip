@@ -713,18 +713,28 @@ __device__ __forceinline__ void small_pipeline(int wave, int nk, Load&& load, Co
 }
 
 // GEMM1: 16x16x128 MFMA on e4m3 x e4m3, or e2m1 x e4m3 with block scales.
-template <bool FP4, int TV>
+template <int WF, int TV>
 __device__ __forceinline__ void gemm1_small_body(const GemmParams& p, const TileInfo& ti, v4f (*red)[8][64]) {
   constexpr int kSmallDepth1 = 2;
   const int K = p.K;
   const int nk = K >> 7;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l16 = lane & 15, lg = lane >> 4;
-  constexpr bool fp4 = FP4;
+  constexpr bool fp4 = WF == kMxfp4;
+  constexpr bool blk = WF == kFp8Block;       // per-tile scales inside the reduction
   const long rowBytes = fp4 ? (K >> 1) : K;
   const int n0 = ti.nt * (kSmCh / 2);
   const uint8_t* Wa = p.wa[ti.wi] + ti.eg * (long)p.N * rowBytes;
   const uint8_t* Wb = p.wb[ti.wi] + ti.eg * (long)p.N * rowBytes;
+  // per-block fp8: the scales of this tile's channel block for K block ks
+  // (one 128-wide step) are sb1[ks] (gate) and sb3[ks] (up)
+  const float* sb1 = nullptr;
+  const float* sb3 = nullptr;
+  if constexpr (blk) {
+    const long base = (ti.eg * (long)(p.N >> 7) + (n0 >> 7)) * (K >> 7);
+    sb1 = reinterpret_cast<const float*>(p.sa[ti.wi]) + base;
+    sb3 = reinterpret_cast<const float*>(p.sb[ti.wi]) + base;
+  }
 
   // Token fragment bytes [0,16) and [16,32) of lane group lg.  Against e4m3
   // weights both operands take bytes [32*lg, 32*lg + 32) of the K step.
@@ -783,11 +793,16 @@ __device__ __forceinline__ void gemm1_small_body(const GemmParams& p, const Tile
     v8i x[TV];
     v8i w[4];
     int sc[4];
+    float bs[2];
   };
   auto load = [&](int ks, St& st) {
     const long kb = (long)ks << 7;
 #pragma unroll
     for (int t = 0; t < TV; ++t) st.x[t] = as_v8i(tok(t, kb + tok_off0), tok(t, kb + tok_off1));
+    if constexpr (blk) {
+      st.bs[0] = sb1[ks];
+      st.bs[1] = sb3[ks];
+    }
     if constexpr (fp4) {
 #pragma unroll
       for (int f = 0; f < 4; ++f) {
@@ -808,6 +823,13 @@ __device__ __forceinline__ void gemm1_small_body(const GemmParams& p, const Tile
 #pragma unroll
         for (int t = 0; t < TV; ++t) acc[f][t] = mfma16_fp4w(st.w[f], st.x[t], acc[f][t], sc);
       }
+    } else if constexpr (blk) {
+      // one K step is one K block: its partial sum times its scale
+      const v4f zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int f = 0; f < 4; ++f)
+#pragma unroll
+        for (int t = 0; t < TV; ++t) acc[f][t] += st.bs[f >> 1] * mfma16_fp8(st.w[f], st.x[t], zero);
     } else {
 #pragma unroll
       for (int f = 0; f < 4; ++f)
@@ -837,7 +859,7 @@ __device__ __forceinline__ void gemm1_small_body(const GemmParams& p, const Tile
   const float xs = p.a_scale[ti.wi][grow - (ti.wi ? p.shared_row0 : 0)];
   const int ch = n0 + f * 16 + 4 * lg;
   float sg[4] = {1.f, 1.f, 1.f, 1.f}, su[4] = {1.f, 1.f, 1.f, 1.f};
-  if (!fp4) {   // e4m3 weights carry one scale per channel
+  if (!fp4 && !blk) {   // per-channel e4m3 weights carry one scale per channel
     const float4 s1 = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(p.sa[ti.wi]) + ti.eg * p.N + ch);
     const float4 s3 = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(p.sb[ti.wi]) + ti.eg * p.N + ch);
     sg[0] = s1.x; sg[1] = s1.y; sg[2] = s1.z; sg[3] = s1.w;
@@ -862,12 +884,13 @@ __global__ __launch_bounds__(256) void gemm1_small_kernel(GemmParams p) {
   MOE_TILE_PROLOGUE(kSmRows);
   // MXFP4 routed weights; the shared group is always fp8
   const bool two = ti.row1 - ti.row0 > 16;
-  if (FMT == kMxfp4 && ti.wi == 0) {
-    if (two) gemm1_small_body<true, 2>(p, ti, red);
-    else gemm1_small_body<true, 1>(p, ti, red);
+  // the routed group takes FMT; the shared group is always per-channel fp8
+  if (FMT != kFp8 && ti.wi == 0) {
+    if (two) gemm1_small_body<FMT, 2>(p, ti, red);
+    else gemm1_small_body<FMT, 1>(p, ti, red);
   } else {
-    if (two) gemm1_small_body<false, 2>(p, ti, red);
-    else gemm1_small_body<false, 1>(p, ti, red);
+    if (two) gemm1_small_body<kFp8, 2>(p, ti, red);
+    else gemm1_small_body<kFp8, 1>(p, ti, red);
   }
 }
 
@@ -882,7 +905,7 @@ __global__ __launch_bounds__(256) void gemm1_small_kernel(GemmParams p) {
 // A tile is kSmCh2 = 128 output channels (8 fragments): with K = I the
 // shortest contraction of the layer, wider tiles keep the launch to about
 // one workgroup per two SIMD pairs.
-template <bool FP4, int TV>
+template <int WF, int TV>
 __device__ __forceinline__ void gemm2_small_body(const GemmParams& p, const TileInfo& ti, v4f (*red)[2 * kSmCh2 / 16][64]) {
   constexpr int kSmallDepth2 = 1;             // registers go to the 8 fragments instead
   constexpr int NF = kSmCh2 / 16;             // channel fragments
@@ -890,10 +913,16 @@ __device__ __forceinline__ void gemm2_small_body(const GemmParams& p, const Tile
   const int nk = K >> 7;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l16 = lane & 15, lg = lane >> 4;
-  constexpr bool fp4 = FP4;
+  constexpr bool fp4 = WF == kMxfp4;
+  constexpr bool blk = WF == kFp8Block;
   const long rowBytes = fp4 ? (K >> 1) : K;
   const int n0 = ti.nt * kSmCh2;
   const uint8_t* W2 = p.wa[ti.wi] + ti.eg * (long)p.N * rowBytes;
+  // per-block fp8: the 128 channels of the tile form one channel block; the
+  // scale of K block ks (one 128-wide step) is sb2[ks]
+  const float* sb2 = nullptr;
+  if constexpr (blk)
+    sb2 = reinterpret_cast<const float*>(p.sa[ti.wi]) + (ti.eg * (long)(p.N >> 7) + (n0 >> 7)) * (K >> 7);
 
   const Operand& td = p.ta[ti.wi];
   const Operand& wd = p.wd[ti.wi];
@@ -931,8 +960,10 @@ __device__ __forceinline__ void gemm2_small_body(const GemmParams& p, const Tile
     uint4 x[TV][4];
     uint4 w[NF][2];
     uint32_t sc[NF];
+    float bs;
   };
   auto load = [&](int ks, St& st) {
+    if constexpr (blk) st.bs = sb2[ks];
 #pragma unroll
     for (int t = 0; t < TV; ++t)
 #pragma unroll
@@ -962,11 +993,23 @@ __device__ __forceinline__ void gemm2_small_body(const GemmParams& p, const Tile
                                 st.w[f][1].x, st.w[f][1].y, st.w[f][1].z, st.w[f][1].w};
         fp8x32_to_bf16(cw, w);
       }
+      if constexpr (blk) {
+        // one K step is one K block: its partial sum times its scale
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+        for (int t = 0; t < TV; ++t) {
+          v4f part = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int t = 0; t < TV; ++t)
-          acc[f][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w[i], as_v8bf(st.x[t][i]), acc[f][t], 0, 0, 0);
+          for (int i = 0; i < 4; ++i)
+            part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w[i], as_v8bf(st.x[t][i]), part, 0, 0, 0);
+          acc[f][t] += st.bs * part;
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int t = 0; t < TV; ++t)
+            acc[f][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w[i], as_v8bf(st.x[t][i]), acc[f][t], 0, 0, 0);
+      }
     }
   };
   small_pipeline<kSmallDepth2, St>(wave, nk, load, compute);
@@ -983,7 +1026,7 @@ __device__ __forceinline__ void gemm2_small_body(const GemmParams& p, const Tile
     const int f = wave * (NF / 4) + ff;
     const int ch = n0 + f * 16 + 4 * lg;
     float s2v[4] = {1.f, 1.f, 1.f, 1.f};
-    if (!fp4) {
+    if (!fp4 && !blk) {
       const float4 s2 = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(p.sa[ti.wi]) + ti.eg * p.N + ch);
       s2v[0] = s2.x; s2v[1] = s2.y; s2v[2] = s2.z; s2v[3] = s2.w;
     }
@@ -1007,12 +1050,13 @@ __global__ __launch_bounds__(256) void gemm2_small_kernel(GemmParams p) {
   MOE_TILE_PROLOGUE(kSmRows);
   // MXFP4 routed weights; the shared group is always fp8
   const bool two = ti.row1 - ti.row0 > 16;
-  if (FMT == kMxfp4 && ti.wi == 0) {
-    if (two) gemm2_small_body<true, 2>(p, ti, red);
-    else gemm2_small_body<true, 1>(p, ti, red);
+  // the routed group takes FMT; the shared group is always per-channel fp8
+  if (FMT != kFp8 && ti.wi == 0) {
+    if (two) gemm2_small_body<FMT, 2>(p, ti, red);
+    else gemm2_small_body<FMT, 1>(p, ti, red);
   } else {
-    if (two) gemm2_small_body<false, 2>(p, ti, red);
-    else gemm2_small_body<false, 1>(p, ti, red);
+    if (two) gemm2_small_body<kFp8, 2>(p, ti, red);
+    else gemm2_small_body<kFp8, 1>(p, ti, red);
   }
 }
 
@@ -1157,10 +1201,9 @@ hipError_t launch_gemm1(int variant, const FfnGroups& g, const RowOperand& x, co
   if (variant == kVariantSmall) {
     p.ntiles = g.inter / (kSmCh / 2);
     const long grid = max_row_tiles(n_rows, g.n_groups, bm) * p.ntiles;
-    if (g.fmt == kMxfp4)
-      hipExtLaunchKernelGGL(gemm1_small_kernel<kMxfp4>, dim3((unsigned)grid), dim3(256), 0, s, ev_start, ev_stop, 0, p);
-    else
-      hipExtLaunchKernelGGL(gemm1_small_kernel<kFp8>, dim3((unsigned)grid), dim3(256), 0, s, ev_start, ev_stop, 0, p);
+    auto kern = g.fmt == kMxfp4 ? gemm1_small_kernel<kMxfp4>
+                                : g.fmt == kFp8Block ? gemm1_small_kernel<kFp8Block> : gemm1_small_kernel<kFp8>;
+    hipExtLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, s, ev_start, ev_stop, 0, p);
   } else {
     p.ntiles = g.inter / (kLgCh / 2);
     const long grid = max_row_tiles(n_rows, g.n_groups, bm) * p.ntiles;
@@ -1193,10 +1236,9 @@ hipError_t launch_gemm2(int variant, const FfnGroups& g, const uint16_t* h, cons
   if (variant == kVariantSmall) {
     p.ntiles = g.hidden / kSmCh2;
     const long grid = max_row_tiles(n_rows, g.n_groups, bm) * p.ntiles;
-    if (g.fmt == kMxfp4)
-      hipExtLaunchKernelGGL(gemm2_small_kernel<kMxfp4>, dim3((unsigned)grid), dim3(256), 0, s, ev_start, ev_stop, 0, p);
-    else
-      hipExtLaunchKernelGGL(gemm2_small_kernel<kFp8>, dim3((unsigned)grid), dim3(256), 0, s, ev_start, ev_stop, 0, p);
+    auto kern = g.fmt == kMxfp4 ? gemm2_small_kernel<kMxfp4>
+                                : g.fmt == kFp8Block ? gemm2_small_kernel<kFp8Block> : gemm2_small_kernel<kFp8>;
+    hipExtLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, s, ev_start, ev_stop, 0, p);
   } else {
     p.ntiles = g.hidden / kLgCh;
     const long grid = max_row_tiles(n_rows, g.n_groups, bm) * p.ntiles;

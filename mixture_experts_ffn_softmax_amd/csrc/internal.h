@@ -78,7 +78,9 @@ hipError_t launch_meta(const float* logits, bool sigmoid, int T, int E, int k, i
                        int bm, hipStream_t s, hipEvent_t ev_start = nullptr);
 
 // ---- grouped expert FFN ---------------------------------------------------
-enum WeightFormat { kFp8 = 0, kMxfp4 = 1 };
+// kFp8Block: e4m3 codes with one fp32 scale per 128 x 128 tile (channel
+// block x K block); only the small GEMM variants take it.
+enum WeightFormat { kFp8 = 0, kMxfp4 = 1, kFp8Block = 3 };
 enum Activation { kActSilu = 0, kActSitu = 1 };   // gate activation of an expert group
 
 // One grouped GEMM launch covers groups 0..n_groups-1.  Rows of group g are

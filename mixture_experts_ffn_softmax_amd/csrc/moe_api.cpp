@@ -82,7 +82,8 @@ moe_status_t check_dim(int32_t v, const char* name) {
 
 moe_status_t check_weights(const moe_weights_t* w, const char* name) {
   if (!w) return fail(MOE_ERR_NULL, "%s is NULL", name);
-  if (w->fmt != MOE_W_FP8_E4M3_PERCHANNEL && w->fmt != MOE_W_MXFP4_E2M1_E8M0_G32)
+  if (w->fmt != MOE_W_FP8_E4M3_PERCHANNEL && w->fmt != MOE_W_MXFP4_E2M1_E8M0_G32 &&
+      w->fmt != MOE_W_FP8_E4M3_BLOCK128)
     return fail(MOE_ERR_UNSUPPORTED, "%s: unknown weight format %d", name, w->fmt);
   if (w->n_experts < 1 || w->n_experts > moe::kMaxExperts)
     return fail(MOE_ERR_SHAPE, "%s: n_experts = %d outside [1, %d]", name, w->n_experts, moe::kMaxExperts);
@@ -126,7 +127,9 @@ size_t ffn_ws(Carve& c, long n_rows, int n_groups, int inter, int32_t** tile_pre
 
 moe::FfnGroups make_groups(const moe_weights_t* r, const moe_weights_t* sh, const int32_t* offsets) {
   moe::FfnGroups g{};
-  g.fmt = r->fmt == MOE_W_MXFP4_E2M1_E8M0_G32 ? moe::kMxfp4 : moe::kFp8;
+  g.fmt = r->fmt == MOE_W_MXFP4_E2M1_E8M0_G32 ? moe::kMxfp4
+          : r->fmt == MOE_W_FP8_E4M3_BLOCK128   ? moe::kFp8Block
+                                                : moe::kFp8;
   g.n_routed = r->n_experts;
   g.n_groups = r->n_experts + (sh ? 1 : 0);
   g.hidden = r->hidden;

@@ -159,13 +159,17 @@ FULL_CASES = {
     # experts, 8 slots) and a second chunk holding one token
     "meta_wave_T256_E32_k8": (256, 128, 128, 32, 8, "fp8", True, False),
     "meta_wave_T65": (65, 128, 128, 5, 2, "fp8", False, False),
+    # per-block fp8 weights (one scale per 128 x 128 tile), with a per-channel
+    # fp8 shared expert beside them in one launch
+    "block_fp8_small": (45, 384, 256, 6, 3, "fp8_block", False, False),
+    "block_fp8_shared": (300, 256, 384, 4, 2, "fp8_block", True, False),
 }
 
 
 # (case, pack): fp8 weights K-blocked (the default) or left row-major
 FULL_RUNS = [(case, True) for case in FULL_CASES] + [
     ("ragged_small_variant", False), ("large_variant_shared", False), ("one_token", False),
-    ("mxfp4_rmsnorm", False), ("mxfp4_k_equals_E", False)]
+    ("mxfp4_rmsnorm", False), ("mxfp4_k_equals_E", False), ("block_fp8_shared", False)]
 
 
 @pytest.mark.parametrize("case,pack", FULL_RUNS)
@@ -337,6 +341,26 @@ def test_forward_full_size(lib, name, score, act):
     assert ratio <= OUT_TOL
 
 
+def test_forward_block_fp8_decode_full_size(lib):
+    """The decode share (64 tokens, H 8192, I 2048, 8 experts top-2) with
+    per-block fp8 weights: all routing metadata and 16 sampled outputs."""
+    inp = moe_synth.custom_inputs(64, 8192, 2048, 8, 2, fmt="fp8_block", seed=12, device=DEV)
+    c = inp["cfg"]
+    T, E, k = c["T"], c["E"], c["k"]
+    say("forward block fp8 decode full size", c)
+    out, dbg, variant = run_forward(inp)
+    say("  variant", variant)
+    ids, w = oracle.route(host(inp["logits"]), k)
+    counts, offsets = oracle.expert_counts_offsets(ids, E)
+    assert (host(dbg["topk_ids"]) == ids).all() and (host(dbg["expert_counts"]) == counts).all()
+    tokens = np.arange(0, T, 4)
+    ref_out = oracle.moe.forward_sampled(bits(inp["x"]), None, k, oracle_weights(inp["routed"], "fp8_block", lazy=True),
+                                         tokens, routing=(ids, w))
+    ratio = tolerance_ratio(bits(out[torch.as_tensor(tokens, device=DEV)]), ref_out)
+    say("  max|err|/rms", ratio)
+    assert ratio <= OUT_TOL
+
+
 # ----------------------------------------------------------------------------
 # moe_expert_ffn and moe_combine on their own
 # ----------------------------------------------------------------------------
@@ -363,6 +387,8 @@ def synthetic_rows(counts, H, seed):
     ([700, 0, 290, 513, 33, 1000, 600, 97], "fp8", True, "silu"),
     ([9, 33, 0, 2, 16, 1, 0, 20], "mxfp4", False, "silu"),
     ([9, 33, 0, 2, 16, 1, 0, 20], "mxfp4", True, "silu"),
+    ([5, 0, 17, 1, 40, 0, 3, 32], "fp8_block", True, "silu"),
+    ([300, 0, 129, 64, 1], "fp8_block", False, "situ"),
     # SiTU in each GEMM1 variant
     ([5, 0, 17, 1, 40, 0, 3, 32], "fp8", True, "situ"),
     ([300, 0, 129, 64, 1], "fp8", True, "situ"),
