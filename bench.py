@@ -46,6 +46,7 @@ def parse():
     ap.add_argument("--copies", type=int, default=3)
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-share measurement")
     ap.add_argument("--no-latent", action="store_true", help="skip the LatentMoE block measurement")
+    ap.add_argument("--no-block", action="store_true", help="skip the per-block fp8 measurement")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=2048,
                     help="tokens in the CPU oracle's sample (FFN + combine of each)")
@@ -147,7 +148,8 @@ class Layer:
         ids = torch.topk(self.inp["logits"], self.k, dim=1).indices
         touched = int(torch.unique(ids).numel())
         per = moe_synth.weight_bytes_per_expert(self.H, self.I, self.cfg["fmt"])
-        scales = (4 * (2 * self.I + self.H)) if self.cfg["fmt"] == "fp8" else 0
+        scales = {"fp8": 4 * (2 * self.I + self.H),
+                  "fp8_block": 4 * 3 * (self.H // 128) * (self.I // 128)}.get(self.cfg["fmt"], 0)
         total = touched * (per + scales)
         if self.shared is not None:
             total += 3 * self.H * self.I + 4 * (2 * self.I + self.H)
@@ -408,6 +410,23 @@ def main():
                             "stage_us_with_events": {n: round(v * 1e3, 2) for n, v in dstage.items()}}
         del dl
         torch.cuda.empty_cache()
+
+    if not args.no_block:
+        log("[bench] per-block fp8 routed weights (128 x 128 tiles): prefill and decode shares")
+        blk = {}
+        for name in ("prefill_block", "decode_block"):
+            bl = Layer(name, args.copies)
+            btl = time_layer(bl, 20, 3)
+            bus = percentiles_us(btl["layer_ms"])
+            fl, _ = bl.flops()
+            wb, io, _ = bl.weight_bytes_touched()
+            blk[name] = {"us_per_layer_dispatch_events": bus,
+                         "TFLOP/s": round(fl / (bus["median"] * 1e-6) / 1e12, 1),
+                         "GB_per_s": round((wb + io) / (bus["median"] * 1e-6) / 1e9, 1),
+                         "gemm_us": {"gemm1": round(btl["g1_ms"] * 1e3, 2), "gemm2": round(btl["g2_ms"] * 1e3, 2)}}
+            del bl
+            torch.cuda.empty_cache()
+        result["fp8_block"] = blk
 
     if not args.no_latent:
         log("[bench] LatentMoE block (512 tokens, hidden 7168, latent 3584, 896 MXFP4 experts top-16, "

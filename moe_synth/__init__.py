@@ -44,6 +44,11 @@ CONFIGS = {
     "decode":  dict(cfg=3, T=64,    H=8192, I=2048, E=8,   k=2,  fmt="fp8",   shared=False, norm=False, skew=False),
     "latent":  dict(cfg=4, T=512,   H=3584, I=3072, E=896, k=16, fmt="mxfp4", shared=False, norm=True,  skew=False),
     "skewed":  dict(cfg=5, T=16384, H=8192, I=2048, E=256, k=8,  fmt="fp8",   shared=False, norm=False, skew=True),
+    # the prefill and decode shares with per-block fp8 routed weights
+    "prefill_block": dict(cfg=7, T=2048, H=8192, I=2048, E=8, k=2, fmt="fp8_block", shared=True, norm=False,
+                          skew=False),
+    "decode_block":  dict(cfg=8, T=64,   H=8192, I=2048, E=8, k=2, fmt="fp8_block", shared=False, norm=False,
+                          skew=False),
 }
 
 T_LOGITS, T_X, T_W1, T_W3, T_W2, T_SW1, T_SW3, T_SW2, T_RANK, T_DOWN, T_UP = range(11)
@@ -262,7 +267,8 @@ def to_numpy(inputs):
 
 
 def weight_bytes_per_expert(H, I, fmt):
-    return 3 * H * I if fmt == "fp8" else 3 * H * I // 2 + 3 * H * I // 32
+    """Code bytes (and MXFP4's block scales) of one expert's W1, W3, W2."""
+    return 3 * H * I if fmt in ("fp8", "fp8_block") else 3 * H * I // 2 + 3 * H * I // 32
 
 
 def ceil_div(a, b):
