@@ -13,6 +13,9 @@ constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 32;
 constexpr int kPermuteChunk = 1024;  // pairs per counting / ranking chunk
 constexpr int kMetaMaxPairs = 16384; // pairs handled by the single-workgroup metadata kernel
+// ... for at most this many experts: its ballot ranking visits every expert
+// present among a wave's 256 pairs, so its cost grows with E
+constexpr int kMetaMaxE = 64;
 constexpr int kMetaRouteMaxE = 32;   // experts it can also route (one lane per token) ...
 constexpr int kMetaRouteMaxT = 256;  // ... for batches of at most this many tokens
 

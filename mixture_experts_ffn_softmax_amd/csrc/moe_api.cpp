@@ -255,7 +255,7 @@ moe_status_t moe_permute(const uint16_t* x, int32_t T, int32_t H, const int32_t*
   int32_t* hist = c.take<int32_t>(chunks * E);
   int32_t* base = c.take<int32_t>(chunks * E);
   hipError_t e;
-  if (T > 0 && pairs <= moe::kMetaMaxPairs) {
+  if (T > 0 && pairs <= moe::kMetaMaxPairs && E <= moe::kMetaMaxE) {
     // reads topk_ids only (no logits): the const is not written through
     e = moe::launch_meta(nullptr, false, T, E, top_k, const_cast<int32_t*>(topk_ids), nullptr, expert_counts,
                          expert_offsets, 0, pair_to_row, row_to_pair, nullptr, 0, s);
@@ -425,12 +425,12 @@ moe_status_t moe_forward(const uint16_t* x, const float* logits, int32_t T, int3
 
   const moe::FfnGroups g = make_groups(routed, sh ? shared : nullptr, L.offsets);
   const long rows = R + (sh ? T : 0);
-  // Up to kMetaMaxPairs pairs, one workgroup computes the whole routing
-  // metadata (and routes, for at most kMetaRouteMaxE experts and
-  // kMetaRouteMaxT tokens: beyond that one CU's routing takes longer than a
-  // grid-wide router launch); beyond kMetaMaxPairs, route / counts / ranks
+  // Up to kMetaMaxPairs pairs and kMetaMaxE experts, one workgroup computes
+  // the whole routing metadata (and routes, for at most kMetaRouteMaxE
+  // experts and kMetaRouteMaxT tokens: beyond that one CU's routing takes
+  // longer than a grid-wide router launch); beyond, route / counts / ranks
   // run as grid-wide kernels.
-  const bool meta = R <= moe::kMetaMaxPairs;
+  const bool meta = R <= moe::kMetaMaxPairs && E <= moe::kMetaMaxE;
   const bool fused_route = meta && E <= moe::kMetaRouteMaxE && T <= moe::kMetaRouteMaxT;
   if (ev && ev[MOE_STAGE_ROUTE]) hipEventRecord((hipEvent_t)ev[MOE_STAGE_ROUTE], s);
   // the layer's first dispatch (router, or the routing metadata kernel) and

@@ -84,6 +84,8 @@ PERMUTE_CASES = [  # T, H, E, k, hot expert
     (2048, 8192, 8, 2, None),
     (1, 128, 1024, 32, None),
     (5000, 128, 64, 4, None),     # 20000 pairs: the grid-wide counting / ranking kernels
+    (300, 128, 64, 4, None),      # the most experts the single-workgroup kernel takes
+    (300, 128, 65, 4, None),      # one more: the grid-wide kernels
 ]
 
 
