@@ -47,6 +47,8 @@ def parse():
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-share measurement")
     ap.add_argument("--no-latent", action="store_true", help="skip the LatentMoE block measurement")
     ap.add_argument("--no-block", action="store_true", help="skip the per-block fp8 measurement")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip the prefill (headline) measurement: for profiling the other workloads alone")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=2048,
                     help="tokens in the CPU oracle's sample (FFN + combine of each)")
@@ -331,18 +333,9 @@ def cpu_baseline(layer, n_tokens, min_seconds=10.0):
                        f"of {n_tokens} sampled tokens (float64 NumPy); {dt:.1f} s wall in total")
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported in this build "
-              "(the multi-GPU expert-parallel path is designed but not built).", file=sys.stderr)
-        sys.exit(2)
+def measure_prefill(args):
+    """The headline line: the prefill share's layer, its rooflines and stages."""
     import torch
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    if args.copy_kernel:
-        copy_kernel(args.copy_kernel)
-        return
-
     log(f"[bench] workload {args.config}: generating inputs ({args.copies} weight copies)")
     layer = Layer(args.config, args.copies)
     c = layer.cfg
@@ -392,7 +385,26 @@ def main():
                            "flops_per_launch": flops_g1, "avg_launch_us": round(g1_ms * 1e3, 2)},
     }
     del layer
-    torch.cuda.empty_cache()
+    return result
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported in this build "
+              "(the multi-GPU expert-parallel path is designed but not built).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_kernel:
+        copy_kernel(args.copy_kernel)
+        return
+
+    result = {"metric": BASELINE_METRIC, "value": None, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+              "warmup": args.warmup, "higher_is_better": True}
+    if not args.no_prefill:
+        result = measure_prefill(args)
+        torch.cuda.empty_cache()
 
     if not args.no_decode:
         log("[bench] decode share (weight-stream bound)")
