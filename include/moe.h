@@ -41,7 +41,9 @@
  *    next synchronisation.  moe_last_error() gives a thread-local message
  *    for the last non-OK return on the calling thread.
  *  - T = 0 is valid and does nothing.  Inputs holding NaN or Inf give
- *    undefined results.
+ *    undefined values, with one exception: the routing ranks a NaN logit
+ *    as -Inf (below every number; equal values by expert index), so that
+ *    every expert id stays in [0, E).
  *  - Limits: 1 <= E <= 1024; 1 <= top_k <= min(E, 32); T * top_k < 2^31;
  *    H and I multiples of 128 (one MFMA contraction step) and at most 65536;
  *    pointers 16-byte aligned.

@@ -71,6 +71,8 @@ struct GemmParams {
   const void* a[2];
   const float* a_scale[2];
   long shared_row0;
+  const int* gather;     // GEMM1, optional: routed row r reads a[0] row gather[r] / gather_k
+  int gather_k;
   Operand ta[2];         // byte addressing of a[0] / a[1]
   const uint8_t* wa[2];  // GEMM1: W1 (gate), GEMM2: W2 -- [0] routed, [1] shared
   const uint8_t* wb[2];  // GEMM1: W3 (up)
@@ -167,9 +169,22 @@ __device__ __forceinline__ TileInfo find_tile(const GemmParams& p, const int* s_
   return ti;
 }
 
+// Row of a[ti.wi] (and a_scale[ti.wi]) that tile row r reads: the shared
+// group's rows start at shared_row0; routed rows are stored in row order
+// (G = kRowsStored), gathered from the token-order rows through row_to_pair / k
+// (G = kRowsGathered, p.gather set), or either, as p.gather says (kRowsAny).
+enum RowSource { kRowsStored = 0, kRowsGathered = 1, kRowsAny = 2 };
+template <int G = kRowsAny>
+__device__ __forceinline__ long a_row(const GemmParams& p, const TileInfo& ti, int r) {
+  if (ti.wi) return r - p.shared_row0;
+  if constexpr (G == kRowsStored) return r;
+  else if constexpr (G == kRowsGathered) return p.gather[r] / p.gather_k;
+  else return p.gather ? p.gather[r] / p.gather_k : r;
+}
 // Start of row r of the row operand (contraction byte 0).
+template <int G = kRowsAny>
 __device__ __forceinline__ const uint8_t* row_ptr(const GemmParams& p, const TileInfo& ti, int r) {
-  return reinterpret_cast<const uint8_t*>(p.a[ti.wi]) + (r - (ti.wi ? p.shared_row0 : 0)) * p.ta[ti.wi].row_pitch;
+  return reinterpret_cast<const uint8_t*>(p.a[ti.wi]) + a_row<G>(p, ti, r) * p.ta[ti.wi].row_pitch;
 }
 
 // Common prologue: exits surplus workgroups, loads the tile prefix, finds the tile.
@@ -241,7 +256,7 @@ __device__ __forceinline__ void gemm1_pp_epilogue(const GemmParams& p, const Til
   for (int t = 0; t < TV; ++t) {
     int grow = ti.row0 + (2 * t + wm) * 32 + l32;
     if (grow >= ti.row1) grow = ti.row1 - 1;
-    xs[t] = p.a_scale[ti.wi][grow - (ti.wi ? p.shared_row0 : 0)];
+    xs[t] = p.a_scale[ti.wi][a_row(p, ti, grow)];
   }
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
@@ -506,7 +521,7 @@ __device__ __forceinline__ void gemm2_pp_body(const GemmParams& p, const TileInf
       const int row = q * 16 + (lane >> 2);
       int r = ti.row0 + row;
       if (r >= ti.row1) r = ti.row1 - 1;
-      src[i] = row_ptr(p, ti, r) + swz64(row, lane & 3) * 16;
+      src[i] = row_ptr<kRowsStored>(p, ti, r) + swz64(row, lane & 3) * 16;
     } else {
       const int row = (q - kDmaT) * 32 + (lane >> 1);
       src[i] = W2 + (long)(n0 + row) * wd.row_pitch + swz32(row, lane & 1) * 16;
@@ -713,7 +728,7 @@ __device__ __forceinline__ void small_pipeline(int wave, int nk, Load&& load, Co
 }
 
 // GEMM1: 16x16x128 MFMA on e4m3 x e4m3, or e2m1 x e4m3 with block scales.
-template <int WF, int TV>
+template <int WF, int TV, int G>
 __device__ __forceinline__ void gemm1_small_body(const GemmParams& p, const TileInfo& ti, v4f (*red)[8][64]) {
   constexpr int kSmallDepth1 = 2;
   const int K = p.K;
@@ -761,7 +776,7 @@ __device__ __forceinline__ void gemm1_small_body(const GemmParams& p, const Tile
   for (int t = 0; t < 2; ++t) {
     int r = ti.row0 + t * 16 + l16;
     if (r >= ti.row1) r = ti.row1 - 1;
-    tp[t] = row_ptr(p, ti, r);
+    tp[t] = row_ptr<G>(p, ti, r);
   }
   const uint8_t* wp[4];
   const uint8_t* sp[4];
@@ -856,7 +871,7 @@ __device__ __forceinline__ void gemm1_small_body(const GemmParams& p, const Tile
   }
   const int grow = ti.row0 + t * 16 + l16;
   if (grow >= ti.row1) return;
-  const float xs = p.a_scale[ti.wi][grow - (ti.wi ? p.shared_row0 : 0)];
+  const float xs = p.a_scale[ti.wi][a_row<G>(p, ti, grow)];
   const int ch = n0 + f * 16 + 4 * lg;
   float sg[4] = {1.f, 1.f, 1.f, 1.f}, su[4] = {1.f, 1.f, 1.f, 1.f};
   if (!fp4 && !blk) {   // per-channel e4m3 weights carry one scale per channel
@@ -877,20 +892,20 @@ __device__ __forceinline__ void gemm1_small_body(const GemmParams& p, const Tile
   *reinterpret_cast<uint2*>(p.h + h_off(p.h_cs, grow, ch)) = make_uint2(b[0] | (b[1] << 16), b[2] | (b[3] << 16));
 }
 
-template <int FMT>
+// G: where the routed rows come from (RowSource: stored, or gathered)
+template <int FMT, int G>
 __global__ __launch_bounds__(256) void gemm1_small_kernel(GemmParams p) {
   __shared__ v4f red[4][8][64];                 // per-wave partial sums
   __shared__ int s_tp[kMaxExperts + 2];
   MOE_TILE_PROLOGUE(kSmRows);
-  // MXFP4 routed weights; the shared group is always fp8
   const bool two = ti.row1 - ti.row0 > 16;
   // the routed group takes FMT; the shared group is always per-channel fp8
   if (FMT != kFp8 && ti.wi == 0) {
-    if (two) gemm1_small_body<FMT, 2>(p, ti, red);
-    else gemm1_small_body<FMT, 1>(p, ti, red);
+    if (two) gemm1_small_body<FMT, 2, G>(p, ti, red);
+    else gemm1_small_body<FMT, 1, G>(p, ti, red);
   } else {
-    if (two) gemm1_small_body<kFp8, 2>(p, ti, red);
-    else gemm1_small_body<kFp8, 1>(p, ti, red);
+    if (two) gemm1_small_body<kFp8, 2, G>(p, ti, red);
+    else gemm1_small_body<kFp8, 1, G>(p, ti, red);
   }
 }
 
@@ -931,7 +946,7 @@ __device__ __forceinline__ void gemm2_small_body(const GemmParams& p, const Tile
   for (int t = 0; t < 2; ++t) {
     int r = ti.row0 + t * 16 + l16;
     if (r >= ti.row1) r = ti.row1 - 1;
-    tp[t] = row_ptr(p, ti, r);
+    tp[t] = row_ptr<kRowsStored>(p, ti, r);
   }
   const uint8_t* wp[NF];
   const uint8_t* sp[NF];
@@ -1175,6 +1190,8 @@ static GemmParams base_params(const FfnGroups& g, const RowOperand& x, const int
     p.ta[i] = x.d[i];
   }
   p.shared_row0 = x.shared_row0;
+  p.gather = x.gather;
+  p.gather_k = x.gather_k;
   return p;
 }
 
@@ -1201,8 +1218,12 @@ hipError_t launch_gemm1(int variant, const FfnGroups& g, const RowOperand& x, co
   if (variant == kVariantSmall) {
     p.ntiles = g.inter / (kSmCh / 2);
     const long grid = max_row_tiles(n_rows, g.n_groups, bm) * p.ntiles;
-    auto kern = g.fmt == kMxfp4 ? gemm1_small_kernel<kMxfp4>
-                                : g.fmt == kFp8Block ? gemm1_small_kernel<kFp8Block> : gemm1_small_kernel<kFp8>;
+    auto kern = x.gather ? (g.fmt == kMxfp4      ? gemm1_small_kernel<kMxfp4, kRowsGathered>
+                            : g.fmt == kFp8Block ? gemm1_small_kernel<kFp8Block, kRowsGathered>
+                                                 : gemm1_small_kernel<kFp8, kRowsGathered>)
+                         : (g.fmt == kMxfp4      ? gemm1_small_kernel<kMxfp4, kRowsStored>
+                            : g.fmt == kFp8Block ? gemm1_small_kernel<kFp8Block, kRowsStored>
+                                                 : gemm1_small_kernel<kFp8, kRowsStored>);
     hipExtLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, s, ev_start, ev_stop, 0, p);
   } else {
     p.ntiles = g.inter / (kLgCh / 2);

@@ -73,12 +73,24 @@ hipError_t launch_quant_scatter(const uint16_t* x, int T, int H, int k, const in
                                 bool blocked, uint8_t* xq_copy, hipStream_t s);
 // For T * k <= kMetaMaxPairs: counts, offsets (+ the extra group), ranks and,
 // when tile_prefix is non-NULL, the tile prefix of the groups for row tiles
-// of bm, in one launch.  logits non-NULL (T <= kMetaRouteMaxT and
-// E <= kMetaRouteMaxE, else hipErrorInvalidValue): routes first, in one wave,
-// and writes ids / w; logits NULL: reads ids (16 waves).
-hipError_t launch_meta(const float* logits, bool sigmoid, int T, int E, int k, int* ids, float* w, int* counts,
-                       int* offsets, int extra_rows, int* pair_to_row, int* row_to_pair, int* tile_prefix,
-                       int bm, hipStream_t s, hipEvent_t ev_start = nullptr);
+// of bm, from the expert ids, in one launch of one workgroup (16 waves).
+hipError_t launch_meta(int T, int E, int k, const int* ids, int* counts, int* offsets, int extra_rows,
+                       int* pair_to_row, int* row_to_pair, int* tile_prefix, int bm, hipStream_t s);
+// Routing from the logits (ids / w; T <= kMetaRouteMaxT, E <= kMetaRouteMaxE,
+// else hipErrorInvalidValue), the metadata of launch_meta, and the per-token
+// quantisation into token order (xq_tok K-blocked in kTokChunk-byte chunks,
+// xs_tok [T]) in one launch: workgroup 0 runs the routing and metadata in one
+// wave, workgroup 1 + t quantises token t.  The two parts read and write
+// disjoint buffers.
+hipError_t launch_meta_quant(const float* logits, bool sigmoid, const uint16_t* x, int T, int H, int E, int k,
+                             int* ids, float* w, int* counts, int* offsets, int extra_rows, int* pair_to_row,
+                             int* row_to_pair, int* tile_prefix, int bm, uint8_t* xq_tok, float* xs_tok,
+                             hipStream_t s, hipEvent_t ev_start = nullptr);
+// Row-major, expert-ordered copy (xq_rows [T*k][H], xs_rows [T*k]; either may
+// be NULL) of the K-blocked token-order quantised rows: row r holds token
+// row_to_pair[r] / k.
+hipError_t launch_rows_from_tokens(const uint8_t* xq_tok, const float* xs_tok, const int* row_to_pair, int T,
+                                   int k, int H, uint8_t* xq_rows, float* xs_rows, hipStream_t s);
 
 // ---- grouped expert FFN ---------------------------------------------------
 // kFp8Block: e4m3 codes with one fp32 scale per 128 x 128 tile (channel
@@ -118,6 +130,11 @@ struct RowOperand {
   const float* s[2];
   long shared_row0;
   Operand d[2];       // byte addressing of q[0] / q[1]
+  // optional gather of the routed rows: row r < shared_row0 reads row
+  // gather[r] / gather_k of q[0] / s[0] (gather = row_to_pair, q[0] the
+  // token-order rows), so that no expert-ordered copy is needed
+  const int* gather = nullptr;
+  int gather_k = 1;
 };
 
 enum GemmVariant { kVariantSmall = 0, kVariantLarge128 = 1, kVariantLarge256 = 2 };

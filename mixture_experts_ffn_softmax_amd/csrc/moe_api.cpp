@@ -257,8 +257,8 @@ moe_status_t moe_permute(const uint16_t* x, int32_t T, int32_t H, const int32_t*
   hipError_t e;
   if (T > 0 && pairs <= moe::kMetaMaxPairs && E <= moe::kMetaMaxE) {
     // reads topk_ids only (no logits): the const is not written through
-    e = moe::launch_meta(nullptr, false, T, E, top_k, const_cast<int32_t*>(topk_ids), nullptr, expert_counts,
-                         expert_offsets, 0, pair_to_row, row_to_pair, nullptr, 0, s);
+    e = moe::launch_meta(T, E, top_k, topk_ids, expert_counts, expert_offsets, 0, pair_to_row, row_to_pair, nullptr,
+                         0, s);
     if (e != hipSuccess) return device_status(e, "meta");
   } else {
     e = moe::launch_counts(topk_ids, (int)pairs, E, hist, base, expert_counts, expert_offsets, 0, s);
@@ -335,11 +335,29 @@ struct ForwardLayout {
   size_t bytes;
 };
 
+// Up to kMetaMaxPairs pairs and kMetaMaxE experts, one workgroup computes
+// the whole routing metadata; for at most kMetaRouteMaxE experts and
+// kMetaRouteMaxT tokens it also routes, in one wave, and runs in the same
+// launch as the quantisation (beyond that one CU's routing takes longer than
+// a grid-wide router launch).  Beyond kMetaMaxPairs pairs or kMetaMaxE
+// experts, route / counts / ranks run as grid-wide kernels.
+static bool meta_path(int32_t T, int32_t k, int32_t E) {
+  return (long)T * k <= moe::kMetaMaxPairs && E <= moe::kMetaMaxE;
+}
+static bool fused_route_path(int32_t T, int32_t k, int32_t E) {
+  return meta_path(T, k, E) && E <= moe::kMetaRouteMaxE && T <= moe::kMetaRouteMaxT;
+}
+
 static ForwardLayout forward_layout(void* ws, int32_t T, int32_t k, int32_t E, int32_t H, int32_t I,
                                     bool shared) {
   ForwardLayout L{};
   Carve c(ws);
   const long R = (long)T * k;
+  // the fused routing path keeps the quantised tokens in token order only
+  // (the gate-up GEMM gathers each routed row's token); the other paths
+  // scatter them to expert-ordered rows, and keep token order for the
+  // shared expert
+  const bool fused = fused_route_path(T, k, E);
   const long rows = R + (shared ? T : 0);
   const long chunks = moe::permute_chunks(R);
   L.ids = c.take<int32_t>(R);
@@ -350,10 +368,10 @@ static ForwardLayout forward_layout(void* ws, int32_t T, int32_t k, int32_t E, i
   L.r2p = c.take<int32_t>(R);
   L.hist = c.take<int32_t>(chunks * E);
   L.base = c.take<int32_t>(chunks * E);
-  L.xq_rows = c.take<uint8_t>((size_t)R * H);
-  L.xs_rows = c.take<float>(R);
-  L.xq_tok = shared ? c.take<uint8_t>((size_t)T * H) : nullptr;
-  L.xs_tok = shared ? c.take<float>(T) : nullptr;
+  L.xq_rows = fused ? nullptr : c.take<uint8_t>((size_t)R * H);
+  L.xs_rows = fused ? nullptr : c.take<float>(R);
+  L.xq_tok = (shared || fused) ? c.take<uint8_t>((size_t)T * H) : nullptr;
+  L.xs_tok = (shared || fused) ? c.take<float>(T) : nullptr;
   L.y_rows = c.take<float>((size_t)rows * H);
   ffn_ws(c, rows, E + (shared ? 1 : 0), I, &L.tile_prefix, &L.h);
   L.bytes = c.used + 256;
@@ -417,7 +435,7 @@ moe_status_t moe_forward(const uint16_t* x, const float* logits, int32_t T, int3
     if (dbg->expert_offsets) L.offsets = dbg->expert_offsets;
     if (dbg->pair_to_row) L.p2r = dbg->pair_to_row;
     if (dbg->row_to_pair) L.r2p = dbg->row_to_pair;
-    if (dbg->xs_rows) L.xs_rows = dbg->xs_rows;
+    if (dbg->xs_rows && L.xs_rows) L.xs_rows = dbg->xs_rows;
   }
   hipStream_t s = (hipStream_t)stream;
   const long R = (long)T * top_k;
@@ -425,46 +443,52 @@ moe_status_t moe_forward(const uint16_t* x, const float* logits, int32_t T, int3
 
   const moe::FfnGroups g = make_groups(routed, sh ? shared : nullptr, L.offsets);
   const long rows = R + (sh ? T : 0);
-  // Up to kMetaMaxPairs pairs and kMetaMaxE experts, one workgroup computes
-  // the whole routing metadata (and routes, for at most kMetaRouteMaxE
-  // experts and kMetaRouteMaxT tokens: beyond that one CU's routing takes
-  // longer than a grid-wide router launch); beyond, route / counts / ranks
-  // run as grid-wide kernels.
-  const bool meta = R <= moe::kMetaMaxPairs && E <= moe::kMetaMaxE;
-  const bool fused_route = meta && E <= moe::kMetaRouteMaxE && T <= moe::kMetaRouteMaxT;
+  const bool meta = meta_path(T, top_k, E);
+  const bool fused_route = fused_route_path(T, top_k, E);
   if (ev && ev[MOE_STAGE_ROUTE]) hipEventRecord((hipEvent_t)ev[MOE_STAGE_ROUTE], s);
-  // the layer's first dispatch (router, or the routing metadata kernel) and
-  // its last (combine) stamp the optional layer events
+  // the layer's first dispatch (router, or the fused routing + quantisation
+  // kernel) and its last (combine) stamp the optional layer events
   const hipEvent_t lev0 = dbg ? (hipEvent_t)dbg->layer_events[0] : nullptr;
   const hipEvent_t lev1 = dbg ? (hipEvent_t)dbg->layer_events[1] : nullptr;
-  if (!fused_route) {
-    e = moe::launch_route(logits, T, E, top_k, sigmoid, L.ids, L.w, s, lev0);
-    if (e != hipSuccess) return device_status(e, "route");
-  }
-
-  if (ev && ev[MOE_STAGE_PERMUTE]) hipEventRecord((hipEvent_t)ev[MOE_STAGE_PERMUTE], s);
-  if (meta) {
-    const int bm = moe::variant_rows(moe::choose_variant(g, rows));
-    e = moe::launch_meta(fused_route ? logits : nullptr, sigmoid, T, E, top_k, L.ids, L.w, L.counts,
-                         L.offsets, sh ? T : 0, L.p2r, L.r2p, L.tile_prefix, bm, s,
-                         fused_route ? lev0 : nullptr);
-    if (e != hipSuccess) return device_status(e, "meta");
-  } else {
-    e = moe::launch_counts(L.ids, (int)R, E, L.hist, L.base, L.counts, L.offsets, sh ? T : 0, s);
-    if (e != hipSuccess) return device_status(e, "counts");
-    e = moe::launch_rank(L.ids, (int)R, E, L.base, L.p2r, L.r2p, s);
-    if (e != hipSuccess) return device_status(e, "rank");
-  }
-  // the layer keeps the quantised rows K-blocked (64-byte chunks); the debug
-  // capture receives a row-major copy
-  e = moe::launch_quant_scatter(x, T, H, top_k, L.p2r, L.xq_rows, L.xs_rows, L.xq_tok, L.xs_tok, true,
-                                dbg ? dbg->xq_rows : nullptr, s);
-  if (e != hipSuccess) return device_status(e, "quant_scatter");
-
   const moe::Operand rows_d = moe::k_blocked_operand(R, moe::kTokChunk);
   const moe::Operand tok_d = moe::k_blocked_operand(T, moe::kTokChunk);
   moe::RowOperand xr{{L.xq_rows, sh ? L.xq_tok : L.xq_rows}, {L.xs_rows, sh ? L.xs_tok : L.xs_rows}, R,
                      {rows_d, sh ? tok_d : rows_d}};
+  if (fused_route) {
+    // routing, metadata and the token-order quantisation in one launch; the
+    // gate-up GEMM gathers each routed row's token through row_to_pair
+    if (ev && ev[MOE_STAGE_PERMUTE]) hipEventRecord((hipEvent_t)ev[MOE_STAGE_PERMUTE], s);
+    const int bm = moe::variant_rows(moe::choose_variant(g, rows));
+    e = moe::launch_meta_quant(logits, sigmoid, x, T, H, E, top_k, L.ids, L.w, L.counts, L.offsets, sh ? T : 0,
+                               L.p2r, L.r2p, L.tile_prefix, bm, L.xq_tok, L.xs_tok, s, lev0);
+    if (e != hipSuccess) return device_status(e, "meta_quant");
+    if (dbg && (dbg->xq_rows || dbg->xs_rows)) {   // the expert-ordered rows, for inspection
+      e = moe::launch_rows_from_tokens(L.xq_tok, L.xs_tok, L.r2p, T, top_k, H, dbg->xq_rows, dbg->xs_rows, s);
+      if (e != hipSuccess) return device_status(e, "rows_from_tokens");
+    }
+    xr = moe::RowOperand{{L.xq_tok, L.xq_tok}, {L.xs_tok, L.xs_tok}, R, {tok_d, tok_d}};
+    xr.gather = L.r2p;
+    xr.gather_k = top_k;
+  } else {
+    e = moe::launch_route(logits, T, E, top_k, sigmoid, L.ids, L.w, s, lev0);
+    if (e != hipSuccess) return device_status(e, "route");
+    if (ev && ev[MOE_STAGE_PERMUTE]) hipEventRecord((hipEvent_t)ev[MOE_STAGE_PERMUTE], s);
+    if (meta) {
+      const int bm = moe::variant_rows(moe::choose_variant(g, rows));
+      e = moe::launch_meta(T, E, top_k, L.ids, L.counts, L.offsets, sh ? T : 0, L.p2r, L.r2p, L.tile_prefix, bm, s);
+      if (e != hipSuccess) return device_status(e, "meta");
+    } else {
+      e = moe::launch_counts(L.ids, (int)R, E, L.hist, L.base, L.counts, L.offsets, sh ? T : 0, s);
+      if (e != hipSuccess) return device_status(e, "counts");
+      e = moe::launch_rank(L.ids, (int)R, E, L.base, L.p2r, L.r2p, s);
+      if (e != hipSuccess) return device_status(e, "rank");
+    }
+    // the layer keeps the quantised rows K-blocked (64-byte chunks); the
+    // debug capture receives a row-major copy
+    e = moe::launch_quant_scatter(x, T, H, top_k, L.p2r, L.xq_rows, L.xs_rows, L.xq_tok, L.xs_tok, true,
+                                  dbg ? dbg->xq_rows : nullptr, s);
+    if (e != hipSuccess) return device_status(e, "quant_scatter");
+  }
   char* vout = dbg ? dbg->variant : nullptr;
   MOE_CHECK(run_ffn(g, xr, rows, L.y_rows, L.tile_prefix, L.h, s, ev, vout,
                     dbg ? sizeof(dbg->variant) : 0, meta, dbg ? dbg->gemm1_events : nullptr,

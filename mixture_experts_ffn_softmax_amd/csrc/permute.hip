@@ -17,9 +17,10 @@
 //   meta_kernel    one workgroup doing all of the above but the quantisation
 //                  (and the grouped GEMMs' tile prefix) when there are at
 //                  most kMetaMaxPairs pairs: one launch instead of four
-//   meta_wave_kernel  the same plus the routing in a single wave, for at most
-//                  kMetaRouteMaxT tokens and kMetaRouteMaxE experts
-//                  (decode-sized batches, where latency is the cost)
+//   meta_quant_kernel  the same plus the routing in a single wave, for at
+//                  most kMetaRouteMaxT tokens and kMetaRouteMaxE experts
+//                  (decode-sized batches, where latency is the cost), with
+//                  the quantisation into token order in the same launch
 // Rows are ordered by expert and, inside an expert, by pair index; this order
 // is unique, so the result is deterministic.  Expert ids outside [0, E) are
 // skipped (their pairs get row -1) so that no access leaves its buffer.
@@ -158,13 +159,13 @@ __device__ __forceinline__ long code_offset(long r, int idx, int H, long cs) {
 // rows_cs / tok_cs: chunk strides of the K-blocked xq_rows / xq_tok (0 =
 // row-major); xq_copy: optional row-major copy of the xq_rows writes.
 template <int CPT>
-__global__ __launch_bounds__(1024) void quant_scatter_kernel(
-    const uint16_t* __restrict__ x, int H, int k, const int* __restrict__ pair_to_row,
-    uint8_t* __restrict__ xq_rows, float* __restrict__ xs_rows, uint8_t* __restrict__ xq_tok,
-    float* __restrict__ xs_tok, long rows_cs, long tok_cs, uint8_t* __restrict__ xq_copy) {
+__device__ __forceinline__ void quant_token(const uint16_t* __restrict__ x, long t, int H, int k,
+                                            const int* __restrict__ pair_to_row, uint8_t* __restrict__ xq_rows,
+                                            float* __restrict__ xs_rows, uint8_t* __restrict__ xq_tok,
+                                            float* __restrict__ xs_tok, long rows_cs, long tok_cs,
+                                            uint8_t* __restrict__ xq_copy) {
   __shared__ float red[16];
   __shared__ int s_rows[kMaxTopK];
-  const long t = blockIdx.x;
   const int nchk = H >> 3;
   const uint4* src = reinterpret_cast<const uint4*>(x + t * H);
   // the token's rows, fetched first so that their latency overlaps the row's
@@ -217,6 +218,14 @@ __global__ __launch_bounds__(1024) void quant_scatter_kernel(
     }
     if (threadIdx.x == 0) xs_tok[t] = s;
   }
+}
+
+template <int CPT>
+__global__ __launch_bounds__(1024) void quant_scatter_kernel(
+    const uint16_t* __restrict__ x, int H, int k, const int* __restrict__ pair_to_row,
+    uint8_t* __restrict__ xq_rows, float* __restrict__ xs_rows, uint8_t* __restrict__ xq_tok,
+    float* __restrict__ xs_tok, long rows_cs, long tok_cs, uint8_t* __restrict__ xq_copy) {
+  quant_token<CPT>(x, blockIdx.x, H, k, pair_to_row, xq_rows, xs_rows, xq_tok, xs_tok, rows_cs, tok_cs, xq_copy);
 }
 
 // ---------------------------------------------------------------------------
@@ -382,7 +391,7 @@ __global__ __launch_bounds__(1024) void meta_kernel(int T, int E, int k, const i
   }
 }
 
-// meta_wave_kernel: the same results as meta_kernel with routing, for at
+// meta_wave_body: the same results as meta_kernel with routing, for at
 // most kMetaRouteMaxT tokens and kMetaRouteMaxE experts, in ONE wave with no
 // workgroup barrier between its phases (decode-sized batches, where each
 // phase of the 16-wave kernel costs a barrier and a memory round trip).
@@ -400,7 +409,12 @@ __device__ __forceinline__ uint32_t wave_route_token(const float* __restrict__ l
   float v[NE];
   const float* row = logits + (long)t * E;
 #pragma unroll
-  for (int i = 0; i < NE; ++i) v[i] = (i < E) ? row[i] : 0.0f;
+  for (int i = 0; i < NE; ++i) {
+    // a NaN logit ranks below every number, so that each pick is a valid
+    // expert (the ids index LDS and the row buffers below)
+    const float l = (i < E) ? row[i] : 0.0f;
+    v[i] = (l == l) ? l : -INFINITY;
+  }
   uint32_t avail = (E >= 32) ? 0xFFFFFFFFu : ((1u << E) - 1u);
   const uint32_t all = avail;
   float vmax = 0.0f, sum = 0.0f;
@@ -436,16 +450,32 @@ __device__ __forceinline__ int wave_inclusive_scan(int v) {
   return v;
 }
 
-__global__ __launch_bounds__(64) void meta_wave_kernel(const float* __restrict__ logits, bool sigmoid, int T,
-                                                       int E, int k, int* __restrict__ ids,
-                                                       float* __restrict__ w, int* __restrict__ counts,
-                                                       int* __restrict__ offsets, int extra_rows,
-                                                       int* __restrict__ pair_to_row,
-                                                       int* __restrict__ row_to_pair,
-                                                       int* __restrict__ tile_prefix, int bm) {
-  __shared__ int s_ids[kMetaRouteMaxT * kMaxTopK];
-  __shared__ uint64_t s_m[kMetaRouteMaxE * kWaveChunks];   // ballot of expert e over chunk i
-  __shared__ int s_base[kMetaRouteMaxE * kWaveChunks];     // first row of chunk i's pairs of e
+// The LDS of the single-wave metadata: a token's pair ids, each expert's
+// ballot per token chunk, and each expert's first row per chunk.
+struct MetaWaveLds {
+  int ids[kMetaRouteMaxT * kMaxTopK];
+  uint64_t m[kMetaRouteMaxE * kWaveChunks];
+  int base[kMetaRouteMaxE * kWaveChunks];
+};
+
+// The single wave's LDS writes are seen by its later reads (the LDS serves a
+// wave's instructions in order); this keeps the compiler from moving them.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Run by the threads 0..63 (one wave) of a block.
+__device__ __forceinline__ void meta_wave_body(const float* __restrict__ logits, bool sigmoid, int T, int E, int k,
+                                               int* __restrict__ ids, float* __restrict__ w,
+                                               int* __restrict__ counts, int* __restrict__ offsets, int extra_rows,
+                                               int* __restrict__ pair_to_row, int* __restrict__ row_to_pair,
+                                               int* __restrict__ tile_prefix, int bm, MetaWaveLds& L) {
+  int* s_ids = L.ids;
+  uint64_t* s_m = L.m;
+  int* s_base = L.base;
+
   const int lane = threadIdx.x;
   const int nch = (T + 63) >> 6;
 
@@ -472,7 +502,7 @@ __global__ __launch_bounds__(64) void meta_wave_kernel(const float* __restrict__
       }
     }
   }
-  __syncthreads();
+  wave_lds_sync();
 
   // ---- lane e: count, offset (scan over the lanes), chunk bases
   int c[kWaveChunks];
@@ -507,7 +537,7 @@ __global__ __launch_bounds__(64) void meta_wave_kernel(const float* __restrict__
     if (lane < G) tile_prefix[lane] = tincl - tiles;
     if (lane == G - 1) tile_prefix[G] = tincl;
   }
-  __syncthreads();
+  wave_lds_sync();
 
   // ---- rows, in pair order (coalesced pair_to_row)
   const int R = T * k;
@@ -520,6 +550,93 @@ __global__ __launch_bounds__(64) void meta_wave_kernel(const float* __restrict__
     pair_to_row[p] = row;
     row_to_pair[row] = p;
   }
+}
+
+// meta_quant_kernel: workgroup 0's first wave computes the routed metadata
+// (meta_wave_body), workgroup 1 + t quantises token t into token order.  The
+// metadata reads only the logits and the quantisation only x, so nothing
+// waits across workgroups.  At most 512 threads per workgroup, so that the
+// routing wave keeps its registers (about 200) without spilling.
+constexpr int kMetaQuantThreads = 512;
+template <int CPT>
+__global__ __launch_bounds__(kMetaQuantThreads) void meta_quant_kernel(const float* __restrict__ logits, bool sigmoid,
+                                                          const uint16_t* __restrict__ x, int T, int H, int E,
+                                                          int k, int* __restrict__ ids, float* __restrict__ w,
+                                                          int* __restrict__ counts, int* __restrict__ offsets,
+                                                          int extra_rows, int* __restrict__ pair_to_row,
+                                                          int* __restrict__ row_to_pair,
+                                                          int* __restrict__ tile_prefix, int bm,
+                                                          uint8_t* __restrict__ xq_tok, float* __restrict__ xs_tok,
+                                                          long tok_cs) {
+  if (blockIdx.x == 0) {
+    __shared__ MetaWaveLds L;
+    if (threadIdx.x < 64)
+      meta_wave_body(logits, sigmoid, T, E, k, ids, w, counts, offsets, extra_rows, pair_to_row, row_to_pair,
+                     tile_prefix, bm, L);
+    return;
+  }
+  quant_token<CPT>(x, (long)blockIdx.x - 1, H, 0, nullptr, nullptr, nullptr, xq_tok, xs_tok, 0, tok_cs, nullptr);
+}
+
+// Expert-ordered, row-major copy of quantised rows from the token-order rows
+// (K-blocked, tok_cs): row r holds token row_to_pair[r] / k.  One block per row.
+__global__ __launch_bounds__(256) void rows_from_tokens_kernel(const uint8_t* __restrict__ xq_tok,
+                                                               const float* __restrict__ xs_tok,
+                                                               const int* __restrict__ row_to_pair, int k, int H,
+                                                               long tok_cs, uint8_t* __restrict__ xq_rows,
+                                                               float* __restrict__ xs_rows) {
+  const long r = blockIdx.x;
+  const long t = row_to_pair[r] / k;
+  if (xq_rows)
+    for (int idx = threadIdx.x; idx < (H >> 3); idx += blockDim.x)
+      *reinterpret_cast<uint2*>(xq_rows + r * H + (long)idx * 8) =
+          *reinterpret_cast<const uint2*>(xq_tok + code_offset(t, idx, H, tok_cs));
+  if (xs_rows && threadIdx.x == 0) xs_rows[r] = xs_tok[t];
+}
+
+hipError_t launch_rows_from_tokens(const uint8_t* xq_tok, const float* xs_tok, const int* row_to_pair, int T,
+                                   int k, int H, uint8_t* xq_rows, float* xs_rows, hipStream_t s) {
+  const long R = (long)T * k;
+  if (R == 0 || (!xq_rows && !xs_rows)) return hipSuccess;
+  rows_from_tokens_kernel<<<(unsigned)R, 256, 0, s>>>(xq_tok, xs_tok, row_to_pair, k, H, (long)T * kTokChunk,
+                                                       xq_rows, xs_rows);
+  return hipGetLastError();
+}
+
+// Threads per token-quantising workgroup and chunks of 8 elements per thread
+// for a row of H elements (H a multiple of 128): at most max_threads, a
+// multiple of 64.
+static void quant_shape(int H, int max_threads, int* threads, int* cpt) {
+  const int chunks = H / 8;
+  int c = 1;
+  while (chunks > max_threads * c) c *= 2;
+  const int t = (chunks + c - 1) / c;
+  *threads = ((t + 63) / 64) * 64;
+  *cpt = c;
+}
+
+hipError_t launch_meta_quant(const float* logits, bool sigmoid, const uint16_t* x, int T, int H, int E, int k,
+                             int* ids, float* w, int* counts, int* offsets, int extra_rows, int* pair_to_row,
+                             int* row_to_pair, int* tile_prefix, int bm, uint8_t* xq_tok, float* xs_tok,
+                             hipStream_t s, hipEvent_t ev_start) {
+  if (T == 0) return hipSuccess;
+  if (!logits || T > kMetaRouteMaxT || E > kMetaRouteMaxE) return hipErrorInvalidValue;
+  int threads = 64, cpt = 1;
+  quant_shape(H, kMetaQuantThreads, &threads, &cpt);
+  const long tok_cs = (long)T * kTokChunk;
+#define MOE_MQ(C)                                                                                           \
+  hipExtLaunchKernelGGL(meta_quant_kernel<C>, dim3(T + 1), dim3(threads), 0, s, ev_start, nullptr, 0, logits, \
+                        sigmoid, x, T, H, E, k, ids, w, counts, offsets, extra_rows, pair_to_row, row_to_pair,  \
+                        tile_prefix, bm, xq_tok, xs_tok, tok_cs)
+  switch (cpt) {
+    case 1: MOE_MQ(1); break;
+    case 2: MOE_MQ(2); break;
+    case 4: MOE_MQ(4); break;
+    case 8: MOE_MQ(8); break;
+    default: MOE_MQ(16); break;   // H up to 65536
+  }
+#undef MOE_MQ
+  return hipGetLastError();
 }
 
 hipError_t launch_counts(const int* ids, int pairs, int E, int* chunk_hist, int* chunk_base,
@@ -544,11 +661,8 @@ hipError_t launch_quant_scatter(const uint16_t* x, int T, int H, int k, const in
   if (T == 0) return hipSuccess;
   const long rows_cs = blocked ? (long)T * k * kTokChunk : 0;
   const long tok_cs = blocked ? (long)T * kTokChunk : 0;
-  const int chunks = H / 8;  // H is a multiple of 128: chunks is a multiple of 16
-  int cpt = 1;
-  while (chunks > 1024 * cpt) cpt *= 2;
-  int threads = (chunks + cpt - 1) / cpt;
-  threads = ((threads + 63) / 64) * 64;
+  int threads = 64, cpt = 1;
+  quant_shape(H, 1024, &threads, &cpt);
 #define MOE_QS(C)                                                                          \
   quant_scatter_kernel<C><<<T, threads, 0, s>>>(x, H, k, pair_to_row, xq_rows, xs_rows, xq_tok, \
                                                 xs_tok, rows_cs, tok_cs, xq_copy)
@@ -562,15 +676,8 @@ hipError_t launch_quant_scatter(const uint16_t* x, int T, int H, int k, const in
   return hipGetLastError();
 }
 
-hipError_t launch_meta(const float* logits, bool sigmoid, int T, int E, int k, int* ids, float* w, int* counts,
-                       int* offsets, int extra_rows, int* pair_to_row, int* row_to_pair, int* tile_prefix,
-                       int bm, hipStream_t s, hipEvent_t ev_start) {
-  if (logits && T <= kMetaRouteMaxT && E <= kMetaRouteMaxE) {
-    hipExtLaunchKernelGGL(meta_wave_kernel, dim3(1), dim3(64), 0, s, ev_start, nullptr, 0, logits, sigmoid, T, E, k,
-                          ids, w, counts, offsets, extra_rows, pair_to_row, row_to_pair, tile_prefix, bm);
-    return hipGetLastError();
-  }
-  if (logits) return hipErrorInvalidValue;   // routing needs T <= kMetaRouteMaxT, E <= kMetaRouteMaxE
+hipError_t launch_meta(int T, int E, int k, const int* ids, int* counts, int* offsets, int extra_rows,
+                       int* pair_to_row, int* row_to_pair, int* tile_prefix, int bm, hipStream_t s) {
   meta_kernel<<<1, 1024, 0, s>>>(T, E, k, ids, counts, offsets, extra_rows, pair_to_row, row_to_pair,
                                  tile_prefix, bm);
   return hipGetLastError();

@@ -40,7 +40,8 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
   for (int i = 0; i < kRouteSlots; ++i) {
     const int e = i * 64 + lane;
     const bool ok = (i < slots) && (e < E);
-    v[i] = ok ? row[e] : 0.0f;
+    const float l = ok ? row[e] : 0.0f;
+    v[i] = (l == l) ? l : -INFINITY;   // a NaN logit ranks below every number
     avail |= ok ? (1u << i) : 0u;
   }
 

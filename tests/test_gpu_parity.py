@@ -14,6 +14,7 @@ import torch
 
 import moe_synth
 import oracle
+from oracle import moe
 from gpu_helpers import (DEV, OUT_TOL, assert_weights_close, bits, check_metadata, host,
                          oracle_weights, run_forward, say, to_device, tolerance_ratio)
 
@@ -258,6 +259,29 @@ def test_forward_route_ties(lib, E, k, score):
     assert tolerance_ratio(bits(out), ref["out_exact"]) <= OUT_TOL
 
 
+@pytest.mark.parametrize("T", [64, 300])
+def test_forward_nan_logits_route_valid_experts(lib, T):
+    """NaN logits (no infinities) rank below every number, equal ones by
+    expert index, as in the oracle's sort; the ids, counts and permutation
+    stay exact whichever router runs (single-wave at T=64, grid-wide at
+    T=300).  Other outputs of such rows are not defined and not checked."""
+    E, k = 8, 2
+    inp = moe_synth.custom_inputs(T, 128, 128, E, k, seed=T)
+    logits = inp["logits"].clone()
+    logits[::5] = float("nan")                 # whole rows
+    logits[1::5, 0:E:3] = float("nan")         # some experts of a row
+    inp["logits"] = logits
+    say("forward nan logits", T)
+    _, dbg, _ = run_forward(to_device(inp))
+    ids, _ = moe.route(logits.numpy(), k)
+    counts, offsets = moe.expert_counts_offsets(ids, E)
+    p2r, r2p, _, _ = moe.permute_rows(ids, offsets, np.zeros((T, 1), np.uint8), np.zeros(T, np.float32))
+    assert (host(dbg["topk_ids"]) == ids).all()
+    assert (host(dbg["expert_counts"]) == counts).all()
+    assert (host(dbg["pair_to_row"]) == p2r).all()
+    assert (host(dbg["row_to_pair"]) == r2p).all()
+
+
 def test_forward_zero_tokens(lib):
     inp = to_device(moe_synth.custom_inputs(0, 256, 128, 4, 2))
     out, _, _ = run_forward(inp, capture=False)
@@ -266,7 +290,7 @@ def test_forward_zero_tokens(lib):
 
 @pytest.mark.parametrize("T", [64, 300])
 def test_forward_dispatch_events(lib, T):
-    """The layer events stamped by the first (routing metadata kernel at T=64,
+    """The layer events stamped by the first (fused routing + quantisation kernel at T=64,
     router at T=300) and last dispatch bracket the GEMMs' own events, and the
     output is the same as without events."""
     inp = to_device(moe_synth.custom_inputs(T, 256, 256, 4, 2, seed=5, shared=True))
