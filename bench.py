@@ -58,6 +58,7 @@ def parse():
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "moe_layer_prefill_hbm_traffic.txt")
+DECODE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "moe_layer_decode_hbm_traffic.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "mixture_experts_ffn_softmax_amd", "csrc", f)
                   for f in ("gemm.hip", "device_common.h", "internal.h")]
 
@@ -70,14 +71,14 @@ def kernel_source_hash():
     return h.hexdigest()
 
 
-def measured_traffic(which):
+def measured_traffic(which, path=TRAFFIC_FILE):
     """HBM bytes per launch of GEMM `which` ("gemm1" / "gemm2") from the
-    committed counter summary, or None when the summary is absent or the
-    kernel sources changed since it was taken."""
-    if not os.path.exists(TRAFFIC_FILE):
+    committed counter summary `path`, or None when the summary is absent or
+    the kernel sources changed since it was taken."""
+    if not os.path.exists(path):
         return None
     fields = {}
-    for line in open(TRAFFIC_FILE):
+    for line in open(path):
         if ":" in line and not line.startswith("#"):
             key, val = line.split(":", 1)
             fields[key.strip()] = val.strip()
@@ -157,6 +158,22 @@ class Layer:
             total += 3 * self.H * self.I + 4 * (2 * self.I + self.H)
         io = self.T * self.H * 2 * 2 + self.T * self.E * 4
         return total, io, touched
+
+    def gemm_bytes(self):
+        """Algorithmic HBM bytes of one gate-up and one down GEMM launch:
+        the touched experts' weights (and scales) read once, the quantised
+        token rows read once, h written and read once (bf16), the fp32
+        expert output rows written once."""
+        total, _, touched = self.weight_bytes_touched()
+        if self.cfg["fmt"] != "fp8":
+            return None, None
+        rows = self.T * self.k + (self.T if self.shared is not None else 0)
+        experts = touched + (1 if self.shared is not None else 0)
+        w13 = experts * (2 * self.H * self.I + 4 * 2 * self.I)
+        w2 = experts * (self.H * self.I + 4 * self.H)
+        g1 = w13 + self.T * (self.H + 4) + rows * self.I * 2
+        g2 = w2 + rows * self.I * 2 + rows * self.H * 4
+        return g1, g2
 
 
 class LatentBlock:
@@ -414,11 +431,21 @@ def main():
         dstage = stage_times(dl, 20)
         dbytes, dio, dtouched = dl.weight_bytes_touched()
         gbs = (dbytes + dio) / (dms * 1e-3) / 1e9
+        g1b, g2b = dl.gemm_bytes()
+        groof = {}
+        for name, nbytes, ms, what in (("gemm1", g1b, dtl["g1_ms"], "gate-up grouped GEMM (fp8 weights streamed once)"),
+                                       ("gemm2", g2b, dtl["g2_ms"], "down grouped GEMM (fp8 weights streamed once)")):
+            gb = nbytes / (ms * 1e-3) / 1e9
+            groof[name] = {"kernel": what, "bound": "hbm", "achieved": round(gb, 1), "peak": PEAK_HBM_GBS,
+                           "unit": "GB/s", "frac": round(gb / PEAK_HBM_GBS, 4),
+                           "traffic": measured_traffic(name, DECODE_TRAFFIC_FILE),
+                           "avg_launch_us": round(ms * 1e3, 2), "bytes_per_launch": nbytes}
         result["decode"] = {"workload": "decode: T=64 H=8192 I=2048 E=8 top_k=2 fp8",
                             "us_per_layer": round(dms * 1e3, 1), "us_per_layer_gpu_events": round(dgpu_ms * 1e3, 1),
                             "us_per_layer_dispatch_events": percentiles_us(dtl["layer_ms"]),
                             "GB_per_s": round(gbs, 1),
                             "frac_hbm": round(gbs / PEAK_HBM_GBS, 4), "algorithmic_bytes": dbytes + dio,
+                            "roofline_gemm1": groof["gemm1"], "roofline_gemm2": groof["gemm2"],
                             "stage_us_with_events": {n: round(v * 1e3, 2) for n, v in dstage.items()}}
         del dl
         torch.cuda.empty_cache()
