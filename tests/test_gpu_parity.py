@@ -162,6 +162,10 @@ FULL_CASES = {
     # experts, 8 slots) and a second chunk holding one token
     "meta_wave_T256_E32_k8": (256, 128, 128, 32, 8, "fp8", True, False),
     "meta_wave_T65": (65, 128, 128, 5, 2, "fp8", False, False),
+    # decode-sized batches whose groups average >= 64 rows: the 128-row
+    # gate-up kernel reading token rows through row_to_pair
+    "gathered_large128_shared": (200, 256, 256, 4, 2, "fp8", True, False),
+    "gathered_large128": (256, 512, 256, 2, 2, "fp8", False, False),
     # per-block fp8 weights (one scale per 128 x 128 tile), with a per-channel
     # fp8 shared expert beside them in one launch
     "block_fp8_small": (45, 384, 256, 6, 3, "fp8_block", False, False),
@@ -172,7 +176,8 @@ FULL_CASES = {
 # (case, pack): fp8 weights K-blocked (the default) or left row-major
 FULL_RUNS = [(case, True) for case in FULL_CASES] + [
     ("ragged_small_variant", False), ("large_variant_shared", False), ("one_token", False),
-    ("mxfp4_rmsnorm", False), ("mxfp4_k_equals_E", False), ("block_fp8_shared", False)]
+    ("mxfp4_rmsnorm", False), ("mxfp4_k_equals_E", False), ("block_fp8_shared", False),
+    ("gathered_large128_shared", False)]
 
 
 @pytest.mark.parametrize("case,pack", FULL_RUNS)
@@ -188,6 +193,8 @@ def test_forward_full(lib, case, pack):
         {key: c[key] for key in ("T", "H", "I", "E", "k", "fmt", "shared", "norm")})
     out, dbg, variant = run_forward(to_device(inp), pack=pack)
     say("  variant", variant)
+    if case.startswith("gathered_large128"):
+        assert "large128" in variant
     ref = oracle.forward(bf16_np(inp["x"]), inp["logits"].numpy(), c["k"],
                          oracle_weights(inp["routed"], c["fmt"]),
                          oracle_weights(inp["shared"], "fp8"),
