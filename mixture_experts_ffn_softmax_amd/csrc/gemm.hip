@@ -121,6 +121,18 @@ __device__ __forceinline__ v4f mfma16_fp4w(const v8i& w, const v8i& x, const v4f
 }
 
 
+// 16 e4m3 codes (4 words) -> 2 x 8 bf16, exact.
+__device__ __forceinline__ void fp8x16_to_bf16(const uint32_t (&w)[4], v8bf (&out)[2]) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const v2bf a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[2 * i], 1.0f, false);
+    const v2bf b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[2 * i], 1.0f, true);
+    const v2bf c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[2 * i + 1], 1.0f, false);
+    const v2bf d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[2 * i + 1], 1.0f, true);
+    out[i] = v8bf{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+  }
+}
+
 // 32 e4m3 codes (8 words) -> 4 x 8 bf16, exact.
 __device__ __forceinline__ void fp8x32_to_bf16(const uint32_t (&w)[8], v8bf (&out)[4]) {
 #pragma unroll
@@ -910,31 +922,36 @@ __global__ __launch_bounds__(256) void gemm1_small_kernel(GemmParams p) {
 }
 
 // GEMM2: 16x16x32 bf16 MFMA; W2 codes converted to bf16 in registers.  Lane
-// group lg takes 32 elements of the 128-wide K step on both operands (the
-// sum over K does not care which, as long as both agree); sub-step i of the 4
-// instructions uses 8 of them.  MXFP4: elements [32*lg, +32) (16 bytes of a
-// 64-byte chunk, so a load reads 16 rows x 64 contiguous bytes); sub-step i:
-// [32*lg + 8i, +8).  e4m3: [16*lg, +16) and [64 + 16*lg, +16), so each of the
-// two loads reads 16 rows of two adjacent 32-byte chunks whole; sub-step i:
-// [64*(i/2) + 16*lg + 8*(i%2), +8).
+// group lg takes a quarter of each K step on both operands (the sum over K
+// does not care which, as long as both agree); sub-step i of the step's
+// instructions uses 8 of them.  MXFP4, 128-wide steps: elements [32*lg, +32)
+// (16 bytes of a 64-byte chunk, so a load reads 16 rows x 64 contiguous
+// bytes); sub-step i of 4: [32*lg + 8i, +8).  e4m3, 64-wide steps: elements
+// [16*lg, +16) (lane groups 0-1 and 2-3 read 16 rows of one 32-byte chunk
+// each, whole); sub-step i of 2: [16*lg + 8i, +8).
 // A tile is kSmCh2 = 128 output channels (8 fragments): with K = I the
 // shortest contraction of the layer, wider tiles keep the launch to about
 // one workgroup per two SIMD pairs.
 template <int WF, int TV>
 __device__ __forceinline__ void gemm2_small_body(const GemmParams& p, const TileInfo& ti, v4f (*red)[2 * kSmCh2 / 16][64]) {
-  constexpr int kSmallDepth2 = 1;             // registers go to the 8 fragments instead
-  constexpr int NF = kSmCh2 / 16;             // channel fragments
-  const int K = p.K;                          // = I
-  const int nk = K >> 7;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int l16 = lane & 15, lg = lane >> 4;
   constexpr bool fp4 = WF == kMxfp4;
   constexpr bool blk = WF == kFp8Block;
+  // K elements per step: e4m3 steps of 64 (16 code bytes per lane and
+  // fragment) keep two steps in flight in the registers one 128-wide step
+  // would take; MXFP4 steps of 128 (16 bytes of codes per lane), one in flight
+  constexpr int KS = fp4 ? 128 : 64;
+  constexpr int XS = KS / 32;                 // 16-byte h pieces per token fragment and step
+  constexpr int kSmallDepth2 = fp4 ? 1 : 2;
+  constexpr int NF = kSmCh2 / 16;             // channel fragments
+  const int K = p.K;                          // = I
+  const int nk = K / KS;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l16 = lane & 15, lg = lane >> 4;
   const long rowBytes = fp4 ? (K >> 1) : K;
   const int n0 = ti.nt * kSmCh2;
   const uint8_t* W2 = p.wa[ti.wi] + ti.eg * (long)p.N * rowBytes;
   // per-block fp8: the 128 channels of the tile form one channel block; the
-  // scale of K block ks (one 128-wide step) is sb2[ks]
+  // scale of the K block of step ks (two 64-wide steps per block) is sb2[ks / 2]
   const float* sb2 = nullptr;
   if constexpr (blk)
     sb2 = reinterpret_cast<const float*>(p.sa[ti.wi]) + (ti.eg * (long)(p.N >> 7) + (n0 >> 7)) * (K >> 7);
@@ -972,55 +989,48 @@ __device__ __forceinline__ void gemm2_small_body(const GemmParams& p, const Tile
     for (int t = 0; t < TV; ++t) acc[f][t] = v4f{0.f, 0.f, 0.f, 0.f};
 
   struct St {
-    uint4 x[TV][4];
-    uint4 w[NF][2];
+    uint4 x[TV][XS];
+    uint4 w[NF];
     uint32_t sc[NF];
     float bs;
   };
   auto load = [&](int ks, St& st) {
-    if constexpr (blk) st.bs = sb2[ks];
+    if constexpr (blk) st.bs = sb2[ks >> 1];
 #pragma unroll
     for (int t = 0; t < TV; ++t)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)   // byte offsets of the bf16 elements of sub-step i
-        st.x[t][i] = hpiece(t, ((long)ks << 8) + (fp4 ? lg * 64 + 16 * i : 128 * (i >> 1) + 32 * lg + 16 * (i & 1)));
+      for (int i = 0; i < XS; ++i)   // byte offsets of the bf16 elements of sub-step i
+        st.x[t][i] = hpiece(t, (long)ks * (2 * KS) + (fp4 ? lg * 64 + 16 * i : 32 * lg + 16 * i));
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
       if constexpr (fp4) {
-        st.w[f][0] = *reinterpret_cast<const uint4*>(wp[f] + (long)ks * op_step(wd, 64));
+        st.w[f] = *reinterpret_cast<const uint4*>(wp[f] + (long)ks * op_step(wd, 64));
         st.sc[f] = sp[f][(long)ks * op_step(p.sd[0], 4)];
       } else {
-        const long k = ((long)ks << 7) + lg * 16;
-        st.w[f][0] = wgt(f, k);
-        st.w[f][1] = wgt(f, k + 64);
+        st.w[f] = wgt(f, (long)ks * KS + lg * 16);
       }
     }
   };
   auto compute = [&](const St& st) {
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
-      v8bf w[4];
-      if constexpr (fp4) {
-        const uint32_t cw[4] = {st.w[f][0].x, st.w[f][0].y, st.w[f][0].z, st.w[f][0].w};
-        fp4x32_to_bf16(cw, e8m0_to_f32(st.sc[f]), w);
-      } else {
-        const uint32_t cw[8] = {st.w[f][0].x, st.w[f][0].y, st.w[f][0].z, st.w[f][0].w,
-                                st.w[f][1].x, st.w[f][1].y, st.w[f][1].z, st.w[f][1].w};
-        fp8x32_to_bf16(cw, w);
-      }
+      v8bf w[XS];
+      const uint32_t cw[4] = {st.w[f].x, st.w[f].y, st.w[f].z, st.w[f].w};
+      if constexpr (fp4) fp4x32_to_bf16(cw, e8m0_to_f32(st.sc[f]), w);
+      else fp8x16_to_bf16(cw, w);
       if constexpr (blk) {
-        // one K step is one K block: its partial sum times its scale
+        // a K step lies inside one K block: its partial sum times the block's scale
 #pragma unroll
         for (int t = 0; t < TV; ++t) {
           v4f part = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
+          for (int i = 0; i < XS; ++i)
             part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w[i], as_v8bf(st.x[t][i]), part, 0, 0, 0);
           acc[f][t] += st.bs * part;
         }
       } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < XS; ++i)
 #pragma unroll
           for (int t = 0; t < TV; ++t)
             acc[f][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w[i], as_v8bf(st.x[t][i]), acc[f][t], 0, 0, 0);
