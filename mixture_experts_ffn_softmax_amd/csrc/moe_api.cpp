@@ -336,16 +336,18 @@ struct ForwardLayout {
 };
 
 // Up to kMetaMaxPairs pairs and kMetaMaxE experts, one workgroup computes
-// the whole routing metadata; for at most kMetaRouteMaxE experts and
-// kMetaRouteMaxT tokens it also routes, in one wave, and runs in the same
-// launch as the quantisation (beyond that one CU's routing takes longer than
-// a grid-wide router launch).  Beyond kMetaMaxPairs pairs or kMetaMaxE
-// experts, route / counts / ranks run as grid-wide kernels.
+// the whole routing metadata.  For at most kMetaRouteMaxE experts (each
+// token's expert set is a 32-bit mask), kMetaRouteMaxT tokens and
+// kMetaRouteMaxPairs pairs it also routes, in the same launch as the
+// quantisation (beyond that one CU's routing takes longer than a grid-wide
+// router launch).  Beyond kMetaMaxPairs pairs or kMetaMaxE experts, route /
+// counts / ranks run as grid-wide kernels.
 static bool meta_path(int32_t T, int32_t k, int32_t E) {
   return (long)T * k <= moe::kMetaMaxPairs && E <= moe::kMetaMaxE;
 }
 static bool fused_route_path(int32_t T, int32_t k, int32_t E) {
-  return meta_path(T, k, E) && E <= moe::kMetaRouteMaxE && T <= moe::kMetaRouteMaxT;
+  return meta_path(T, k, E) && E <= moe::kMetaRouteMaxE && T <= moe::kMetaRouteMaxT &&
+         (long)T * k <= moe::kMetaRouteMaxPairs;
 }
 
 static ForwardLayout forward_layout(void* ws, int32_t T, int32_t k, int32_t E, int32_t H, int32_t I,

@@ -391,21 +391,24 @@ __global__ __launch_bounds__(1024) void meta_kernel(int T, int E, int k, const i
   }
 }
 
-// meta_wave_body: the same results as meta_kernel with routing, for at
-// most kMetaRouteMaxT tokens and kMetaRouteMaxE experts, in ONE wave with no
-// workgroup barrier between its phases (decode-sized batches, where each
-// phase of the 16-wave kernel costs a barrier and a memory round trip).
-// Lane l routes tokens l, l + 64, ... (chunk i = t / 64) and keeps each
-// token's expert set as a bit mask.  A token picks distinct experts, so the
-// rank of pair (t, j) among the pairs of its expert e is the number of
-// earlier tokens that picked e: the pairs of chunks before i plus a popcount
-// of the ballot of e over chunk i below lane t % 64.
-constexpr int kWaveChunks = kMetaRouteMaxT / 64;
+// meta_route_body: the same results as meta_kernel with routing, for at
+// most kMetaRouteMaxT tokens, kMetaRouteMaxE experts and kMetaRouteMaxPairs
+// pairs, in one workgroup of kMetaQuantThreads threads.  Tokens are cut into
+// chunks of 64; wave w routes chunks w, w + W, ... one token per lane, and
+// keeps each token's expert set as a bit mask.  A token picks distinct
+// experts, so the rank of pair (t, j) among the pairs of its expert e is the
+// number of earlier tokens that picked e: the pairs of e in the chunks
+// before t's (a scan over the chunks) plus a popcount of the ballot of e
+// over t's chunk below lane t % 64.
+constexpr int kMetaQuantThreads = 512;
+constexpr int kMetaWavesR = kMetaQuantThreads / 64;
+constexpr int kMetaRouteChunks = kMetaRouteMaxT / 64;
+static_assert(kMetaRouteChunks <= 64, "one lane per token chunk in the chunk scan");
 
 template <int NE>
 __device__ __forceinline__ uint32_t wave_route_token(const float* __restrict__ logits, bool sigmoid, int t,
                                                      int E, int k, int* __restrict__ ids,
-                                                     float* __restrict__ w, int* s_ids) {
+                                                     float* __restrict__ w, uint8_t* s_ids) {
   float v[NE];
   const float* row = logits + (long)t * E;
 #pragma unroll
@@ -433,7 +436,7 @@ __device__ __forceinline__ uint32_t wave_route_token(const float* __restrict__ l
     ex[j] = sigmoid ? 1.0f / (1.0f + expf(-bv)) : expf(bv - vmax);
     sum += ex[j];
     ids[(long)t * k + j] = bi;
-    s_ids[t * k + j] = bi;
+    s_ids[t * k + j] = (uint8_t)bi;
   }
   for (int j = 0; j < k; ++j) w[(long)t * k + j] = ex[j] / sum;
   return all & ~avail;
@@ -450,114 +453,100 @@ __device__ __forceinline__ int wave_inclusive_scan(int v) {
   return v;
 }
 
-// The LDS of the single-wave metadata: a token's pair ids, each expert's
-// ballot per token chunk, and each expert's first row per chunk.
-struct MetaWaveLds {
-  int ids[kMetaRouteMaxT * kMaxTopK];
-  uint64_t m[kMetaRouteMaxE * kWaveChunks];
-  int base[kMetaRouteMaxE * kWaveChunks];
+// The LDS of the routing metadata: each pair's expert, each expert's ballot
+// per token chunk, each expert's first row per chunk (relative to the
+// expert's first row), and each expert's count and first row.
+struct MetaRouteLds {
+  uint8_t ids[kMetaRouteMaxPairs];
+  uint64_t m[kMetaRouteMaxE][kMetaRouteChunks];
+  int base[kMetaRouteMaxE][kMetaRouteChunks];
+  int tot[kMetaRouteMaxE];
+  int off[kMetaRouteMaxE];
 };
 
-// The single wave's LDS writes are seen by its later reads (the LDS serves a
-// wave's instructions in order); this keeps the compiler from moving them.
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+// Routes chunks wave, wave + W, ... and records each expert's ballot per chunk.
+template <int NE>
+__device__ __forceinline__ void route_chunks(const float* __restrict__ logits, bool sigmoid, int T, int E, int k,
+                                             int* __restrict__ ids, float* __restrict__ w, MetaRouteLds& L) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nch = (T + 63) >> 6;
+  for (int c = wave; c < nch; c += kMetaWavesR) {
+    const int t = c * 64 + lane;
+    const uint32_t set = (t < T) ? wave_route_token<NE>(logits, sigmoid, t, E, k, ids, w, L.ids) : 0u;
+    for (int e = 0; e < E; ++e) {
+      const uint64_t m = __ballot((set >> e) & 1u);
+      if (lane == 0) L.m[e][c] = m;
+    }
+  }
 }
 
-// Run by the threads 0..63 (one wave) of a block.
-__device__ __forceinline__ void meta_wave_body(const float* __restrict__ logits, bool sigmoid, int T, int E, int k,
-                                               int* __restrict__ ids, float* __restrict__ w,
-                                               int* __restrict__ counts, int* __restrict__ offsets, int extra_rows,
-                                               int* __restrict__ pair_to_row, int* __restrict__ row_to_pair,
-                                               int* __restrict__ tile_prefix, int bm, MetaWaveLds& L) {
-  int* s_ids = L.ids;
-  uint64_t* s_m = L.m;
-  int* s_base = L.base;
-
-  const int lane = threadIdx.x;
+// Run by all kMetaQuantThreads threads of a workgroup (it holds barriers).
+__device__ __forceinline__ void meta_route_body(const float* __restrict__ logits, bool sigmoid, int T, int E, int k,
+                                                int* __restrict__ ids, float* __restrict__ w,
+                                                int* __restrict__ counts, int* __restrict__ offsets, int extra_rows,
+                                                int* __restrict__ pair_to_row, int* __restrict__ row_to_pair,
+                                                int* __restrict__ tile_prefix, int bm, MetaRouteLds& L) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nch = (T + 63) >> 6;
 
-  // ---- route; the expert set of each of this lane's tokens
-  uint32_t set[kWaveChunks];
-#pragma unroll
-  for (int i = 0; i < kWaveChunks; ++i) {
-    const int t = i * 64 + lane;
-    set[i] = 0;
-    if (t < T) {
-      if (E <= 8) set[i] = wave_route_token<8>(logits, sigmoid, t, E, k, ids, w, s_ids);
-      else if (E <= 16) set[i] = wave_route_token<16>(logits, sigmoid, t, E, k, ids, w, s_ids);
-      else set[i] = wave_route_token<kMetaRouteMaxE>(logits, sigmoid, t, E, k, ids, w, s_ids);
-    }
-  }
+  // ---- route; each expert's ballot over each chunk
+  if (E <= 8) route_chunks<8>(logits, sigmoid, T, E, k, ids, w, L);
+  else if (E <= 16) route_chunks<16>(logits, sigmoid, T, E, k, ids, w, L);
+  else route_chunks<kMetaRouteMaxE>(logits, sigmoid, T, E, k, ids, w, L);
+  __syncthreads();
 
-  // ---- per expert and chunk: the ballot of the tokens that picked it
-  for (int e = 0; e < E; ++e) {
-#pragma unroll
-    for (int i = 0; i < kWaveChunks; ++i) {
-      if (i < nch) {
-        const uint64_t m = __ballot((set[i] >> e) & 1u);
-        if (lane == 0) s_m[e * kWaveChunks + i] = m;
-      }
-    }
+  // ---- per expert (one wave each): the chunk scan, lane c = chunk c
+  for (int e = wave; e < E; e += kMetaWavesR) {
+    const int v = (lane < nch) ? (int)__popcll(L.m[e][lane]) : 0;
+    const int incl = wave_inclusive_scan(v);
+    L.base[e][lane] = incl - v;
+    if (lane == 63) L.tot[e] = incl;
   }
-  wave_lds_sync();
+  __syncthreads();
 
-  // ---- lane e: count, offset (scan over the lanes), chunk bases
-  int c[kWaveChunks];
-  int cnt = 0;
-#pragma unroll
-  for (int i = 0; i < kWaveChunks; ++i) {
-    c[i] = (lane < E && i < nch) ? (int)__popcll(s_m[lane * kWaveChunks + i]) : 0;
-    cnt += c[i];
-  }
-  const int incl = wave_inclusive_scan(cnt);
-  const int total = __shfl(incl, E - 1, 64);
-  const int off = incl - cnt;
-  if (lane < E) {
-    counts[lane] = cnt;
-    offsets[lane] = off;
-    int run = off;
-#pragma unroll
-    for (int i = 0; i < kWaveChunks; ++i) {
-      s_base[lane * kWaveChunks + i] = run;
-      run += c[i];
+  // ---- wave 0, lane e: count, offset (a scan over the lanes), tile prefix
+  if (wave == 0) {
+    const int cnt = (lane < E) ? L.tot[lane] : 0;
+    const int incl = wave_inclusive_scan(cnt);
+    const int total = __shfl(incl, E - 1, 64);
+    if (lane < E) {
+      counts[lane] = cnt;
+      offsets[lane] = incl - cnt;
+      L.off[lane] = incl - cnt;
+    }
+    if (lane == 0) {
+      offsets[E] = total;
+      if (extra_rows > 0) offsets[E + 1] = total + extra_rows;
+    }
+    if (tile_prefix) {
+      const int G = E + (extra_rows > 0 ? 1 : 0);
+      const int rows = (lane < E) ? cnt : (lane == E ? extra_rows : 0);
+      const int tiles = (lane < G && rows > 0) ? (rows + bm - 1) / bm : 0;
+      const int tincl = wave_inclusive_scan(tiles);
+      if (lane < G) tile_prefix[lane] = tincl - tiles;
+      if (lane == G - 1) tile_prefix[G] = tincl;
     }
   }
-  if (lane == 0) {
-    offsets[E] = total;
-    if (extra_rows > 0) offsets[E + 1] = total + extra_rows;
-  }
-  if (tile_prefix) {
-    const int G = E + (extra_rows > 0 ? 1 : 0);
-    const int rows = (lane < E) ? cnt : (lane == E ? extra_rows : 0);
-    const int tiles = (lane < G && rows > 0) ? (rows + bm - 1) / bm : 0;
-    const int tincl = wave_inclusive_scan(tiles);
-    if (lane < G) tile_prefix[lane] = tincl - tiles;
-    if (lane == G - 1) tile_prefix[G] = tincl;
-  }
-  wave_lds_sync();
+  __syncthreads();
 
   // ---- rows, in pair order (coalesced pair_to_row)
   const int R = T * k;
-  for (int p = lane; p < R; p += 64) {
+  for (int p = tid; p < R; p += kMetaQuantThreads) {
     const int t = p / k;
-    const int e = s_ids[p];
-    const int i = t >> 6, tl = t & 63;
+    const int e = L.ids[p];
+    const int c = t >> 6, tl = t & 63;
     const uint64_t below = (tl == 0) ? 0ull : (~0ull >> (64 - tl));
-    const int row = s_base[e * kWaveChunks + i] + (int)__popcll(s_m[e * kWaveChunks + i] & below);
+    const int row = L.off[e] + L.base[e][c] + (int)__popcll(L.m[e][c] & below);
     pair_to_row[p] = row;
     row_to_pair[row] = p;
   }
 }
 
-// meta_quant_kernel: workgroup 0's first wave computes the routed metadata
-// (meta_wave_body), workgroup 1 + t quantises token t into token order.  The
+// meta_quant_kernel: workgroup 0 computes the routing and its metadata
+// (meta_route_body), workgroup 1 + t quantises token t into token order.  The
 // metadata reads only the logits and the quantisation only x, so nothing
-// waits across workgroups.  At most 512 threads per workgroup, so that the
-// routing wave keeps its registers (about 200) without spilling.
-constexpr int kMetaQuantThreads = 512;
+// waits across workgroups.  kMetaQuantThreads (512) threads per workgroup, so
+// that a routing lane keeps its registers (about 200) without spilling.
 template <int CPT>
 __global__ __launch_bounds__(kMetaQuantThreads) void meta_quant_kernel(const float* __restrict__ logits, bool sigmoid,
                                                           const uint16_t* __restrict__ x, int T, int H, int E,
@@ -569,10 +558,9 @@ __global__ __launch_bounds__(kMetaQuantThreads) void meta_quant_kernel(const flo
                                                           uint8_t* __restrict__ xq_tok, float* __restrict__ xs_tok,
                                                           long tok_cs) {
   if (blockIdx.x == 0) {
-    __shared__ MetaWaveLds L;
-    if (threadIdx.x < 64)
-      meta_wave_body(logits, sigmoid, T, E, k, ids, w, counts, offsets, extra_rows, pair_to_row, row_to_pair,
-                     tile_prefix, bm, L);
+    __shared__ MetaRouteLds L;
+    meta_route_body(logits, sigmoid, T, E, k, ids, w, counts, offsets, extra_rows, pair_to_row, row_to_pair,
+                    tile_prefix, bm, L);
     return;
   }
   quant_token<CPT>(x, (long)blockIdx.x - 1, H, 0, nullptr, nullptr, nullptr, xq_tok, xs_tok, 0, tok_cs, nullptr);
@@ -620,9 +608,13 @@ hipError_t launch_meta_quant(const float* logits, bool sigmoid, const uint16_t* 
                              int* row_to_pair, int* tile_prefix, int bm, uint8_t* xq_tok, float* xs_tok,
                              hipStream_t s, hipEvent_t ev_start) {
   if (T == 0) return hipSuccess;
-  if (!logits || T > kMetaRouteMaxT || E > kMetaRouteMaxE) return hipErrorInvalidValue;
+  if (!logits || T > kMetaRouteMaxT || E > kMetaRouteMaxE || (long)T * k > kMetaRouteMaxPairs)
+    return hipErrorInvalidValue;
+  // every workgroup has kMetaQuantThreads threads: the metadata workgroup
+  // needs all of them, the quantising ones take CPT chunks of 8 per thread
   int threads = 64, cpt = 1;
   quant_shape(H, kMetaQuantThreads, &threads, &cpt);
+  threads = kMetaQuantThreads;
   const long tok_cs = (long)T * kTokChunk;
 #define MOE_MQ(C)                                                                                           \
   hipExtLaunchKernelGGL(meta_quant_kernel<C>, dim3(T + 1), dim3(threads), 0, s, ev_start, nullptr, 0, logits, \

@@ -190,8 +190,12 @@ def test_workspace_sizes_grow(lib):
     w = fp8_weights(E=8, H=8192, I=2048)
     a = lib.moe_forward_workspace_size(64, 2, ctypes.byref(w), 0)
     b = lib.moe_forward_workspace_size(2048, 2, ctypes.byref(w), 0)
-    # h (bf16), y (fp32) and the xq rows dominate: ~ rows * (2I + 4H + H)
-    assert b > a and b >= 4096 * (2 * 2048 + 5 * 8192)
+    # h (bf16) and y (fp32) per row, plus the quantised tokens kept in token
+    # order (up to 32 experts and 4096 tokens, routed in the quantising launch)
+    assert b > a and b >= 4096 * (2 * 2048 + 4 * 8192) + 2048 * 8192
+    # beyond 32 experts the quantised rows are scattered to expert order
+    w64 = fp8_weights(E=64, H=8192, I=2048)
+    assert lib.moe_forward_workspace_size(2048, 2, ctypes.byref(w64), 0) >= 4096 * (2 * 2048 + 5 * 8192)
     assert lib.moe_forward_workspace_size(-1, 2, ctypes.byref(w), 0) == 0
 
 
