@@ -178,6 +178,13 @@ __device__ __forceinline__ TileInfo find_tile(const GemmParams& p, const int* s_
   ti.row0 = p.offsets[lo] + mt * bm;
   ti.wi = (lo < p.n_routed) ? 0 : 1;
   ti.eg = ti.wi ? 0 : lo;
+  // the tile is the workgroup's: keep its fields in scalar registers
+  ti.g = __builtin_amdgcn_readfirstlane(ti.g);
+  ti.nt = __builtin_amdgcn_readfirstlane(ti.nt);
+  ti.row0 = __builtin_amdgcn_readfirstlane(ti.row0);
+  ti.row1 = __builtin_amdgcn_readfirstlane(ti.row1);
+  ti.wi = __builtin_amdgcn_readfirstlane(ti.wi);
+  ti.eg = __builtin_amdgcn_readfirstlane((int)ti.eg);
   return ti;
 }
 
