@@ -18,7 +18,8 @@ constexpr int kMetaMaxPairs = 16384; // pairs handled by the single-workgroup me
 constexpr int kMetaMaxE = 64;
 constexpr int kMetaRouteMaxE = 32;   // experts the one-workgroup router handles (bit masks) ...
 constexpr int kMetaRouteMaxT = 4096; // ... for batches of at most this many tokens ...
-constexpr int kMetaRouteMaxPairs = 16384;  // ... and pairs
+constexpr int kMetaRouteMaxPairs = 16384;  // ... and pairs; the same launch quantises
+constexpr int kMetaQuantMaxH = 32768;      // tokens of at most this many elements
 
 // Byte addressing of a matrix operand with rows of K contraction bytes: byte k
 // of row r sits at r * row_pitch + (k >> kc_shift) * chunk_stride +
@@ -78,11 +79,12 @@ hipError_t launch_quant_scatter(const uint16_t* x, int T, int H, int k, const in
 hipError_t launch_meta(int T, int E, int k, const int* ids, int* counts, int* offsets, int extra_rows,
                        int* pair_to_row, int* row_to_pair, int* tile_prefix, int bm, hipStream_t s);
 // Routing from the logits (ids / w; T <= kMetaRouteMaxT, E <= kMetaRouteMaxE,
-// T * k <= kMetaRouteMaxPairs, else hipErrorInvalidValue), the metadata of
-// launch_meta, and the per-token quantisation into token order (xq_tok
-// K-blocked in kTokChunk-byte chunks, xs_tok [T]) in one launch: workgroup 0
-// routes and builds the metadata, workgroup 1 + t quantises token t.  The
-// two parts read and write disjoint buffers.
+// T * k <= kMetaRouteMaxPairs, H <= kMetaQuantMaxH, else
+// hipErrorInvalidValue), the metadata of launch_meta, and the per-token
+// quantisation into token order (xq_tok K-blocked in kTokChunk-byte chunks,
+// xs_tok [T]) in one launch: workgroup 0 routes and builds the metadata,
+// workgroup 1 + i quantises tokens 2i and 2i + 1.  The two parts read and
+// write disjoint buffers.
 hipError_t launch_meta_quant(const float* logits, bool sigmoid, const uint16_t* x, int T, int H, int E, int k,
                              int* ids, float* w, int* counts, int* offsets, int extra_rows, int* pair_to_row,
                              int* row_to_pair, int* tile_prefix, int bm, uint8_t* xq_tok, float* xs_tok,

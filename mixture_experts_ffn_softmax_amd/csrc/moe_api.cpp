@@ -345,9 +345,9 @@ struct ForwardLayout {
 static bool meta_path(int32_t T, int32_t k, int32_t E) {
   return (long)T * k <= moe::kMetaMaxPairs && E <= moe::kMetaMaxE;
 }
-static bool fused_route_path(int32_t T, int32_t k, int32_t E) {
+static bool fused_route_path(int32_t T, int32_t k, int32_t E, int32_t H) {
   return meta_path(T, k, E) && E <= moe::kMetaRouteMaxE && T <= moe::kMetaRouteMaxT &&
-         (long)T * k <= moe::kMetaRouteMaxPairs;
+         (long)T * k <= moe::kMetaRouteMaxPairs && H <= moe::kMetaQuantMaxH;
 }
 
 static ForwardLayout forward_layout(void* ws, int32_t T, int32_t k, int32_t E, int32_t H, int32_t I,
@@ -359,7 +359,7 @@ static ForwardLayout forward_layout(void* ws, int32_t T, int32_t k, int32_t E, i
   // (the gate-up GEMM gathers each routed row's token); the other paths
   // scatter them to expert-ordered rows, and keep token order for the
   // shared expert
-  const bool fused = fused_route_path(T, k, E);
+  const bool fused = fused_route_path(T, k, E, H);
   const long rows = R + (shared ? T : 0);
   const long chunks = moe::permute_chunks(R);
   L.ids = c.take<int32_t>(R);
@@ -446,7 +446,7 @@ moe_status_t moe_forward(const uint16_t* x, const float* logits, int32_t T, int3
   const moe::FfnGroups g = make_groups(routed, sh ? shared : nullptr, L.offsets);
   const long rows = R + (sh ? T : 0);
   const bool meta = meta_path(T, top_k, E);
-  const bool fused_route = fused_route_path(T, top_k, E);
+  const bool fused_route = fused_route_path(T, top_k, E, H);
   if (ev && ev[MOE_STAGE_ROUTE]) hipEventRecord((hipEvent_t)ev[MOE_STAGE_ROUTE], s);
   // the layer's first dispatch (router, or the fused routing + quantisation
   // kernel) and its last (combine) stamp the optional layer events

@@ -184,18 +184,12 @@ __device__ __forceinline__ void quant_token(const uint16_t* __restrict__ x, long
   }
   amax = block_max(amax, red);
   const float s = (amax == 0.0f) ? 1.0f : amax / kE4M3Max;
+  const float r = e4m3_recip(s);
   uint2 q8[CPT];
 #pragma unroll
   for (int c = 0; c < CPT; ++c) {
     const uint32_t wds[4] = {in[c].x, in[c].y, in[c].z, in[c].w};
-    uint32_t packed[2] = {0u, 0u};
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t lo = e4m3_encode(bf16_lo(wds[q]) / s);
-      const uint32_t hi = e4m3_encode(bf16_hi(wds[q]) / s);
-      packed[q >> 1] |= (lo | (hi << 8)) << ((q & 1) * 16);
-    }
-    q8[c] = make_uint2(packed[0], packed[1]);
+    q8[c] = e4m3_encode8(wds, s, r);
   }
   for (int j = 0; j < k; ++j) {
     const int r = s_rows[j];
@@ -405,41 +399,90 @@ constexpr int kMetaWavesR = kMetaQuantThreads / 64;
 constexpr int kMetaRouteChunks = kMetaRouteMaxT / 64;
 static_assert(kMetaRouteChunks <= 64, "one lane per token chunk in the chunk scan");
 
+// Token t's logits, loaded without branches: a token past T reads the last
+// row and an index past E reads the last logit (neither is used: the caller
+// skips t >= T and the selection masks experts >= E).
 template <int NE>
-__device__ __forceinline__ uint32_t wave_route_token(const float* __restrict__ logits, bool sigmoid, int t,
-                                                     int E, int k, int* __restrict__ ids,
-                                                     float* __restrict__ w, uint8_t* s_ids) {
-  float v[NE];
-  const float* row = logits + (long)t * E;
+__device__ __forceinline__ void load_logits(const float* __restrict__ logits, int t, int T, int E, float (&v)[NE]) {
+  const float* row = logits + (long)(t < T ? t : T - 1) * E;
 #pragma unroll
-  for (int i = 0; i < NE; ++i) {
-    // a NaN logit ranks below every number, so that each pick is a valid
-    // expert (the ids index LDS and the row buffers below)
-    const float l = (i < E) ? row[i] : 0.0f;
-    v[i] = (l == l) ? l : -INFINITY;
+  for (int i = 0; i < NE; ++i) v[i] = row[i < E ? i : E - 1];
+}
+
+// Routes D tokens per lane at once (t[d], live[d]: t[d] < T), the same
+// selection and weight arithmetic as route_kernel: descending logit, equal
+// logits by lower index, NaN below every number; w_j = e^(l_j - l_0) / sum
+// (softmax) or sigmoid(l_j) / sum.  The D tokens' chains are independent, so
+// their instructions interleave: one token's selection is a serial chain of
+// compares and selects, latency-bound on its own.  Writes ids, w and the
+// picks to s_ids for live tokens; returns each token's expert set as a mask.
+template <int NE, int D>
+__device__ __forceinline__ void route_tokens(const float (&raw)[D][NE], bool sigmoid, const int (&t)[D],
+                                             const bool (&live)[D], int E, int k, int* __restrict__ ids,
+                                             float* __restrict__ w, uint8_t* s_ids, uint32_t (&set)[D]) {
+  float v[D][NE];
+#pragma unroll
+  for (int d = 0; d < D; ++d)
+#pragma unroll
+    for (int i = 0; i < NE; ++i) v[d][i] = (raw[d][i] == raw[d][i]) ? raw[d][i] : -INFINITY;
+  const uint32_t all = (E >= 32) ? 0xFFFFFFFFu : ((1u << E) - 1u);
+  uint32_t avail[D];
+  float vmax[D], sum[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    avail[d] = all;
+    vmax[d] = 0.0f;
+    sum[d] = 0.0f;
   }
-  uint32_t avail = (E >= 32) ? 0xFFFFFFFFu : ((1u << E) - 1u);
-  const uint32_t all = avail;
-  float vmax = 0.0f, sum = 0.0f;
-  float ex[kMaxTopK];
+  // the picks and the sum of their scores (ascending scan: a strictly larger
+  // value replaces the pick, so equal values keep the lower index; the first
+  // available expert is taken whatever its value, as every value may be
+  // -inf); bitwise, without branches, so that the scan compiles to selects.
+  // The loops over picks stay rolled: k is up to 32.
+#pragma unroll 1
   for (int j = 0; j < k; ++j) {
-    float bv = -INFINITY;
-    int bi = 0x7FFFFFFF;
+    float bv[D];
+    int bi[D];
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      bv[d] = -INFINITY;
+      bi[d] = -1;
+    }
 #pragma unroll
     for (int i = 0; i < NE; ++i)
-      if (((avail >> i) & 1u) && (v[i] > bv || (v[i] == bv && i < bi))) {
-        bv = v[i];
-        bi = i;
+#pragma unroll
+      for (int d = 0; d < D; ++d) {
+        const bool take = (((avail[d] >> i) & 1u) != 0u) & ((v[d][i] > bv[d]) | (bi[d] < 0));
+        bv[d] = take ? v[d][i] : bv[d];
+        bi[d] = take ? i : bi[d];
       }
-    avail &= ~(1u << bi);
-    if (j == 0) vmax = bv;
-    ex[j] = sigmoid ? 1.0f / (1.0f + expf(-bv)) : expf(bv - vmax);
-    sum += ex[j];
-    ids[(long)t * k + j] = bi;
-    s_ids[t * k + j] = (uint8_t)bi;
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      avail[d] &= ~(1u << bi[d]);
+      if (j == 0) vmax[d] = bv[d];
+      sum[d] += sigmoid ? 1.0f / (1.0f + expf(-bv[d])) : expf(bv[d] - vmax[d]);
+      if (live[d]) {
+        ids[(long)t[d] * k + j] = bi[d];
+        s_ids[t[d] * k + j] = (uint8_t)bi[d];
+      }
+    }
   }
-  for (int j = 0; j < k; ++j) w[(long)t * k + j] = ex[j] / sum;
-  return all & ~avail;
+  // the weights: each pick's value fetched again by its index
+#pragma unroll 1
+  for (int j = 0; j < k; ++j) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      if (!live[d]) continue;
+      const int bi = s_ids[t[d] * k + j];
+      float bv = v[d][0];
+#pragma unroll
+      for (int i = 1; i < NE; ++i) bv = (i == bi) ? v[d][i] : bv;
+      const float ex = sigmoid ? 1.0f / (1.0f + expf(-bv)) : expf(bv - vmax[d]);
+      w[(long)t[d] * k + j] = ex / sum[d];
+    }
+  }
+#pragma unroll
+  for (int d = 0; d < D; ++d) set[d] = live[d] ? (all & ~avail[d]) : 0u;
 }
 
 // Inclusive prefix sum over the 64 lanes of a wave.
@@ -464,18 +507,35 @@ struct MetaRouteLds {
   int off[kMetaRouteMaxE];
 };
 
-// Routes chunks wave, wave + W, ... and records each expert's ballot per chunk.
-template <int NE>
+// Routes chunks wave, wave + W, ... (D of them at a time, interleaved) and
+// records each expert's ballot per chunk.
+template <int NE, int D>
 __device__ __forceinline__ void route_chunks(const float* __restrict__ logits, bool sigmoid, int T, int E, int k,
                                              int* __restrict__ ids, float* __restrict__ w, MetaRouteLds& L) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nch = (T + 63) >> 6;
-  for (int c = wave; c < nch; c += kMetaWavesR) {
-    const int t = c * 64 + lane;
-    const uint32_t set = (t < T) ? wave_route_token<NE>(logits, sigmoid, t, E, k, ids, w, L.ids) : 0u;
-    for (int e = 0; e < E; ++e) {
-      const uint64_t m = __ballot((set >> e) & 1u);
-      if (lane == 0) L.m[e][c] = m;
+  constexpr int kCPW = kMetaRouteChunks / kMetaWavesR;   // chunks per wave, at most
+#pragma unroll 1
+  for (int i0 = 0; i0 < kCPW && wave + i0 * kMetaWavesR < nch; i0 += D) {
+    float raw[D][NE];
+    int t[D];
+    bool live[D];
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      t[d] = (wave + (i0 + d) * kMetaWavesR) * 64 + lane;
+      live[d] = t[d] < T;
+      load_logits<NE>(logits, t[d], T, E, raw[d]);
+    }
+    uint32_t set[D];
+    route_tokens<NE, D>(raw, sigmoid, t, live, E, k, ids, w, L.ids, set);
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      const int c = wave + (i0 + d) * kMetaWavesR;
+      if (c < nch)
+        for (int e = 0; e < E; ++e) {
+          const uint64_t m = __ballot((set[d] >> e) & 1u);
+          if (lane == 0) L.m[e][c] = m;
+        }
     }
   }
 }
@@ -489,10 +549,17 @@ __device__ __forceinline__ void meta_route_body(const float* __restrict__ logits
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nch = (T + 63) >> 6;
 
-  // ---- route; each expert's ballot over each chunk
-  if (E <= 8) route_chunks<8>(logits, sigmoid, T, E, k, ids, w, L);
-  else if (E <= 16) route_chunks<16>(logits, sigmoid, T, E, k, ids, w, L);
-  else route_chunks<kMetaRouteMaxE>(logits, sigmoid, T, E, k, ids, w, L);
+  // ---- route; each expert's ballot over each chunk.  Up to one chunk per
+  // wave one token per lane; beyond, several chunks interleaved per lane
+  if (nch <= kMetaWavesR) {
+    if (E <= 8) route_chunks<8, 1>(logits, sigmoid, T, E, k, ids, w, L);
+    else if (E <= 16) route_chunks<16, 1>(logits, sigmoid, T, E, k, ids, w, L);
+    else route_chunks<kMetaRouteMaxE, 1>(logits, sigmoid, T, E, k, ids, w, L);
+  } else {
+    if (E <= 8) route_chunks<8, 4>(logits, sigmoid, T, E, k, ids, w, L);
+    else if (E <= 16) route_chunks<16, 4>(logits, sigmoid, T, E, k, ids, w, L);
+    else route_chunks<kMetaRouteMaxE, 2>(logits, sigmoid, T, E, k, ids, w, L);
+  }
   __syncthreads();
 
   // ---- per expert (one wave each): the chunk scan, lane c = chunk c
@@ -542,8 +609,63 @@ __device__ __forceinline__ void meta_route_body(const float* __restrict__ logits
   }
 }
 
+// Quantises tokens t0 and t0 + 1 (if < T) into the K-blocked token-order
+// rows with one workgroup of kMetaQuantThreads threads.  Piece q (8
+// elements) of the pair: token (q >> 3) & 1, 64-byte chunk q >> 4, piece
+// q & 7 of the chunk, so the 16 lanes writing one chunk of both tokens write
+// one whole 128-byte line (the two tokens' chunks are adjacent).  A thread
+// serves one token: its lanes' token bit does not change with the step j.
+template <int CPT>
+__device__ __forceinline__ void quant_token_pair(const uint16_t* __restrict__ x, int t0, int T, int H,
+                                                 uint8_t* __restrict__ xq_tok, float* __restrict__ xs_tok,
+                                                 long tok_cs) {
+  __shared__ float red[2][kMetaQuantThreads / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tt = (tid >> 3) & 1;
+  const int t = t0 + tt;
+  const bool live = t < T;
+  const int nchk = H >> 3;                    // pieces per token
+  uint4 in[CPT];
+  float amax = 0.0f;
+#pragma unroll
+  for (int j = 0; j < CPT; ++j) {
+    const int q = tid + j * kMetaQuantThreads;
+    const int idx = (q >> 4) * 8 + (q & 7);
+    in[j] = (live && idx < nchk) ? *reinterpret_cast<const uint4*>(x + (long)t * H + (long)idx * 8)
+                                 : make_uint4(0, 0, 0, 0);
+    const uint32_t wds[4] = {in[j].x, in[j].y, in[j].z, in[j].w};
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq)
+      amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(wds[qq])), fabsf(bf16_hi(wds[qq]))));
+  }
+  // the two tokens' maxima: lanes of token 0 and 1 alternate in groups of 8
+  float m0 = wave_max(tt == 0 ? amax : 0.0f);
+  float m1 = wave_max(tt == 1 ? amax : 0.0f);
+  if (lane == 0) {
+    red[0][wv] = m0;
+    red[1][wv] = m1;
+  }
+  __syncthreads();
+  float a = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kMetaQuantThreads / 64; ++i) a = fmaxf(a, red[tt][i]);
+  const float s = (a == 0.0f) ? 1.0f : a / kE4M3Max;
+  const float r = e4m3_recip(s);
+  if (!live) return;
+#pragma unroll
+  for (int j = 0; j < CPT; ++j) {
+    const int q = tid + j * kMetaQuantThreads;
+    const int idx = (q >> 4) * 8 + (q & 7);
+    if (idx >= nchk) continue;
+    const uint32_t wds[4] = {in[j].x, in[j].y, in[j].z, in[j].w};
+    *reinterpret_cast<uint2*>(xq_tok + code_offset(t, idx, H, tok_cs)) = e4m3_encode8(wds, s, r);
+  }
+  if ((tid & 15) == 8 * tt && tid < 16) xs_tok[t] = s;
+}
+
 // meta_quant_kernel: workgroup 0 computes the routing and its metadata
-// (meta_route_body), workgroup 1 + t quantises token t into token order.  The
+// (meta_route_body), workgroup 1 + i quantises tokens 2i and 2i + 1 into
+// token order (quant_token_pair).  The
 // metadata reads only the logits and the quantisation only x, so nothing
 // waits across workgroups.  kMetaQuantThreads (512) threads per workgroup, so
 // that a routing lane keeps its registers (about 200) without spilling.
@@ -563,7 +685,7 @@ __global__ __launch_bounds__(kMetaQuantThreads) void meta_quant_kernel(const flo
                     tile_prefix, bm, L);
     return;
   }
-  quant_token<CPT>(x, (long)blockIdx.x - 1, H, 0, nullptr, nullptr, nullptr, xq_tok, xs_tok, 0, tok_cs, nullptr);
+  quant_token_pair<CPT>(x, 2 * ((int)blockIdx.x - 1), T, H, xq_tok, xs_tok, tok_cs);
 }
 
 // Expert-ordered, row-major copy of quantised rows from the token-order rows
@@ -608,16 +730,19 @@ hipError_t launch_meta_quant(const float* logits, bool sigmoid, const uint16_t* 
                              int* row_to_pair, int* tile_prefix, int bm, uint8_t* xq_tok, float* xs_tok,
                              hipStream_t s, hipEvent_t ev_start) {
   if (T == 0) return hipSuccess;
-  if (!logits || T > kMetaRouteMaxT || E > kMetaRouteMaxE || (long)T * k > kMetaRouteMaxPairs)
+  if (!logits || T > kMetaRouteMaxT || E > kMetaRouteMaxE || (long)T * k > kMetaRouteMaxPairs ||
+      H > kMetaQuantMaxH)
     return hipErrorInvalidValue;
   // every workgroup has kMetaQuantThreads threads: the metadata workgroup
-  // needs all of them, the quantising ones take CPT chunks of 8 per thread
+  // needs all of them, the quantising ones take CPT pieces of 8 elements of
+  // a token pair per thread
   int threads = 64, cpt = 1;
-  quant_shape(H, kMetaQuantThreads, &threads, &cpt);
+  quant_shape(2 * H, kMetaQuantThreads, &threads, &cpt);
   threads = kMetaQuantThreads;
   const long tok_cs = (long)T * kTokChunk;
+  const unsigned grid = 1 + (unsigned)((T + 1) / 2);
 #define MOE_MQ(C)                                                                                           \
-  hipExtLaunchKernelGGL(meta_quant_kernel<C>, dim3(T + 1), dim3(threads), 0, s, ev_start, nullptr, 0, logits, \
+  hipExtLaunchKernelGGL(meta_quant_kernel<C>, dim3(grid), dim3(threads), 0, s, ev_start, nullptr, 0, logits, \
                         sigmoid, x, T, H, E, k, ids, w, counts, offsets, extra_rows, pair_to_row, row_to_pair,  \
                         tile_prefix, bm, xq_tok, xs_tok, tok_cs)
   switch (cpt) {
@@ -625,7 +750,7 @@ hipError_t launch_meta_quant(const float* logits, bool sigmoid, const uint16_t* 
     case 2: MOE_MQ(2); break;
     case 4: MOE_MQ(4); break;
     case 8: MOE_MQ(8); break;
-    default: MOE_MQ(16); break;   // H up to 65536
+    default: MOE_MQ(16); break;   // H up to kMetaQuantMaxH
   }
 #undef MOE_MQ
   return hipGetLastError();

@@ -166,6 +166,10 @@ FULL_CASES = {
     # gate-up kernel reading token rows through row_to_pair
     "gathered_large128_shared": (200, 256, 256, 4, 2, "fp8", True, False),
     "gathered_large128": (256, 512, 256, 2, 2, "fp8", False, False),
+    # wide tokens: the fused quantisation's 8- and 16-piece-per-thread forms
+    # (an odd token count leaves the last token pair half empty)
+    "wide_H16384_odd_T": (7, 16384, 128, 4, 2, "fp8", True, False),
+    "wide_H32768": (5, 32768, 128, 4, 2, "fp8", False, False),
     # per-block fp8 weights (one scale per 128 x 128 tile), with a per-channel
     # fp8 shared expert beside them in one launch
     "block_fp8_small": (45, 384, 256, 6, 3, "fp8_block", False, False),
