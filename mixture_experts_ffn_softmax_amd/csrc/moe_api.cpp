@@ -345,21 +345,33 @@ struct ForwardLayout {
 static bool meta_path(int32_t T, int32_t k, int32_t E) {
   return (long)T * k <= moe::kMetaMaxPairs && E <= moe::kMetaMaxE;
 }
-static bool fused_route_path(int32_t T, int32_t k, int32_t E, int32_t H) {
-  return meta_path(T, k, E) && E <= moe::kMetaRouteMaxE && T <= moe::kMetaRouteMaxT &&
-         (long)T * k <= moe::kMetaRouteMaxPairs && H <= moe::kMetaQuantMaxH;
+// The one-launch path's gate-up GEMM gathers token rows.  That costs the
+// small kernel (fragments read straight from memory) little up to decode
+// sizes but much beyond (+100 us on the 2048-token per-block fp8 share), so
+// past kGatherSmallMaxT tokens the path is taken only where the large
+// kernels (rows staged through LDS) run.
+constexpr int32_t kGatherSmallMaxT = 256;
+static bool fused_route_path(int32_t T, int32_t k, const moe_weights_t* routed, bool shared) {
+  const int32_t E = routed->n_experts, H = routed->hidden;
+  if (!(meta_path(T, k, E) && E <= moe::kMetaRouteMaxE && T <= moe::kMetaRouteMaxT &&
+        (long)T * k <= moe::kMetaRouteMaxPairs && H <= moe::kMetaQuantMaxH))
+    return false;
+  if (T <= kGatherSmallMaxT) return true;
+  // only the format, the shape and the group count decide the variant
+  const moe::FfnGroups g = make_groups(routed, shared ? routed : nullptr, nullptr);
+  return moe::choose_variant(g, (long)T * k + (shared ? T : 0)) != moe::kVariantSmall;
 }
 
-static ForwardLayout forward_layout(void* ws, int32_t T, int32_t k, int32_t E, int32_t H, int32_t I,
-                                    bool shared) {
+static ForwardLayout forward_layout(void* ws, int32_t T, int32_t k, const moe_weights_t* routed, bool shared) {
   ForwardLayout L{};
   Carve c(ws);
+  const int32_t E = routed->n_experts, H = routed->hidden, I = routed->inter;
   const long R = (long)T * k;
   // the fused routing path keeps the quantised tokens in token order only
   // (the gate-up GEMM gathers each routed row's token); the other paths
   // scatter them to expert-ordered rows, and keep token order for the
   // shared expert
-  const bool fused = fused_route_path(T, k, E, H);
+  const bool fused = fused_route_path(T, k, routed, shared);
   const long rows = R + (shared ? T : 0);
   const long chunks = moe::permute_chunks(R);
   L.ids = c.take<int32_t>(R);
@@ -382,7 +394,7 @@ static ForwardLayout forward_layout(void* ws, int32_t T, int32_t k, int32_t E, i
 
 size_t moe_forward_workspace_size(int32_t T, int32_t top_k, const moe_weights_t* routed, int32_t use_shared) {
   if (!routed || T < 0 || top_k < 1 || routed->n_experts < 1) return 0;
-  return forward_layout(nullptr, T, top_k, routed->n_experts, routed->hidden, routed->inter, use_shared != 0)
+  return forward_layout(nullptr, T, top_k, routed, use_shared != 0)
       .bytes;
 }
 
@@ -428,7 +440,7 @@ moe_status_t moe_forward(const uint16_t* x, const float* logits, int32_t T, int3
     return fail(MOE_ERR_WORKSPACE, "workspace %zu B < %zu B", ws ? ws_bytes : 0, need_ws);
   MOE_CHECK(need(ws, "ws"));
 
-  ForwardLayout L = forward_layout(ws, T, top_k, E, H, I, sh);
+  ForwardLayout L = forward_layout(ws, T, top_k, routed, sh);
   void* const* ev = dbg ? dbg->events : nullptr;
   if (dbg) {
     if (dbg->topk_ids) L.ids = dbg->topk_ids;
@@ -446,7 +458,7 @@ moe_status_t moe_forward(const uint16_t* x, const float* logits, int32_t T, int3
   const moe::FfnGroups g = make_groups(routed, sh ? shared : nullptr, L.offsets);
   const long rows = R + (sh ? T : 0);
   const bool meta = meta_path(T, top_k, E);
-  const bool fused_route = fused_route_path(T, top_k, E, H);
+  const bool fused_route = fused_route_path(T, top_k, routed, sh);
   if (ev && ev[MOE_STAGE_ROUTE]) hipEventRecord((hipEvent_t)ev[MOE_STAGE_ROUTE], s);
   // the layer's first dispatch (router, or the fused routing + quantisation
   // kernel) and its last (combine) stamp the optional layer events
