@@ -263,9 +263,9 @@ def time_layer(layer, steps, warmup):
     around the whole region (`gpu_ms`), the per-layer durations (`layer_ms`,
     a list) from the start/stop events the layer's own first and last
     dispatches stamp, and the average GEMM1 / GEMM2 launch ms (`g1_ms`,
-    `g2_ms`) from the events their dispatches stamp.  Dispatch-stamped events
-    add no packets to the stream; the region's two records are outside the
-    layers."""
+    `g2_ms`) from the events their dispatches stamp, in a second pass over
+    the same steps.  Dispatch-stamped events add no packets to the stream;
+    the region's two records are outside the layers."""
     import torch
     for i in range(warmup):
         layer.step(i)
@@ -276,10 +276,15 @@ def time_layer(layer, steps, warmup):
     t0 = time.perf_counter()
     region[0].record()
     for i in range(steps):
-        layer.step(i, gemm_events=ge[i][:2], layer_events=ge[i][2])
+        layer.step(i, layer_events=ge[i][2])
     region[1].record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    # the GEMMs' own events in a second pass of the same steps, so that no
+    # layer is timed with two kinds of event on one dispatch
+    for i in range(steps):
+        layer.step(i, gemm_events=ge[i][:2])
+    torch.cuda.synchronize()
     return dict(ms=(t1 - t0) * 1e3 / steps, gpu_ms=region[0].elapsed_time(region[1]) / steps,
                 layer_ms=[c[0].elapsed_time(c[1]) for _, _, c in ge],
                 g1_ms=sum(a.elapsed_time(b) for (a, b), _, _ in ge) / steps,
