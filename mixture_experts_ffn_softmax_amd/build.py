@@ -21,8 +21,9 @@ ARCH = "gfx950"
 # -packed-fp32-ops: keep the compiler from forming packed fp32 instructions.
 # -disable-promote-alloca-to-lds: keep per-thread address arrays in registers
 # rather than moving them into LDS (which the GEMM tiles need).
+# -fvisibility=hidden: the library exports only the C ABI of include/moe.h.
 COMMON = [
-    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-mllvm", "-disable-promote-alloca-to-lds",
     "-Wno-unused-command-line-argument",

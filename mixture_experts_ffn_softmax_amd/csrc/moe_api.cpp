@@ -2,7 +2,11 @@
 // launch sequencing.  Validation runs on the host before anything is
 // enqueued and touches no device state, so every error path can be exercised
 // without a GPU.  See include/moe.h for the contract of each entry point.
+// the C ABI is the library's only exported interface (built with hidden
+// visibility otherwise)
+#pragma GCC visibility push(default)
 #include "../../include/moe.h"
+#pragma GCC visibility pop
 
 #include <hip/hip_runtime.h>
 
