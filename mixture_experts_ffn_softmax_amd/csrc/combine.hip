@@ -7,7 +7,9 @@
 // of the routed sum before the up-projection, with the shared experts on a
 // separate path).
 //
-// One workgroup per token.  Each thread owns CPT chunks of 8 channels, reads
+// One workgroup per token (with RMSNorm, which needs the whole row), or per
+// token and slice of 256 chunks (without: more workgroups for small T).
+// Each thread owns CPT chunks of 8 channels, reads
 // the k fp32 expert rows with 16-byte loads (coalesced along the row),
 // accumulates w_j * y in fp32 in slot order, optionally normalises, adds the
 // shared row and stores bf16 (round to nearest even): the output is rounded
@@ -37,6 +39,8 @@ __global__ __launch_bounds__(1024) void combine_kernel(const float* __restrict__
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[c][i] = 0.0f;
 
+  // this workgroup's slice of the row's chunks (the whole row when gridDim.y = 1)
+  const int base = blockIdx.y * blockDim.x * CPT;
   for (int j = 0; j < k; ++j) {
     const int r = pair_to_row[t * k + j];
     const float w = topk_w[t * k + j];
@@ -44,7 +48,7 @@ __global__ __launch_bounds__(1024) void combine_kernel(const float* __restrict__
     const float4* src = reinterpret_cast<const float4*>(y_rows + (long)r * H);
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
-      const int idx = threadIdx.x + c * blockDim.x;
+      const int idx = base + threadIdx.x + c * blockDim.x;
       if (idx < nchk) {
         const float4 v0 = src[2 * idx], v1 = src[2 * idx + 1];
         acc[c][0] += w * v0.x; acc[c][1] += w * v0.y; acc[c][2] += w * v0.z; acc[c][3] += w * v0.w;
@@ -63,7 +67,7 @@ __global__ __launch_bounds__(1024) void combine_kernel(const float* __restrict__
     const float inv = 1.0f / sqrtf(ss / (float)H + eps);
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
-      const int idx = threadIdx.x + c * blockDim.x;
+      const int idx = base + threadIdx.x + c * blockDim.x;
       if (idx < nchk) {
         const float4 g0 = reinterpret_cast<const float4*>(gamma)[2 * idx];
         const float4 g1 = reinterpret_cast<const float4*>(gamma)[2 * idx + 1];
@@ -76,7 +80,7 @@ __global__ __launch_bounds__(1024) void combine_kernel(const float* __restrict__
 
 #pragma unroll
   for (int c = 0; c < CPT; ++c) {
-    const int idx = threadIdx.x + c * blockDim.x;
+    const int idx = base + threadIdx.x + c * blockDim.x;
     if (idx >= nchk) continue;
     if (y_shared) {
       const float4* sh = reinterpret_cast<const float4*>(y_shared + t * H);
@@ -96,12 +100,17 @@ hipError_t launch_combine(const float* y_rows, const int* pair_to_row, const flo
                           uint16_t* out, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop) {
   if (T == 0) return hipSuccess;
   const int chunks = H / 8;
-  int cpt = 1;
-  while (chunks > 1024 * cpt) cpt *= 2;
-  int threads = (chunks + cpt - 1) / cpt;
-  threads = ((threads + 63) / 64) * 64;
-#define MOE_CB(C)                                                                               \
-  hipExtLaunchKernelGGL(combine_kernel<C>, dim3(T), dim3(threads), 0, s, ev_start, ev_stop, 0, y_rows, \
+  int cpt = 1, threads, slices = 1;
+  if (gamma) {   // the norm needs the whole row in one workgroup
+    while (chunks > 1024 * cpt) cpt *= 2;
+    threads = (chunks + cpt - 1) / cpt;
+    threads = ((threads + 63) / 64) * 64;
+  } else {       // one chunk per thread, slices of 256 chunks
+    threads = chunks < 256 ? ((chunks + 63) / 64) * 64 : 256;
+    slices = (chunks + threads - 1) / threads;
+  }
+#define MOE_CB(C)                                                                                          \
+  hipExtLaunchKernelGGL(combine_kernel<C>, dim3(T, slices), dim3(threads), 0, s, ev_start, ev_stop, 0, y_rows, \
                         pair_to_row, w, H, k, y_shared, gamma, eps, out)
   switch (cpt) {
     case 1: MOE_CB(1); break;
