@@ -446,8 +446,11 @@ def test_expert_ffn(lib, counts, fmt, pack, act):
     assert ratio <= OUT_TOL
 
 
+# (3, 2176, ...): 272 chunks of 8 channels, so the sliced form (no RMSNorm)
+# ends with a slice of 16 chunks
 @pytest.mark.parametrize("T,H,k,shared,norm", [(50, 256, 2, False, False), (17, 384, 4, True, True),
-                                               (8, 8192, 8, True, False)])
+                                               (8, 8192, 8, True, False), (3, 2176, 3, True, False),
+                                               (5, 2176, 2, False, True)])
 def test_combine(lib, T, H, k, shared, norm):
     say("combine", T, H, k, shared, norm)
     g = torch.Generator().manual_seed(T * k)
