@@ -1281,7 +1281,7 @@ hipError_t launch_gemm2(int variant, const FfnGroups& g, const uint16_t* h, cons
     p.ntiles = g.hidden / kLgCh;
     const long grid = max_row_tiles(n_rows, g.n_groups, bm) * p.ntiles;
     if (variant == kVariantLarge256)
-      hipExtLaunchKernelGGL(gemm2_pp_kernel<256, 6>, dim3((unsigned)grid), dim3(256), 0, s, ev_start, ev_stop, 0, p);
+      hipExtLaunchKernelGGL(gemm2_pp_kernel<256, 4>, dim3((unsigned)grid), dim3(256), 0, s, ev_start, ev_stop, 0, p);
     else
       hipExtLaunchKernelGGL(gemm2_pp_kernel<128, 8>, dim3((unsigned)grid), dim3(256), 0, s, ev_start, ev_stop, 0, p);
   }
