@@ -175,8 +175,10 @@ enum {
  * gate-up / down GEMM's own dispatch (hipExtLaunchKernel) at its start and
  * end: its duration with no extra packets on the stream.  layer_events[0] /
  * [1], when non-NULL, are stamped the same way by the layer's first dispatch
- * (the router or the routing metadata kernel) at its start and by its last
- * (the combine) at its end: the whole layer's duration (moe_forward only).
+ * (the router, or the routing + quantisation kernel) at its start and by its
+ * last (the combine) at its end: the whole layer's duration (moe_forward
+ * only).  A dispatch that stamps events costs the stream a little more than
+ * one that does not: time the layer and the GEMMs in separate calls.
  */
 typedef struct {
   int32_t* topk_ids;       /* [T][k]   */

@@ -17,10 +17,11 @@
 //   meta_kernel    one workgroup doing all of the above but the quantisation
 //                  (and the grouped GEMMs' tile prefix) when there are at
 //                  most kMetaMaxPairs pairs: one launch instead of four
-//   meta_quant_kernel  the same plus the routing in a single wave, for at
-//                  most kMetaRouteMaxT tokens and kMetaRouteMaxE experts
-//                  (decode-sized batches, where latency is the cost), with
-//                  the quantisation into token order in the same launch
+//   meta_quant_kernel  the same plus the routing, in one workgroup, for at
+//                  most kMetaRouteMaxT tokens and kMetaRouteMaxE experts,
+//                  with the quantisation into token order in the same launch
+//                  (the other workgroups); the gate-up GEMM then gathers the
+//                  routed rows through row_to_pair
 // Rows are ordered by expert and, inside an expert, by pair index; this order
 // is unique, so the result is deterministic.  Expert ids outside [0, E) are
 // skipped (their pairs get row -1) so that no access leaves its buffer.
