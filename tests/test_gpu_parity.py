@@ -166,6 +166,12 @@ FULL_CASES = {
     # gate-up kernel reading token rows through row_to_pair
     "gathered_large128_shared": (200, 256, 256, 4, 2, "fp8", True, False),
     "gathered_large128": (256, 512, 256, 2, 2, "fp8", False, False),
+    # either side of the path choices: one-launch routing with the small
+    # kernels up to 256 tokens, past that only with the large ones; up to
+    # 4096 tokens with the large ones, past that the grid-wide router
+    "path_T257_small": (257, 256, 128, 16, 2, "fp8", False, False),
+    "path_T4096_large": (4096, 256, 128, 8, 1, "fp8", False, False),
+    "path_T4097_large": (4097, 256, 128, 8, 1, "fp8", False, False),
     # wide tokens: the fused quantisation's 8- and 16-piece-per-thread forms
     # (an odd token count leaves the last token pair half empty)
     "wide_H16384_odd_T": (7, 16384, 128, 4, 2, "fp8", True, False),
