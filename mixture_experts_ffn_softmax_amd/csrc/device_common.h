@@ -11,6 +11,15 @@ namespace moe {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+
+// 16-byte load marked non-temporal, for data a workgroup reads once and no
+// other workgroup of the launch is expected to re-read (streamed weights):
+// the caches then do not keep it at the expense of operands that are re-read.
+__device__ __forceinline__ uint4 load_stream16(const uint8_t* p) {
+  const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 // Largest finite e4m3 magnitude; per-row scales are amax / kE4M3Max.
 constexpr float kE4M3Max = 448.0f;

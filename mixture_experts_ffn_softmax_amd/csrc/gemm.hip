@@ -814,7 +814,7 @@ __device__ __forceinline__ void gemm1_small_body(const GemmParams& p, const Tile
     return *reinterpret_cast<const uint4*>(tp[t] + ((k >> td.kc_shift) * td.chunk_stride + (k & ((1L << td.kc_shift) - 1))));
   };
   auto wgt = [&](int f, long k) {
-    return *reinterpret_cast<const uint4*>(wp[f] + ((k >> wd.kc_shift) * wd.chunk_stride + (k & ((1L << wd.kc_shift) - 1))));
+    return load_stream16(wp[f] + ((k >> wd.kc_shift) * wd.chunk_stride + (k & ((1L << wd.kc_shift) - 1))));
   };
 
   v4f acc[4][TV];
@@ -840,7 +840,7 @@ __device__ __forceinline__ void gemm1_small_body(const GemmParams& p, const Tile
     if constexpr (fp4) {
 #pragma unroll
       for (int f = 0; f < 4; ++f) {
-        const uint4 b0 = *reinterpret_cast<const uint4*>(wp[f] + (long)ks * op_step(wd, 64));
+        const uint4 b0 = load_stream16(wp[f] + (long)ks * op_step(wd, 64));
         st.w[f] = v8i{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, 0, 0, 0, 0};
         st.sc[f] = (int)*reinterpret_cast<const uint32_t*>(sp[f] + (long)ks * op_step(p.sd[ti.wi], 4));
       }
@@ -986,7 +986,7 @@ __device__ __forceinline__ void gemm2_small_body(const GemmParams& p, const Tile
     return *reinterpret_cast<const uint4*>(tp[t] + ((k >> td.kc_shift) * td.chunk_stride + (k & ((1L << td.kc_shift) - 1))));
   };
   auto wgt = [&](int f, long k) {
-    return *reinterpret_cast<const uint4*>(wp[f] + ((k >> wd.kc_shift) * wd.chunk_stride + (k & ((1L << wd.kc_shift) - 1))));
+    return load_stream16(wp[f] + ((k >> wd.kc_shift) * wd.chunk_stride + (k & ((1L << wd.kc_shift) - 1))));
   };
 
   v4f acc[NF][TV];
@@ -1011,7 +1011,7 @@ __device__ __forceinline__ void gemm2_small_body(const GemmParams& p, const Tile
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
       if constexpr (fp4) {
-        st.w[f] = *reinterpret_cast<const uint4*>(wp[f] + (long)ks * op_step(wd, 64));
+        st.w[f] = load_stream16(wp[f] + (long)ks * op_step(wd, 64));
         st.sc[f] = sp[f][(long)ks * op_step(p.sd[0], 4)];
       } else {
         st.w[f] = wgt(f, (long)ks * KS + lg * 16);
