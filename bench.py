@@ -34,7 +34,7 @@ sys.path.insert(0, ROOT)
 PEAK_FP8_TFLOPS = 5000.0     # MI355X dense fp8 MFMA
 PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
-BASELINE_METRIC = "MoE layer µs & fp8 TFLOP/s (% MFMA peak); decode weight-stream GB/s (% HBM)"
+LAYER_METRIC = "MoE layer µs & fp8 TFLOP/s (% MFMA peak); decode weight-stream GB/s (% HBM)"
 
 
 def parse():
@@ -378,7 +378,7 @@ def measure_prefill(args):
         f"gemm1 {g1_ms * 1e3:.1f} us, gemm2 {g2_ms * 1e3:.1f} us; stages with events (us): "
         + ", ".join(f"{n} {v * 1e3:.1f}" for n, v in stage.items()))
     result = {
-        "metric": BASELINE_METRIC,
+        "metric": LAYER_METRIC,
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -416,8 +416,9 @@ def measure_prefill(args):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported in this build "
-              "(the multi-GPU expert-parallel path is designed but not built).", file=sys.stderr)
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported: the layer is "
+              "measured on one device's share (the expert-parallel path across GPUs is not "
+              "implemented).", file=sys.stderr)
         sys.exit(2)
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
@@ -425,7 +426,7 @@ def main():
         copy_kernel(args.copy_kernel)
         return
 
-    result = {"metric": BASELINE_METRIC, "value": None, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+    result = {"metric": LAYER_METRIC, "value": None, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
               "warmup": args.warmup, "higher_is_better": True}
     if not args.no_prefill:
         result = measure_prefill(args)
