@@ -119,13 +119,20 @@ def e8m0_decode(scales):
     return np.ldexp(1.0, b - 127)
 
 
+# byte b -> (value of its low nibble, value of its high nibble): the two
+# elements one packed byte holds, in element order
+_E2M1_PAIRS = np.stack([e2m1_decode(np.arange(256) & 0xF), e2m1_decode(np.arange(256) >> 4)], axis=-1)
+
+
 def mxfp4_decode(packed, scales, group=32):
     """MXFP4 matrix [N][K/2] + scales [N][K/group] -> float64 [N][K]."""
-    vals = e2m1_decode(e2m1_unpack(packed))
+    p = np.asarray(packed, dtype=np.uint8)
+    vals = _E2M1_PAIRS[p].reshape(p.shape[:-1] + (p.shape[-1] * 2,))   # = e2m1_decode(e2m1_unpack(p))
     sc = e8m0_decode(scales)
-    n, k = vals.shape[-2], vals.shape[-1]
-    return (vals.reshape(vals.shape[:-1] + (k // group, group))
-            * sc[..., None]).reshape(vals.shape[:-2] + (n, k))
+    k = vals.shape[-1]
+    blocks = vals.reshape(vals.shape[:-1] + (k // group, group))        # a view of vals
+    blocks *= sc[..., None]                                             # each element times its block's scale
+    return vals
 
 
 # ----------------------------------------------------------------------------

@@ -115,6 +115,22 @@ def test_nibble_order():
     check_nibble_order()
 
 
+def test_mxfp4_decode_nibbles():
+    # Every byte through mxfp4_decode: element 2i is the low nibble's value
+    # (OCP E2M1 magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6; bit 3 the sign), element
+    # 2i + 1 the high nibble's, times the block scale 2^(b - 127).
+    mag = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    val = lambda c: -mag[c & 7] if c & 8 else mag[c & 7]  # noqa: E731
+    packed = np.arange(256, dtype=np.uint8).reshape(16, 16)     # 16 rows of K = 32
+    for b, f in ((127, 1.0), (125, 0.25)):
+        w = codecs.mxfp4_decode(packed, np.full((16, 1), b, dtype=np.uint8))
+        want = np.array([[val(int(x) & 15) * f, val(int(x) >> 4) * f] for x in range(256)]).reshape(16, 32)
+        assert np.array_equal(w, want)
+    # 0x21: element 0 = code 1 = 0.5, element 1 = code 2 = 1.0; 0xF7: 6, -6
+    w = codecs.mxfp4_decode(np.array([[0x21, 0xF7] * 16], dtype=np.uint8), np.array([[127, 127]], dtype=np.uint8))
+    assert list(w[0, :4]) == [0.5, 1.0, 6.0, -6.0]
+
+
 def test_e8m0():
     assert list(codecs.e8m0_decode(np.array([127, 128, 126, 0, 254]))) == [1.0, 2.0, 0.5, 2.0 ** -127, 2.0 ** 127]
     with pytest.raises(ValueError):
