@@ -126,3 +126,96 @@ def check_metadata(dbg, ref, T, k, E, shared):
 
 
 __all__ = ["moe_synth"]
+
+
+# ----------------------------------------------------------------------------
+# full-size workloads: sampled tokens that reach every expert
+# ----------------------------------------------------------------------------
+
+
+def cover_tokens(ids, n_experts, must=()):
+    """Tokens, starting with ``must``, chosen greedily (most experts not yet
+    reached first) until every expert that any token routes to appears among
+    the chosen tokens' pairs.  Returns them in the order chosen."""
+    ids = np.asarray(ids)
+    T = ids.shape[0]
+    onehot = np.zeros((T, n_experts), dtype=bool)
+    onehot[np.arange(T)[:, None], ids] = True
+    present = onehot.any(axis=0)
+    chosen, covered = [], np.zeros(n_experts, dtype=bool)
+    for t in must:
+        if t not in chosen:
+            chosen.append(int(t))
+            covered |= onehot[t]
+    while (present & ~covered).any():
+        t = int(np.argmax((onehot & ~covered).sum(axis=1)))
+        chosen.append(t)
+        covered |= onehot[t]
+    return chosen
+
+
+def edge_tokens(counts, offsets, row_to_pair, k, tile):
+    """Tokens whose rows sit where tiling is ragged or indices are large: the
+    first and last rows of the hottest expert's last row tile (``tile`` rows
+    per tile), the last row of the least-loaded non-empty expert, and the
+    last routed row overall."""
+    counts = np.asarray(counts)
+    hot = int(np.argmax(counts))
+    first_of_last = int(offsets[hot]) + ((int(counts[hot]) - 1) // tile) * tile
+    nz = np.flatnonzero(counts)
+    cold = int(nz[np.argmin(counts[nz])])
+    rows = [first_of_last, int(offsets[hot + 1]) - 1, int(offsets[cold + 1]) - 1, int(offsets[-1]) - 1]
+    return [int(row_to_pair[r]) // k for r in rows], rows
+
+
+class OneExpert:
+    """Expert e of a stacked weight tensor as a one-expert stack."""
+
+    def __init__(self, stack, e):
+        self.stack, self.e = stack, e
+        self.shape = (1,) + tuple(stack.shape[1:])
+
+    def __getitem__(self, i):
+        assert i == 0
+        return self.stack[self.e]
+
+
+class SampledOracle:
+    """The oracle's layer output for a chosen set of tokens, built from the
+    oracle's own steps in the order ``oracle.moe.forward_sampled`` takes them
+    (quantise the chosen tokens, permute their pairs, the expert FFN of each
+    expert's rows, combine).  Rows of different experts are independent, so
+    each expert's FFN runs once, for all chosen tokens' rows of that expert,
+    on a thread pool, when a subset of the tokens first needs it; ``output``
+    then combines any subset of the chosen tokens."""
+
+    def __init__(self, x_bits, ids, w, tokens, weights, gamma=None, eps=1e-6, threads=None):
+        import os
+        self.tokens = np.asarray(tokens, dtype=np.int64)
+        self.weights, self.gamma, self.eps = weights, gamma, eps
+        xq, xs = oracle.quantize_tokens(np.asarray(x_bits)[self.tokens])
+        self.sub_ids = np.asarray(ids)[self.tokens]
+        self.w = np.asarray(w)[self.tokens]
+        _, self.off = oracle.expert_counts_offsets(self.sub_ids, weights.n_experts)
+        self.p2r, _, self.q, self.s = oracle.permute_rows(self.sub_ids, self.off, xq, xs)
+        self.y = np.zeros((len(self.tokens) * self.sub_ids.shape[1], weights.hidden))
+        self.done = set()
+        self.threads = threads or min(16, os.cpu_count() or 1)
+
+    def _expert(self, e):
+        r0, r1 = int(self.off[e]), int(self.off[e + 1])
+        wt = self.weights
+        one = ExpertWeights(wt.fmt, *(OneExpert(getattr(wt, n), e) for n in ("w1", "w3", "w2", "s1", "s3", "s2")),
+                            activation=wt.activation, beta=wt.beta)
+        self.y[r0:r1] = oracle.expert_ffn(self.q[r0:r1], self.s[r0:r1], np.array([0, r1 - r0]), one)[0]
+
+    def output(self, idx):
+        """float64 output (before the bf16 rounding) of chosen tokens ``idx``
+        (positions in ``tokens``)."""
+        import concurrent.futures
+        idx = np.asarray(idx)
+        need = sorted(set(int(e) for e in np.unique(self.sub_ids[idx])) - self.done)
+        with concurrent.futures.ThreadPoolExecutor(self.threads) as ex:
+            list(ex.map(self._expert, need))
+        self.done.update(need)
+        return oracle.combine(self.y, self.p2r[idx], self.w[idx], None, self.gamma, self.eps, rounded=False)

@@ -15,7 +15,7 @@ import torch
 import moe_synth
 import oracle
 from oracle import moe
-from gpu_helpers import (DEV, OUT_TOL, assert_weights_close, bits, check_metadata, host,
+from gpu_helpers import (DEV, OUT_TOL, assert_weights_close, bits, check_metadata, edge_tokens, host,
                          oracle_weights, run_forward, say, to_device, tolerance_ratio)
 
 pytestmark = pytest.mark.gpu
@@ -341,13 +341,15 @@ def test_forward_deterministic(lib):
 # whole layer, the full-size workloads: all metadata, sampled outputs
 # ----------------------------------------------------------------------------
 
-SAMPLED = {"prefill": 24, "decode": 64, "latent": 3, "skewed": 4}
+# The many-expert workloads (latent, skewed) with the default router and
+# activation are checked on tokens that reach every expert in
+# test_gpu_coverage.py.
+SAMPLED = {"prefill": 24, "decode": 64, "latent": 3}
 
 
-FULL_SIZE_RUNS = [(name, "softmax", "silu") for name in SAMPLED] + [
-    ("latent", "sigmoid", "situ"),      # the LatentMoE layer with its own router and activation
-    ("prefill", "sigmoid", "situ"),
-]
+FULL_SIZE_RUNS = [("prefill", "softmax", "silu"), ("decode", "softmax", "silu"),
+                  ("latent", "sigmoid", "situ"),      # the LatentMoE layer with its own router and activation
+                  ("prefill", "sigmoid", "situ")]
 
 
 @pytest.mark.parametrize("name,score,act", FULL_SIZE_RUNS)
@@ -366,6 +368,10 @@ def test_forward_full_size(lib, name, score, act):
     rng = np.random.default_rng(c["cfg"])
     n = SAMPLED[name]
     tokens = np.arange(T) if n >= T else np.sort(rng.choice(T, n, replace=False))
+    # plus the tokens of the hottest expert's last (ragged) row tile and of the last row
+    tile = int(variant.split("/")[0].lstrip("smalrge"))
+    edge, _ = edge_tokens(counts, offsets, r2p, k, tile)
+    tokens = np.unique(np.concatenate([tokens, np.asarray(edge, dtype=np.int64)]))
     tok_d = torch.as_tensor(tokens, device=DEV)
     # quantised bytes of the sampled tokens' rows
     xq, xs = oracle.quantize_tokens(bits(inp["x"][tok_d]))
