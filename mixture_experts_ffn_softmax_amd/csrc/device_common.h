@@ -21,6 +21,15 @@ __device__ __forceinline__ uint4 load_stream16(const uint8_t* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// A weight load of the small GEMMs: non-temporal when NT (each weight tile
+// is read by about one row tile of the launch, so caching it gains nothing),
+// an ordinary load when several row tiles re-read it.
+template <bool NT>
+__device__ __forceinline__ uint4 load_w16(const uint8_t* p) {
+  if constexpr (NT) return load_stream16(p);
+  else return *reinterpret_cast<const uint4*>(p);
+}
+
 // Largest finite e4m3 magnitude; per-row scales are amax / kE4M3Max.
 constexpr float kE4M3Max = 448.0f;
 
@@ -110,7 +119,9 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 // Block-wide max / sum of one value per thread (blockDim.x a multiple of 64
-// or a single partial wave); `red` needs blockDim.x / 64 floats.
+// or a single partial wave); `red` needs blockDim.x / 64 floats.  A block of
+// one wave returns straight after the wave reduction, with no barrier: LDS
+// written before the call is not yet published to the other lanes.
 __device__ __forceinline__ float block_max(float v, float* red) {
   v = wave_max(v);
   const int nw = (blockDim.x + 63) >> 6;

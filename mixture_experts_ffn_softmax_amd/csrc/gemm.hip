@@ -747,7 +747,8 @@ __device__ __forceinline__ void small_pipeline(int wave, int nk, Load&& load, Co
 }
 
 // GEMM1: 16x16x128 MFMA on e4m3 x e4m3, or e2m1 x e4m3 with block scales.
-template <int WF, int TV, int G>
+// NT: weights loaded non-temporally (see load_w16).
+template <int WF, int TV, int G, bool NT>
 __device__ __forceinline__ void gemm1_small_body(const GemmParams& p, const TileInfo& ti, v4f (*red)[8][64]) {
   constexpr int kSmallDepth1 = 2;
   const int K = p.K;
@@ -814,7 +815,7 @@ __device__ __forceinline__ void gemm1_small_body(const GemmParams& p, const Tile
     return *reinterpret_cast<const uint4*>(tp[t] + ((k >> td.kc_shift) * td.chunk_stride + (k & ((1L << td.kc_shift) - 1))));
   };
   auto wgt = [&](int f, long k) {
-    return load_stream16(wp[f] + ((k >> wd.kc_shift) * wd.chunk_stride + (k & ((1L << wd.kc_shift) - 1))));
+    return load_w16<NT>(wp[f] + ((k >> wd.kc_shift) * wd.chunk_stride + (k & ((1L << wd.kc_shift) - 1))));
   };
 
   v4f acc[4][TV];
@@ -840,7 +841,7 @@ __device__ __forceinline__ void gemm1_small_body(const GemmParams& p, const Tile
     if constexpr (fp4) {
 #pragma unroll
       for (int f = 0; f < 4; ++f) {
-        const uint4 b0 = load_stream16(wp[f] + (long)ks * op_step(wd, 64));
+        const uint4 b0 = load_w16<NT>(wp[f] + (long)ks * op_step(wd, 64));
         st.w[f] = v8i{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, 0, 0, 0, 0};
         st.sc[f] = (int)*reinterpret_cast<const uint32_t*>(sp[f] + (long)ks * op_step(p.sd[ti.wi], 4));
       }
@@ -912,7 +913,7 @@ __device__ __forceinline__ void gemm1_small_body(const GemmParams& p, const Tile
 }
 
 // G: where the routed rows come from (RowSource: stored, or gathered)
-template <int FMT, int G>
+template <int FMT, int G, bool NT>
 __global__ __launch_bounds__(256) void gemm1_small_kernel(GemmParams p) {
   __shared__ v4f red[4][8][64];                 // per-wave partial sums
   __shared__ int s_tp[kMaxExperts + 2];
@@ -920,11 +921,11 @@ __global__ __launch_bounds__(256) void gemm1_small_kernel(GemmParams p) {
   const bool two = ti.row1 - ti.row0 > 16;
   // the routed group takes FMT; the shared group is always per-channel fp8
   if (FMT != kFp8 && ti.wi == 0) {
-    if (two) gemm1_small_body<FMT, 2, G>(p, ti, red);
-    else gemm1_small_body<FMT, 1, G>(p, ti, red);
+    if (two) gemm1_small_body<FMT, 2, G, NT>(p, ti, red);
+    else gemm1_small_body<FMT, 1, G, NT>(p, ti, red);
   } else {
-    if (two) gemm1_small_body<kFp8, 2, G>(p, ti, red);
-    else gemm1_small_body<kFp8, 1, G>(p, ti, red);
+    if (two) gemm1_small_body<kFp8, 2, G, NT>(p, ti, red);
+    else gemm1_small_body<kFp8, 1, G, NT>(p, ti, red);
   }
 }
 
@@ -939,7 +940,7 @@ __global__ __launch_bounds__(256) void gemm1_small_kernel(GemmParams p) {
 // A tile is kSmCh2 = 128 output channels (8 fragments): with K = I the
 // shortest contraction of the layer, wider tiles keep the launch to about
 // one workgroup per two SIMD pairs.
-template <int WF, int TV>
+template <int WF, int TV, bool NT>
 __device__ __forceinline__ void gemm2_small_body(const GemmParams& p, const TileInfo& ti, v4f (*red)[2 * kSmCh2 / 16][64]) {
   constexpr bool fp4 = WF == kMxfp4;
   constexpr bool blk = WF == kFp8Block;
@@ -986,7 +987,7 @@ __device__ __forceinline__ void gemm2_small_body(const GemmParams& p, const Tile
     return *reinterpret_cast<const uint4*>(tp[t] + ((k >> td.kc_shift) * td.chunk_stride + (k & ((1L << td.kc_shift) - 1))));
   };
   auto wgt = [&](int f, long k) {
-    return load_stream16(wp[f] + ((k >> wd.kc_shift) * wd.chunk_stride + (k & ((1L << wd.kc_shift) - 1))));
+    return load_w16<NT>(wp[f] + ((k >> wd.kc_shift) * wd.chunk_stride + (k & ((1L << wd.kc_shift) - 1))));
   };
 
   v4f acc[NF][TV];
@@ -1011,7 +1012,7 @@ __device__ __forceinline__ void gemm2_small_body(const GemmParams& p, const Tile
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
       if constexpr (fp4) {
-        st.w[f] = load_stream16(wp[f] + (long)ks * op_step(wd, 64));
+        st.w[f] = load_w16<NT>(wp[f] + (long)ks * op_step(wd, 64));
         st.sc[f] = sp[f][(long)ks * op_step(p.sd[0], 4)];
       } else {
         st.w[f] = wgt(f, (long)ks * KS + lg * 16);
@@ -1075,20 +1076,19 @@ __device__ __forceinline__ void gemm2_small_body(const GemmParams& p, const Tile
   }
 }
 
-template <int FMT>
+template <int FMT, bool NT>
 __global__ __launch_bounds__(256) void gemm2_small_kernel(GemmParams p) {
   __shared__ v4f red[4][2 * kSmCh2 / 16][64];
   __shared__ int s_tp[kMaxExperts + 2];
   MOE_TILE_PROLOGUE(kSmRows);
-  // MXFP4 routed weights; the shared group is always fp8
   const bool two = ti.row1 - ti.row0 > 16;
   // the routed group takes FMT; the shared group is always per-channel fp8
   if (FMT != kFp8 && ti.wi == 0) {
-    if (two) gemm2_small_body<FMT, 2>(p, ti, red);
-    else gemm2_small_body<FMT, 1>(p, ti, red);
+    if (two) gemm2_small_body<FMT, 2, NT>(p, ti, red);
+    else gemm2_small_body<FMT, 1, NT>(p, ti, red);
   } else {
-    if (two) gemm2_small_body<kFp8, 2>(p, ti, red);
-    else gemm2_small_body<kFp8, 1>(p, ti, red);
+    if (two) gemm2_small_body<kFp8, 2, NT>(p, ti, red);
+    else gemm2_small_body<kFp8, 1, NT>(p, ti, red);
   }
 }
 
@@ -1181,6 +1181,10 @@ int choose_variant(const FfnGroups& g, long n_rows) {
   return avg >= 384 ? kVariantLarge256 : kVariantLarge128;
 }
 
+bool small_streams_weights(const FfnGroups& g, long n_rows) {
+  return n_rows <= (long)kSmRows * (g.n_groups > 0 ? g.n_groups : 1);
+}
+
 int variant_rows(int variant) {
   return variant == kVariantLarge256 ? 256 : variant == kVariantLarge128 ? 128 : kSmRows;
 }
@@ -1235,12 +1239,16 @@ hipError_t launch_gemm1(int variant, const FfnGroups& g, const RowOperand& x, co
   if (variant == kVariantSmall) {
     p.ntiles = g.inter / (kSmCh / 2);
     const long grid = max_row_tiles(n_rows, g.n_groups, bm) * p.ntiles;
-    auto kern = x.gather ? (g.fmt == kMxfp4      ? gemm1_small_kernel<kMxfp4, kRowsGathered>
-                            : g.fmt == kFp8Block ? gemm1_small_kernel<kFp8Block, kRowsGathered>
-                                                 : gemm1_small_kernel<kFp8, kRowsGathered>)
-                         : (g.fmt == kMxfp4      ? gemm1_small_kernel<kMxfp4, kRowsStored>
-                            : g.fmt == kFp8Block ? gemm1_small_kernel<kFp8Block, kRowsStored>
-                                                 : gemm1_small_kernel<kFp8, kRowsStored>);
+    auto pick = [&](auto nt) {
+      constexpr bool NT = decltype(nt)::value;
+      return x.gather ? (g.fmt == kMxfp4      ? gemm1_small_kernel<kMxfp4, kRowsGathered, NT>
+                         : g.fmt == kFp8Block ? gemm1_small_kernel<kFp8Block, kRowsGathered, NT>
+                                              : gemm1_small_kernel<kFp8, kRowsGathered, NT>)
+                      : (g.fmt == kMxfp4      ? gemm1_small_kernel<kMxfp4, kRowsStored, NT>
+                         : g.fmt == kFp8Block ? gemm1_small_kernel<kFp8Block, kRowsStored, NT>
+                                              : gemm1_small_kernel<kFp8, kRowsStored, NT>);
+    };
+    auto kern = small_streams_weights(g, n_rows) ? pick(std::true_type{}) : pick(std::false_type{});
     hipExtLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, s, ev_start, ev_stop, 0, p);
   } else {
     p.ntiles = g.inter / (kLgCh / 2);
@@ -1274,8 +1282,12 @@ hipError_t launch_gemm2(int variant, const FfnGroups& g, const uint16_t* h, cons
   if (variant == kVariantSmall) {
     p.ntiles = g.hidden / kSmCh2;
     const long grid = max_row_tiles(n_rows, g.n_groups, bm) * p.ntiles;
-    auto kern = g.fmt == kMxfp4 ? gemm2_small_kernel<kMxfp4>
-                                : g.fmt == kFp8Block ? gemm2_small_kernel<kFp8Block> : gemm2_small_kernel<kFp8>;
+    auto pick = [&](auto nt) {
+      constexpr bool NT = decltype(nt)::value;
+      return g.fmt == kMxfp4 ? gemm2_small_kernel<kMxfp4, NT>
+                             : g.fmt == kFp8Block ? gemm2_small_kernel<kFp8Block, NT> : gemm2_small_kernel<kFp8, NT>;
+    };
+    auto kern = small_streams_weights(g, n_rows) ? pick(std::true_type{}) : pick(std::false_type{});
     hipExtLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, s, ev_start, ev_stop, 0, p);
   } else {
     p.ntiles = g.hidden / kLgCh;

@@ -143,6 +143,11 @@ struct RowOperand {
 enum GemmVariant { kVariantSmall = 0, kVariantLarge128 = 1, kVariantLarge256 = 2 };
 
 int choose_variant(const FfnGroups& g, long n_rows);
+// The small variant streams its weights with non-temporal loads when the
+// groups average at most one row tile (kSmRows rows): each weight tile is then
+// read by about one workgroup.  With more rows per group several row tiles
+// re-read each weight tile, and ordinary (cached) loads serve them.
+bool small_streams_weights(const FfnGroups& g, long n_rows);
 int variant_rows(int variant);          // rows per tile
 const char* variant_name(int variant);
 long max_row_tiles(long n_rows, int n_groups, int bm);
