@@ -29,6 +29,30 @@ def _p(t):
     return ctypes.c_void_p(0 if t is None else t.data_ptr())
 
 
+def _need(t, name, dtype, ndim=None, optional=False):
+    """Checks that tensor ``t`` is a contiguous device tensor of ``dtype``
+    (and ``ndim`` dimensions): the library reads raw pointers, so a wrong
+    dtype or a strided view would be misread rather than converted."""
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _nbytes(t):
+    return t.numel() * t.element_size()
+
+
 def _stream(stream):
     s = torch.cuda.current_stream() if stream is None else stream
     return ctypes.c_void_p(s.cuda_stream)
@@ -49,6 +73,11 @@ class Weights:
         self.tensors = {k: v.contiguous() for k, v in d.items()}
         t = self.tensors
         self.fmt = {"fp8": MOE_W_FP8, "mxfp4": MOE_W_MXFP4, "fp8_block": _lib.MOE_W_FP8_BLOCK}[fmt]
+        scale_dtype = torch.uint8 if fmt == "mxfp4" else torch.float32
+        for key in ("w1", "w3", "w2"):
+            _need(t.get(key), key, torch.uint8, 3)
+        for key in ("s1", "s3", "s2"):
+            _need(t.get(key), key, scale_dtype, 3 if fmt != "fp8" else 2)
         E, I = t["w1"].shape[0], t["w1"].shape[1]
         H = t["w2"].shape[1]
         self.n_experts, self.hidden, self.inter = E, H, I
@@ -74,6 +103,13 @@ class Weights:
         return ctypes.byref(self.c)
 
 
+# dtypes of the intermediates a debug capture may receive
+_DEBUG_DTYPES = dict(topk_ids=torch.int32, topk_w=torch.float32, expert_counts=torch.int32,
+                     expert_offsets=torch.int32, pair_to_row=torch.int32, row_to_pair=torch.int32,
+                     xq_rows=torch.uint8, xs_rows=torch.float32, latent=torch.bfloat16,
+                     core_out=torch.bfloat16)
+
+
 def _empty(shape, dtype, device):
     return torch.empty(shape, dtype=dtype, device=device)
 
@@ -83,6 +119,9 @@ def _score(score):
 
 
 def moe_route(logits, top_k, topk_ids=None, topk_w=None, score="softmax", stream=None):
+    _need(logits, "logits", torch.float32, 2)
+    _need(topk_ids, "topk_ids", torch.int32, 2, optional=True)
+    _need(topk_w, "topk_w", torch.float32, 2, optional=True)
     T, E = logits.shape
     dev = logits.device
     topk_ids = _empty((T, top_k), torch.int32, dev) if topk_ids is None else topk_ids
@@ -94,6 +133,8 @@ def moe_route(logits, top_k, topk_ids=None, topk_w=None, score="softmax", stream
 
 def moe_permute(x, topk_ids, n_experts, token_order=False, stream=None):
     """Returns dict(counts, offsets, pair_to_row, row_to_pair, xq_rows, xs_rows[, xq_tok, xs_tok])."""
+    _need(x, "x", torch.bfloat16, 2)
+    _need(topk_ids, "topk_ids", torch.int32, 2)
     T, H = x.shape
     k = topk_ids.shape[1]
     dev = x.device
@@ -117,6 +158,9 @@ def moe_permute(x, topk_ids, n_experts, token_order=False, stream=None):
 
 
 def moe_expert_ffn(xq_rows, xs_rows, expert_offsets, weights, stream=None):
+    _need(xq_rows, "xq_rows", torch.uint8, 2)
+    _need(xs_rows, "xs_rows", torch.float32, 1)
+    _need(expert_offsets, "expert_offsets", torch.int32, 1)
     n_rows = xq_rows.shape[0]
     dev = xq_rows.device
     y = _empty((n_rows, weights.hidden), torch.float32, dev)
@@ -129,6 +173,11 @@ def moe_expert_ffn(xq_rows, xs_rows, expert_offsets, weights, stream=None):
 
 def moe_combine(y_rows, pair_to_row, topk_w, y_shared=None, norm_gamma=None, norm_eps=1e-6,
                 stream=None):
+    _need(y_rows, "y_rows", torch.float32, 2)
+    _need(pair_to_row, "pair_to_row", torch.int32, 2)
+    _need(topk_w, "topk_w", torch.float32, 2)
+    _need(y_shared, "y_shared", torch.float32, 2, optional=True)
+    _need(norm_gamma, "norm_gamma", torch.float32, 1, optional=True)
     T, k = pair_to_row.shape
     H = y_rows.shape[1]
     out = _empty((T, H), torch.bfloat16, y_rows.device)
@@ -152,6 +201,11 @@ def moe_forward(x, logits, top_k, routed, shared=None, norm_gamma=None, norm_eps
     by the gate-up / down GEMM's dispatch; ``layer_events``: (start, stop)
     stamped by the layer's first and last dispatch.  Returns ``out`` (and the
     chosen kernel variant string when debug is given)."""
+    _need(x, "x", torch.bfloat16, 2)
+    _need(logits, "logits", torch.float32, 2)
+    _need(norm_gamma, "norm_gamma", torch.float32, 1, optional=True)
+    _need(out, "out", torch.bfloat16, 2, optional=True)
+    _need(ws, "ws", torch.uint8, 1, optional=True)
     T, H = x.shape
     dev = x.device
     out = _empty((T, H), torch.bfloat16, dev) if out is None else out
@@ -162,6 +216,7 @@ def moe_forward(x, logits, top_k, routed, shared=None, norm_gamma=None, norm_eps
     if debug is not None or any(v is not None for v in (events, gemm1_events, gemm2_events, layer_events)):
         dbg = MoeDebug()
         for key, t in (debug or {}).items():
+            _need(t, f"debug[{key}]", _DEBUG_DTYPES[key])
             setattr(dbg, key, t.data_ptr())
         for i, ev in enumerate(events or []):
             if ev is not None:
@@ -175,7 +230,7 @@ def moe_forward(x, logits, top_k, routed, shared=None, norm_gamma=None, norm_eps
     check(lib().moe_forward(_p(x), _p(logits), T, top_k, _score(score), routed.ref(), int(shared is not None),
                             shared.ref() if shared is not None else None, _p(norm_gamma),
                             float(norm_eps), _p(out), ctypes.byref(dbg) if dbg is not None else None,
-                            _p(ws), ws.numel(), _stream(stream)))
+                            _p(ws), _nbytes(ws), _stream(stream)))
     if debug is not None:
         return out, dbg.variant.decode()
     return out
@@ -221,6 +276,12 @@ class LatentWeights:
 
 def moe_linear(a, weights, addend=None, out_dtype=torch.bfloat16, out=None, stream=None):
     """out = a W^T (+ addend before the bf16 rounding)."""
+    _need(a, "a", torch.bfloat16, 2)
+    _need(addend, "addend", torch.float32, 2, optional=True)
+    if out is not None and out.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("out must be bfloat16 or float32")
+    if out is not None:
+        _need(out, "out", out.dtype, 2)
     M = a.shape[0]
     if out is None:
         out = _empty((M, weights.c.n_out), out_dtype, a.device)
@@ -242,6 +303,11 @@ def moe_latent_forward(x, logits, top_k, latent, routed, norm_gamma=None, norm_e
     ``layer_events`` bracket the block, ``gemm1_events`` / ``gemm2_events``
     the routed core's GEMMs.  Returns ``out`` (and the core's kernel variant
     string when debug is given)."""
+    _need(x, "x", torch.bfloat16, 2)
+    _need(logits, "logits", torch.float32, 2)
+    _need(norm_gamma, "norm_gamma", torch.float32, 1, optional=True)
+    _need(out, "out", torch.bfloat16, 2, optional=True)
+    _need(ws, "ws", torch.uint8, 1, optional=True)
     T = x.shape[0]
     out = _empty((T, latent.hidden), torch.bfloat16, x.device) if out is None else out
     nbytes = latent_forward_workspace_size(T, top_k, latent, routed)
@@ -251,6 +317,7 @@ def moe_latent_forward(x, logits, top_k, latent, routed, norm_gamma=None, norm_e
     if debug is not None or any(v is not None for v in (layer_events, gemm1_events, gemm2_events)):
         dbg = MoeDebug()
         for key, t in (debug or {}).items():
+            _need(t, f"debug[{key}]", _DEBUG_DTYPES[key])
             setattr(dbg, key, t.data_ptr())
         for name, evs in (("layer_events", layer_events), ("gemm1_events", gemm1_events),
                           ("gemm2_events", gemm2_events)):
@@ -258,7 +325,7 @@ def moe_latent_forward(x, logits, top_k, latent, routed, norm_gamma=None, norm_e
                 getattr(dbg, name)[i] = ev.cuda_event
     check(lib().moe_latent_forward(_p(x), _p(logits), T, top_k, _score(score), latent.ref(), routed.ref(),
                                    _p(norm_gamma), float(norm_eps), _p(out),
-                                   ctypes.byref(dbg) if dbg is not None else None, _p(ws), ws.numel(),
+                                   ctypes.byref(dbg) if dbg is not None else None, _p(ws), _nbytes(ws),
                                    _stream(stream)))
     if debug is not None:
         return out, dbg.variant.decode()

@@ -169,8 +169,8 @@ __device__ __forceinline__ void quant_token(const uint16_t* __restrict__ x, long
   __shared__ int s_rows[kMaxTopK];
   const int nchk = H >> 3;
   const uint4* src = reinterpret_cast<const uint4*>(x + t * H);
-  // the token's rows, fetched first so that their latency overlaps the row's
-  // (block_max's barrier publishes them)
+  // the token's rows, fetched first so that their latency overlaps the row's;
+  // a barrier after the amax reduction publishes them to every lane
   if (threadIdx.x < k) s_rows[threadIdx.x] = pair_to_row[t * k + threadIdx.x];
   uint4 in[CPT];
   float amax = 0.0f;
@@ -184,6 +184,8 @@ __device__ __forceinline__ void quant_token(const uint16_t* __restrict__ x, long
       amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(wds[q])), fabsf(bf16_hi(wds[q]))));
   }
   amax = block_max(amax, red);
+  // block_max has barriers only when the block has more than one wave
+  if (blockDim.x <= 64) __syncthreads();
   const float s = (amax == 0.0f) ? 1.0f : amax / kE4M3Max;
   const float r = e4m3_recip(s);
   uint2 q8[CPT];
