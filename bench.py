@@ -49,6 +49,10 @@ def parse():
     ap.add_argument("--no-block", action="store_true", help="skip the per-block fp8 measurement")
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the prefill (headline) measurement: for profiling the other workloads alone")
+    ap.add_argument("--no-tiny", action="store_true", help="skip the tiny (launch-latency) workload")
+    ap.add_argument("--no-skewed", action="store_true", help="skip the skewed 256-expert whole layer")
+    ap.add_argument("--no-latent-core", action="store_true", help="skip the LatentMoE expert core alone")
+    ap.add_argument("--no-sclk", action="store_true", help="skip sampling the shader clock under load")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=2048,
                     help="tokens in the CPU oracle's sample (FFN + combine of each)")
@@ -153,6 +157,7 @@ class Layer:
         per = moe_synth.weight_bytes_per_expert(self.H, self.I, self.cfg["fmt"])
         scales = {"fp8": 4 * (2 * self.I + self.H),
                   "fp8_block": 4 * 3 * (self.H // 128) * (self.I // 128)}.get(self.cfg["fmt"], 0)
+        # (MXFP4: the per-expert figure already holds the e8m0 scales)
         total = touched * (per + scales)
         if self.shared is not None:
             total += 3 * self.H * self.I + 4 * (2 * self.I + self.H)
@@ -247,6 +252,55 @@ def dense_rates(block, reps=20):
         res[name] = {"us": round(us, 2), "TFLOP/s": round(flops / (us * 1e-6) / 1e12, 1),
                      "frac_bf16_peak": round(flops / (us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4)}
     return res
+
+
+def rocm_version():
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            return f.read().strip()
+    except OSError:
+        return None
+
+
+def sample_sclk(layer, seconds=3.0):
+    """The shader clock while the layer runs back to back: rocm-smi (a child
+    process) reads the clocks once the GPU has been busy for a second.
+    Returns the reported SCLK string, or None."""
+    import subprocess
+    import threading
+
+    import torch
+    box = {}
+
+    def probe():
+        time.sleep(1.0)
+        try:
+            r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=20)
+            box["out"] = r.stdout
+        except Exception as e:  # noqa: BLE001 (best effort: the tool may be absent)
+            box["err"] = str(e)
+
+    th = threading.Thread(target=probe)
+    th.start()
+    t0, i = time.perf_counter(), 0
+    while th.is_alive() or time.perf_counter() - t0 < seconds:
+        layer.step(i)
+        i += 1
+        if i % 20 == 0:
+            torch.cuda.synchronize()
+            if time.perf_counter() - t0 > 30:
+                break
+    torch.cuda.synchronize()
+    th.join()
+    try:
+        data = json.loads(box.get("out", ""))
+        for card in data.values():
+            for key, val in card.items():
+                if "sclk" in key.lower():
+                    return str(val)
+    except ValueError:
+        pass
+    return None
 
 
 def make_events(n):
@@ -413,6 +467,77 @@ def measure_prefill(args):
     return result
 
 
+def measure_small(name, steps, warmup):
+    """The tiny workload: launch-latency bound, so only microseconds."""
+    import torch
+    layer = Layer(name, 1)
+    c = layer.cfg
+    tl = time_layer(layer, steps, warmup)
+    res = {"workload": f"{name}: T={c['T']} H={c['H']} I={c['I']} E={c['E']} top_k={c['k']} {c['fmt']}",
+           "us_per_layer": round(tl["ms"] * 1e3, 2), "us_per_layer_gpu_events": round(tl["gpu_ms"] * 1e3, 2),
+           "us_per_layer_dispatch_events": percentiles_us(tl["layer_ms"]),
+           "gemm_us": {"gemm1": round(tl["g1_ms"] * 1e3, 2), "gemm2": round(tl["g2_ms"] * 1e3, 2)},
+           "bound": "launch latency (fractions of a roofline are not meaningful at this size)"}
+    del layer
+    torch.cuda.empty_cache()
+    return res
+
+
+def measure_skewed(steps, warmup):
+    """The skewed whole layer (16384 tokens, 256 experts, top-8, Zipf-biased
+    router, hottest expert ~5x the mean): fp8 MFMA bound."""
+    import torch
+    layer = Layer("skewed", 1)
+    c = layer.cfg
+    tl = time_layer(layer, steps, warmup)
+    flops, flops_g1 = layer.flops()
+    wb, io, touched = layer.weight_bytes_touched()
+    ms = tl["ms"]
+    ids = torch.topk(layer.inp["logits"], layer.k, dim=1).indices
+    counts = torch.bincount(ids.flatten(), minlength=layer.E).float()
+    g1, g2 = tl["g1_ms"], tl["g2_ms"]
+    res = {"workload": f"skewed: T={c['T']} H={c['H']} I={c['I']} E={c['E']} top_k={c['k']} fp8, "
+                       f"Zipf-biased router (alpha {c['alpha']:.4f})",
+           "us_per_layer": round(ms * 1e3, 1), "us_per_layer_gpu_events": round(tl["gpu_ms"] * 1e3, 1),
+           "us_per_layer_dispatch_events": percentiles_us(tl["layer_ms"]),
+           "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 1),
+           "frac_fp8_peak": round(flops / (ms * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4),
+           "GB_per_s": round((wb + io) / (ms * 1e-3) / 1e9, 1),
+           "frac_hbm": round((wb + io) / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+           "algorithmic_bytes": wb + io, "flops_per_layer": flops, "touched_experts": touched,
+           "alpha": c["alpha"], "hottest_over_mean": round(float(counts.max() / counts.mean()), 3),
+           "gemm_us": {"gemm1": round(g1 * 1e3, 1), "gemm2": round(g2 * 1e3, 1)},
+           "gemm_frac": {"gemm1_fp8": round(flops_g1 / (g1 * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4),
+                         "gemm2_bf16": round((flops - flops_g1) / (g2 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}}
+    del layer
+    torch.cuda.empty_cache()
+    return res
+
+
+def measure_latent_core(steps, warmup):
+    """The LatentMoE expert core alone (512 tokens of latent 3584, 896 MXFP4
+    experts 3584 -> 3072 -> 3584, top-16, RMSNorm): HBM bound on the touched
+    experts' weights."""
+    import torch
+    layer = Layer("latent", 1)
+    c = layer.cfg
+    tl = time_layer(layer, steps, warmup)
+    flops, _ = layer.flops()
+    wb, io, touched = layer.weight_bytes_touched()
+    ms = tl["ms"]
+    res = {"workload": f"latent core: T={c['T']} H={c['H']} I={c['I']} E={c['E']} top_k={c['k']} mxfp4 +RMSNorm",
+           "us_per_layer": round(ms * 1e3, 1), "us_per_layer_gpu_events": round(tl["gpu_ms"] * 1e3, 1),
+           "us_per_layer_dispatch_events": percentiles_us(tl["layer_ms"]),
+           "GB_per_s": round((wb + io) / (ms * 1e-3) / 1e9, 1),
+           "frac_hbm": round((wb + io) / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+           "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 1),
+           "algorithmic_bytes": wb + io, "touched_experts": touched,
+           "gemm_us": {"gemm1": round(tl["g1_ms"] * 1e3, 1), "gemm2": round(tl["g2_ms"] * 1e3, 1)}}
+    del layer
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -431,6 +556,26 @@ def main():
     if not args.no_prefill:
         result = measure_prefill(args)
         torch.cuda.empty_cache()
+    result["rocm_version"] = rocm_version()
+    result["torch_hip"] = torch.version.hip
+    if not args.no_sclk and not args.no_prefill:
+        log("[bench] shader clock under load (rocm-smi while the prefill layer runs)")
+        sl = Layer(args.config, 1)
+        result["sclk_under_load"] = sample_sclk(sl)
+        del sl
+        torch.cuda.empty_cache()
+
+    if not args.no_tiny:
+        log("[bench] tiny workload (launch latency)")
+        result["tiny"] = measure_small("tiny", max(args.steps, 200), args.warmup)
+
+    if not args.no_skewed:
+        log("[bench] skewed whole layer (16384 tokens, 256 experts top-8)")
+        result["skewed"] = measure_skewed(min(args.steps, 20), min(args.warmup, 3))
+
+    if not args.no_latent_core:
+        log("[bench] LatentMoE expert core alone (512 tokens, 896 MXFP4 experts top-16, RMSNorm)")
+        result["latent_core"] = measure_latent_core(min(args.steps, 20), min(args.warmup, 3))
 
     if not args.no_decode:
         log("[bench] decode share (weight-stream bound)")
