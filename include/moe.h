@@ -33,7 +33,9 @@
  *    copies device data to the host and never reads device data on the
  *    host.  All work is enqueued on `stream`, so every call can be captured
  *    into a HIP graph.  No global mutable state: calls on different streams
- *    with distinct workspaces may run concurrently.
+ *    with distinct workspaces may run concurrently.  The one exception is
+ *    moe_forward_noalloc, whose workspace is a per-device scratch array the
+ *    library holds (see there).
  *  - Errors: arguments are validated on the host before anything is enqueued;
  *    on a non-OK return nothing has been enqueued or written.  A launch
  *    failure reported by the runtime returns MOE_ERR_DEVICE (work enqueued
@@ -306,6 +308,33 @@ moe_status_t moe_forward(const uint16_t* x, const float* logits, int32_t T, int3
                          const moe_weights_t* shared, const float* norm_gamma, float norm_eps,
                          uint16_t* out, moe_debug_t* dbg, void* ws, size_t ws_bytes,
                          void* stream);
+
+/*
+ * moe_forward_noalloc -- moe_forward for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  The arguments and results are moe_forward's, without the
+ * workspace: the call uses a scratch array of MOE_NOALLOC_SCRATCH_BYTES that
+ * the library holds on each device (a file-scope device array, allocated when
+ * the library's code is loaded on that device and kept until the process
+ * ends).  The call itself allocates and frees nothing.
+ *   - Limit: a call whose moe_forward_workspace_size exceeds
+ *     MOE_NOALLOC_SCRATCH_BYTES returns MOE_ERR_WORKSPACE with nothing
+ *     enqueued.  64 MiB holds, for instance, the 8-expert decode share
+ *     (H 8192, I 2048, top-2, shared expert) up to about 560 tokens.
+ *   - The stream must belong to the current device (else
+ *     MOE_ERR_UNSUPPORTED).  The scratch address of a device is looked up
+ *     (hipGetSymbolAddress) on the first call with that device current.
+ *   - Every call on a device shares that device's scratch, and the scratch
+ *     keeps the last call's contents (every buffer the layer carves from it
+ *     is fully written before it is read).  Calls that overlap in time on
+ *     one device -- on different streams, or from different threads --
+ *     race on the scratch: order them on one stream.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+moe_status_t moe_forward_noalloc(const uint16_t* x, const float* logits, int32_t T, int32_t top_k,
+                                 int32_t score, const moe_weights_t* routed, int32_t use_shared,
+                                 const moe_weights_t* shared, const float* norm_gamma, float norm_eps,
+                                 uint16_t* out, moe_debug_t* dbg, void* stream);
 
 /*
  * moe_pack_weights -- copy row-major expert weights into the K-blocked

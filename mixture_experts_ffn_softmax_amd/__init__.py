@@ -17,7 +17,7 @@ from ._lib import (MOE_LAYOUT_K_BLOCKED, MOE_LAYOUT_ROW_MAJOR, MOE_LIN_BF16, MOE
                    check)
 
 __all__ = ["Weights", "Linear", "LatentWeights", "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine",
-           "moe_forward", "forward_workspace_size", "moe_linear", "moe_latent_forward",
+           "moe_forward", "moe_forward_noalloc", "forward_workspace_size", "moe_linear", "moe_latent_forward",
            "latent_forward_workspace_size", "MoeError", "lib"]
 
 
@@ -231,6 +231,35 @@ def moe_forward(x, logits, top_k, routed, shared=None, norm_gamma=None, norm_eps
                             shared.ref() if shared is not None else None, _p(norm_gamma),
                             float(norm_eps), _p(out), ctypes.byref(dbg) if dbg is not None else None,
                             _p(ws), _nbytes(ws), _stream(stream)))
+    if debug is not None:
+        return out, dbg.variant.decode()
+    return out
+
+
+def moe_forward_noalloc(x, logits, top_k, routed, shared=None, norm_gamma=None, norm_eps=1e-6, out=None,
+                        debug=None, score="softmax", stream=None):
+    """moe_forward with the library's per-device scratch as its workspace:
+    the call allocates nothing on the device (``out`` may be passed in for a
+    call that allocates nothing at all).  Calls that need more than
+    MOE_NOALLOC_SCRATCH_BYTES of workspace raise MoeError (MOE_ERR_WORKSPACE).
+    ``debug`` as for moe_forward.  Returns ``out`` (and the variant string
+    when debug is given)."""
+    _need(x, "x", torch.bfloat16, 2)
+    _need(logits, "logits", torch.float32, 2)
+    _need(norm_gamma, "norm_gamma", torch.float32, 1, optional=True)
+    _need(out, "out", torch.bfloat16, 2, optional=True)
+    T, H = x.shape
+    out = _empty((T, H), torch.bfloat16, x.device) if out is None else out
+    dbg = None
+    if debug is not None:
+        dbg = MoeDebug()
+        for key, t in debug.items():
+            _need(t, f"debug[{key}]", _DEBUG_DTYPES[key])
+            setattr(dbg, key, t.data_ptr())
+    check(lib().moe_forward_noalloc(_p(x), _p(logits), T, top_k, _score(score), routed.ref(),
+                                    int(shared is not None), shared.ref() if shared is not None else None,
+                                    _p(norm_gamma), float(norm_eps), _p(out),
+                                    ctypes.byref(dbg) if dbg is not None else None, _stream(stream)))
     if debug is not None:
         return out, dbg.variant.decode()
     return out

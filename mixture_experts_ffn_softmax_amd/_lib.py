@@ -21,11 +21,12 @@ STAGE_NAMES = ["route", "permute", "gemm1", "gemm2", "combine"]
 MOE_ACT_SILU, MOE_ACT_SITU = 0, 1
 MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
 MOE_LIN_MXFP4, MOE_LIN_BF16 = 0, 1
+MOE_NOALLOC_SCRATCH_BYTES = 64 << 20   # the scratch moe_forward_noalloc holds per device
 
 # Every function include/moe.h declares.
 EXPORTS = [
     "moe_route", "moe_permute_workspace_size", "moe_permute", "moe_expert_ffn_workspace_size",
-    "moe_expert_ffn", "moe_combine", "moe_forward_workspace_size", "moe_forward",
+    "moe_expert_ffn", "moe_combine", "moe_forward_workspace_size", "moe_forward", "moe_forward_noalloc",
     "moe_pack_weights", "moe_linear", "moe_latent_forward_workspace_size", "moe_latent_forward",
     "moe_status_string", "moe_last_error", "moe_version",
 ]
@@ -86,6 +87,7 @@ SIGNATURES = {
     "moe_combine": (_I32, [_VP, _VP, _VP, _I32, _I32, _I32, _VP, _VP, _F32, _VP, _VP]),
     "moe_forward_workspace_size": (_SZ, [_I32, _I32, _WP, _I32]),
     "moe_forward": (_I32, [_VP, _VP, _I32, _I32, _I32, _WP, _I32, _WP, _VP, _F32, _VP, _DP, _VP, _SZ, _VP]),
+    "moe_forward_noalloc": (_I32, [_VP, _VP, _I32, _I32, _I32, _WP, _I32, _WP, _VP, _F32, _VP, _DP, _VP]),
     "moe_pack_weights": (_I32, [_WP, _WP, _VP]),
     "moe_linear": (_I32, [_VP, _I32, _LP, _VP, _VP, _VP, _VP]),
     "moe_latent_forward_workspace_size": (_SZ, [_I32, _I32, _WP, _LTP]),

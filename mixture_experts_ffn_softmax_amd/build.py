@@ -15,7 +15,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe.so")
-SOURCES = ["route.hip", "permute.hip", "gemm.hip", "combine.hip", "dense.hip", "moe_api.cpp"]
+SOURCES = ["route.hip", "permute.hip", "gemm.hip", "combine.hip", "dense.hip", "noalloc.hip", "moe_api.cpp"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops: keep the compiler from forming packed fp32 instructions.

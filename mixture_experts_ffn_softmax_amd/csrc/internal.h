@@ -172,6 +172,12 @@ hipError_t launch_pack_kblocked(const uint8_t* src, uint8_t* dst, int E, int N, 
 // The same for chunks of 4 bytes (C = 4; K a multiple of 4).
 hipError_t launch_pack_kblocked4(const uint8_t* src, uint8_t* dst, int E, int N, int K, hipStream_t s);
 
+// ---- fixed scratch (moe_forward_noalloc) -----------------------------------
+// Device address of the library's scratch array on device `dev`, which must
+// be the current device: looked up with hipGetSymbolAddress on the first
+// call for that device and kept for the rest of the process.
+hipError_t noalloc_scratch(int dev, void** ptr);
+
 // ---- combine --------------------------------------------------------------
 hipError_t launch_combine(const float* y_rows, const int* pair_to_row, const float* w, int T,
                           int H, int k, const float* y_shared, const float* gamma, float eps,

@@ -402,15 +402,16 @@ size_t moe_forward_workspace_size(int32_t T, int32_t top_k, const moe_weights_t*
       .bytes;
 }
 
-moe_status_t moe_forward(const uint16_t* x, const float* logits, int32_t T, int32_t top_k,
-                         int32_t score, const moe_weights_t* routed, int32_t use_shared, const moe_weights_t* shared,
-                         const float* norm_gamma, float norm_eps, uint16_t* out, moe_debug_t* dbg,
-                         void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+// moe_forward's argument checks other than the workspace (host only).
+static moe_status_t check_forward(const uint16_t* x, const float* logits, int32_t T, int32_t top_k, int32_t score,
+                                  const moe_weights_t* routed, int32_t use_shared, const moe_weights_t* shared,
+                                  const float* norm_gamma, float norm_eps, uint16_t* out, const moe_debug_t* dbg) {
   MOE_CHECK(check_weights(routed, "routed"));
   const int32_t E = routed->n_experts, H = routed->hidden, I = routed->inter;
   MOE_CHECK(check_route_shape(T, E, top_k));
   MOE_CHECK(check_score(score));
-  const bool sigmoid = score == MOE_SCORE_SIGMOID;
   if (use_shared) {
     MOE_CHECK(check_weights(shared, "shared"));
     if (shared->n_experts != 1) return fail(MOE_ERR_SHAPE, "shared expert must have n_experts = 1");
@@ -438,6 +439,19 @@ moe_status_t moe_forward(const uint16_t* x, const float* logits, int32_t T, int3
     MOE_CHECK(opt(dbg->xq_rows, "dbg.xq_rows"));
     MOE_CHECK(opt(dbg->xs_rows, "dbg.xs_rows"));
   }
+  return ok();
+}
+
+extern "C" {
+
+moe_status_t moe_forward(const uint16_t* x, const float* logits, int32_t T, int32_t top_k,
+                         int32_t score, const moe_weights_t* routed, int32_t use_shared, const moe_weights_t* shared,
+                         const float* norm_gamma, float norm_eps, uint16_t* out, moe_debug_t* dbg,
+                         void* ws, size_t ws_bytes, void* stream) {
+  MOE_CHECK(check_forward(x, logits, T, top_k, score, routed, use_shared, shared, norm_gamma, norm_eps, out, dbg));
+  if (T == 0) return ok();
+  const int32_t E = routed->n_experts, H = routed->hidden;
+  const bool sigmoid = score == MOE_SCORE_SIGMOID;
   const bool sh = use_shared != 0;
   const size_t need_ws = moe_forward_workspace_size(T, top_k, routed, use_shared);
   if (!ws || ws_bytes < need_ws)
@@ -518,6 +532,35 @@ moe_status_t moe_forward(const uint16_t* x, const float* logits, int32_t T, int3
   if (e != hipSuccess) return device_status(e, "combine");
   if (ev && ev[MOE_N_STAGES]) hipEventRecord((hipEvent_t)ev[MOE_N_STAGES], s);
   return ok();
+}
+
+moe_status_t moe_forward_noalloc(const uint16_t* x, const float* logits, int32_t T, int32_t top_k, int32_t score,
+                                 const moe_weights_t* routed, int32_t use_shared, const moe_weights_t* shared,
+                                 const float* norm_gamma, float norm_eps, uint16_t* out, moe_debug_t* dbg,
+                                 void* stream) {
+  MOE_CHECK(check_forward(x, logits, T, top_k, score, routed, use_shared, shared, norm_gamma, norm_eps, out, dbg));
+  if (T == 0) return ok();
+  const size_t need_ws = moe_forward_workspace_size(T, top_k, routed, use_shared);
+  if (need_ws > MOE_NOALLOC_SCRATCH_BYTES)
+    return fail(MOE_ERR_WORKSPACE,
+                "this call needs %zu B of scratch; moe_forward_noalloc holds %zu B per device "
+                "(use moe_forward with a workspace of that size)",
+                need_ws, (size_t)MOE_NOALLOC_SCRATCH_BYTES);
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return device_status(e, "hipGetDevice");
+  if (stream) {
+    int sdev = -1;
+    e = hipStreamGetDevice((hipStream_t)stream, &sdev);
+    if (e != hipSuccess) return device_status(e, "hipStreamGetDevice");
+    if (sdev != dev)
+      return fail(MOE_ERR_UNSUPPORTED, "the stream belongs to device %d but device %d is current", sdev, dev);
+  }
+  void* scratch = nullptr;
+  e = moe::noalloc_scratch(dev, &scratch);
+  if (e != hipSuccess) return device_status(e, "scratch address (hipGetSymbolAddress)");
+  return moe_forward(x, logits, T, top_k, score, routed, use_shared, shared, norm_gamma, norm_eps, out, dbg,
+                     scratch, MOE_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 // ---------------------------------------------------------------------------

@@ -293,3 +293,28 @@ def test_latent_forward_validation(lib):
     d.latent = MIS
     assert call(dbg=d) == MOE_ERR_ALIGN
     assert call(T=0) == MOE_OK
+
+
+def test_forward_noalloc_validation(lib):
+    """The no-alloc entry point checks its arguments as moe_forward does, and
+    rejects a call whose workspace would exceed its scratch, all before any
+    device call."""
+    fn = lib.moe_forward_noalloc
+    w = fp8_weights()
+    sh = fp8_weights(E=1)
+
+    def call(T=16, k=2, routed=w, use_shared=0, shared=None, out=A, x=A, score=0):
+        return fn(x, A, T, k, score, ctypes.byref(routed), use_shared,
+                  ctypes.byref(shared) if shared is not None else None, None, 1e-6, out, None, None)
+
+    assert call(k=9) == MOE_ERR_SHAPE
+    assert call(use_shared=1) == MOE_ERR_NULL
+    assert call(out=None) == MOE_ERR_NULL
+    assert call(x=MIS) == MOE_ERR_ALIGN
+    assert call(score=5) == MOE_ERR_UNSUPPORTED
+    assert call(T=0) == MOE_OK
+    big = fp8_weights(E=8, H=8192, I=2048)
+    need = lib.moe_forward_workspace_size(4096, 2, ctypes.byref(big), 1)
+    assert need > _lib.MOE_NOALLOC_SCRATCH_BYTES
+    assert call(T=4096, routed=big, use_shared=1, shared=fp8_weights(E=1, H=8192, I=2048)) == MOE_ERR_WORKSPACE
+    assert b"scratch" in lib.moe_last_error()
