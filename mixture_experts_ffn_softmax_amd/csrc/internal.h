@@ -94,6 +94,10 @@ hipError_t launch_meta_quant(const float* logits, bool sigmoid, const uint16_t* 
 // row_to_pair[r] / k.
 hipError_t launch_rows_from_tokens(const uint8_t* xq_tok, const float* xs_tok, const int* row_to_pair, int T,
                                    int k, int H, uint8_t* xq_rows, float* xs_rows, hipStream_t s);
+// The same rows K-blocked (kTokChunk-byte chunks over T*k rows, as the
+// grouped GEMMs read them), with their scales; both outputs required.
+hipError_t launch_rows_kblocked(const uint8_t* xq_tok, const float* xs_tok, const int* row_to_pair, int T, int k,
+                                int H, uint8_t* xq_rows, float* xs_rows, hipStream_t s);
 
 // ---- grouped expert FFN ---------------------------------------------------
 // kFp8Block: e4m3 codes with one fp32 scale per 128 x 128 tile (channel

@@ -365,6 +365,17 @@ static bool fused_route_path(int32_t T, int32_t k, const moe_weights_t* routed, 
   const moe::FfnGroups g = make_groups(routed, shared ? routed : nullptr, nullptr);
   return moe::choose_variant(g, (long)T * k + (shared ? T : 0)) != moe::kVariantSmall;
 }
+// On the one-launch routing path the large kernels read expert-ordered rows
+// that a copy kernel writes from the token-order rows: their direct-to-LDS
+// loads of gathered rows fetch scattered 64-byte half lines, which cost the
+// 256-row gate-up GEMM about 40 us on the 2048-token prefill share, against
+// about 10 us for the copy.  The small kernels read their token fragments
+// straight into registers and gather them for little cost.
+static bool fused_rows_copied(int32_t T, int32_t k, const moe_weights_t* routed, bool shared) {
+  if (!fused_route_path(T, k, routed, shared)) return false;
+  const moe::FfnGroups g = make_groups(routed, shared ? routed : nullptr, nullptr);
+  return moe::choose_variant(g, (long)T * k + (shared ? T : 0)) != moe::kVariantSmall;
+}
 
 static ForwardLayout forward_layout(void* ws, int32_t T, int32_t k, const moe_weights_t* routed, bool shared) {
   ForwardLayout L{};
@@ -376,6 +387,7 @@ static ForwardLayout forward_layout(void* ws, int32_t T, int32_t k, const moe_we
   // scatter them to expert-ordered rows, and keep token order for the
   // shared expert
   const bool fused = fused_route_path(T, k, routed, shared);
+  const bool rows_needed = !fused || fused_rows_copied(T, k, routed, shared);
   const long rows = R + (shared ? T : 0);
   const long chunks = moe::permute_chunks(R);
   L.ids = c.take<int32_t>(R);
@@ -386,8 +398,8 @@ static ForwardLayout forward_layout(void* ws, int32_t T, int32_t k, const moe_we
   L.r2p = c.take<int32_t>(R);
   L.hist = c.take<int32_t>(chunks * E);
   L.base = c.take<int32_t>(chunks * E);
-  L.xq_rows = fused ? nullptr : c.take<uint8_t>((size_t)R * H);
-  L.xs_rows = fused ? nullptr : c.take<float>(R);
+  L.xq_rows = rows_needed ? c.take<uint8_t>((size_t)R * H) : nullptr;
+  L.xs_rows = rows_needed ? c.take<float>(R) : nullptr;
   L.xq_tok = (shared || fused) ? c.take<uint8_t>((size_t)T * H) : nullptr;
   L.xs_tok = (shared || fused) ? c.take<float>(T) : nullptr;
   L.y_rows = c.take<float>((size_t)rows * H);
@@ -498,9 +510,16 @@ moe_status_t moe_forward(const uint16_t* x, const float* logits, int32_t T, int3
       e = moe::launch_rows_from_tokens(L.xq_tok, L.xs_tok, L.r2p, T, top_k, H, dbg->xq_rows, dbg->xs_rows, s);
       if (e != hipSuccess) return device_status(e, "rows_from_tokens");
     }
-    xr = moe::RowOperand{{L.xq_tok, L.xq_tok}, {L.xs_tok, L.xs_tok}, R, {tok_d, tok_d}};
-    xr.gather = L.r2p;
-    xr.gather_k = top_k;
+    if (fused_rows_copied(T, top_k, routed, sh)) {
+      e = moe::launch_rows_kblocked(L.xq_tok, L.xs_tok, L.r2p, T, top_k, H, L.xq_rows, L.xs_rows, s);
+      if (e != hipSuccess) return device_status(e, "rows_kblocked");
+      xr = moe::RowOperand{{L.xq_rows, sh ? L.xq_tok : L.xq_rows}, {L.xs_rows, sh ? L.xs_tok : L.xs_rows}, R,
+                           {rows_d, sh ? tok_d : rows_d}};
+    } else {
+      xr = moe::RowOperand{{L.xq_tok, L.xq_tok}, {L.xs_tok, L.xs_tok}, R, {tok_d, tok_d}};
+      xr.gather = L.r2p;
+      xr.gather_k = top_k;
+    }
   } else {
     e = moe::launch_route(logits, T, E, top_k, sigmoid, L.ids, L.w, s, lev0);
     if (e != hipSuccess) return device_status(e, "route");

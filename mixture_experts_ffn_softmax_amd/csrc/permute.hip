@@ -707,6 +707,39 @@ __global__ __launch_bounds__(256) void rows_from_tokens_kernel(const uint8_t* __
   if (xs_rows && threadIdx.x == 0) xs_rows[r] = xs_tok[t];
 }
 
+// K-blocked expert-ordered rows from the K-blocked token-order rows: 16
+// bytes per thread, consecutive threads on consecutive bytes of the
+// destination (chunk c of rows 0..R-1 is contiguous there), so the writes
+// coalesce; each 64-byte chunk row of a token is read by 4 threads.
+__global__ __launch_bounds__(256) void rows_kblocked_kernel(const uint8_t* __restrict__ xq_tok,
+                                                            const float* __restrict__ xs_tok,
+                                                            const int* __restrict__ row_to_pair, int k, long R,
+                                                            long tok_cs, long n16, uint8_t* __restrict__ xq_rows,
+                                                            float* __restrict__ xs_rows) {
+  for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += (long)gridDim.x * blockDim.x) {
+    const long q = i & 3;                // 16-byte piece of the 64-byte chunk row
+    const long rc = i >> 2;              // chunk c of row r: rc = c * R + r
+    const long c = rc / R;
+    const long r = rc - c * R;
+    const long t = row_to_pair[r] / k;
+    *reinterpret_cast<uint4*>(xq_rows + (rc << 6) + (q << 4)) =
+        *reinterpret_cast<const uint4*>(xq_tok + c * tok_cs + (t << 6) + (q << 4));
+    if (c == 0 && q == 0) xs_rows[r] = xs_tok[t];
+  }
+}
+
+hipError_t launch_rows_kblocked(const uint8_t* xq_tok, const float* xs_tok, const int* row_to_pair, int T, int k,
+                                int H, uint8_t* xq_rows, float* xs_rows, hipStream_t s) {
+  const long R = (long)T * k;
+  if (R == 0) return hipSuccess;
+  const long n16 = R * (H / kTokChunk) * 4;
+  long blocks = (n16 + 255) / 256;
+  if (blocks > 16384) blocks = 16384;
+  rows_kblocked_kernel<<<(unsigned)blocks, 256, 0, s>>>(xq_tok, xs_tok, row_to_pair, k, R, (long)T * kTokChunk, n16,
+                                                        xq_rows, xs_rows);
+  return hipGetLastError();
+}
+
 hipError_t launch_rows_from_tokens(const uint8_t* xq_tok, const float* xs_tok, const int* row_to_pair, int T,
                                    int k, int H, uint8_t* xq_rows, float* xs_rows, hipStream_t s) {
   const long R = (long)T * k;
