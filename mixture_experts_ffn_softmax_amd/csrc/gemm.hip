@@ -252,6 +252,16 @@ __device__ __forceinline__ void pp_wait(int ks, int nk) {
   else wait_barrier<0>();
 }
 
+// Ring depth for a short tile's body: as many stages of `stage` bytes as the
+// kernel's ring of `ring` bytes holds, at most 8, and such that the direct-to-
+// LDS loads in flight stay within the vmcnt range (`per` per wave per stage).
+constexpr int short_stages(int ring, int stage, int per) {
+  int n = ring / stage;
+  if (n > 8) n = 8;
+  while ((n - 1) * per >= 64) --n;
+  return n;
+}
+
 // Valid token fragments of wave row wm in a tile with `vr` valid rows.
 template <int TF>
 __device__ __forceinline__ int valid_frags(int vr, int wm) {
@@ -478,6 +488,26 @@ __global__ __launch_bounds__(256, 1) void gemm1_pp_kernel(GemmParams p) {
   __syncthreads();   // every thread has its tile: the ring is free
   const int vr = min(BM, ti.row1 - ti.row0);
   const int wm = __builtin_amdgcn_readfirstlane(threadIdx.x >> 7);
+  // a short tile (the last of a ragged group) stages only the rows it has:
+  // 64 or 128 token rows per stage instead of BM, so that fewer direct-to-LDS
+  // loads are in flight (their throughput falls as more are outstanding)
+  // and, its stages being smaller, as deep a ring as the LDS holds (its
+  // loop is bound by the weight stream's latency, not by the MFMAs)
+  constexpr int S64 = short_stages(STAGES * kStage, (64 + kLgCh) * 64, 5);
+  constexpr int S128 = short_stages(STAGES * kStage, (128 + kLgCh) * 64, 6);
+  if (BM > 64 && vr <= 64) {
+    if (valid_frags<1>(vr, wm) == 0) gemm1_pp_body<64, S64, 0, SITU>(p, ti, smem);
+    else gemm1_pp_body<64, S64, 1, SITU>(p, ti, smem);
+    return;
+  }
+  if (BM > 128 && vr <= 128) {
+    switch (valid_frags<2>(vr, wm)) {
+      case 0: gemm1_pp_body<128, S128, 0, SITU>(p, ti, smem); break;
+      case 1: gemm1_pp_body<128, S128, 1, SITU>(p, ti, smem); break;
+      default: gemm1_pp_body<128, S128, 2, SITU>(p, ti, smem); break;
+    }
+    return;
+  }
   switch (valid_frags<TF>(vr, wm)) {
     case 0: gemm1_pp_body<BM, STAGES, 0, SITU>(p, ti, smem); break;
     case 1: gemm1_pp_body<BM, STAGES, 1, SITU>(p, ti, smem); break;
@@ -700,6 +730,22 @@ __global__ __launch_bounds__(256, 1) void gemm2_pp_kernel(GemmParams p) {
   __syncthreads();   // every thread has its tile: the ring is free
   const int vr = min(BM, ti.row1 - ti.row0);
   const int wm = __builtin_amdgcn_readfirstlane(threadIdx.x >> 7);
+  // a short tile stages only the rows it has (as in the gate-up GEMM)
+  constexpr int S64 = short_stages(STAGES * kStage, 64 * 64 + kLgCh * 32, 3);
+  constexpr int S128 = short_stages(STAGES * kStage, 128 * 64 + kLgCh * 32, 4);
+  if (BM > 64 && vr <= 64) {
+    if (valid_frags<1>(vr, wm) == 0) gemm2_pp_body<64, S64, 0>(p, ti, smem);
+    else gemm2_pp_body<64, S64, 1>(p, ti, smem);
+    return;
+  }
+  if (BM > 128 && vr <= 128) {
+    switch (valid_frags<2>(vr, wm)) {
+      case 0: gemm2_pp_body<128, S128, 0>(p, ti, smem); break;
+      case 1: gemm2_pp_body<128, S128, 1>(p, ti, smem); break;
+      default: gemm2_pp_body<128, S128, 2>(p, ti, smem); break;
+    }
+    return;
+  }
   switch (valid_frags<TF>(vr, wm)) {
     case 0: gemm2_pp_body<BM, STAGES, 0>(p, ti, smem); break;
     case 1: gemm2_pp_body<BM, STAGES, 1>(p, ti, smem); break;
