@@ -10,7 +10,8 @@
 // One workgroup per token (with RMSNorm, which needs the whole row), or per
 // token and slice of 256 chunks (without: more workgroups for small T).
 // Each thread owns CPT chunks of 8 channels, reads
-// the k fp32 expert rows with 16-byte loads (coalesced along the row),
+// the k fp32 expert rows with 16-byte loads (coalesced along the row, a few
+// pairs' loads in flight at once),
 // accumulates w_j * y in fp32 in slot order, optionally normalises, adds the
 // shared row and stores bf16 (round to nearest even): the output is rounded
 // once.
@@ -41,18 +42,53 @@ __global__ __launch_bounds__(1024) void combine_kernel(const float* __restrict__
 
   // this workgroup's slice of the row's chunks (the whole row when gridDim.y = 1)
   const int base = blockIdx.y * blockDim.x * CPT;
-  for (int j = 0; j < k; ++j) {
-    const int r = pair_to_row[t * k + j];
-    const float w = topk_w[t * k + j];
-    if (r < 0) continue;
-    const float4* src = reinterpret_cast<const float4*>(y_rows + (long)r * H);
+  // the shared row's loads go out with the first pairs' (it is added last;
+  // wide rows, CPT > 2, load it at the end to keep their registers)
+  constexpr bool kEarlyShared = CPT <= 2;
+  float4 sh[kEarlyShared ? CPT : 1][2];
+  if (kEarlyShared && y_shared) {
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
       const int idx = base + threadIdx.x + c * blockDim.x;
       if (idx < nchk) {
-        const float4 v0 = src[2 * idx], v1 = src[2 * idx + 1];
-        acc[c][0] += w * v0.x; acc[c][1] += w * v0.y; acc[c][2] += w * v0.z; acc[c][3] += w * v0.w;
-        acc[c][4] += w * v1.x; acc[c][5] += w * v1.y; acc[c][6] += w * v1.z; acc[c][7] += w * v1.w;
+        const float4* src = reinterpret_cast<const float4*>(y_shared + t * H);
+        sh[c][0] = src[2 * idx];
+        sh[c][1] = src[2 * idx + 1];
+      }
+    }
+  }
+  // pairs in batches of KB: a batch's rows and weights are read first, then
+  // all of its row loads are issued, then summed in slot order (the same sum
+  // as one pair at a time, without a round trip per pair)
+  constexpr int KB = CPT == 1 ? 4 : (CPT == 2 ? 2 : 1);
+  for (int j0 = 0; j0 < k; j0 += KB) {
+    int r[KB];
+    float w[KB];
+#pragma unroll
+    for (int j = 0; j < KB; ++j) {
+      const bool in = j0 + j < k;
+      r[j] = in ? pair_to_row[t * k + j0 + j] : -1;
+      w[j] = in ? topk_w[t * k + j0 + j] : 0.0f;
+    }
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int idx = base + threadIdx.x + c * blockDim.x;
+      if (idx >= nchk) continue;
+      float4 v[KB][2];
+#pragma unroll
+      for (int j = 0; j < KB; ++j)
+        if (r[j] >= 0) {
+          const float4* src = reinterpret_cast<const float4*>(y_rows + (long)r[j] * H);
+          v[j][0] = src[2 * idx];
+          v[j][1] = src[2 * idx + 1];
+        }
+#pragma unroll
+      for (int j = 0; j < KB; ++j) {
+        if (r[j] < 0) continue;
+        const float4 v0 = v[j][0], v1 = v[j][1];
+        const float wj = w[j];
+        acc[c][0] += wj * v0.x; acc[c][1] += wj * v0.y; acc[c][2] += wj * v0.z; acc[c][3] += wj * v0.w;
+        acc[c][4] += wj * v1.x; acc[c][5] += wj * v1.y; acc[c][6] += wj * v1.z; acc[c][7] += wj * v1.w;
       }
     }
   }
@@ -83,8 +119,15 @@ __global__ __launch_bounds__(1024) void combine_kernel(const float* __restrict__
     const int idx = base + threadIdx.x + c * blockDim.x;
     if (idx >= nchk) continue;
     if (y_shared) {
-      const float4* sh = reinterpret_cast<const float4*>(y_shared + t * H);
-      const float4 v0 = sh[2 * idx], v1 = sh[2 * idx + 1];
+      float4 v0, v1;
+      if constexpr (kEarlyShared) {
+        v0 = sh[c][0];
+        v1 = sh[c][1];
+      } else {
+        const float4* src = reinterpret_cast<const float4*>(y_shared + t * H);
+        v0 = src[2 * idx];
+        v1 = src[2 * idx + 1];
+      }
       acc[c][0] += v0.x; acc[c][1] += v0.y; acc[c][2] += v0.z; acc[c][3] += v0.w;
       acc[c][4] += v1.x; acc[c][5] += v1.y; acc[c][6] += v1.z; acc[c][7] += v1.w;
     }

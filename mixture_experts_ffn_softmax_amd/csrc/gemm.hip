@@ -162,7 +162,7 @@ struct TileInfo {
 };
 
 // Locates tile L: group g is the largest with tile_prefix[g] * ntiles <= L.
-__device__ __forceinline__ TileInfo find_tile(const GemmParams& p, const int* s_tp, long L, int bm) {
+__device__ __forceinline__ TileInfo find_tile(const GemmParams& p, const int* s_tp, const int* s_off, long L, int bm) {
   int lo = 0, hi = p.n_groups - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
@@ -174,8 +174,8 @@ __device__ __forceinline__ TileInfo find_tile(const GemmParams& p, const int* s_
   const int mcount = s_tp[lo + 1] - s_tp[lo];
   ti.nt = (int)(local / mcount);
   const int mt = (int)(local - (long)ti.nt * mcount);
-  ti.row1 = p.offsets[lo + 1];
-  ti.row0 = p.offsets[lo] + mt * bm;
+  ti.row1 = s_off[lo + 1];
+  ti.row0 = s_off[lo] + mt * bm;
   ti.wi = (lo < p.n_routed) ? 0 : 1;
   ti.eg = ti.wi ? 0 : lo;
   // the tile is the workgroup's: keep its fields in scalar registers
@@ -206,13 +206,20 @@ __device__ __forceinline__ const uint8_t* row_ptr(const GemmParams& p, const Til
   return reinterpret_cast<const uint8_t*>(p.a[ti.wi]) + a_row<G>(p, ti, r) * p.ta[ti.wi].row_pitch;
 }
 
-// Common prologue: exits surplus workgroups, loads the tile prefix, finds the tile.
+// Common prologue: loads the tile prefix and the group offsets into s_tp
+// (kTileLds ints: the prefix, then the offsets at kOffLds) in one round
+// trip, exits surplus workgroups, finds the tile.
+constexpr int kOffLds = kMaxExperts + 2;
+constexpr int kTileLds = 2 * kOffLds;
 #define MOE_TILE_PROLOGUE(BMROWS)                                                 \
-  const long total_ = (long)p.tile_prefix[p.n_groups] * p.ntiles;               \
-  if ((long)blockIdx.x >= total_) return;                                        \
-  for (int i_ = threadIdx.x; i_ <= p.n_groups; i_ += blockDim.x) s_tp[i_] = p.tile_prefix[i_]; \
+  for (int i_ = threadIdx.x; i_ <= p.n_groups; i_ += blockDim.x) {               \
+    s_tp[i_] = p.tile_prefix[i_];                                                \
+    s_tp[kOffLds + i_] = p.offsets[i_];                                          \
+  }                                                                              \
   __syncthreads();                                                               \
-  const TileInfo ti = find_tile(p, s_tp, xcd_remap(blockIdx.x, total_), BMROWS)
+  const long total_ = (long)s_tp[p.n_groups] * p.ntiles;                         \
+  if ((long)blockIdx.x >= total_) return;                                        \
+  const TileInfo ti = find_tile(p, s_tp, s_tp + kOffLds, xcd_remap(blockIdx.x, total_), BMROWS)
 
 constexpr int kLgCh = 256;    // channel rows per tile
 
@@ -480,9 +487,9 @@ template <int BM, int STAGES, bool SITU>
 __global__ __launch_bounds__(256, 1) void gemm1_pp_kernel(GemmParams p) {
   constexpr int kStage = (BM + kLgCh) * 64;
   constexpr int TF = BM / 64;
-  // the tile-prefix table lives in the ring until the first DMA is issued
+  // the tile-prefix table and offsets live in the ring until the first DMA is issued
   __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * kStage];
-  static_assert(STAGES * kStage >= (kMaxExperts + 2) * 4, "tile prefix fits in the ring");
+  static_assert(STAGES * kStage >= kTileLds * 4, "tile prefix and offsets fit in the ring");
   int* s_tp = reinterpret_cast<int*>(smem);
   MOE_TILE_PROLOGUE(BM);
   __syncthreads();   // every thread has its tile: the ring is free
@@ -722,9 +729,9 @@ template <int BM, int STAGES>
 __global__ __launch_bounds__(256, 1) void gemm2_pp_kernel(GemmParams p) {
   constexpr int kStage = BM * 64 + kLgCh * 32;
   constexpr int TF = BM / 64;
-  // the tile-prefix table lives in the ring until the first DMA is issued
+  // the tile-prefix table and offsets live in the ring until the first DMA is issued
   __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * kStage];
-  static_assert(STAGES * kStage >= (kMaxExperts + 2) * 4, "tile prefix fits in the ring");
+  static_assert(STAGES * kStage >= kTileLds * 4, "tile prefix and offsets fit in the ring");
   int* s_tp = reinterpret_cast<int*>(smem);
   MOE_TILE_PROLOGUE(BM);
   __syncthreads();   // every thread has its tile: the ring is free
@@ -773,20 +780,34 @@ constexpr int kSmCh2 = 128;   // GEMM2 output channels per tile: 8 fragments
 // Steps ks = wave, wave + 4, ... < nk of this wave through D register sets:
 // load(ks, set) fills a set, compute(set) consumes it; the loads of the next
 // D - 1 steps are in flight while a step computes.
-template <int D, class St, class Load, class Compute>
-__device__ __forceinline__ void small_pipeline(int wave, int nk, Load&& load, Compute&& compute) {
+// K steps wave, wave + 4, ... of a small-variant tile, D in flight.  The
+// first D steps' weight loads are issued before `rows` runs (it locates the
+// tile's rows, which may take a dependent load of the gather table) and
+// before their row-operand loads, so the weight stream starts one round
+// trip earlier.
+template <int D, class St, class LoadW, class Rows, class LoadX, class Compute>
+__device__ __forceinline__ void small_pipeline(int wave, int nk, LoadW&& load_w, Rows&& rows, LoadX&& load_x,
+                                               Compute&& compute) {
   const int n = nk > wave ? (nk - wave + 3) >> 2 : 0;
   St st[D];
   static_for<D>([&](auto jc) {
     constexpr int j = decltype(jc)::value;
-    if (j < n) load(wave + 4 * j, st[j]);
+    if (j < n) load_w(wave + 4 * j, st[j]);
+  });
+  rows();
+  static_for<D>([&](auto jc) {
+    constexpr int j = decltype(jc)::value;
+    if (j < n) load_x(wave + 4 * j, st[j]);
   });
   for (int i = 0; i < n; i += D) {
     static_for<D>([&](auto jc) {
       constexpr int j = decltype(jc)::value;
       if (i + j < n) {
         compute(st[j]);
-        if (i + j + D < n) load(wave + 4 * (i + j + D), st[j]);
+        if (i + j + D < n) {
+          load_x(wave + 4 * (i + j + D), st[j]);
+          load_w(wave + 4 * (i + j + D), st[j]);
+        }
       }
     });
   }
@@ -838,12 +859,14 @@ __device__ __forceinline__ void gemm1_small_body(const GemmParams& p, const Tile
   const Operand& td = p.ta[ti.wi];
   const Operand& wd = p.wd[ti.wi];
   const uint8_t* tp[2];
+  auto rows = [&]() {
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    int r = ti.row0 + t * 16 + l16;
-    if (r >= ti.row1) r = ti.row1 - 1;
-    tp[t] = row_ptr<G>(p, ti, r);
-  }
+    for (int t = 0; t < 2; ++t) {
+      int r = ti.row0 + t * 16 + l16;
+      if (r >= ti.row1) r = ti.row1 - 1;
+      tp[t] = row_ptr<G>(p, ti, r);
+    }
+  };
   const uint8_t* wp[4];
   const uint8_t* sp[4];
 #pragma unroll
@@ -876,10 +899,13 @@ __device__ __forceinline__ void gemm1_small_body(const GemmParams& p, const Tile
     int sc[4];
     float bs[2];
   };
-  auto load = [&](int ks, St& st) {
+  auto load_x = [&](int ks, St& st) {
     const long kb = (long)ks << 7;
 #pragma unroll
     for (int t = 0; t < TV; ++t) st.x[t] = as_v8i(tok(t, kb + tok_off0), tok(t, kb + tok_off1));
+  };
+  auto load_w = [&](int ks, St& st) {
+    const long kb = (long)ks << 7;
     if constexpr (blk) {
       st.bs[0] = sb1[ks];
       st.bs[1] = sb3[ks];
@@ -918,7 +944,7 @@ __device__ __forceinline__ void gemm1_small_body(const GemmParams& p, const Tile
         for (int t = 0; t < TV; ++t) acc[f][t] = mfma16_fp8(st.w[f], st.x[t], acc[f][t]);
     }
   };
-  small_pipeline<kSmallDepth1, St>(wave, nk, load, compute);
+  small_pipeline<kSmallDepth1, St>(wave, nk, load_w, rows, load_x, compute);
 
 #pragma unroll
   for (int f = 0; f < 4; ++f)
@@ -962,7 +988,7 @@ __device__ __forceinline__ void gemm1_small_body(const GemmParams& p, const Tile
 template <int FMT, int G, bool NT>
 __global__ __launch_bounds__(256) void gemm1_small_kernel(GemmParams p) {
   __shared__ v4f red[4][8][64];                 // per-wave partial sums
-  __shared__ int s_tp[kMaxExperts + 2];
+  __shared__ int s_tp[kTileLds];
   MOE_TILE_PROLOGUE(kSmRows);
   const bool two = ti.row1 - ti.row0 > 16;
   // the routed group takes FMT; the shared group is always per-channel fp8
@@ -1012,13 +1038,25 @@ __device__ __forceinline__ void gemm2_small_body(const GemmParams& p, const Tile
 
   const Operand& td = p.ta[ti.wi];
   const Operand& wd = p.wd[ti.wi];
-  const uint8_t* tp[2];
+  // wave w's share of the epilogue: channel fragments (NF / 4) w + ff; the
+  // per-channel scales are fetched with the rows
+  float4 es2[NF / 4];
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    int r = ti.row0 + t * 16 + l16;
-    if (r >= ti.row1) r = ti.row1 - 1;
-    tp[t] = row_ptr<kRowsStored>(p, ti, r);
-  }
+  for (int ff = 0; ff < NF / 4; ++ff) es2[ff] = make_float4(1.f, 1.f, 1.f, 1.f);
+  const uint8_t* tp[2];
+  auto rows = [&]() {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      int r = ti.row0 + t * 16 + l16;
+      if (r >= ti.row1) r = ti.row1 - 1;
+      tp[t] = row_ptr<kRowsStored>(p, ti, r);
+    }
+    if (!fp4 && !blk)
+#pragma unroll
+      for (int ff = 0; ff < NF / 4; ++ff)
+        es2[ff] = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(p.sa[ti.wi]) + ti.eg * p.N + n0 +
+                                                   (wave * (NF / 4) + ff) * 16 + 4 * lg);
+  };
   const uint8_t* wp[NF];
   const uint8_t* sp[NF];
 #pragma unroll
@@ -1048,13 +1086,15 @@ __device__ __forceinline__ void gemm2_small_body(const GemmParams& p, const Tile
     uint32_t sc[NF];
     float bs;
   };
-  auto load = [&](int ks, St& st) {
-    if constexpr (blk) st.bs = sb2[ks >> 1];
+  auto load_x = [&](int ks, St& st) {
 #pragma unroll
     for (int t = 0; t < TV; ++t)
 #pragma unroll
       for (int i = 0; i < XS; ++i)   // byte offsets of the bf16 elements of sub-step i
         st.x[t][i] = hpiece(t, (long)ks * (2 * KS) + (fp4 ? lg * 64 + 16 * i : 32 * lg + 16 * i));
+  };
+  auto load_w = [&](int ks, St& st) {
+    if constexpr (blk) st.bs = sb2[ks >> 1];
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
       if constexpr (fp4) {
@@ -1091,7 +1131,7 @@ __device__ __forceinline__ void gemm2_small_body(const GemmParams& p, const Tile
       }
     }
   };
-  small_pipeline<kSmallDepth2, St>(wave, nk, load, compute);
+  small_pipeline<kSmallDepth2, St>(wave, nk, load_w, rows, load_x, compute);
 
 #pragma unroll
   for (int f = 0; f < NF; ++f)
@@ -1104,11 +1144,7 @@ __device__ __forceinline__ void gemm2_small_body(const GemmParams& p, const Tile
   for (int ff = 0; ff < NF / 4; ++ff) {
     const int f = wave * (NF / 4) + ff;
     const int ch = n0 + f * 16 + 4 * lg;
-    float s2v[4] = {1.f, 1.f, 1.f, 1.f};
-    if (!fp4 && !blk) {
-      const float4 s2 = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(p.sa[ti.wi]) + ti.eg * p.N + ch);
-      s2v[0] = s2.x; s2v[1] = s2.y; s2v[2] = s2.z; s2v[3] = s2.w;
-    }
+    const float s2v[4] = {es2[ff].x, es2[ff].y, es2[ff].z, es2[ff].w};
 #pragma unroll
     for (int t = 0; t < TV; ++t) {
       v4f s = red[0][f * 2 + t][lane];
@@ -1125,7 +1161,7 @@ __device__ __forceinline__ void gemm2_small_body(const GemmParams& p, const Tile
 template <int FMT, bool NT>
 __global__ __launch_bounds__(256) void gemm2_small_kernel(GemmParams p) {
   __shared__ v4f red[4][2 * kSmCh2 / 16][64];
-  __shared__ int s_tp[kMaxExperts + 2];
+  __shared__ int s_tp[kTileLds];
   MOE_TILE_PROLOGUE(kSmRows);
   const bool two = ti.row1 - ti.row0 > 16;
   // the routed group takes FMT; the shared group is always per-channel fp8
