@@ -9,6 +9,7 @@
 
 namespace moe {
 
+constexpr int kNumCUs = 256;        // gfx950: 8 XCDs x 32 CUs
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 32;
 constexpr int kPermuteChunk = 1024;  // pairs per counting / ranking chunk

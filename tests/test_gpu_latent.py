@@ -54,6 +54,8 @@ LINEAR_CASES = [  # M, n_out, n_in, fmt, output
     (300, 384, 512, "bf16", "bf16"),
     (130, 128, 256, "bf16", "add"),        # addend before the rounding
     (257, 640, 384, "mxfp4", "add"),
+    (2048, 1024, 320, "mxfp4", "bf16"),    # 128-row tiles; 5 K steps (not a multiple of the pipeline depth)
+    (1100, 2048, 448, "bf16", "add"),      # 128-row tiles, ragged last tile, 7 K steps
 ]
 
 
@@ -143,6 +145,9 @@ BLOCK_CASES = {
     "sigmoid_situ_shared": (70, 256, 256, 128, 16, 4, 128, "sigmoid", "situ"),
     "one_token": (1, 256, 128, 128, 8, 2, 128, "softmax", "silu"),
     "ragged_rows": (131, 512, 256, 128, 8, 2, 384, "softmax", "silu"),
+    # enough rows and channels for 128-row tiles in the up-projection and both
+    # shared GEMMs (64-row tiles in the down-projection)
+    "wide_shared": (1100, 2048, 128, 128, 8, 2, 2048, "softmax", "silu"),
 }
 
 
