@@ -99,25 +99,83 @@ _E2M1_MIDS_DOWN = (0.25, 1.25, 2.5, 5.0)   # a tie here goes to the lower (even)
 _E2M1_MIDS_UP = (0.75, 1.75, 3.5)          # a tie here goes to the upper (even) code
 
 
-def mxfp4_rows(w, group=32):
-    """float32 [N][K] -> (packed uint8 [N][K/2], e8m0 uint8 [N][K/group])."""
-    N, K = w.shape
-    wb = w.reshape(N, K // group, group)
-    amax = wb.abs().amax(dim=2)
+def _mxfp4_codes(w, group=32):
+    """float32 [..., K] -> (e2m1 codes int32 [..., K], e8m0 biased exponents
+    int32 [..., K/group]): scale 2^(floor(log2 amax) - 2) per block, codes by
+    round to nearest, ties to even."""
+    wb = w.reshape(*w.shape[:-1], w.shape[-1] // group, group)
+    amax = wb.abs().amax(dim=-1)
     e = torch.floor(torch.log2(torch.where(amax > 0, amax, torch.ones_like(amax)))) - 2
     e = torch.where(amax > 0, e, torch.full_like(e, -127.0)).clamp(-127, 127)
     v = wb / torch.pow(2.0, e)[..., None]
     mag = v.abs().clamp(max=6.0)
-    code = torch.zeros_like(mag, dtype=torch.uint8)
+    code = torch.zeros(mag.shape, dtype=torch.int32, device=w.device)
     for m in _E2M1_MIDS_DOWN:
-        code += (mag > m).to(torch.uint8)
+        code += (mag > m).int()
     for m in _E2M1_MIDS_UP:
-        code += (mag >= m).to(torch.uint8)
-    code = code | ((v < 0) & (code > 0)).to(torch.uint8) << 3
-    code = code.reshape(N, K)
+        code += (mag >= m).int()
+    code = code | (((v < 0) & (code > 0)).int() << 3)
+    return code.reshape(w.shape), (e + 127).int()
+
+
+def _words(vals, bits):
+    """int32 [..., n] of `bits`-bit fields (n * bits a multiple of 32) ->
+    int32 words [..., n * bits / 32], field i of a word at bit i * bits, so
+    that the words viewed as bytes list the fields in order (little endian)."""
+    per = 32 // bits
+    v = vals.reshape(*vals.shape[:-1], -1, per).long()
+    w = (v << (torch.arange(per, device=vals.device, dtype=torch.int64) * bits)).sum(dim=-1)
+    return torch.where(w >= 2 ** 31, w - 2 ** 32, w).int()
+
+
+def _mxfp4_words(w, group=32):
+    """float32 [..., K], K % 128 == 0 -> (codes as int32 words [..., K/8],
+    e8m0 scales as int32 words [..., K/128]); viewed as bytes they are the
+    packed codes [..., K/2] (element 2i in the low nibble of byte i) and the
+    scales [..., K/32].  Built from whole 32-bit words: no byte-wise device
+    kernels (a byte-wise conversion or copy per tensor, for every expert,
+    was most of the generator's launches)."""
+    code, e = _mxfp4_codes(w, group)
+    return _words(code, 4), _words(e, 8)
+
+
+def _mxfp4_rows_bytes(w, group=32):
+    """The same encoding built byte by byte (any K % group == 0)."""
+    N, K = w.shape
+    code, e = _mxfp4_codes(w, group)
+    code = code.to(torch.uint8)
     packed = (code[:, 0::2] | (code[:, 1::2] << 4)).contiguous()
-    scale = (e + 127).to(torch.uint8).contiguous()
-    return packed, scale
+    return packed, e.to(torch.uint8).contiguous()
+
+
+def mxfp4_rows(w, group=32):
+    """float32 [N][K] -> (packed uint8 [N][K/2], e8m0 uint8 [N][K/group])."""
+    if w.shape[1] % 128 == 0 and group == 32:
+        cw, sw = _mxfp4_words(w, group)
+        return cw.view(torch.uint8), sw.view(torch.uint8)
+    return _mxfp4_rows_bytes(w, group)
+
+
+# experts quantised together by expert_weights (MXFP4): bounds the float32
+# temporaries to a few GB at the LatentMoE shape
+_MX_CHUNK = 16
+
+
+def _mxfp4_experts(cfg, device, tid, n_experts, shape):
+    """MXFP4 weights of n_experts experts of `shape` [N][K] (K % 128 == 0):
+    each expert drawn from its own generator, quantised a chunk of experts at
+    a time, stacked as int32 words and viewed as bytes at the end."""
+    N, K = shape
+    codes = torch.empty((n_experts, N, K // 8), dtype=torch.int32, device=device)
+    scales = torch.empty((n_experts, N, K // 128), dtype=torch.int32, device=device)
+    buf = torch.empty((min(_MX_CHUNK, max(n_experts, 1)), N, K), dtype=torch.float32, device=device)
+    for e0 in range(0, n_experts, _MX_CHUNK):
+        c = min(_MX_CHUNK, n_experts - e0)
+        for i in range(c):
+            torch.randn(shape, generator=_gen(device, seed_of(cfg, tid, e0 + i)), device=device, out=buf[i])
+        w = buf[:c] * WEIGHT_STD
+        codes[e0:e0 + c], scales[e0:e0 + c] = _mxfp4_words(w)
+    return codes.view(torch.uint8), scales.view(torch.uint8)
 
 
 def expert_weights(cfg, device, fmt, n_experts, hidden, inter, tensors=(T_W1, T_W3, T_W2)):
@@ -125,6 +183,9 @@ def expert_weights(cfg, device, fmt, n_experts, hidden, inter, tensors=(T_W1, T_
     out = {}
     shapes = {tensors[0]: (inter, hidden), tensors[1]: (inter, hidden), tensors[2]: (hidden, inter)}
     for name, tid in zip(("1", "3", "2"), tensors):
+        if fmt == "mxfp4" and shapes[tid][1] % 128 == 0:
+            out["w" + name], out["s" + name] = _mxfp4_experts(cfg, device, tid, n_experts, shapes[tid])
+            continue
         codes, scales = [], []
         for e in range(n_experts):
             w = randn(shapes[tid], device, seed_of(cfg, tid, e), WEIGHT_STD)
