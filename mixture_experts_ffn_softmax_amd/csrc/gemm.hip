@@ -774,8 +774,15 @@ __global__ __launch_bounds__(256, 1) void gemm2_pp_kernel(GemmParams p) {
 // most 16 valid rows skips its second token fragment (loads and MFMAs).
 
 constexpr int kSmRows = 32;   // token rows per tile: 2 fragments of 16
+constexpr int kMdRows = 64;   // the medium variant's: 4 fragments of 16
 constexpr int kSmCh = 64;     // GEMM1 channel rows per tile: 4 fragments (2 gate + 2 up)
 constexpr int kSmCh2 = 128;   // GEMM2 output channels per tile: 8 fragments
+constexpr int kMdCh2 = 64;    // the medium variant's: 4 fragments
+// per-block fp8 groups averaging at least this many rows take the medium
+// variant: 64-row tiles halve the weight fragments loaded per flop (on the
+// 2048-token prefill share the gate-up GEMM runs 508 us instead of 575; the
+// down GEMM is unchanged)
+constexpr long kMdMinAvgRows = 48;
 
 // Steps ks = wave, wave + 4, ... < nk of this wave through D register sets:
 // load(ks, set) fills a set, compute(set) consumes it; the loads of the next
@@ -815,8 +822,10 @@ __device__ __forceinline__ void small_pipeline(int wave, int nk, LoadW&& load_w,
 
 // GEMM1: 16x16x128 MFMA on e4m3 x e4m3, or e2m1 x e4m3 with block scales.
 // NT: weights loaded non-temporally (see load_w16).
-template <int WF, int TV, int G, bool NT>
-__device__ __forceinline__ void gemm1_small_body(const GemmParams& p, const TileInfo& ti, v4f (*red)[8][64]) {
+// TVM: token fragments of the kernel's row tile (2 or 4); TV <= TVM of them
+// hold rows of this tile.
+template <int WF, int TV, int G, bool NT, int TVM>
+__device__ __forceinline__ void gemm1_small_body(const GemmParams& p, const TileInfo& ti, v4f (*red)[4 * TVM][64]) {
   constexpr int kSmallDepth1 = 2;
   const int K = p.K;
   const int nk = K >> 7;
@@ -858,10 +867,10 @@ __device__ __forceinline__ void gemm1_small_body(const GemmParams& p, const Tile
   // is addressed through its operand's layout
   const Operand& td = p.ta[ti.wi];
   const Operand& wd = p.wd[ti.wi];
-  const uint8_t* tp[2];
+  const uint8_t* tp[TV];
   auto rows = [&]() {
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int t = 0; t < TV; ++t) {
       int r = ti.row0 + t * 16 + l16;
       if (r >= ti.row1) r = ti.row1 - 1;
       tp[t] = row_ptr<G>(p, ti, r);
@@ -949,24 +958,15 @@ __device__ __forceinline__ void gemm1_small_body(const GemmParams& p, const Tile
 #pragma unroll
   for (int f = 0; f < 4; ++f)
 #pragma unroll
-    for (int t = 0; t < TV; ++t) red[wave][f * 2 + t][lane] = acc[f][t];
+    for (int t = 0; t < TV; ++t) red[wave][f * TVM + t][lane] = acc[f][t];
   __syncthreads();
 
-  // wave w: gate fragment f = w >> 1 (up fragment f + 2), token fragment t = w & 1
-  const int f = wave >> 1, t = wave & 1;
-  if (t >= TV) return;
-  v4f gsum = red[0][f * 2 + t][lane], usum = red[0][(f + 2) * 2 + t][lane];
-#pragma unroll
-  for (int q = 1; q < 4; ++q) {
-    gsum += red[q][f * 2 + t][lane];
-    usum += red[q][(f + 2) * 2 + t][lane];
-  }
-  const int grow = ti.row0 + t * 16 + l16;
-  if (grow >= ti.row1) return;
-  const float xs = p.a_scale[ti.wi][a_row<G>(p, ti, grow)];
+  // wave w: gate fragment f = w >> 1 (up fragment f + 2), token fragments
+  // t = (w & 1) + 2j
+  const int f = wave >> 1;
   const int ch = n0 + f * 16 + 4 * lg;
   float sg[4] = {1.f, 1.f, 1.f, 1.f}, su[4] = {1.f, 1.f, 1.f, 1.f};
-  if (!fp4 && !blk) {   // per-channel e4m3 weights carry one scale per channel
+  if (!fp4 && !blk && (wave & 1) < TV) {   // per-channel e4m3 weights carry one scale per channel
     const float4 s1 = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(p.sa[ti.wi]) + ti.eg * p.N + ch);
     const float4 s3 = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(p.sb[ti.wi]) + ti.eg * p.N + ch);
     sg[0] = s1.x; sg[1] = s1.y; sg[2] = s1.z; sg[3] = s1.w;
@@ -974,31 +974,49 @@ __device__ __forceinline__ void gemm1_small_body(const GemmParams& p, const Tile
   }
   const bool use_situ = p.act[ti.wi] == kActSitu;
   const float beta = p.beta[ti.wi];
-  uint32_t b[4];
 #pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const float g = gsum[v] * xs * sg[v];
-    const float u = usum[v] * xs * su[v];
-    b[v] = bf16_rne((use_situ ? situ(g, beta) : silu(g)) * u);
+  for (int t = wave & 1; t < TV; t += 2) {
+    v4f gsum = red[0][f * TVM + t][lane], usum = red[0][(f + 2) * TVM + t][lane];
+#pragma unroll
+    for (int q = 1; q < 4; ++q) {
+      gsum += red[q][f * TVM + t][lane];
+      usum += red[q][(f + 2) * TVM + t][lane];
+    }
+    const int grow = ti.row0 + t * 16 + l16;
+    if (grow >= ti.row1) continue;
+    const float xs = p.a_scale[ti.wi][a_row<G>(p, ti, grow)];
+    uint32_t b[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const float g = gsum[v] * xs * sg[v];
+      const float u = usum[v] * xs * su[v];
+      b[v] = bf16_rne((use_situ ? situ(g, beta) : silu(g)) * u);
+    }
+    *reinterpret_cast<uint2*>(p.h + h_off(p.h_cs, grow, ch)) = make_uint2(b[0] | (b[1] << 16), b[2] | (b[3] << 16));
   }
-  *reinterpret_cast<uint2*>(p.h + h_off(p.h_cs, grow, ch)) = make_uint2(b[0] | (b[1] << 16), b[2] | (b[3] << 16));
 }
 
 // G: where the routed rows come from (RowSource: stored, or gathered)
-template <int FMT, int G, bool NT>
+// ROWS: rows per tile, 32 (small variant) or 64 (medium variant: twice the
+// rows per weight byte, for batches where many row tiles re-read each
+// expert's weights).
+template <int FMT, int G, bool NT, int ROWS = kSmRows>
 __global__ __launch_bounds__(256) void gemm1_small_kernel(GemmParams p) {
-  __shared__ v4f red[4][8][64];                 // per-wave partial sums
+  constexpr int TVM = ROWS / 16;
+  __shared__ v4f red[4][4 * TVM][64];           // per-wave partial sums
   __shared__ int s_tp[kTileLds];
-  MOE_TILE_PROLOGUE(kSmRows);
-  const bool two = ti.row1 - ti.row0 > 16;
+  MOE_TILE_PROLOGUE(ROWS);
+  const int vr = ti.row1 - ti.row0;
   // the routed group takes FMT; the shared group is always per-channel fp8
-  if (FMT != kFp8 && ti.wi == 0) {
-    if (two) gemm1_small_body<FMT, 2, G, NT>(p, ti, red);
-    else gemm1_small_body<FMT, 1, G, NT>(p, ti, red);
-  } else {
-    if (two) gemm1_small_body<kFp8, 2, G, NT>(p, ti, red);
-    else gemm1_small_body<kFp8, 1, G, NT>(p, ti, red);
-  }
+  auto run = [&](auto fc) {
+    constexpr int F = decltype(fc)::value;
+    if (TVM > 2 && vr > 48) gemm1_small_body<F, TVM, G, NT, TVM>(p, ti, red);
+    else if (TVM > 2 && vr > 32) gemm1_small_body<F, (TVM > 2 ? 3 : 2), G, NT, TVM>(p, ti, red);
+    else if (vr > 16) gemm1_small_body<F, 2, G, NT, TVM>(p, ti, red);
+    else gemm1_small_body<F, 1, G, NT, TVM>(p, ti, red);
+  };
+  if (FMT != kFp8 && ti.wi == 0) run(std::integral_constant<int, FMT>{});
+  else run(std::integral_constant<int, kFp8>{});
 }
 
 // GEMM2: 16x16x32 bf16 MFMA; W2 codes converted to bf16 in registers.  Lane
@@ -1012,8 +1030,10 @@ __global__ __launch_bounds__(256) void gemm1_small_kernel(GemmParams p) {
 // A tile is kSmCh2 = 128 output channels (8 fragments): with K = I the
 // shortest contraction of the layer, wider tiles keep the launch to about
 // one workgroup per two SIMD pairs.
-template <int WF, int TV, bool NT>
-__device__ __forceinline__ void gemm2_small_body(const GemmParams& p, const TileInfo& ti, v4f (*red)[2 * kSmCh2 / 16][64]) {
+// CH: output channels of the kernel's tile (kSmCh2 or kMdCh2); TVM, TV as
+// in the gate-up body.
+template <int WF, int TV, bool NT, int TVM, int CH>
+__device__ __forceinline__ void gemm2_small_body(const GemmParams& p, const TileInfo& ti, v4f (*red)[TVM * CH / 16][64]) {
   constexpr bool fp4 = WF == kMxfp4;
   constexpr bool blk = WF == kFp8Block;
   // K elements per step: e4m3 steps of 64 (16 code bytes per lane and
@@ -1022,13 +1042,13 @@ __device__ __forceinline__ void gemm2_small_body(const GemmParams& p, const Tile
   constexpr int KS = fp4 ? 128 : 64;
   constexpr int XS = KS / 32;                 // 16-byte h pieces per token fragment and step
   constexpr int kSmallDepth2 = fp4 ? 1 : 2;
-  constexpr int NF = kSmCh2 / 16;             // channel fragments
+  constexpr int NF = CH / 16;                 // channel fragments
   const int K = p.K;                          // = I
   const int nk = K / KS;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l16 = lane & 15, lg = lane >> 4;
   const long rowBytes = fp4 ? (K >> 1) : K;
-  const int n0 = ti.nt * kSmCh2;
+  const int n0 = ti.nt * CH;
   const uint8_t* W2 = p.wa[ti.wi] + ti.eg * (long)p.N * rowBytes;
   // per-block fp8: the 128 channels of the tile form one channel block; the
   // scale of the K block of step ks (two 64-wide steps per block) is sb2[ks / 2]
@@ -1043,10 +1063,10 @@ __device__ __forceinline__ void gemm2_small_body(const GemmParams& p, const Tile
   float4 es2[NF / 4];
 #pragma unroll
   for (int ff = 0; ff < NF / 4; ++ff) es2[ff] = make_float4(1.f, 1.f, 1.f, 1.f);
-  const uint8_t* tp[2];
+  const uint8_t* tp[TV];
   auto rows = [&]() {
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int t = 0; t < TV; ++t) {
       int r = ti.row0 + t * 16 + l16;
       if (r >= ti.row1) r = ti.row1 - 1;
       tp[t] = row_ptr<kRowsStored>(p, ti, r);
@@ -1136,7 +1156,7 @@ __device__ __forceinline__ void gemm2_small_body(const GemmParams& p, const Tile
 #pragma unroll
   for (int f = 0; f < NF; ++f)
 #pragma unroll
-    for (int t = 0; t < TV; ++t) red[wave][f * 2 + t][lane] = acc[f][t];
+    for (int t = 0; t < TV; ++t) red[wave][f * TVM + t][lane] = acc[f][t];
   __syncthreads();
 
   // wave w: channel fragments 2w and 2w + 1, every valid token fragment
@@ -1147,9 +1167,9 @@ __device__ __forceinline__ void gemm2_small_body(const GemmParams& p, const Tile
     const float s2v[4] = {es2[ff].x, es2[ff].y, es2[ff].z, es2[ff].w};
 #pragma unroll
     for (int t = 0; t < TV; ++t) {
-      v4f s = red[0][f * 2 + t][lane];
+      v4f s = red[0][f * TVM + t][lane];
 #pragma unroll
-      for (int q = 1; q < 4; ++q) s += red[q][f * 2 + t][lane];
+      for (int q = 1; q < 4; ++q) s += red[q][f * TVM + t][lane];
       const int grow = ti.row0 + t * 16 + l16;
       if (grow < ti.row1)
         *reinterpret_cast<float4*>(p.y + (long)grow * p.N + ch) =
@@ -1158,20 +1178,25 @@ __device__ __forceinline__ void gemm2_small_body(const GemmParams& p, const Tile
   }
 }
 
-template <int FMT, bool NT>
+// ROWS, CH: rows and output channels per tile: 32 x 128 (small variant) or
+// 64 x 64 (medium variant).
+template <int FMT, bool NT, int ROWS = kSmRows, int CH = kSmCh2>
 __global__ __launch_bounds__(256) void gemm2_small_kernel(GemmParams p) {
-  __shared__ v4f red[4][2 * kSmCh2 / 16][64];
+  constexpr int TVM = ROWS / 16;
+  __shared__ v4f red[4][TVM * CH / 16][64];
   __shared__ int s_tp[kTileLds];
-  MOE_TILE_PROLOGUE(kSmRows);
-  const bool two = ti.row1 - ti.row0 > 16;
+  MOE_TILE_PROLOGUE(ROWS);
+  const int vr = ti.row1 - ti.row0;
   // the routed group takes FMT; the shared group is always per-channel fp8
-  if (FMT != kFp8 && ti.wi == 0) {
-    if (two) gemm2_small_body<FMT, 2, NT>(p, ti, red);
-    else gemm2_small_body<FMT, 1, NT>(p, ti, red);
-  } else {
-    if (two) gemm2_small_body<kFp8, 2, NT>(p, ti, red);
-    else gemm2_small_body<kFp8, 1, NT>(p, ti, red);
-  }
+  auto run = [&](auto fc) {
+    constexpr int F = decltype(fc)::value;
+    if (TVM > 2 && vr > 48) gemm2_small_body<F, TVM, NT, TVM, CH>(p, ti, red);
+    else if (TVM > 2 && vr > 32) gemm2_small_body<F, (TVM > 2 ? 3 : 2), NT, TVM, CH>(p, ti, red);
+    else if (vr > 16) gemm2_small_body<F, 2, NT, TVM, CH>(p, ti, red);
+    else gemm2_small_body<F, 1, NT, TVM, CH>(p, ti, red);
+  };
+  if (FMT != kFp8 && ti.wi == 0) run(std::integral_constant<int, FMT>{});
+  else run(std::integral_constant<int, kFp8>{});
 }
 
 // ============================================================================
@@ -1259,7 +1284,8 @@ long max_row_tiles(long n_rows, int n_groups, int bm) { return (n_rows + bm - 1)
 int choose_variant(const FfnGroups& g, long n_rows) {
   const bool large_ok = g.fmt == kFp8 && (g.hidden % kLgCh) == 0 && (g.inter % (kLgCh / 2)) == 0;
   const long avg = n_rows / (g.n_groups > 0 ? g.n_groups : 1);
-  if (!large_ok || avg < 64) return kVariantSmall;
+  if (!large_ok) return g.fmt == kFp8Block && avg >= kMdMinAvgRows ? kVariantMedium : kVariantSmall;
+  if (avg < 64) return kVariantSmall;
   return avg >= 384 ? kVariantLarge256 : kVariantLarge128;
 }
 
@@ -1268,11 +1294,14 @@ bool small_streams_weights(const FfnGroups& g, long n_rows) {
 }
 
 int variant_rows(int variant) {
-  return variant == kVariantLarge256 ? 256 : variant == kVariantLarge128 ? 128 : kSmRows;
+  return variant == kVariantLarge256 ? 256 : variant == kVariantLarge128 ? 128 : variant == kVariantMedium ? kMdRows : kSmRows;
 }
 
 const char* variant_name(int variant) {
-  return variant == kVariantLarge256 ? "large256" : variant == kVariantLarge128 ? "large128" : "small32";
+  return variant == kVariantLarge256 ? "large256"
+         : variant == kVariantLarge128 ? "large128"
+         : variant == kVariantMedium   ? "medium64"
+                                       : "small32";
 }
 
 hipError_t launch_tile_prefix(const int* offsets, int n_groups, int bm, int* tile_prefix, hipStream_t s) {
@@ -1318,19 +1347,23 @@ hipError_t launch_gemm1(int variant, const FfnGroups& g, const RowOperand& x, co
   p.h = h;
   p.h_cs = n_rows * kHChunk;
   const int bm = variant_rows(variant);
-  if (variant == kVariantSmall) {
+  if (variant_in_registers(variant)) {
     p.ntiles = g.inter / (kSmCh / 2);
     const long grid = max_row_tiles(n_rows, g.n_groups, bm) * p.ntiles;
-    auto pick = [&](auto nt) {
+    auto pick = [&](auto nt, auto rows) {
       constexpr bool NT = decltype(nt)::value;
-      return x.gather ? (g.fmt == kMxfp4      ? gemm1_small_kernel<kMxfp4, kRowsGathered, NT>
-                         : g.fmt == kFp8Block ? gemm1_small_kernel<kFp8Block, kRowsGathered, NT>
-                                              : gemm1_small_kernel<kFp8, kRowsGathered, NT>)
-                      : (g.fmt == kMxfp4      ? gemm1_small_kernel<kMxfp4, kRowsStored, NT>
-                         : g.fmt == kFp8Block ? gemm1_small_kernel<kFp8Block, kRowsStored, NT>
-                                              : gemm1_small_kernel<kFp8, kRowsStored, NT>);
+      constexpr int R = decltype(rows)::value;
+      return x.gather ? (g.fmt == kMxfp4      ? gemm1_small_kernel<kMxfp4, kRowsGathered, NT, R>
+                         : g.fmt == kFp8Block ? gemm1_small_kernel<kFp8Block, kRowsGathered, NT, R>
+                                              : gemm1_small_kernel<kFp8, kRowsGathered, NT, R>)
+                      : (g.fmt == kMxfp4      ? gemm1_small_kernel<kMxfp4, kRowsStored, NT, R>
+                         : g.fmt == kFp8Block ? gemm1_small_kernel<kFp8Block, kRowsStored, NT, R>
+                                              : gemm1_small_kernel<kFp8, kRowsStored, NT, R>);
     };
-    auto kern = small_streams_weights(g, n_rows) ? pick(std::true_type{}) : pick(std::false_type{});
+    using Sm = std::integral_constant<int, kSmRows>;
+    using Md = std::integral_constant<int, kMdRows>;
+    auto kern = variant == kVariantMedium ? pick(std::false_type{}, Md{})
+                : small_streams_weights(g, n_rows) ? pick(std::true_type{}, Sm{}) : pick(std::false_type{}, Sm{});
     hipExtLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, s, ev_start, ev_stop, 0, p);
   } else {
     p.ntiles = g.inter / (kLgCh / 2);
@@ -1361,15 +1394,24 @@ hipError_t launch_gemm2(int variant, const FfnGroups& g, const uint16_t* h, cons
   }
   p.y = y;
   const int bm = variant_rows(variant);
-  if (variant == kVariantSmall) {
-    p.ntiles = g.hidden / kSmCh2;
+  if (variant_in_registers(variant)) {
+    const bool md = variant == kVariantMedium;
+    p.ntiles = g.hidden / (md ? kMdCh2 : kSmCh2);
     const long grid = max_row_tiles(n_rows, g.n_groups, bm) * p.ntiles;
-    auto pick = [&](auto nt) {
+    auto pick = [&](auto nt, auto rows, auto ch) {
       constexpr bool NT = decltype(nt)::value;
-      return g.fmt == kMxfp4 ? gemm2_small_kernel<kMxfp4, NT>
-                             : g.fmt == kFp8Block ? gemm2_small_kernel<kFp8Block, NT> : gemm2_small_kernel<kFp8, NT>;
+      constexpr int R = decltype(rows)::value, C = decltype(ch)::value;
+      return g.fmt == kMxfp4      ? gemm2_small_kernel<kMxfp4, NT, R, C>
+             : g.fmt == kFp8Block ? gemm2_small_kernel<kFp8Block, NT, R, C>
+                                  : gemm2_small_kernel<kFp8, NT, R, C>;
     };
-    auto kern = small_streams_weights(g, n_rows) ? pick(std::true_type{}) : pick(std::false_type{});
+    using Sm = std::integral_constant<int, kSmRows>;
+    using Md = std::integral_constant<int, kMdRows>;
+    using SmC = std::integral_constant<int, kSmCh2>;
+    using MdC = std::integral_constant<int, kMdCh2>;
+    auto kern = md ? pick(std::false_type{}, Md{}, MdC{})
+                : small_streams_weights(g, n_rows) ? pick(std::true_type{}, Sm{}, SmC{})
+                                                   : pick(std::false_type{}, Sm{}, SmC{});
     hipExtLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, s, ev_start, ev_stop, 0, p);
   } else {
     p.ntiles = g.hidden / kLgCh;

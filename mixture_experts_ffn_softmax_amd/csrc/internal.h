@@ -145,7 +145,13 @@ struct RowOperand {
   int gather_k = 1;
 };
 
-enum GemmVariant { kVariantSmall = 0, kVariantLarge128 = 1, kVariantLarge256 = 2 };
+// small: 32-row tiles, operands straight into registers (weight streaming);
+// medium: the same kernels with 64-row tiles, for per-block fp8 batches with
+// many rows per group (the large kernels take per-channel fp8 only);
+// large: 128- or 256-row tiles staged through an LDS ring (per-channel fp8).
+enum GemmVariant { kVariantSmall = 0, kVariantLarge128 = 1, kVariantLarge256 = 2, kVariantMedium = 3 };
+// The variants whose kernels read their row fragments straight into registers.
+inline bool variant_in_registers(int v) { return v == kVariantSmall || v == kVariantMedium; }
 
 int choose_variant(const FfnGroups& g, long n_rows);
 // The small variant streams its weights with non-temporal loads when the

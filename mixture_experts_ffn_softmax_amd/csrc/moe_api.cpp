@@ -363,7 +363,7 @@ static bool fused_route_path(int32_t T, int32_t k, const moe_weights_t* routed, 
   if (T <= kGatherSmallMaxT) return true;
   // only the format, the shape and the group count decide the variant
   const moe::FfnGroups g = make_groups(routed, shared ? routed : nullptr, nullptr);
-  return moe::choose_variant(g, (long)T * k + (shared ? T : 0)) != moe::kVariantSmall;
+  return !moe::variant_in_registers(moe::choose_variant(g, (long)T * k + (shared ? T : 0)));
 }
 // On the one-launch routing path the large kernels read expert-ordered rows
 // that a copy kernel writes from the token-order rows: their direct-to-LDS
@@ -374,7 +374,7 @@ static bool fused_route_path(int32_t T, int32_t k, const moe_weights_t* routed, 
 static bool fused_rows_copied(int32_t T, int32_t k, const moe_weights_t* routed, bool shared) {
   if (!fused_route_path(T, k, routed, shared)) return false;
   const moe::FfnGroups g = make_groups(routed, shared ? routed : nullptr, nullptr);
-  return moe::choose_variant(g, (long)T * k + (shared ? T : 0)) != moe::kVariantSmall;
+  return !moe::variant_in_registers(moe::choose_variant(g, (long)T * k + (shared ? T : 0)));
 }
 
 static ForwardLayout forward_layout(void* ws, int32_t T, int32_t k, const moe_weights_t* routed, bool shared) {

@@ -410,6 +410,36 @@ def test_forward_block_fp8_decode_full_size(lib):
     assert ratio <= OUT_TOL
 
 
+def test_forward_block_fp8_prefill_full_size(lib):
+    """The prefill share (2048 tokens, H 8192, I 2048, 8 experts top-2, a
+    per-channel fp8 shared expert) with per-block fp8 routed weights, which
+    takes the 64-row medium variant: all routing metadata, and the outputs of
+    tokens that reach every expert, the first and last rows of the hottest
+    expert's last (ragged) 64-row tile, the least-loaded expert's last row and
+    the last routed row."""
+    from gpu_helpers import cover_tokens
+    inp = moe_synth.custom_inputs(2048, 8192, 2048, 8, 2, fmt="fp8_block", seed=13, device=DEV, shared=True)
+    c = inp["cfg"]
+    T, E, k = c["T"], c["E"], c["k"]
+    say("forward block fp8 prefill full size", c)
+    out, dbg, variant = run_forward(inp)
+    say("  variant", variant)
+    assert "medium64" in variant
+    ids, w = oracle.route(host(inp["logits"]), k)
+    counts, offsets = oracle.expert_counts_offsets(ids, E)
+    p2r, r2p, _, _ = oracle.permute_rows(ids, offsets, np.zeros((T, 1), np.uint8), np.zeros(T, np.float32))
+    check_metadata(dbg, dict(topk_ids=ids, topk_w=w, counts=counts, offsets=offsets, pair_to_row=p2r,
+                             row_to_pair=r2p), T, k, E, shared=True)
+    edge, _ = edge_tokens(counts, offsets, r2p, k, 64)
+    tokens = np.array(sorted(set(cover_tokens(ids, E, must=edge)) | {0, T - 1}))
+    ref_out = oracle.moe.forward_sampled(bits(inp["x"]), None, k, oracle_weights(inp["routed"], "fp8_block", lazy=True),
+                                         tokens, shared=oracle_weights(inp["shared"], "fp8", lazy=True),
+                                         routing=(ids, w))
+    ratio = tolerance_ratio(bits(out[torch.as_tensor(tokens, device=DEV)]), ref_out)
+    say("  max|err|/rms", ratio, "over", len(tokens), "tokens")
+    assert ratio <= OUT_TOL
+
+
 # ----------------------------------------------------------------------------
 # moe_expert_ffn and moe_combine on their own
 # ----------------------------------------------------------------------------
