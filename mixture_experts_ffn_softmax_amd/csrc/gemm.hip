@@ -540,13 +540,38 @@ __device__ __forceinline__ BfPair fp8x16_to_bf16(const uint4& w) {
                 v8bf{e[0], e[1], g[0], g[1], h[0], h[1], k[0], k[1]}};
 }
 
+// The same 16 codes times a per-block scale s, each product rounded once to
+// bf16 (the code widened exactly to binary32, multiplied in binary32, then
+// rounded to nearest even).
+__device__ __forceinline__ BfPair fp8x16_to_bf16_scaled(const uint4& w, float s) {
+  const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+  __bf16 o[16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const v2f lo = __builtin_amdgcn_cvt_pk_f32_fp8(wd[i], false);
+    const v2f hi = __builtin_amdgcn_cvt_pk_f32_fp8(wd[i], true);
+    o[4 * i] = (__bf16)(lo[0] * s);
+    o[4 * i + 1] = (__bf16)(lo[1] * s);
+    o[4 * i + 2] = (__bf16)(hi[0] * s);
+    o[4 * i + 3] = (__bf16)(hi[1] * s);
+  }
+  return BfPair{v8bf{o[0], o[1], o[2], o[3], o[4], o[5], o[6], o[7]},
+                v8bf{o[8], o[9], o[10], o[11], o[12], o[13], o[14], o[15]}};
+}
+
 // GEMM2: K step of 32 elements.  LDS stage: BM h rows of 32 bf16 (64 bytes,
 // swz64) then 256 W2 rows of 32 codes (32 bytes, swz32).  Wave (wm, wn) owns
 // the interleaved token fragments of wave row wm and output channels
 // [wn * 128, +128).  W2 fragments are widened to bf16 one step ahead: the
 // conversions of step k+1 run between the MFMAs of step k, which do not
 // depend on them, so the vector unit works while the matrix core does.
-template <int BM, int STAGES, int TV>
+// BLK: per-block fp8 W2 (the routed group of the per-block format).  A
+// wave's 128 channels are one channel block, so the scale of a K block (four
+// steps) is one number per wave; it is applied to the codes as they are
+// widened (each product rounded once to bf16, a relative error of at most
+// 2^-9 per weight, the size of h's own rounding) rather than to partial sums,
+// for which a 128 x 128 wave tile has no registers left.
+template <int BM, int STAGES, int TV, bool BLK>
 __device__ __forceinline__ void gemm2_pp_body(const GemmParams& p, const TileInfo& ti, uint8_t* smem) {
   constexpr int kTokBytes = BM * 64;
   constexpr int kStage = kTokBytes + kLgCh * 32;
@@ -565,6 +590,24 @@ __device__ __forceinline__ void gemm2_pp_body(const GemmParams& p, const TileInf
   const uint8_t* W2 = p.wa[ti.wi] + ti.eg * (long)p.N * K;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // per-block scales of this wave's channel block, one per K block (at most
+  // 128): lane l holds those of K blocks l and l + 64, loaded before any
+  // direct-to-LDS load is issued and waited for at once, so that no later
+  // wait for them drains the ring's loads; a step takes its scale with a
+  // lane read
+  const int nkb = K >> 7;
+  float sv0 = 1.0f, sv1 = 1.0f;
+  if constexpr (BLK) {
+    const float* sbw =
+        reinterpret_cast<const float*>(p.sa[ti.wi]) + (ti.eg * (long)(p.N >> 7) + (n0 >> 7) + (wave & 1)) * nkb;
+    if (lane < nkb) sv0 = sbw[lane];
+    if (lane + 64 < nkb) sv1 = sbw[lane + 64];
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+  }
+  auto scale_of = [&](int kb) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(kb < 64 ? sv0 : sv1), kb & 63));
+  };
+  auto widen = [&](const uint4& raw, float sc) { return BLK ? fp8x16_to_bf16_scaled(raw, sc) : fp8x16_to_bf16(raw); };
 
   const uint8_t* src[kPer];
   const Operand& wd = p.wd[ti.wi];
@@ -625,10 +668,11 @@ __device__ __forceinline__ void gemm2_pp_body(const GemmParams& p, const TileInf
 
   BfPair xa[TA], xb[TA], wa[NF], wb[NF];
   if constexpr (TV > 0) {
+    const float sc0 = BLK ? scale_of(0) : 1.0f;
 #pragma unroll
     for (int t = 0; t < TV; ++t) xa[t] = rdx(smem + xoff(t));
 #pragma unroll
-    for (int f = 0; f < NF; ++f) wa[f] = fp8x16_to_bf16(rdw(smem, f));
+    for (int f = 0; f < NF; ++f) wa[f] = widen(rdw(smem, f), sc0);
   }
 
   auto step = [&](auto steady, int ks, const BfPair (&xc)[TA], const BfPair (&wc)[NF], BfPair (&xn)[TA],
@@ -639,6 +683,9 @@ __device__ __forceinline__ void gemm2_pp_body(const GemmParams& p, const TileInf
     const bool next = kSteady || ks + 1 < nk;
     const bool more = kSteady || ks + STAGES < nk;
     const uint8_t* stn = smem + ((ks + 1) % STAGES) * kStage;
+    // the scale of step ks+1's K block (the last step reads a valid entry it does not use)
+    float scn = 1.0f;
+    if constexpr (BLK && TV > 0) scn = scale_of(min((ks + 1) >> 2, nkb - 1));
     uint4 raw[NF];
     static_for<NF>([&](auto fc) {
       constexpr int f = decltype(fc)::value;
@@ -664,15 +711,16 @@ __device__ __forceinline__ void gemm2_pp_body(const GemmParams& p, const TileInf
         acc[f][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wc[f].b, xc[t].b, acc[f][t], 0, 0, 0);
       if constexpr (TV > 0) {
         if (next && f > 0) {
-          wn_[f - 1] = fp8x16_to_bf16(raw[f - 1]);
-          if (f == NF - 1) wn_[f] = fp8x16_to_bf16(raw[f]);
+          wn_[f - 1] = widen(raw[f - 1], scn);
+          if (f == NF - 1) wn_[f] = widen(raw[f], scn);
         }
       }
       if constexpr (TV > 0) {
         // per group: 2*TV MFMAs; DS reads: the 4 raw W2 fragments (group 0)
         // and one token fragment (2 reads); 8 conversions per W2 fragment
         constexpr int kReads = (f == 0 ? NF : 0) + (f < TV ? 2 : 0);
-        constexpr int kCvt = (f == 0) ? 0 : (f == NF - 1 ? 16 : 8);
+        constexpr int kCvtF = BLK ? 32 : 8;    // vector instructions per widened fragment
+        constexpr int kCvt = (f == 0) ? 0 : (f == NF - 1 ? 2 * kCvtF : kCvtF);
         constexpr int kCvtPer = (kCvt + 2 * TV - 1) / (2 * TV);
         static_for<2 * TV>([&](auto ic) {
           constexpr int i = decltype(ic)::value;
@@ -701,15 +749,17 @@ __device__ __forceinline__ void gemm2_pp_body(const GemmParams& p, const TileInf
   }
   if (ks < nk) step(tail, ks, xa, wa, xb, wb);
 
-  // ---- epilogue: y = acc * s2 in fp32.  Lane holds token l32 of each
-  // token fragment and channels 8q + 4hh .. +3 of each channel fragment.
+  // ---- epilogue: y = acc * s2 in fp32 (per-block: the scales are in acc
+  // already).  Lane holds token l32 of each token fragment and channels
+  // 8q + 4hh .. +3 of each channel fragment.
   if constexpr (TV > 0) {
     const float* S2 = reinterpret_cast<const float*>(p.sa[ti.wi]) + ti.eg * p.N + n0 + wn * 128;
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
       float4 s2v[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) s2v[q] = *reinterpret_cast<const float4*>(S2 + f * 32 + 8 * q + 4 * hh);
+      for (int q = 0; q < 4; ++q)
+        s2v[q] = BLK ? make_float4(1.f, 1.f, 1.f, 1.f) : *reinterpret_cast<const float4*>(S2 + f * 32 + 8 * q + 4 * hh);
 #pragma unroll
       for (int t = 0; t < TV; ++t) {
         const int grow = ti.row0 + (2 * t + wm) * 32 + l32;
@@ -725,7 +775,35 @@ __device__ __forceinline__ void gemm2_pp_body(const GemmParams& p, const TileInf
   }
 }
 
-template <int BM, int STAGES>
+// BLKK: the routed group has per-block fp8 weights (the shared group is
+// always per-channel).  A tile takes the body for its valid rows; a short
+// tile stages only the rows it has (as in the gate-up GEMM).  The dispatch is
+// written out in the kernel (a macro, not a helper function, which changed
+// the register allocation of the per-channel kernel's tile set-up).
+#define MOE_G2_TILE(B)                                                                  \
+  if (BM > 64 && vr <= 64) {                                                            \
+    if (valid_frags<1>(vr, wm) == 0) gemm2_pp_body<64, S64, 0, B>(p, ti, smem);         \
+    else gemm2_pp_body<64, S64, 1, B>(p, ti, smem);                                     \
+    return;                                                                             \
+  }                                                                                     \
+  if (BM > 128 && vr <= 128) {                                                          \
+    switch (valid_frags<2>(vr, wm)) {                                                   \
+      case 0: gemm2_pp_body<128, S128, 0, B>(p, ti, smem); break;                       \
+      case 1: gemm2_pp_body<128, S128, 1, B>(p, ti, smem); break;                       \
+      default: gemm2_pp_body<128, S128, 2, B>(p, ti, smem); break;                      \
+    }                                                                                   \
+    return;                                                                             \
+  }                                                                                     \
+  switch (valid_frags<TF>(vr, wm)) {                                                    \
+    case 0: gemm2_pp_body<BM, STAGES, 0, B>(p, ti, smem); break;                        \
+    case 1: gemm2_pp_body<BM, STAGES, 1, B>(p, ti, smem); break;                        \
+    case 2: gemm2_pp_body<BM, STAGES, 2, B>(p, ti, smem); break;                        \
+    case 3: if constexpr (TF >= 3) gemm2_pp_body<BM, STAGES, 3, B>(p, ti, smem); break; \
+    default: if constexpr (TF >= 4) gemm2_pp_body<BM, STAGES, 4, B>(p, ti, smem); break; \
+  }                                                                                     \
+  return
+
+template <int BM, int STAGES, bool BLKK>
 __global__ __launch_bounds__(256, 1) void gemm2_pp_kernel(GemmParams p) {
   constexpr int kStage = BM * 64 + kLgCh * 32;
   constexpr int TF = BM / 64;
@@ -737,30 +815,16 @@ __global__ __launch_bounds__(256, 1) void gemm2_pp_kernel(GemmParams p) {
   __syncthreads();   // every thread has its tile: the ring is free
   const int vr = min(BM, ti.row1 - ti.row0);
   const int wm = __builtin_amdgcn_readfirstlane(threadIdx.x >> 7);
-  // a short tile stages only the rows it has (as in the gate-up GEMM)
   constexpr int S64 = short_stages(STAGES * kStage, 64 * 64 + kLgCh * 32, 3);
   constexpr int S128 = short_stages(STAGES * kStage, 128 * 64 + kLgCh * 32, 4);
-  if (BM > 64 && vr <= 64) {
-    if (valid_frags<1>(vr, wm) == 0) gemm2_pp_body<64, S64, 0>(p, ti, smem);
-    else gemm2_pp_body<64, S64, 1>(p, ti, smem);
-    return;
-  }
-  if (BM > 128 && vr <= 128) {
-    switch (valid_frags<2>(vr, wm)) {
-      case 0: gemm2_pp_body<128, S128, 0>(p, ti, smem); break;
-      case 1: gemm2_pp_body<128, S128, 1>(p, ti, smem); break;
-      default: gemm2_pp_body<128, S128, 2>(p, ti, smem); break;
+  if constexpr (BLKK) {
+    if (ti.wi == 0) {
+      MOE_G2_TILE(true);
     }
-    return;
   }
-  switch (valid_frags<TF>(vr, wm)) {
-    case 0: gemm2_pp_body<BM, STAGES, 0>(p, ti, smem); break;
-    case 1: gemm2_pp_body<BM, STAGES, 1>(p, ti, smem); break;
-    case 2: gemm2_pp_body<BM, STAGES, 2>(p, ti, smem); break;
-    case 3: if constexpr (TF >= 3) gemm2_pp_body<BM, STAGES, 3>(p, ti, smem); break;
-    default: if constexpr (TF >= 4) gemm2_pp_body<BM, STAGES, 4>(p, ti, smem); break;
-  }
+  MOE_G2_TILE(false);
 }
+#undef MOE_G2_TILE
 // ============================================================================
 // small variants (decode-sized groups; fp8 or MXFP4 weights)
 // ============================================================================
@@ -1289,6 +1353,28 @@ int choose_variant(const FfnGroups& g, long n_rows) {
   return avg >= 384 ? kVariantLarge256 : kVariantLarge128;
 }
 
+// The down GEMM's variant: as the gate-up GEMM's, except that per-block fp8
+// weights may take the large kernels (their block scale is one number per
+// wave and K block there, applied as the codes are widened), which the
+// gate-up GEMM cannot (its scale must apply to fp8 partial sums).
+int choose_down_variant(const FfnGroups& g, long n_rows) {
+  if (g.fmt != kFp8Block) return choose_variant(g, n_rows);
+  // the large kernel holds a wave's K-block scales in two lanes' registers
+  const bool large_ok = (g.hidden % kLgCh) == 0 && (g.inter % (kLgCh / 2)) == 0 && g.inter <= 128 * 128;
+  const long avg = n_rows / (g.n_groups > 0 ? g.n_groups : 1);
+  if (!large_ok || avg < 64) return choose_variant(g, n_rows);
+  return avg >= 384 ? kVariantLarge256 : kVariantLarge128;
+}
+
+int shared_gate_up_variant(const FfnGroups& g, long n_rows, long shared_rows) {
+  if (g.fmt != kFp8Block || g.n_groups <= g.n_routed || !variant_in_registers(choose_variant(g, n_rows))) return -1;
+  if ((g.hidden % kLgCh) != 0 || (g.inter % (kLgCh / 2)) != 0 || shared_rows < 64) return -1;
+  // 256-row tiles only when they alone fill the chip (a launch of one group
+  // has no other groups' tiles beside it)
+  const long tiles256 = (shared_rows + 255) / 256 * (g.inter / (kLgCh / 2));
+  return tiles256 >= kNumCUs ? kVariantLarge256 : kVariantLarge128;
+}
+
 bool small_streams_weights(const FfnGroups& g, long n_rows) {
   return n_rows <= (long)kSmRows * (g.n_groups > 0 ? g.n_groups : 1);
 }
@@ -1328,7 +1414,9 @@ static GemmParams base_params(const FfnGroups& g, const RowOperand& x, const int
 }
 
 hipError_t launch_gemm1(int variant, const FfnGroups& g, const RowOperand& x, const int* tile_prefix,
-                        long n_rows, uint16_t* h, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop) {
+                        long n_rows, uint16_t* h, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop,
+                        long grid_rows) {
+  if (grid_rows < 0) grid_rows = n_rows;
   GemmParams p = base_params(g, x, tile_prefix);
   p.K = g.hidden;
   p.N = g.inter;
@@ -1349,7 +1437,7 @@ hipError_t launch_gemm1(int variant, const FfnGroups& g, const RowOperand& x, co
   const int bm = variant_rows(variant);
   if (variant_in_registers(variant)) {
     p.ntiles = g.inter / (kSmCh / 2);
-    const long grid = max_row_tiles(n_rows, g.n_groups, bm) * p.ntiles;
+    const long grid = max_row_tiles(grid_rows, g.n_groups, bm) * p.ntiles;
     auto pick = [&](auto nt, auto rows) {
       constexpr bool NT = decltype(nt)::value;
       constexpr int R = decltype(rows)::value;
@@ -1367,7 +1455,7 @@ hipError_t launch_gemm1(int variant, const FfnGroups& g, const RowOperand& x, co
     hipExtLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, s, ev_start, ev_stop, 0, p);
   } else {
     p.ntiles = g.inter / (kLgCh / 2);
-    const long grid = max_row_tiles(n_rows, g.n_groups, bm) * p.ntiles;
+    const long grid = max_row_tiles(grid_rows, g.n_groups, bm) * p.ntiles;
     const bool situ = g.act[0] == kActSitu || (g.n_groups > g.n_routed && g.act[1] == kActSitu);
     auto kern = variant == kVariantLarge256 ? (situ ? gemm1_pp_kernel<256, 4, true> : gemm1_pp_kernel<256, 4, false>)
                                             : (situ ? gemm1_pp_kernel<128, 6, true> : gemm1_pp_kernel<128, 6, false>);
@@ -1416,10 +1504,10 @@ hipError_t launch_gemm2(int variant, const FfnGroups& g, const uint16_t* h, cons
   } else {
     p.ntiles = g.hidden / kLgCh;
     const long grid = max_row_tiles(n_rows, g.n_groups, bm) * p.ntiles;
-    if (variant == kVariantLarge256)
-      hipExtLaunchKernelGGL(gemm2_pp_kernel<256, 4>, dim3((unsigned)grid), dim3(256), 0, s, ev_start, ev_stop, 0, p);
-    else
-      hipExtLaunchKernelGGL(gemm2_pp_kernel<128, 8>, dim3((unsigned)grid), dim3(256), 0, s, ev_start, ev_stop, 0, p);
+    const bool blk = g.fmt == kFp8Block;
+    auto kern = variant == kVariantLarge256 ? (blk ? gemm2_pp_kernel<256, 4, true> : gemm2_pp_kernel<256, 4, false>)
+                                            : (blk ? gemm2_pp_kernel<128, 8, true> : gemm2_pp_kernel<128, 8, false>);
+    hipExtLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, s, ev_start, ev_stop, 0, p);
   }
   return hipGetLastError();
 }

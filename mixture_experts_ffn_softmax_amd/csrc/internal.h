@@ -147,13 +147,21 @@ struct RowOperand {
 
 // small: 32-row tiles, operands straight into registers (weight streaming);
 // medium: the same kernels with 64-row tiles, for per-block fp8 batches with
-// many rows per group (the large kernels take per-channel fp8 only);
-// large: 128- or 256-row tiles staged through an LDS ring (per-channel fp8).
+// many rows per group (the large gate-up kernel takes per-channel fp8 only);
+// large: 128- or 256-row tiles staged through an LDS ring (per-channel fp8,
+// and per-block fp8 in the down GEMM).
 enum GemmVariant { kVariantSmall = 0, kVariantLarge128 = 1, kVariantLarge256 = 2, kVariantMedium = 3 };
 // The variants whose kernels read their row fragments straight into registers.
 inline bool variant_in_registers(int v) { return v == kVariantSmall || v == kVariantMedium; }
 
 int choose_variant(const FfnGroups& g, long n_rows);
+// The down GEMM's variant: choose_variant's, except that per-block fp8
+// weights may take the large kernels (the gate-up GEMM's may not).
+int choose_down_variant(const FfnGroups& g, long n_rows);
+// With per-block fp8 routed weights the gate-up GEMM runs the register-fed
+// kernels; the shared group (per-channel fp8, shared_rows rows) then takes a
+// launch of its own on the large kernel: its variant, or -1 (one launch).
+int shared_gate_up_variant(const FfnGroups& g, long n_rows, long shared_rows);
 // The small variant streams its weights with non-temporal loads when the
 // groups average at most one row tile (kSmRows rows): each weight tile is then
 // read by about one workgroup.  With more rows per group several row tiles
@@ -168,9 +176,11 @@ hipError_t launch_tile_prefix(const int* offsets, int n_groups, int bm, int* til
 // GEMM1: h[r][n] = bf16(SiLU(g) * u) for the gate/up pair of channel n.  h is
 // K-blocked for GEMM2: kHChunk-byte chunks (32 channels) over n_rows rows.
 // ev_start / ev_stop (may be NULL): stamped by the GEMM1 dispatch itself.
+// grid_rows (>= 0): the rows the launch's groups hold, when fewer than
+// n_rows (a launch over some of the groups); sizes the grid only.
 hipError_t launch_gemm1(int variant, const FfnGroups& g, const RowOperand& x, const int* tile_prefix,
                         long n_rows, uint16_t* h, hipStream_t s, hipEvent_t ev_start = nullptr,
-                        hipEvent_t ev_stop = nullptr);
+                        hipEvent_t ev_stop = nullptr, long grid_rows = -1);
 // GEMM2: y[r][j] = (h_r . W2[j]) * s2[j] in fp32; h as GEMM1 writes it.
 hipError_t launch_gemm2(int variant, const FfnGroups& g, const uint16_t* h, const int* tile_prefix,
                         long n_rows, float* y, hipStream_t s, hipEvent_t ev_start = nullptr,

@@ -18,6 +18,7 @@ namespace moe {
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef float v2f __attribute__((ext_vector_type(2)));
 
 // 32 e2m1 codes (4 words, element 2i in the low nibble of byte i) times 2^e
 // -> 4 x 8 bf16, exact for normal results.

@@ -123,8 +123,11 @@ struct Carve {
   }
 };
 
+// tile_prefix[0..n_groups] serves the gate-up GEMM, the next n_groups + 1
+// entries the down GEMM when it takes another row-tile height, the last two a
+// gate-up launch of the shared group alone.
 size_t ffn_ws(Carve& c, long n_rows, int n_groups, int inter, int32_t** tile_prefix, uint16_t** h) {
-  *tile_prefix = c.take<int32_t>(n_groups + 1);
+  *tile_prefix = c.take<int32_t>(2 * (n_groups + 1) + 2);
   *h = c.take<uint16_t>((size_t)n_rows * inter);
   return c.used;
 }
@@ -162,21 +165,55 @@ moe_status_t run_ffn(const moe::FfnGroups& g, const moe::RowOperand& x, long n_r
                      char* variant_out, size_t variant_len, bool tile_prefix_ready = false,
                      void* const* gemm1_events = nullptr, void* const* gemm2_events = nullptr) {
   const int variant = moe::choose_variant(g, n_rows);
-  if (variant_out)
-    snprintf(variant_out, variant_len, "%s/%s", moe::variant_name(variant),
-             g.fmt == moe::kMxfp4 ? "mxfp4" : "fp8");
+  const int variant2 = moe::choose_down_variant(g, n_rows);
+  const long shared_rows = g.n_groups > g.n_routed ? n_rows - x.shared_row0 : 0;
+  const int variant_sh = moe::shared_gate_up_variant(g, n_rows, shared_rows);
+  // the down GEMM's tile prefix, when its tiles have another height, and
+  // that of the shared group's own gate-up launch
+  int32_t* tile_prefix2 = variant2 == variant ? tile_prefix : tile_prefix + g.n_groups + 1;
+  int32_t* tile_prefix_sh = tile_prefix + 2 * (g.n_groups + 1);
+  if (variant_out) {
+    snprintf(variant_out, variant_len, "%s/%s", moe::variant_name(variant), g.fmt == moe::kMxfp4 ? "mxfp4" : "fp8");
+    size_t used = strlen(variant_out);
+    if (variant2 != variant)
+      snprintf(variant_out + used, variant_len - used, "/down:%s", moe::variant_name(variant2));
+    used = strlen(variant_out);
+    if (variant_sh >= 0)
+      snprintf(variant_out + used, variant_len - used, "/shared:%s", moe::variant_name(variant_sh));
+  }
   hipError_t e = hipSuccess;
   if (!tile_prefix_ready) {
     e = moe::launch_tile_prefix(g.offsets, g.n_groups, moe::variant_rows(variant), tile_prefix, s);
     if (e != hipSuccess) return device_status(e, "tile_prefix");
   }
+  if (variant2 != variant) {
+    e = moe::launch_tile_prefix(g.offsets, g.n_groups, moe::variant_rows(variant2), tile_prefix2, s);
+    if (e != hipSuccess) return device_status(e, "tile_prefix");
+  }
+  // the shared group alone: group 0 of a launch whose offsets start at its own
+  moe::FfnGroups g_sh = g;
+  if (variant_sh >= 0) {
+    g_sh.offsets = g.offsets + g.n_routed;
+    g_sh.n_groups = 1;
+    g_sh.n_routed = 0;
+    e = moe::launch_tile_prefix(g_sh.offsets, 1, moe::variant_rows(variant_sh), tile_prefix_sh, s);
+    if (e != hipSuccess) return device_status(e, "tile_prefix");
+  }
   if (events && events[MOE_STAGE_GEMM1]) hipEventRecord((hipEvent_t)events[MOE_STAGE_GEMM1], s);
-  e = moe::launch_gemm1(variant, g, x, tile_prefix, n_rows, h, s,
-                        gemm1_events ? (hipEvent_t)gemm1_events[0] : nullptr,
-                        gemm1_events ? (hipEvent_t)gemm1_events[1] : nullptr);
+  hipEvent_t g1_start = gemm1_events ? (hipEvent_t)gemm1_events[0] : nullptr;
+  hipEvent_t g1_stop = gemm1_events ? (hipEvent_t)gemm1_events[1] : nullptr;
+  if (variant_sh >= 0) {
+    moe::FfnGroups g_routed = g;
+    g_routed.n_groups = g.n_routed;
+    e = moe::launch_gemm1(variant, g_routed, x, tile_prefix, n_rows, h, s, g1_start, nullptr, x.shared_row0);
+    if (e == hipSuccess)
+      e = moe::launch_gemm1(variant_sh, g_sh, x, tile_prefix_sh, n_rows, h, s, nullptr, g1_stop, shared_rows);
+  } else {
+    e = moe::launch_gemm1(variant, g, x, tile_prefix, n_rows, h, s, g1_start, g1_stop);
+  }
   if (e != hipSuccess) return device_status(e, "gemm1");
   if (events && events[MOE_STAGE_GEMM2]) hipEventRecord((hipEvent_t)events[MOE_STAGE_GEMM2], s);
-  e = moe::launch_gemm2(variant, g, h, tile_prefix, n_rows, y, s,
+  e = moe::launch_gemm2(variant2, g, h, tile_prefix2, n_rows, y, s,
                         gemm2_events ? (hipEvent_t)gemm2_events[0] : nullptr,
                         gemm2_events ? (hipEvent_t)gemm2_events[1] : nullptr);
   if (e != hipSuccess) return device_status(e, "gemm2");
