@@ -47,6 +47,8 @@ def parse():
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-share measurement")
     ap.add_argument("--no-latent", action="store_true", help="skip the LatentMoE block measurement")
     ap.add_argument("--no-block", action="store_true", help="skip the per-block fp8 measurement")
+    ap.add_argument("--no-block-decode", action="store_true",
+                    help="per-block fp8: time the prefill share only (for kernel traces of one workload)")
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the prefill (headline) measurement: for profiling the other workloads alone")
     ap.add_argument("--no-tiny", action="store_true", help="skip the tiny (launch-latency) workload")
@@ -616,7 +618,7 @@ def main():
     if not args.no_block:
         log("[bench] per-block fp8 routed weights (128 x 128 tiles): prefill and decode shares")
         blk = {}
-        for name in ("prefill_block", "decode_block"):
+        for name in ("prefill_block",) + (() if args.no_block_decode else ("decode_block",)):
             bl = Layer(name, args.copies)
             btl = time_layer(bl, 20, 3)
             bus = percentiles_us(btl["layer_ms"])

@@ -386,30 +386,28 @@ struct ForwardLayout {
 static bool meta_path(int32_t T, int32_t k, int32_t E) {
   return (long)T * k <= moe::kMetaMaxPairs && E <= moe::kMetaMaxE;
 }
-// The one-launch path's gate-up GEMM gathers token rows.  That costs the
-// small kernel (fragments read straight from memory) little up to decode
-// sizes but much beyond (+100 us on the 2048-token per-block fp8 share), so
-// past kGatherSmallMaxT tokens the path is taken only where the large
-// kernels (rows staged through LDS) run.
+// The one-launch path's gate-up GEMM reads token-order rows: gathered
+// through row_to_pair by the register-fed kernels up to kGatherSmallMaxT
+// tokens, beyond that (and always for the large kernels) from an
+// expert-ordered copy.
 constexpr int32_t kGatherSmallMaxT = 256;
 static bool fused_route_path(int32_t T, int32_t k, const moe_weights_t* routed, bool shared) {
+  (void)shared;
   const int32_t E = routed->n_experts, H = routed->hidden;
-  if (!(meta_path(T, k, E) && E <= moe::kMetaRouteMaxE && T <= moe::kMetaRouteMaxT &&
-        (long)T * k <= moe::kMetaRouteMaxPairs && H <= moe::kMetaQuantMaxH))
-    return false;
-  if (T <= kGatherSmallMaxT) return true;
-  // only the format, the shape and the group count decide the variant
-  const moe::FfnGroups g = make_groups(routed, shared ? routed : nullptr, nullptr);
-  return !moe::variant_in_registers(moe::choose_variant(g, (long)T * k + (shared ? T : 0)));
+  return meta_path(T, k, E) && E <= moe::kMetaRouteMaxE && T <= moe::kMetaRouteMaxT &&
+         (long)T * k <= moe::kMetaRouteMaxPairs && H <= moe::kMetaQuantMaxH;
 }
 // On the one-launch routing path the large kernels read expert-ordered rows
 // that a copy kernel writes from the token-order rows: their direct-to-LDS
 // loads of gathered rows fetch scattered 64-byte half lines, which cost the
 // 256-row gate-up GEMM about 40 us on the 2048-token prefill share, against
-// about 10 us for the copy.  The small kernels read their token fragments
-// straight into registers and gather them for little cost.
+// about 10 us for the copy.  The register-fed kernels gather their token
+// fragments for little cost at decode sizes but not beyond (+100 us on the
+// 2048-token per-block fp8 share), so past kGatherSmallMaxT tokens they too
+// read the copy.
 static bool fused_rows_copied(int32_t T, int32_t k, const moe_weights_t* routed, bool shared) {
   if (!fused_route_path(T, k, routed, shared)) return false;
+  if (T > kGatherSmallMaxT) return true;
   const moe::FfnGroups g = make_groups(routed, shared ? routed : nullptr, nullptr);
   return !moe::variant_in_registers(moe::choose_variant(g, (long)T * k + (shared ? T : 0)));
 }

@@ -167,8 +167,9 @@ FULL_CASES = {
     "gathered_large128_shared": (200, 256, 256, 4, 2, "fp8", True, False),
     "gathered_large128": (256, 512, 256, 2, 2, "fp8", False, False),
     # either side of the path choices: one-launch routing with the small
-    # kernels up to 256 tokens, past that only with the large ones; up to
-    # 4096 tokens with the large ones, past that the grid-wide router
+    # kernels gathering token rows up to 256 tokens, past that reading an
+    # expert-ordered copy (as the large kernels always do); up to 4096
+    # tokens one-launch routing, past that the grid-wide router
     "path_T257_small": (257, 256, 128, 16, 2, "fp8", False, False),
     "path_T4096_large": (4096, 256, 128, 8, 1, "fp8", False, False),
     "path_T4097_large": (4097, 256, 128, 8, 1, "fp8", False, False),
