@@ -130,8 +130,13 @@ typedef enum {
  *                applied to that tile's partial sum inside the reduction:
  *                out[n] = sum_kb s[n/128][kb] * sum_{k in kb} a[k] W[n][k]
  *                ([Ling] §5, per-block scaling; the [128, 128] block-wise
- *                format of the Kimi K3 page, §3.7).  Routed experts only;
- *                runs on the weight-streaming (small) GEMM variant.
+ *                format of the Kimi K3 page, §3.7).  Routed experts only.
+ *                The gate-up GEMM runs on the register-fed kernels, which
+ *                sum each K block and scale the fp32 partial; the down GEMM
+ *                of large batches (from 64 rows per expert on average) runs
+ *                on the LDS-staged kernel, which applies the scale to each
+ *                weight as it is widened (bf16(code * s), one rounding of at
+ *                most 2^-9 relative, the size of h's own bf16 rounding).
  *   fmt = MXFP4: w1, w3  uint8 [E][I][H/2]    s1, s3  uint8 [E][I][H/32]
  *                w2      uint8 [E][H][I/2]    s2      uint8 [E][H][I/32]
  *                (element 2i in the low nibble of byte i; scale 255 = NaN is

@@ -36,12 +36,13 @@
 //   large: BM rows x 256 channel rows per workgroup, 4 waves in a 2 x 2
 //          layout, 32x32 MFMA fragments.  Tiles stream through a ring of
 //          LDS stages filled by direct-to-LDS loads (global_load_lds), issued
-//          STAGES-1 steps ahead; waits and barriers are explicit.  fp8
-//          weights.
+//          STAGES-1 steps ahead; waits and barriers are explicit.
+//          Per-channel fp8 weights, and per-block fp8 in the down GEMM.
 //   small: 32 rows x 64 channel rows, the 4 waves split the K steps and read
 //          their fragments straight from memory into registers, then reduce
 //          through LDS.  For decode-sized groups, where the weight stream is
-//          the bound; fp8 and MXFP4 weights.
+//          the bound; fp8, per-block fp8 and MXFP4 weights (64-row tiles:
+//          the medium variant, for per-block fp8 batches with many rows).
 #include <math.h>
 
 #include <type_traits>
