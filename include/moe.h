@@ -131,12 +131,14 @@ typedef enum {
  *                out[n] = sum_kb s[n/128][kb] * sum_{k in kb} a[k] W[n][k]
  *                ([Ling] §5, per-block scaling; the [128, 128] block-wise
  *                format of the Kimi K3 page, §3.7).  Routed experts only.
- *                The gate-up GEMM runs on the register-fed kernels, which
- *                sum each K block and scale the fp32 partial; the down GEMM
- *                of large batches (from 64 rows per expert on average) runs
- *                on the LDS-staged kernel, which applies the scale to each
- *                weight as it is widened (bf16(code * s), one rounding of at
- *                most 2^-9 relative, the size of h's own bf16 rounding).
+ *                Small batches run the register-fed kernels, which sum each
+ *                K block and scale the fp32 partial.  From 64 rows per
+ *                expert on average the LDS-staged kernels run: the gate-up
+ *                GEMM takes the scale's power of two in the MFMA and its
+ *                mantissa by rescaling the fp32 accumulators at each K
+ *                block; the down GEMM applies the scale to each weight as
+ *                it is widened (bf16(code * s), one rounding of at most
+ *                2^-9 relative, the size of h's own bf16 rounding).
  *   fmt = MXFP4: w1, w3  uint8 [E][I][H/2]    s1, s3  uint8 [E][I][H/32]
  *                w2      uint8 [E][H][I/2]    s2      uint8 [E][H][I/32]
  *                (element 2i in the low nibble of byte i; scale 255 = NaN is

@@ -283,9 +283,13 @@ __device__ __forceinline__ int valid_frags(int vr, int wm) {
 // h = bf16(act(g) * u) goes straight to the K-blocked h: a 32-channel
 // fragment is one 64-byte chunk row, so the four q stores of a fragment fill
 // 32 consecutive chunk rows (2 KB).
-template <int TV, int TA, typename Act>
+// BLK: per-block fp8 weights; the accumulators hold the sums in units of
+// the last K block's scale mantissas mg / mu (see gemm1_pp_body), which
+// replace the per-channel scales.
+template <int TV, int TA, bool BLK = false, typename Act>
 __device__ __forceinline__ void gemm1_pp_epilogue(const GemmParams& p, const TileInfo& ti, int n0, int wm, int wn,
-                                                  int l32, int hh, const v16f (&acc)[4][TA], Act act) {
+                                                  int l32, int hh, const v16f (&acc)[4][TA], Act act,
+                                                  float mg = 1.0f, float mu = 1.0f) {
   const float* S1 = reinterpret_cast<const float*>(p.sa[ti.wi]) + ti.eg * p.N;
   const float* S3 = reinterpret_cast<const float*>(p.sb[ti.wi]) + ti.eg * p.N;
   float xs[TV];
@@ -301,8 +305,8 @@ __device__ __forceinline__ void gemm1_pp_epilogue(const GemmParams& p, const Til
     float4 s1v[4], s3v[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      s1v[q] = *reinterpret_cast<const float4*>(S1 + ch0 + 8 * q + 4 * hh);
-      s3v[q] = *reinterpret_cast<const float4*>(S3 + ch0 + 8 * q + 4 * hh);
+      s1v[q] = BLK ? make_float4(mg, mg, mg, mg) : *reinterpret_cast<const float4*>(S1 + ch0 + 8 * q + 4 * hh);
+      s3v[q] = BLK ? make_float4(mu, mu, mu, mu) : *reinterpret_cast<const float4*>(S3 + ch0 + 8 * q + 4 * hh);
     }
 #pragma unroll
     for (int t = 0; t < TV; ++t) {
@@ -332,7 +336,16 @@ __device__ __forceinline__ void gemm1_pp_epilogue(const GemmParams& p, const Til
 // n0.., then W3 rows n0..), 64 bytes of the K step each (swz64).  SITU:
 // some group uses SiTU (a separate instantiation, so that the SiLU-only
 // kernel carries no second epilogue and its register allocation is unchanged).
-template <int BM, int STAGES, int TV, bool SITU>
+// BLK: per-block fp8 weights (the routed group of the per-block format).
+// The workgroup's 128 gate (and 128 up) channels are one channel block, so a
+// K block (two steps) has one gate and one up scale s = m * 2^e (m in [1, 2)).
+// The exponent enters the MFMA as its e8m0 weight scale (exact); the
+// mantissa cannot, so the accumulators are kept in units of the current
+// block's mantissa: at each block start they are multiplied by
+// m_previous / m_current, and the epilogue multiplies by the last block's m.
+// (A zero or subnormal scale gives e8m0 0, i.e. 2^-127, with the mantissa of
+// the block before: its products fall below binary32's range.)
+template <int BM, int STAGES, int TV, bool SITU, bool BLK = false>
 __device__ __forceinline__ void gemm1_pp_body(const GemmParams& p, const TileInfo& ti, uint8_t* smem) {
   constexpr int kRows = BM + kLgCh;
   constexpr int kStage = kRows * 64;
@@ -351,6 +364,38 @@ __device__ __forceinline__ void gemm1_pp_body(const GemmParams& p, const TileInf
   const uint8_t* W3 = p.wb[ti.wi] + ti.eg * (long)p.N * K;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+
+  // per-block scales of the gate and up channel blocks (at most 128 K
+  // blocks): lane l holds those of K blocks l and l + 64, loaded and waited
+  // for before any direct-to-LDS load is issued
+  const int nkb = K >> 7;
+  float sg0 = 1.0f, sg1 = 1.0f, su0 = 1.0f, su1 = 1.0f;
+  if constexpr (BLK) {
+    const long base = (ti.eg * (long)(p.N >> 7) + (n0 >> 7)) * nkb;
+    const float* S1b = reinterpret_cast<const float*>(p.sa[ti.wi]) + base;
+    const float* S3b = reinterpret_cast<const float*>(p.sb[ti.wi]) + base;
+    if (lane < nkb) {
+      sg0 = S1b[lane];
+      su0 = S3b[lane];
+    }
+    if (lane + 64 < nkb) {
+      sg1 = S1b[lane + 64];
+      su1 = S3b[lane + 64];
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+  }
+  auto lane_pick = [&](float v0, float v1, int kb) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(kb < 64 ? v0 : v1), kb & 63));
+  };
+  // e8m0 exponent and mantissa of a block scale
+  auto blk_exp = [](float sc) { return (int)((__float_as_uint(sc) >> 23) & 0xFFu); };
+  auto blk_mant = [](float sc, float prev) {
+    const uint32_t b = __float_as_uint(sc);
+    const float m = ((b >> 23) & 0xFFu) ? __uint_as_float((b & 0x807FFFFFu) | 0x3F800000u) : sc * 0x1p127f;
+    return m != 0.0f ? m : prev;
+  };
+  float mg = 1.0f, mu = 1.0f;   // mantissas of the current K block
+  int eg8 = 127, eu8 = 127;     // e8m0 exponents of the current K block
 
   // this lane's source of each of the wave's dma16 per stage, advanced by one
   // K step after every issue (stages are issued in order)
@@ -417,9 +462,25 @@ __device__ __forceinline__ void gemm1_pp_body(const GemmParams& p, const TileInf
 
   // one K step on register set (xc, wc), reading step ks+1 into (xn, wn_).
   // steady = true: step ks+1 exists and step ks+STAGES is to be loaded.
+  // Per-block: an even step starts a K block (nk is even: K is a multiple
+  // of 256 for these kernels).
   auto step = [&](auto steady, int ks, const v8i (&xc)[TA], const v8i (&wc)[NF], v8i (&xn)[TA],
                   v8i (&wn_)[NF]) {
     constexpr bool kSteady = decltype(steady)::value;
+    float rg = 1.0f, ru = 1.0f;
+    if constexpr (BLK) {
+      if ((ks & 1) == 0) {
+        const int kb = ks >> 1;
+        const float sg = lane_pick(sg0, sg1, kb), su = lane_pick(su0, su1, kb);
+        const float mg2 = blk_mant(sg, mg), mu2 = blk_mant(su, mu);
+        rg = mg / mg2;
+        ru = mu / mu2;
+        mg = mg2;
+        mu = mu2;
+        eg8 = blk_exp(sg);
+        eu8 = blk_exp(su);
+      }
+    }
     if (kSteady) wait_barrier<(STAGES - 2) * kPer>();
     else pp_wait<(STAGES - 2) * kPer, STAGES, kPer>(ks, nk);
     const bool next = kSteady || ks + 1 < nk;
@@ -436,8 +497,21 @@ __device__ __forceinline__ void gemm1_pp_body(const GemmParams& p, const TileInf
           if (f < TV) xn[f] = rd(stn + xoff(f));
         }
       }
+      if constexpr (BLK) {
+        // at a block start (r != 1 only there) the sums so far move to the
+        // new block's mantissa; the block's exponent scales the weights
+        const float r = f < 2 ? rg : ru;
+        const int e8 = f < 2 ? eg8 : eu8;
 #pragma unroll
-      for (int t = 0; t < TV; ++t) acc[f][t] = mfma32_fp8(wc[f], xc[t], acc[f][t]);
+        for (int t = 0; t < TV; ++t) {
+          if ((ks & 1) == 0) acc[f][t] = acc[f][t] * r;
+          acc[f][t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wc[f], xc[t], acc[f][t], 0, 0, 0, e8, 0,
+                                                                      kE8m0One);
+        }
+      } else {
+#pragma unroll
+        for (int t = 0; t < TV; ++t) acc[f][t] = mfma32_fp8(wc[f], xc[t], acc[f][t]);
+      }
       if constexpr (TV > 0) {
         constexpr int kReads = 2 + (f < TV ? 2 : 0);
         static_for<(TV > kReads ? TV : kReads)>([&](auto ic) {
@@ -473,18 +547,45 @@ __device__ __forceinline__ void gemm1_pp_body(const GemmParams& p, const TileInf
       // the product with the linear factor g instead of beta tanh(g / beta)
       const bool use_situ = p.act[ti.wi] == kActSitu;
       const float beta = p.beta[ti.wi], rbeta = 1.0f / beta;
-      gemm1_pp_epilogue<TV, TA>(p, ti, n0, wm, wn, l32, hh, acc, [=](float g) {
+      gemm1_pp_epilogue<TV, TA, BLK>(p, ti, n0, wm, wn, l32, hh, acc, [=](float g) {
         const float sig = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * g));
         const float th = 1.0f - 2.0f * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(2.8853900817779268f * g * rbeta));
         return (use_situ ? beta * th : g) * sig;
-      });
+      }, mg, mu);
     } else {
-      gemm1_pp_epilogue<TV, TA>(p, ti, n0, wm, wn, l32, hh, acc, [](float g) { return silu_fast(g); });
+      gemm1_pp_epilogue<TV, TA, BLK>(p, ti, n0, wm, wn, l32, hh, acc, [](float g) { return silu_fast(g); }, mg, mu);
     }
   }
 }
 
-template <int BM, int STAGES, bool SITU>
+// BLKK: the routed group has per-block fp8 weights (the shared group is
+// always per-channel).  The tile dispatch is written out in the kernel (a
+// macro), as in the down GEMM, so that the per-channel kernel's code is
+// that of the plain dispatch.
+#define MOE_G1_TILE(B)                                                                          \
+  if (BM > 64 && vr <= 64) {                                                                    \
+    if (valid_frags<1>(vr, wm) == 0) gemm1_pp_body<64, S64, 0, SITU, B>(p, ti, smem);           \
+    else gemm1_pp_body<64, S64, 1, SITU, B>(p, ti, smem);                                       \
+    return;                                                                                     \
+  }                                                                                             \
+  if (BM > 128 && vr <= 128) {                                                                  \
+    switch (valid_frags<2>(vr, wm)) {                                                           \
+      case 0: gemm1_pp_body<128, S128, 0, SITU, B>(p, ti, smem); break;                         \
+      case 1: gemm1_pp_body<128, S128, 1, SITU, B>(p, ti, smem); break;                         \
+      default: gemm1_pp_body<128, S128, 2, SITU, B>(p, ti, smem); break;                        \
+    }                                                                                           \
+    return;                                                                                     \
+  }                                                                                             \
+  switch (valid_frags<TF>(vr, wm)) {                                                            \
+    case 0: gemm1_pp_body<BM, STAGES, 0, SITU, B>(p, ti, smem); break;                          \
+    case 1: gemm1_pp_body<BM, STAGES, 1, SITU, B>(p, ti, smem); break;                          \
+    case 2: gemm1_pp_body<BM, STAGES, 2, SITU, B>(p, ti, smem); break;                          \
+    case 3: if constexpr (TF >= 3) gemm1_pp_body<BM, STAGES, 3, SITU, B>(p, ti, smem); break;   \
+    default: if constexpr (TF >= 4) gemm1_pp_body<BM, STAGES, 4, SITU, B>(p, ti, smem); break;  \
+  }                                                                                             \
+  return
+
+template <int BM, int STAGES, bool SITU, bool BLKK = false>
 __global__ __launch_bounds__(256, 1) void gemm1_pp_kernel(GemmParams p) {
   constexpr int kStage = (BM + kLgCh) * 64;
   constexpr int TF = BM / 64;
@@ -503,27 +604,14 @@ __global__ __launch_bounds__(256, 1) void gemm1_pp_kernel(GemmParams p) {
   // loop is bound by the weight stream's latency, not by the MFMAs)
   constexpr int S64 = short_stages(STAGES * kStage, (64 + kLgCh) * 64, 5);
   constexpr int S128 = short_stages(STAGES * kStage, (128 + kLgCh) * 64, 6);
-  if (BM > 64 && vr <= 64) {
-    if (valid_frags<1>(vr, wm) == 0) gemm1_pp_body<64, S64, 0, SITU>(p, ti, smem);
-    else gemm1_pp_body<64, S64, 1, SITU>(p, ti, smem);
-    return;
-  }
-  if (BM > 128 && vr <= 128) {
-    switch (valid_frags<2>(vr, wm)) {
-      case 0: gemm1_pp_body<128, S128, 0, SITU>(p, ti, smem); break;
-      case 1: gemm1_pp_body<128, S128, 1, SITU>(p, ti, smem); break;
-      default: gemm1_pp_body<128, S128, 2, SITU>(p, ti, smem); break;
+  if constexpr (BLKK) {
+    if (ti.wi == 0) {
+      MOE_G1_TILE(true);
     }
-    return;
   }
-  switch (valid_frags<TF>(vr, wm)) {
-    case 0: gemm1_pp_body<BM, STAGES, 0, SITU>(p, ti, smem); break;
-    case 1: gemm1_pp_body<BM, STAGES, 1, SITU>(p, ti, smem); break;
-    case 2: gemm1_pp_body<BM, STAGES, 2, SITU>(p, ti, smem); break;
-    case 3: if constexpr (TF >= 3) gemm1_pp_body<BM, STAGES, 3, SITU>(p, ti, smem); break;
-    default: if constexpr (TF >= 4) gemm1_pp_body<BM, STAGES, 4, SITU>(p, ti, smem); break;
-  }
+  MOE_G1_TILE(false);
 }
+#undef MOE_G1_TILE
 
 // 32 e4m3 codes (4 words, 16 per half-lane K slice) -> the two bf16 halves
 // of a 32x32x16 fragment pair, exact.
@@ -1347,24 +1435,31 @@ hipError_t launch_pack_kblocked(const uint8_t* src, uint8_t* dst, int E, int N, 
 long max_row_tiles(long n_rows, int n_groups, int bm) { return (n_rows + bm - 1) / bm + n_groups; }
 
 int choose_variant(const FfnGroups& g, long n_rows) {
-  const bool large_ok = g.fmt == kFp8 && (g.hidden % kLgCh) == 0 && (g.inter % (kLgCh / 2)) == 0;
+  const bool shapes_ok = (g.hidden % kLgCh) == 0 && (g.inter % (kLgCh / 2)) == 0;
   const long avg = n_rows / (g.n_groups > 0 ? g.n_groups : 1);
-  if (!large_ok) return g.fmt == kFp8Block && avg >= kMdMinAvgRows ? kVariantMedium : kVariantSmall;
+  if (g.fmt == kFp8Block) {
+    // the large gate-up kernel's per-block form: 128-row tiles (its
+    // accumulator rescaling needs the registers the 256-row tile uses), a
+    // wave's K-block scales held in two lanes' registers
+    if (shapes_ok && g.hidden <= 128 * 128 && avg >= 64) return kVariantLarge128;
+    return avg >= kMdMinAvgRows ? kVariantMedium : kVariantSmall;
+  }
+  if (g.fmt != kFp8 || !shapes_ok) return kVariantSmall;
   if (avg < 64) return kVariantSmall;
   return avg >= 384 ? kVariantLarge256 : kVariantLarge128;
 }
 
-// The down GEMM's variant: as the gate-up GEMM's, except that per-block fp8
-// weights may take the large kernels (their block scale is one number per
-// wave and K block there, applied as the codes are widened), which the
-// gate-up GEMM cannot (its scale must apply to fp8 partial sums).
+// The down GEMM's variant: as the gate-up GEMM's, except for per-block fp8
+// weights, which take the 256-row large kernel too (their block scale is
+// one number per wave and K block there, applied as the codes are widened;
+// the gate-up kernel's per-block form runs 128-row tiles only).
 int choose_down_variant(const FfnGroups& g, long n_rows) {
   if (g.fmt != kFp8Block) return choose_variant(g, n_rows);
   // the large kernel holds a wave's K-block scales in two lanes' registers
   const bool large_ok = (g.hidden % kLgCh) == 0 && (g.inter % (kLgCh / 2)) == 0 && g.inter <= 128 * 128;
   const long avg = n_rows / (g.n_groups > 0 ? g.n_groups : 1);
-  if (!large_ok || avg < 64) return choose_variant(g, n_rows);
-  return avg >= 384 ? kVariantLarge256 : kVariantLarge128;
+  if (large_ok && avg >= 64) return avg >= 384 ? kVariantLarge256 : kVariantLarge128;
+  return avg >= kMdMinAvgRows ? kVariantMedium : kVariantSmall;
 }
 
 int shared_gate_up_variant(const FfnGroups& g, long n_rows, long shared_rows) {
@@ -1458,8 +1553,11 @@ hipError_t launch_gemm1(int variant, const FfnGroups& g, const RowOperand& x, co
     p.ntiles = g.inter / (kLgCh / 2);
     const long grid = max_row_tiles(grid_rows, g.n_groups, bm) * p.ntiles;
     const bool situ = g.act[0] == kActSitu || (g.n_groups > g.n_routed && g.act[1] == kActSitu);
+    // per-block fp8 takes the 128-row kernel only (choose_variant)
+    const bool blk = g.fmt == kFp8Block;
     auto kern = variant == kVariantLarge256 ? (situ ? gemm1_pp_kernel<256, 4, true> : gemm1_pp_kernel<256, 4, false>)
-                                            : (situ ? gemm1_pp_kernel<128, 6, true> : gemm1_pp_kernel<128, 6, false>);
+                : blk ? (situ ? gemm1_pp_kernel<128, 6, true, true> : gemm1_pp_kernel<128, 6, false, true>)
+                      : (situ ? gemm1_pp_kernel<128, 6, true> : gemm1_pp_kernel<128, 6, false>);
     hipExtLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, s, ev_start, ev_stop, 0, p);
   }
   return hipGetLastError();

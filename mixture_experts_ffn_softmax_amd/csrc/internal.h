@@ -147,16 +147,16 @@ struct RowOperand {
 
 // small: 32-row tiles, operands straight into registers (weight streaming);
 // medium: the same kernels with 64-row tiles, for per-block fp8 batches with
-// many rows per group (the large gate-up kernel takes per-channel fp8 only);
-// large: 128- or 256-row tiles staged through an LDS ring (per-channel fp8,
-// and per-block fp8 in the down GEMM).
+// many rows per group but too few for the large kernels;
+// large: 128- or 256-row tiles staged through an LDS ring (per-channel fp8;
+// per-block fp8 in 128-row gate-up tiles and in the down GEMM).
 enum GemmVariant { kVariantSmall = 0, kVariantLarge128 = 1, kVariantLarge256 = 2, kVariantMedium = 3 };
 // The variants whose kernels read their row fragments straight into registers.
 inline bool variant_in_registers(int v) { return v == kVariantSmall || v == kVariantMedium; }
 
 int choose_variant(const FfnGroups& g, long n_rows);
 // The down GEMM's variant: choose_variant's, except that per-block fp8
-// weights may take the large kernels (the gate-up GEMM's may not).
+// weights may take the 256-row large kernel (the gate-up GEMM's 128 only).
 int choose_down_variant(const FfnGroups& g, long n_rows);
 // With per-block fp8 routed weights the gate-up GEMM runs the register-fed
 // kernels; the shared group (per-channel fp8, shared_rows rows) then takes a

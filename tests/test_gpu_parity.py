@@ -179,13 +179,16 @@ FULL_CASES = {
     "wide_H32768": (5, 32768, 128, 4, 2, "fp8", False, False),
     # per-block fp8 weights (one scale per 128 x 128 tile), with a per-channel
     # fp8 shared expert beside them in one launch; from 64 rows per group on
-    # average the down GEMM takes the large kernels (128- and 256-row tiles,
-    # the block scale applied as the codes are widened), the gate-up GEMM
-    # the medium one, and from 64 tokens on the shared expert's gate-up GEMM
-    # a large-kernel launch of its own
+    # average both GEMMs take the large kernels (the gate-up GEMM 128-row
+    # tiles with the block exponent in the MFMA and the mantissa carried by
+    # the accumulators, the down GEMM 128- or 256-row tiles with the block
+    # scale applied as the codes are widened)
     "block_fp8_small": (45, 384, 256, 6, 3, "fp8_block", False, False),
     "block_fp8_shared": (300, 256, 384, 4, 2, "fp8_block", True, False),
     "block_fp8_large128_down": (300, 256, 256, 4, 2, "fp8_block", False, False),
+    # 48-63 rows per group: the medium gate-up kernel, with the shared expert
+    # in a large-kernel gate-up launch of its own
+    "block_fp8_medium_shared_split": (80, 256, 256, 4, 2, "fp8_block", True, False),
     "block_fp8_large256_down_ragged_shared": (1000, 256, 512, 4, 2, "fp8_block", True, False),
 }
 
@@ -213,11 +216,9 @@ def test_forward_full(lib, case, pack):
     if case.startswith("gathered_large128"):
         assert "large128" in variant
     if case == "block_fp8_shared" or case.startswith("block_fp8_large"):
-        assert ("down:large256" if "large256" in case else "down:large128") in variant
-    if case == "block_fp8_shared":
-        assert "shared:large128" in variant
-    if case == "block_fp8_large256_down_ragged_shared":
-        assert "shared:large128" in variant
+        assert variant == ("large128/fp8/down:large256" if "large256" in case else "large128/fp8")
+    if case == "block_fp8_medium_shared_split":
+        assert variant.startswith("medium64") and "shared:large128" in variant
     ref = oracle.forward(bf16_np(inp["x"]), inp["logits"].numpy(), c["k"],
                          oracle_weights(inp["routed"], c["fmt"]),
                          oracle_weights(inp["shared"], "fp8"),
@@ -426,11 +427,10 @@ def test_forward_block_fp8_decode_full_size(lib):
 def test_forward_block_fp8_prefill_full_size(lib):
     """The prefill share (2048 tokens, H 8192, I 2048, 8 experts top-2, a
     per-channel fp8 shared expert) with per-block fp8 routed weights, which
-    takes the 64-row medium variant in the routed gate-up GEMM, the 128-row
-    large one in the shared expert's gate-up launch and the 256-row large one
+    takes the 128-row large variant in the gate-up GEMM and the 256-row one
     in the down GEMM: all routing metadata, and the outputs of tokens that
     reach every expert, the first and last rows of the hottest expert's last
-    (ragged) 64-row and 256-row tiles, the least-loaded expert's last row and
+    (ragged) 128-row and 256-row tiles, the least-loaded expert's last row and
     the last routed row."""
     from gpu_helpers import cover_tokens
     inp = moe_synth.custom_inputs(2048, 8192, 2048, 8, 2, fmt="fp8_block", seed=13, device=DEV, shared=True)
@@ -439,13 +439,13 @@ def test_forward_block_fp8_prefill_full_size(lib):
     say("forward block fp8 prefill full size", c)
     out, dbg, variant = run_forward(inp)
     say("  variant", variant)
-    assert variant.startswith("medium64") and "down:large256" in variant and "shared:large128" in variant
+    assert variant.startswith("large128") and "down:large256" in variant
     ids, w = oracle.route(host(inp["logits"]), k)
     counts, offsets = oracle.expert_counts_offsets(ids, E)
     p2r, r2p, _, _ = oracle.permute_rows(ids, offsets, np.zeros((T, 1), np.uint8), np.zeros(T, np.float32))
     check_metadata(dbg, dict(topk_ids=ids, topk_w=w, counts=counts, offsets=offsets, pair_to_row=p2r,
                              row_to_pair=r2p), T, k, E, shared=True)
-    edge = edge_tokens(counts, offsets, r2p, k, 64)[0] + edge_tokens(counts, offsets, r2p, k, 256)[0]
+    edge = edge_tokens(counts, offsets, r2p, k, 128)[0] + edge_tokens(counts, offsets, r2p, k, 256)[0]
     tokens = np.array(sorted(set(cover_tokens(ids, E, must=edge)) | {0, T - 1}))
     ref_out = oracle.moe.forward_sampled(bits(inp["x"]), None, k, oracle_weights(inp["routed"], "fp8_block", lazy=True),
                                          tokens, shared=oracle_weights(inp["shared"], "fp8", lazy=True),
