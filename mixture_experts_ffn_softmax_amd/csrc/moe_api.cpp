@@ -391,8 +391,7 @@ static bool meta_path(int32_t T, int32_t k, int32_t E) {
 // tokens, beyond that (and always for the large kernels) from an
 // expert-ordered copy.
 constexpr int32_t kGatherSmallMaxT = 256;
-static bool fused_route_path(int32_t T, int32_t k, const moe_weights_t* routed, bool shared) {
-  (void)shared;
+static bool fused_route_path(int32_t T, int32_t k, const moe_weights_t* routed) {
   const int32_t E = routed->n_experts, H = routed->hidden;
   return meta_path(T, k, E) && E <= moe::kMetaRouteMaxE && T <= moe::kMetaRouteMaxT &&
          (long)T * k <= moe::kMetaRouteMaxPairs && H <= moe::kMetaQuantMaxH;
@@ -406,7 +405,7 @@ static bool fused_route_path(int32_t T, int32_t k, const moe_weights_t* routed, 
 // 2048-token per-block fp8 share), so past kGatherSmallMaxT tokens they too
 // read the copy.
 static bool fused_rows_copied(int32_t T, int32_t k, const moe_weights_t* routed, bool shared) {
-  if (!fused_route_path(T, k, routed, shared)) return false;
+  if (!fused_route_path(T, k, routed)) return false;
   if (T > kGatherSmallMaxT) return true;
   const moe::FfnGroups g = make_groups(routed, shared ? routed : nullptr, nullptr);
   return !moe::variant_in_registers(moe::choose_variant(g, (long)T * k + (shared ? T : 0)));
@@ -421,7 +420,7 @@ static ForwardLayout forward_layout(void* ws, int32_t T, int32_t k, const moe_we
   // (the gate-up GEMM gathers each routed row's token); the other paths
   // scatter them to expert-ordered rows, and keep token order for the
   // shared expert
-  const bool fused = fused_route_path(T, k, routed, shared);
+  const bool fused = fused_route_path(T, k, routed);
   const bool rows_needed = !fused || fused_rows_copied(T, k, routed, shared);
   const long rows = R + (shared ? T : 0);
   const long chunks = moe::permute_chunks(R);
@@ -523,7 +522,7 @@ moe_status_t moe_forward(const uint16_t* x, const float* logits, int32_t T, int3
   const moe::FfnGroups g = make_groups(routed, sh ? shared : nullptr, L.offsets);
   const long rows = R + (sh ? T : 0);
   const bool meta = meta_path(T, top_k, E);
-  const bool fused_route = fused_route_path(T, top_k, routed, sh);
+  const bool fused_route = fused_route_path(T, top_k, routed);
   if (ev && ev[MOE_STAGE_ROUTE]) hipEventRecord((hipEvent_t)ev[MOE_STAGE_ROUTE], s);
   // the layer's first dispatch (router, or the fused routing + quantisation
   // kernel) and its last (combine) stamp the optional layer events
