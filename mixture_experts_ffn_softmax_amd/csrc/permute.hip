@@ -397,7 +397,7 @@ __global__ __launch_bounds__(1024) void meta_kernel(int T, int E, int k, const i
 // number of earlier tokens that picked e: the pairs of e in the chunks
 // before t's (a scan over the chunks) plus a popcount of the ballot of e
 // over t's chunk below lane t % 64.
-constexpr int kMetaQuantThreads = 512;
+constexpr int kMetaQuantThreads = 1024;
 constexpr int kMetaWavesR = kMetaQuantThreads / 64;
 constexpr int kMetaRouteChunks = kMetaRouteMaxT / 64;
 static_assert(kMetaRouteChunks <= 64, "one lane per token chunk in the chunk scan");
@@ -559,9 +559,9 @@ __device__ __forceinline__ void meta_route_body(const float* __restrict__ logits
     else if (E <= 16) route_chunks<16, 1>(logits, sigmoid, T, E, k, ids, w, L);
     else route_chunks<kMetaRouteMaxE, 1>(logits, sigmoid, T, E, k, ids, w, L);
   } else {
-    if (E <= 8) route_chunks<8, 4>(logits, sigmoid, T, E, k, ids, w, L);
-    else if (E <= 16) route_chunks<16, 4>(logits, sigmoid, T, E, k, ids, w, L);
-    else route_chunks<kMetaRouteMaxE, 2>(logits, sigmoid, T, E, k, ids, w, L);
+    if (E <= 8) route_chunks<8, 2>(logits, sigmoid, T, E, k, ids, w, L);
+    else if (E <= 16) route_chunks<16, 2>(logits, sigmoid, T, E, k, ids, w, L);
+    else route_chunks<kMetaRouteMaxE, 1>(logits, sigmoid, T, E, k, ids, w, L);
   }
   __syncthreads();
 
@@ -670,8 +670,10 @@ __device__ __forceinline__ void quant_token_pair(const uint16_t* __restrict__ x,
 // (meta_route_body), workgroup 1 + i quantises tokens 2i and 2i + 1 into
 // token order (quant_token_pair).  The
 // metadata reads only the logits and the quantisation only x, so nothing
-// waits across workgroups.  kMetaQuantThreads (512) threads per workgroup, so
-// that a routing lane keeps its registers (about 200) without spilling.
+// waits across workgroups.  kMetaQuantThreads (1024) threads per workgroup:
+// sixteen routing waves, four per SIMD to hide each other's dependent
+// chains, with at most two chunks interleaved per lane so that a routing
+// lane fits the 128 registers that many waves leave it (64 used).
 template <int CPT>
 __global__ __launch_bounds__(kMetaQuantThreads) void meta_quant_kernel(const float* __restrict__ logits, bool sigmoid,
                                                           const uint16_t* __restrict__ x, int T, int H, int E,
@@ -781,12 +783,12 @@ hipError_t launch_meta_quant(const float* logits, bool sigmoid, const uint16_t* 
   hipExtLaunchKernelGGL(meta_quant_kernel<C>, dim3(grid), dim3(threads), 0, s, ev_start, nullptr, 0, logits, \
                         sigmoid, x, T, H, E, k, ids, w, counts, offsets, extra_rows, pair_to_row, row_to_pair,  \
                         tile_prefix, bm, xq_tok, xs_tok, tok_cs)
+  static_assert(2 * kMetaQuantMaxH / 8 <= 8 * kMetaQuantThreads, "a token pair takes at most 8 pieces per thread");
   switch (cpt) {
     case 1: MOE_MQ(1); break;
     case 2: MOE_MQ(2); break;
     case 4: MOE_MQ(4); break;
-    case 8: MOE_MQ(8); break;
-    default: MOE_MQ(16); break;   // H up to kMetaQuantMaxH
+    default: MOE_MQ(8); break;   // H up to kMetaQuantMaxH
   }
 #undef MOE_MQ
   return hipGetLastError();
