@@ -404,6 +404,51 @@ def test_forward_full_size(lib, name, score, act):
     assert ratio <= OUT_TOL
 
 
+@pytest.mark.parametrize("T,pack", [(300, True), (1000, False)])
+def test_forward_block_fp8_special_scales(lib, T, pack):
+    """Per-block fp8 on the large kernels (T tokens, H 512, I 384, 4 experts
+    top-2 + a per-channel shared expert; the gate-up GEMM's 128-row tiles,
+    the down GEMM's 128- or 256-row ones) with the block scales the kernels'
+    split of a scale into its power of two (the MFMA's e8m0 scale) and its
+    mantissa (carried by rescaling the accumulators, or applied as the down
+    GEMM's weights are widened) treats specially: exact powers of two
+    (mantissa 1), all-zero blocks (scale and codes 0), zero scales over
+    non-zero codes and subnormal scales (e8m0 0), between blocks of ordinary
+    scales, so that neighbouring K blocks' exponents jump.  Every output
+    element against the oracle.  (Spreading the scales themselves over
+    powers of two far apart makes each output hang on a few large terms, and
+    the bf16 rounding of h then exceeds the output bar on any path: 2^+-20
+    gave 0.027-0.032 x RMS on the register-fed kernels, which sum each block
+    exactly.)"""
+    H, I, E, k = 512, 384, 4, 2
+    inp = moe_synth.custom_inputs(T, H, I, E, k, fmt="fp8_block", seed=21, shared=True)
+    r = inp["routed"]
+    g = torch.Generator().manual_seed(21 + T)
+    for wn, sn in (("w1", "s1"), ("w3", "s3"), ("w2", "s2")):
+        sc, w = r[sn], r[wn]                     # float32 [E][N/128][K/128], uint8 [E][N][K]
+        pick = torch.rand(sc.shape, generator=g)
+        p2 = pick < 0.1
+        sc[p2] = torch.pow(2.0, torch.round(torch.log2(sc[p2])))
+        sc[(pick >= 0.1) & (pick < 0.15)] = 1e-40     # subnormal
+        sc[(pick >= 0.15) & (pick < 0.2)] = 0.0       # zero scale over non-zero codes
+        zero = pick >= 0.9                           # all-zero blocks
+        sc[zero] = 0.0
+        for e, nb, kb in zero.nonzero().tolist():
+            w[e, nb * 128:(nb + 1) * 128, kb * 128:(kb + 1) * 128] = 0
+    say("forward block fp8 special scales", T, "packed" if pack else "row-major")
+    out, dbg, variant = run_forward(to_device(inp), pack=pack)
+    say("  variant", variant)
+    assert variant.startswith("large128") and ("down:large256" in variant) == (T >= 1000)
+    ref = oracle.forward(bf16_np(inp["x"]), inp["logits"].numpy(), k, oracle_weights(inp["routed"], "fp8_block"),
+                         oracle_weights(inp["shared"], "fp8"), None, inp["eps"])
+    check_metadata(dbg, ref, T, k, E, True)
+    out_b = bits(out)
+    assert np.isfinite(oracle.codecs.bf16_decode(out_b)).all()
+    ratio = tolerance_ratio(out_b, ref["out_exact"])
+    say("  max|err|/rms", ratio)
+    assert ratio <= OUT_TOL
+
+
 def test_forward_block_fp8_decode_full_size(lib):
     """The decode share (64 tokens, H 8192, I 2048, 8 experts top-2) with
     per-block fp8 weights: all routing metadata and 16 sampled outputs."""
