@@ -89,7 +89,11 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int* __restrict__ chun
 }
 
 // Block of 256 threads = 4 waves per chunk of 1024 pairs; wave w ranks pairs
-// [w*256, w*256+256) of the chunk in four windows of 64, in order.
+// [w*256, w*256+256) of the chunk in four windows of 64, in order: a pair's
+// rank is its expert's count so far in the wave plus the number of earlier
+// lanes of the window with the same expert (found by matching the expert id
+// bit by bit with ballots, so the cost does not grow with the number of
+// distinct experts in the window).
 __global__ __launch_bounds__(256) void rank_kernel(const int* __restrict__ ids, int pairs, int E,
                                                    const int* __restrict__ chunk_base,
                                                    int* __restrict__ pair_to_row,
@@ -125,22 +129,30 @@ __global__ __launch_bounds__(256) void rank_kernel(const int* __restrict__ ids, 
   }
   __syncthreads();
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const uint64_t gt_mask = ~lt_mask & ~(1ull << lane);
+  // id bits to match: E - 1 fits in nbits bits
+  const int nbits = E > 1 ? 32 - __builtin_clz((unsigned)(E - 1)) : 0;
 #pragma unroll
   for (int win = 0; win < 4; ++win) {
     const long p = cbase + w * 256 + win * 64 + lane;
     const int e = my_e[win];
-    uint64_t pending = __ballot(e >= 0);
-    int row = -1;
-    while (pending) {
-      const int leader = __ffsll((unsigned long long)pending) - 1;
-      const int el = __builtin_amdgcn_readlane(e, leader);
-      const uint64_t same = __ballot(e == el) & pending;
-      if (e == el) row = cnt[w][el] + __popcll(same & lt_mask);
-      __builtin_amdgcn_wave_barrier();
-      if (lane == leader) cnt[w][el] += __popcll(same);
-      __builtin_amdgcn_wave_barrier();
-      pending &= ~same;
+    // the window's lanes with this lane's expert: one ballot per id bit
+    // (lanes without an expert are outside the first mask)
+    uint64_t same = __ballot(e >= 0);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t ones = __ballot(bit);
+      same &= bit ? ones : ~ones;
     }
+    int row = -1;
+    const int before = (int)__popcll(same & lt_mask);
+    if (e >= 0) row = cnt[w][e] + before;
+    // every lane's read of its expert's count precedes the update (one
+    // wave's LDS operations complete in order); the expert's last lane in
+    // the window advances it past the window's pairs
+    __builtin_amdgcn_wave_barrier();
+    if (e >= 0 && (same & gt_mask) == 0) cnt[w][e] += before + 1;
+    __builtin_amdgcn_wave_barrier();
     if (p < pairs) {
       pair_to_row[p] = row;
       if (row >= 0) row_to_pair[row] = (int)p;
