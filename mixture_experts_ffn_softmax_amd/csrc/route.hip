@@ -25,19 +25,23 @@ __device__ __forceinline__ bool route_better(float va, int ia, float vb, int ib)
   return va > vb || (va == vb && ia < ib);
 }
 
+// SLOTS: logits held per lane (E <= 64 * SLOTS), so that each round scans
+// only the slots the expert count needs.
+template <int SLOTS>
 __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ logits, int T, int E,
                                                     int k, bool sigmoid, int* __restrict__ ids,
                                                     float* __restrict__ w) {
+  static_assert(SLOTS <= kRouteSlots, "at most kMaxExperts experts");
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   const float* row = logits + (size_t)t * E;
   const int slots = (E + 63) >> 6;
 
-  float v[kRouteSlots];
+  float v[SLOTS];
   uint32_t avail = 0;
 #pragma unroll
-  for (int i = 0; i < kRouteSlots; ++i) {
+  for (int i = 0; i < SLOTS; ++i) {
     const int e = i * 64 + lane;
     const bool ok = (i < slots) && (e < E);
     const float l = ok ? row[e] : 0.0f;
@@ -51,7 +55,7 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
     float bv = -INFINITY;
     int bi = 0x7FFFFFFF;
 #pragma unroll
-    for (int i = 0; i < kRouteSlots; ++i) {
+    for (int i = 0; i < SLOTS; ++i) {
       const int e = i * 64 + lane;
       if (((avail >> i) & 1u) && route_better(v[i], e, bv, bi)) {
         bv = v[i];
@@ -85,8 +89,13 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
 hipError_t launch_route(const float* logits, int T, int E, int k, bool sigmoid, int* ids, float* w,
                         hipStream_t s, hipEvent_t ev_start) {
   if (T == 0) return hipSuccess;
-  hipExtLaunchKernelGGL(route_kernel, dim3((T + 3) / 4), dim3(256), 0, s, ev_start, nullptr, 0, logits, T, E, k,
-                        sigmoid, ids, w);
+#define MOE_RT(S) \
+  hipExtLaunchKernelGGL(route_kernel<S>, dim3((T + 3) / 4), dim3(256), 0, s, ev_start, nullptr, 0, logits, T, E, k, \
+                        sigmoid, ids, w)
+  if (E <= 64) MOE_RT(1);
+  else if (E <= 256) MOE_RT(4);
+  else MOE_RT(kRouteSlots);
+#undef MOE_RT
   return hipGetLastError();
 }
 
