@@ -49,40 +49,70 @@ __global__ __launch_bounds__(256) void hist_kernel(const int* __restrict__ ids, 
   for (int e = threadIdx.x; e < E; e += 256) chunk_hist[(long)blockIdx.x * E + e] = h[e];
 }
 
-// One block of 1024 threads; thread e owns expert e.
+// One block of 1024 threads.  Thread t works on expert t % E and on the
+// (t / E)-th of P = min(1024 / E, chunks) contiguous ranges of chunks, so that
+// with few experts most threads still have loads in flight; each pass keeps
+// eight chunk loads of a thread in flight.  The bases come out as if one
+// thread per expert walked its chunks in order.
 __global__ __launch_bounds__(1024) void scan_kernel(const int* __restrict__ chunk_hist, int chunks,
                                                     int E, int* __restrict__ chunk_base,
                                                     int* __restrict__ counts,
                                                     int* __restrict__ offsets, int extra_rows) {
   __shared__ int off[kMaxExperts];
+  __shared__ int part[1024];
   __shared__ int tmp[16];
-  const int e = threadIdx.x;
+  const int t = threadIdx.x;
+  const int Eg = E > 0 ? E : 1;
+  const int P = max(1, min(1024 / Eg, chunks));
+  const int cpp = (chunks + P - 1) / P;
+  const int e = t % Eg, p = t / Eg;
+  const bool act = E > 0 && p < P;
+  const int c0 = act ? min(p * cpp, chunks) : 0;
+  const int c1 = act ? min(c0 + cpp, chunks) : 0;
+  int sum = 0;
+  int c = c0;
+  for (; c + 8 <= c1; c += 8) {
+    int a[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a[i] = chunk_hist[(long)(c + i) * E + e];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sum += a[i];
+  }
+  for (; c < c1; ++c) sum += chunk_hist[(long)c * E + e];
+  if (act) part[t] = sum;                     // part[p * E + e]
+  __syncthreads();
   int total = 0;
-  if (e < E) {
-    int c = 0;
-    for (; c + 4 <= chunks; c += 4) {
-      const int a0 = chunk_hist[(long)(c + 0) * E + e];
-      const int a1 = chunk_hist[(long)(c + 1) * E + e];
-      const int a2 = chunk_hist[(long)(c + 2) * E + e];
-      const int a3 = chunk_hist[(long)(c + 3) * E + e];
-      total += a0 + a1 + a2 + a3;
-    }
-    for (; c < chunks; ++c) total += chunk_hist[(long)c * E + e];
-    off[e] = total;
+  if (t < E) {
+    for (int q = 0; q < P; ++q) total += part[q * E + t];
+    off[t] = total;
   }
   __syncthreads();
   const int all = block_exclusive_scan_1024(off, tmp, E);
-  if (e < E) {
-    counts[e] = total;
-    offsets[e] = off[e];
+  if (t < E) {
+    counts[t] = total;
+    offsets[t] = off[t];
+  }
+  if (act) {
     int run = off[e];
-    for (int c = 0; c < chunks; ++c) {
+    for (int q = 0; q < p; ++q) run += part[q * E + e];
+    c = c0;
+    for (; c + 8 <= c1; c += 8) {
+      int a[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) a[i] = chunk_hist[(long)(c + i) * E + e];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        chunk_base[(long)(c + i) * E + e] = run;
+        run += a[i];
+      }
+    }
+    for (; c < c1; ++c) {
       const int n = chunk_hist[(long)c * E + e];
       chunk_base[(long)c * E + e] = run;
       run += n;
     }
   }
-  if (e == 0) {
+  if (t == 0) {
     offsets[E] = all;
     if (extra_rows > 0) offsets[E + 1] = all + extra_rows;
   }

@@ -87,6 +87,7 @@ PERMUTE_CASES = [  # T, H, E, k, hot expert
     (5000, 128, 64, 4, None),     # 20000 pairs: the grid-wide counting / ranking kernels
     (300, 128, 64, 4, None),      # the most experts the single-workgroup kernel takes
     (300, 128, 65, 4, None),      # one more: the grid-wide kernels
+    (2300, 128, 256, 8, None),    # 18 chunks over 4 ranges of 5, 5, 5 and 3 chunks per expert
 ]
 
 
