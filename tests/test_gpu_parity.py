@@ -88,6 +88,7 @@ PERMUTE_CASES = [  # T, H, E, k, hot expert
     (300, 128, 64, 4, None),      # the most experts the single-workgroup kernel takes
     (300, 128, 65, 4, None),      # one more: the grid-wide kernels
     (2300, 128, 256, 8, None),    # 18 chunks over 4 ranges of 5, 5, 5 and 3 chunks per expert
+    (20000, 128, 1, 1, None),     # one expert, 20 chunks: one chunk per scanning thread
 ]
 
 
