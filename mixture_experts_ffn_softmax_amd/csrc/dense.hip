@@ -56,14 +56,19 @@ __global__ __launch_bounds__(256, 2) void dense_kernel(DenseParams p) {
   const int l32 = lane & 31, hi = lane >> 5;
 
   // the row tiles of one channel tile are consecutive, so that they read its
-  // weights while they are in the XCD's L2
+  // weights while they are in the XCD's L2; with a K split, workgroup z of
+  // a tile contracts K range [z K / ns, (z + 1) K / ns) into partial z
+  const int ns = p.ksplit > 1 ? p.ksplit : 1;
   const long tiles_m = (p.M + BM - 1) / BM;
-  const long t = xcd_remap(blockIdx.x, tiles_m * p.tiles_n);
+  const long tiles = tiles_m * p.tiles_n;
+  const long tz = xcd_remap(blockIdx.x, tiles * ns);
+  const int kz = (int)(tz / tiles);
+  const long t = tz - (long)kz * tiles;
   const int m0 = (int)(t % tiles_m) * BM;
   const int tn = (int)(t / tiles_m);
   constexpr bool gate_up = MODE == kDnGateUp;
   const int n0 = tn * (gate_up ? 64 : 128);
-  const int K = p.K, nk = K / kDnK;
+  const int K = p.K, kw = K / ns, kb = kz * kw, nk = kw / kDnK;
 
   // staging: A (and bf16 B) chunk q = tid + 256 i is row q >> 3, chunk q & 7
   auto b_row = [&](int r) -> long { return gate_up ? (long)(n0 + (r & 63)) : (long)(n0 + r); };
@@ -76,13 +81,13 @@ __global__ __launch_bounds__(256, 2) void dense_kernel(DenseParams p) {
   for (int i = 0; i < AQ; ++i) {
     const int q = tid + 256 * i, r = q >> 3, c = q & 7;
     const int gr = min(m0 + r, p.M - 1);
-    asrc[i] = p.a + (long)gr * p.lda + c * 8;
+    asrc[i] = p.a + (long)gr * p.lda + kb + c * 8;
   }
   if constexpr (!FP4)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int q = tid + 256 * i, r = q >> 3, c = q & 7;
-      bsrc[i] = reinterpret_cast<const uint16_t*>(b_mat(r)) + b_row(r) * K + c * 8;
+      bsrc[i] = reinterpret_cast<const uint16_t*>(b_mat(r)) + b_row(r) * K + kb + c * 8;
     }
   // fragment rows: A rows wm * BM / 2 + 32f + l32; B rows wn*64 + 32j + l32,
   // or in the gate-up mode the gate rows wn*32 + l32 (j = 0) and the up rows
@@ -99,8 +104,8 @@ __global__ __launch_bounds__(256, 2) void dense_kernel(DenseParams p) {
   if constexpr (FP4)
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      fcode[j] = b_mat(br[j]) + b_row(br[j]) * (K / 2) + hi * 16;
-      fscale[j] = (gate_up && br[j] >= 64 ? p.bs3 : p.bs) + b_row(br[j]) * (K / 32) + hi;
+      fcode[j] = b_mat(br[j]) + b_row(br[j]) * (K / 2) + kb / 2 + hi * 16;
+      fscale[j] = (gate_up && br[j] >= 64 ? p.bs3 : p.bs) + b_row(br[j]) * (K / 32) + kb / 32 + hi;
     }
 
   // one step's operands in registers (native vectors: HIP's uint4 struct
@@ -239,7 +244,7 @@ __global__ __launch_bounds__(256, 2) void dense_kernel(DenseParams p) {
           const long n = n0 + wn * 64 + 32 * j + l32;
           const long o = (long)m * p.ldc + n;
           const float y = acc[f][j][v];
-          if constexpr (MODE == kDnStoreF32) reinterpret_cast<float*>(p.c)[o] = y;
+          if constexpr (MODE == kDnStoreF32) reinterpret_cast<float*>(p.c)[(long)kz * p.M * p.ldc + o] = y;
           else if constexpr (MODE == kDnAddBf16) reinterpret_cast<uint16_t*>(p.c)[o] = (uint16_t)bf16_rne(y + add[f][j][v]);
           else reinterpret_cast<uint16_t*>(p.c)[o] = (uint16_t)bf16_rne(y);
         }
@@ -278,6 +283,56 @@ hipError_t launch_dense(const DenseParams& p_in, hipStream_t s, hipEvent_t ev_st
   }
 #undef MOE_DN
 #undef MOE_DN_LAUNCH
+  return hipGetLastError();
+}
+
+// out[m][n] = bf16(part[0][m][n] + part[1][m][n] + ...), four channels per
+// thread (N is a multiple of 128).
+__global__ __launch_bounds__(256) void dense_split_sum_kernel(const float* __restrict__ part, int ns, int M, int N,
+                                                              uint16_t* __restrict__ out, long ldc) {
+  const long mn = (long)M * N;
+  const long i = ((long)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= mn) return;
+  float4 v = *reinterpret_cast<const float4*>(part + i);
+  for (int z = 1; z < ns; ++z) {
+    const float4 w = *reinterpret_cast<const float4*>(part + (long)z * mn + i);
+    v.x += w.x;
+    v.y += w.y;
+    v.z += w.z;
+    v.w += w.w;
+  }
+  const long m = i / N, n = i - m * N;
+  *reinterpret_cast<uint2*>(out + m * ldc + n) =
+      make_uint2(bf16_rne(v.x) | (bf16_rne(v.y) << 16), bf16_rne(v.z) | (bf16_rne(v.w) << 16));
+}
+
+hipError_t launch_dense_splitk(const DenseParams& p_in, int ksplit, float* part, hipStream_t s,
+                               hipEvent_t ev_start, hipEvent_t ev_stop) {
+  if (p_in.M == 0) return hipSuccess;
+  if (ksplit < 1 || p_in.mode != kDnStoreBf16 || p_in.K % (kDnK * ksplit) != 0 || p_in.N % 128 != 0)
+    return hipErrorInvalidValue;
+  DenseParams p = p_in;
+  p.mode = kDnStoreF32;
+  p.c = part;
+  p.ldc = p.N;
+  p.ksplit = ksplit;
+  p.tiles_n = p.N / 128;
+  // 128-row tiles once the split gives them half the CUs (each weight tile
+  // is then read by half as many workgroups as with 64-row tiles)
+  const long tiles128 = (long)((p.M + 127) / 128) * p.tiles_n;
+  const int bm = tiles128 * ksplit >= kNumCUs / 2 ? 128 : 64;
+  const long grid = (long)((p.M + bm - 1) / bm) * p.tiles_n * ksplit;
+  const bool fp4 = p.bfmt == kMxfp4;
+  if (bm == 128) {
+    if (fp4) hipExtLaunchKernelGGL(dense_kernel<true, kDnStoreF32, 128, 4>, dim3((unsigned)grid), dim3(256), 0, s, ev_start, nullptr, 0, p);
+    else hipExtLaunchKernelGGL(dense_kernel<false, kDnStoreF32, 128, 3>, dim3((unsigned)grid), dim3(256), 0, s, ev_start, nullptr, 0, p);
+  } else {
+    if (fp4) hipExtLaunchKernelGGL(dense_kernel<true, kDnStoreF32, 64, 8>, dim3((unsigned)grid), dim3(256), 0, s, ev_start, nullptr, 0, p);
+    else hipExtLaunchKernelGGL(dense_kernel<false, kDnStoreF32, 64, 5>, dim3((unsigned)grid), dim3(256), 0, s, ev_start, nullptr, 0, p);
+  }
+  const long groups = (long)p.M * p.N / 4;
+  hipExtLaunchKernelGGL(dense_split_sum_kernel, dim3((unsigned)((groups + 255) / 256)), dim3(256), 0, s, nullptr, ev_stop,
+                        0, part, ksplit, p.M, p.N, reinterpret_cast<uint16_t*>(p_in.c), p_in.ldc);
   return hipGetLastError();
 }
 

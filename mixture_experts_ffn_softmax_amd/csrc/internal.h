@@ -228,8 +228,15 @@ struct DenseParams {
   int act;              // kDnGateUp: Activation and beta
   float beta;
   int tiles_n;          // set by launch_dense
+  int ksplit;           // set by launch_dense_splitk: workgroups per tile, each a K range
 };
 hipError_t launch_dense(const DenseParams& p, hipStream_t s, hipEvent_t ev_start = nullptr,
                         hipEvent_t ev_stop = nullptr);
+// kDnStoreBf16 with K split over `ksplit` workgroups per tile: each writes an
+// fp32 partial into part[z][M][N] (ksplit * M * N floats), then one pass sums
+// the partials in order z = 0, 1, ... and rounds once into p.c.  K must be a
+// multiple of 64 * ksplit.
+hipError_t launch_dense_splitk(const DenseParams& p, int ksplit, float* part, hipStream_t s,
+                               hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 
 }  // namespace moe

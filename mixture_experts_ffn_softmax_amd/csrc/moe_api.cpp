@@ -809,12 +809,18 @@ moe_status_t moe_latent_forward(const uint16_t* x, const float* logits, int32_t 
   uint16_t* lat = (dbg && dbg->latent) ? dbg->latent : L.lat;
   uint16_t* core = (dbg && dbg->core_out) ? dbg->core_out : L.core;
 
-  // down-projection -> latent (bf16)
+  // down-projection -> latent (bf16).  When even 64-row tiles leave CUs
+  // idle (512 tokens: 224 tiles), two workgroups per tile each contract half
+  // of K into fp32 partials, which the routed core's workspace holds until
+  // they are summed (the core's kernels come after on the same stream).
   moe::DenseParams dp = dense_params(x, T, &lw->down);
   dp.mode = moe::kDnStoreBf16;
   dp.c = lat;
   dp.ldc = Lt;
-  hipError_t e = moe::launch_dense(dp, s, lev0, nullptr);
+  const long tiles64 = (long)((T + 63) / 64) * (Lt / 128);
+  const bool split = tiles64 < moe::kNumCUs && Hm % (2 * 64) == 0 && L.core_bytes >= (size_t)2 * T * Lt * sizeof(float);
+  hipError_t e = split ? moe::launch_dense_splitk(dp, 2, static_cast<float*>(L.core_ws), s, lev0, nullptr)
+                       : moe::launch_dense(dp, s, lev0, nullptr);
   if (e != hipSuccess) return device_status(e, "down-projection");
 
   // the routed core over the latent, with its RMSNorm, no shared expert
