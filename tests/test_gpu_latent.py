@@ -182,7 +182,9 @@ def test_latent_forward(lib, case):
 def test_latent_forward_full_size(lib):
     """The whole block at full size (512 tokens, hidden 7168, latent 3584, 896
     MXFP4 experts top-16, bf16 shared experts 7168 -> 6144 -> 7168): all
-    routing metadata, and the outputs of 3 sampled tokens."""
+    routing metadata, the latent of every token (the down-projection, whose
+    K is split over two workgroups per tile at this size), and the outputs
+    of 3 sampled tokens."""
     blk = moe_synth.latent_block_inputs(**moe_synth.LATENT_BLOCK, device=DEV)
     c = blk["cfg"]
     T, E, k = c["T"], c["E"], c["k"]
@@ -195,8 +197,10 @@ def test_latent_forward_full_size(lib):
     assert (host(dbg["expert_counts"]) == counts).all()
     assert (host(dbg["pair_to_row"]) == p2r).all()
     assert (host(dbg["row_to_pair"]) == r2p).all()
-    tokens = np.sort(np.random.default_rng(c["cfg"]).choice(T, 3, replace=False))
     down = LinearWeights("mxfp4", host(blk["down"]["w"]), host(blk["down"]["s"]))
+    X = codecs.bf16_decode(bits(blk["x"]))
+    check_bf16_close(bits(dbg["latent"]), latent.linear(X, down), acc_bound(X, down))
+    tokens = np.sort(np.random.default_rng(c["cfg"]).choice(T, 3, replace=False))
     up = LinearWeights("mxfp4", host(blk["up"]["w"]), host(blk["up"]["s"]))
     from gpu_helpers import DeviceStack
     routed = ExpertWeights("mxfp4", *(DeviceStack(blk["routed"][n]) for n in ("w1", "w3", "w2", "s1", "s3", "s2")))
